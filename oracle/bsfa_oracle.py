@@ -1,0 +1,267 @@
+"""CPU oracle for exact-score-gated block-sparse causal prefill attention (BSFA).
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or execute this
+module: only the test suite, the entry point's smoke check and the benchmark's CPU-baseline
+leg use it. It shares no code, constants or helpers with the HIP library.
+
+It is deliberately plain and slow: one (batch, head, query block) at a time, one key block at a
+time, in the order the method describes, with numpy doing each matrix product. Floating point
+is float32 by default (the precision the oracle is asked to compute in); pass
+``dtype=np.float64`` for a float64 run.
+
+Sources (page title, then the part of the page followed):
+  * "Block Sparse Flash Attention" (paper notes), Method:
+      - Overall Architecture: inputs Q, K, V and the threshold slice of the chosen budget; the
+        output is renormalised over the retained blocks; the causal diagonal region always goes
+        to aggregation.
+      - Key Designs 1 (Offline Threshold Calibration): k-th highest visible off-diagonal block
+        maximum per sample, averaged over samples; -inf where fewer than k candidates exist;
+        positions past the calibrated length reuse the last calibrated position.
+      - Key Designs 2 (Exact-Score Gating), keep-rule equation: s_max over the whole query-key
+        score tile of scaled pre-softmax scores; keep iff s_max >= T.
+      - Key Designs 3 (Selective Streaming Aggregation): online softmax on kept blocks; a
+        rejected block touches neither V, nor the exponentials, nor m, l, O.
+      - A Worked Example.
+  * "Skipping attention blocks was the easy part" (BLASST blog), sections "FlashAttention"
+    (running max m, running sum l, accumulator O, rescale by exp(m_old - m_new)) and
+    "Vote, then skip" (skip iff block max minus running max < ln(lambda); any row that wants
+    the block vetoes the skip).
+
+Readings taken where the pages are silent or ambiguous (each is listed in the design notes):
+  * keep uses ">=" (the paper notes follow the main text; the simplified algorithm uses ">").
+  * Off-diagonal key blocks of query block i are the blocks wholly before the block's first
+    row, j < n_off(i) = floor(i*Bq/Bk); the diagonal region is n_off(i) <= j < n_end(i).
+  * Key blocks are visited in ascending order, so the diagonal region comes last.
+  * Thresholds are per query head; GQA maps query head h to KV head h // G.
+  * The relative gate compares max over the tile's rows of (row max of the block - running row
+    max before the block) with ln(lambda); lambda = 0 means never skip.
+  * Rows past the end of a ragged last block do not exist (blocks are clipped to N).
+
+Pins (tests that tie each function to something other than itself) are in
+tests/test_oracle_pins.py; every public function here is pinned.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+GATE_DENSE = "dense"
+GATE_ABSOLUTE = "absolute"
+GATE_RELATIVE = "relative"
+_MODES = (GATE_DENSE, GATE_ABSOLUTE, GATE_RELATIVE)
+
+
+def num_blocks(n: int, block: int) -> int:
+    """Number of blocks of size ``block`` covering ``n`` positions (the last one may be short)."""
+    return (n + block - 1) // block
+
+
+def key_block_range(i: int, n: int, block_q: int, block_k: int) -> tuple[int, int]:
+    """(n_off, n_end) for query block i of a length-n causal prefill.
+
+    Key blocks j < n_off lie wholly before the query block's first row, so every pair in them is
+    visible: these are the off-diagonal candidates the gate acts on. Blocks n_off <= j < n_end
+    hold the causal diagonal region (they need the causal mask and always run); blocks at or
+    past n_end are invisible to every row of the block. ("Block Sparse Flash Attention",
+    Method > Key Designs 2, on the causal diagonal region and on unequal tile shapes.)
+    """
+    n_off = (i * block_q) // block_k
+    last_row = min((i + 1) * block_q, n) - 1
+    n_end = last_row // block_k + 1
+    return n_off, n_end
+
+
+def effective_threshold(table: np.ndarray, budget_slice: int, h: int, i: int) -> float:
+    """T_eff(h, i) = T[slice][h][min(i, T_len - 1)].
+
+    Query blocks past the calibrated length reuse the final calibrated position's threshold
+    ("Block Sparse Flash Attention", Method > Key Designs 1, last paragraph).
+    """
+    t_len = table.shape[2]
+    return float(table[budget_slice, h, min(i, t_len - 1)])
+
+
+@dataclass
+class OracleResult:
+    out: np.ndarray          # [B, N, Hq, d]; NaN rows for query blocks not computed
+    kept_counts: np.ndarray  # [B, Hq, nqb] int64, kept OFF-diagonal blocks; -1 if not computed
+    stat: np.ndarray         # [B, Hq, nqb, nkb] gate statistic per visible block; NaN elsewhere
+    keep: np.ndarray         # [B, Hq, nqb, nkb] bool; True for kept blocks and the diagonal region
+    margin: np.ndarray       # [B, Hq, nqb, nkb] stat - threshold (off-diagonal only); NaN elsewhere
+
+
+def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
+                   scale: float | None = None, table: np.ndarray | None = None,
+                   budget_slice: int = 0, log_lambda: float = -math.inf,
+                   forced_keep: np.ndarray | None = None, band: float = 1e-2,
+                   query_blocks=None, dtype=np.float32) -> OracleResult:
+    """Gated causal prefill attention, one (b, h, i) work unit at a time.
+
+    Q: [B, N, Hq, d]; K, V: [B, N, Hkv, d] with Hq % Hkv == 0.
+    mode: "dense" (keep everything), "absolute" (keep iff s_max >= T_eff(h, i) from ``table``
+    [n_budgets][Hq][T_len] at ``budget_slice``) or "relative" (keep iff
+    max_r(rowmax_j[r] - m[r]) >= log_lambda).
+    forced_keep: optional [B, Hq, nqb, nkb] decisions adopted where |margin| <= band (the
+    near-tie rule used when comparing against a device that rounds differently).
+    query_blocks: optional iterable of query-block indices to compute (default: all).
+    """
+    if mode not in _MODES:
+        raise ValueError(f"unknown gate mode {mode!r}")
+    Q = np.asarray(Q, dtype=dtype)
+    K = np.asarray(K, dtype=dtype)
+    V = np.asarray(V, dtype=dtype)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    if K.shape != (B, N, Hkv, d) or V.shape != K.shape or Hq % Hkv != 0:
+        raise ValueError("shape mismatch")
+    if mode == GATE_ABSOLUTE and table is None:
+        raise ValueError("absolute gate needs a threshold table")
+    G = Hq // Hkv
+    sc = dtype(1.0 / math.sqrt(d) if scale is None else scale)
+    nqb, nkb = num_blocks(N, block_q), num_blocks(N, block_k)
+    blocks = range(nqb) if query_blocks is None else sorted(set(int(x) for x in query_blocks))
+
+    out = np.full((B, N, Hq, d), np.nan, dtype=dtype)
+    kept_counts = np.full((B, Hq, nqb), -1, dtype=np.int64)
+    stat = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
+    keep_mask = np.zeros((B, Hq, nqb, nkb), dtype=bool)
+    margin = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
+
+    with np.errstate(invalid="ignore", over="ignore"):
+        for b in range(B):
+            for h in range(Hq):
+                g = h // G                                   # GQA: query head -> its KV head
+                for i in blocks:
+                    r0, r1 = i * block_q, min((i + 1) * block_q, N)
+                    q = Q[b, r0:r1, h, :]
+                    R = r1 - r0
+                    # online-softmax state (BLASST blog, "FlashAttention"): m, l, O on chip
+                    m = np.full(R, -np.inf, dtype=dtype)
+                    l = np.zeros(R, dtype=dtype)
+                    o = np.zeros((R, d), dtype=dtype)
+                    n_off, n_end = key_block_range(i, N, block_q, block_k)
+                    te = (effective_threshold(table, budget_slice, h, i)
+                          if mode == GATE_ABSOLUTE else None)
+                    kept = 0
+                    for j in range(n_end):                    # ascending; diagonal region last
+                        c0, c1 = j * block_k, min((j + 1) * block_k, N)
+                        # exact scaled pre-softmax scores of the whole tile (keep-rule equation)
+                        s = (q @ K[b, c0:c1, g, :].T) * sc
+                        if j >= n_off:
+                            # causal diagonal region: mask future keys, always aggregated
+                            rows = np.arange(r0, r1)[:, None]
+                            cols = np.arange(c0, c1)[None, :]
+                            s = np.where(cols > rows, dtype(-np.inf), s)
+                            stat[b, h, i, j] = float(s.max())
+                            keep = True
+                        else:
+                            rmax = s.max(axis=1)
+                            if mode == GATE_RELATIVE:
+                                # each row tests itself against its running max; one row that
+                                # wants the block vetoes the skip
+                                st = float((rmax - m).max())
+                                thr = float(log_lambda)
+                            else:
+                                st = float(rmax.max())            # s_max over the whole tile
+                                thr = te if mode == GATE_ABSOLUTE else -math.inf
+                            stat[b, h, i, j] = st
+                            mg = st - thr
+                            margin[b, h, i, j] = mg
+                            keep = st >= thr
+                            if forced_keep is not None and abs(mg) <= band:
+                                keep = bool(forced_keep[b, h, i, j])
+                            kept += int(keep)
+                        keep_mask[b, h, i, j] = keep
+                        if not keep:
+                            continue        # skipped: no V, no exp, m, l and O untouched
+                        rmax = s.max(axis=1)
+                        m_new = np.maximum(m, rmax)
+                        alpha = np.exp(m - m_new)              # exp(-inf) = 0 on the first block
+                        p = np.exp(s - m_new[:, None])
+                        l = alpha * l + p.sum(axis=1)
+                        o = alpha[:, None] * o + p @ V[b, c0:c1, g, :]
+                        m = m_new
+                    out[b, r0:r1, h, :] = o / l[:, None]     # renormalise over kept + diagonal
+                    kept_counts[b, h, i] = kept
+    return OracleResult(out, kept_counts, stat, keep_mask, margin)
+
+
+def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float | None = None,
+                              dtype=np.float32) -> np.ndarray:
+    """s_max[b, h, i, j] for every off-diagonal block j < n_off(i); NaN elsewhere.
+
+    The maximum of the scaled pre-softmax scores over the whole Bq x Bk tile
+    ("Block Sparse Flash Attention", Method > Key Designs 2, keep-rule equation). The scores of
+    one (b, h, i) against all its off-diagonal keys come from one matrix product, then each
+    Bk-wide column group is reduced.
+    """
+    Q = np.asarray(Q, dtype=dtype)
+    K = np.asarray(K, dtype=dtype)
+    B, N, Hq, d = Q.shape
+    Hkv = K.shape[2]
+    G = Hq // Hkv
+    sc = dtype(1.0 / math.sqrt(d) if scale is None else scale)
+    nqb, nkb = num_blocks(N, block_q), num_blocks(N, block_k)
+    sm = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            g = h // G
+            for i in range(nqb):
+                n_off, _ = key_block_range(i, N, block_q, block_k)
+                if n_off == 0:
+                    continue
+                r0, r1 = i * block_q, min((i + 1) * block_q, N)
+                s = (Q[b, r0:r1, h, :] @ K[b, :n_off * block_k, g, :].T) * sc
+                sm[b, h, i, :n_off] = s.reshape(r1 - r0, n_off, block_k).max(axis=(0, 2))
+    return sm
+
+
+def kth_highest(maxima: np.ndarray, n_off: int, k: int) -> float:
+    """k-th highest of the first n_off block maxima (1-indexed), or -inf if n_off < k.
+
+    ("Block Sparse Flash Attention", Method > Key Designs 1: sort the maxima and take the k-th
+    highest; a -inf threshold where the position has too few off-diagonal candidates.)
+    """
+    if n_off < k:
+        return -math.inf
+    return float(np.sort(maxima[:n_off])[::-1][k - 1])
+
+
+def calibrate(samples, *, block_q: int, block_k: int, budgets, scale: float | None = None,
+              dtype=np.float32) -> np.ndarray:
+    """Offline threshold calibration: T[n_budgets][Hq][T_len] (float32).
+
+    samples: iterable of (Q, K) pairs of equal shape [B, N, Hq, d] / [B, N, Hkv, d]; every
+    batch entry counts as one calibration sample. For each sample, head and query block the
+    k-th highest off-diagonal block maximum is taken; thresholds are the arithmetic mean over
+    samples ("Block Sparse Flash Attention", Method > Key Designs 1). T_len = number of query
+    blocks of the calibration length.
+    """
+    budgets = [int(k) for k in budgets]
+    acc = None
+    count = 0
+    shape0 = None
+    for Q, K in samples:
+        Q = np.asarray(Q)
+        if shape0 is None:
+            shape0 = Q.shape
+        elif Q.shape[1:] != shape0[1:]:
+            raise ValueError("calibration samples must share one shape")
+        sm = off_diagonal_block_maxima(Q, K, block_q=block_q, block_k=block_k, scale=scale,
+                                       dtype=dtype)
+        B, Hq, nqb, _ = sm.shape
+        N = Q.shape[1]
+        if acc is None:
+            acc = np.zeros((len(budgets), Hq, nqb), dtype=np.float64)
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(nqb):
+                    n_off, _ = key_block_range(i, N, block_q, block_k)
+                    for kk, k in enumerate(budgets):
+                        acc[kk, h, i] += kth_highest(sm[b, h, i], n_off, k)
+            count += 1
+    if count == 0:
+        raise ValueError("no calibration samples")
+    return (acc / count).astype(np.float32)

@@ -1,0 +1,403 @@
+"""Pins for the CPU oracle: each check ties it to something other than itself.
+
+Sources: "Block Sparse Flash Attention" (paper notes), Method (Key Designs 1-3, A Worked
+Example); "Skipping attention blocks was the easy part" (BLASST blog), "Vote, then skip".
+References are torch's scaled_dot_product_attention (float64, CPU, explicit masks), brute-force
+float64 block maxima from one full score matrix, values printed on the pages, and closed forms.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import (GATE_ABSOLUTE, GATE_DENSE, GATE_RELATIVE, calibrate, key_block_range,
+                    kth_highest, oracle_prefill)
+from pins_util import (block_mask_to_token_mask, brute_block_max, causal_mask,
+                       diagonal_region_mask, first_offdiag_blocks, full_scores,
+                       quantized_normal, sdpa_masked)
+
+
+def _rand(seed, B, N, Hq, Hkv, d):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((B, N, Hq, d)).astype(np.float32),
+            rng.standard_normal((B, N, Hkv, d)).astype(np.float32),
+            rng.standard_normal((B, N, Hkv, d)).astype(np.float32))
+
+
+def _const_table(value, Hq, t_len, n_budgets=1):
+    return np.full((n_budgets, Hq, t_len), value, dtype=np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# Block structure
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("N,Bq,Bk", [(384, 64, 64), (1000, 128, 64), (200, 64, 32), (300, 32, 64),
+                                     (129, 128, 64)])
+def test_block_ranges_match_brute_force(N, Bq, Bk):
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    nqb = -(-N // Bq)
+    for i in range(nqb):
+        n_off, n_end = key_block_range(i, N, Bq, Bk)
+        assert n_off == noff[i]
+        last_row = min((i + 1) * Bq, N) - 1
+        # n_end: one past the last key block holding a key <= the block's last row
+        assert n_end == max(j for j in range(-(-N // Bk)) if j * Bk <= last_row) + 1
+
+
+def test_block_ranges_named_tiles():
+    # Bq = Bk: diagonal region is block i alone; Bq = 2 Bk: blocks 2i and 2i + 1
+    assert [key_block_range(i, 1024, 64, 64) for i in (0, 5)] == [(0, 1), (5, 6)]
+    assert [key_block_range(i, 1024, 128, 64) for i in (0, 3)] == [(0, 2), (6, 8)]
+
+
+# ---------------------------------------------------------------------------------------------
+# The worked example printed on the page
+# ---------------------------------------------------------------------------------------------
+def _worked_example_problem(maxima):
+    """Embed the page's example: query block 5 sees 5 off-diagonal key blocks (Bq = Bk = 64,
+    d = 64, scale 1/8). Query row 320 is 8 e0, the other rows of block 5 are zero; key block j
+    holds one key with e0-component maxima[j] and zeros elsewhere, so the tile maxima are
+    exactly the printed values."""
+    N, d = 384, 64
+    rng = np.random.default_rng(11)
+    Q = np.zeros((1, N, 1, d), np.float32)
+    K = np.zeros((1, N, 1, d), np.float32)
+    V = rng.standard_normal((1, N, 1, d)).astype(np.float32)
+    Q[0, 320, 0, 0] = 8.0
+    for j, v in enumerate(maxima):
+        K[0, 64 * j + 7, 0, 0] = v
+    K[0, 320:, 0, :] = rng.standard_normal((64, d)).astype(np.float32) * 0.25
+    return Q, K, V
+
+
+def test_worked_example_from_page(golden_dir):
+    ex = json.load(open(os.path.join(golden_dir, "worked_example.json")))
+    maxima = ex["block_maxima"]
+    Q, K, V = _worked_example_problem(maxima)
+    table = _const_table(ex["threshold"], 1, 6)
+    r = oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE, table=table)
+    np.testing.assert_array_equal(r.stat[0, 0, 5, :5], maxima)          # exact tile maxima
+    kept = [maxima[j] for j in range(5) if r.keep[0, 0, 5, j]]
+    skipped = [maxima[j] for j in range(5) if not r.keep[0, 0, 5, j]]
+    assert sorted(kept) == sorted(ex["kept_maxima"])
+    assert sorted(skipped) == sorted(ex["skipped_maxima"])
+    assert r.kept_counts[0, 0, 5] == ex["kept_count"]
+    assert r.keep[0, 0, 5, 5]                                            # diagonal extra
+    # renormalisation over kept + diagonal, skipped blocks out of the denominator; the block
+    # scoring 5 raises the running max after 4 was accumulated (rescale path)
+    ref = sdpa_masked(Q, K, V, block_mask_to_token_mask(r.keep, 384, 64, 64), scale=0.125)
+    np.testing.assert_allclose(r.out[0, 320:], ref[0, 320:], rtol=0, atol=2e-6)
+
+
+@pytest.mark.parametrize("T,expected", [(4.0, 2), (3.5, 3), (-math.inf, 5), (math.inf, 0),
+                                        (5.0, 1), (5.0000005, 0)])
+def test_worked_example_threshold_edges(T, expected):
+    # ">=" reading: a block whose max equals T is kept
+    maxima = [1.0, 4.0, 2.0, 5.0, 3.5]
+    Q, K, V = _worked_example_problem(maxima)
+    r = oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE,
+                       table=_const_table(T, 1, 6))
+    assert r.kept_counts[0, 0, 5] == expected
+
+
+# ---------------------------------------------------------------------------------------------
+# Special cases that reduce to library attention
+# ---------------------------------------------------------------------------------------------
+CASES = [  # B, N, Hq, Hkv, d, Bq, Bk
+    (1, 256, 2, 1, 32, 64, 64),
+    (2, 200, 4, 2, 16, 64, 32),     # batch, GQA, ragged tail
+    (1, 300, 2, 2, 8, 128, 64),     # Bq = 2 Bk, ragged
+    (1, 130, 2, 1, 16, 32, 64),     # Bq < Bk
+]
+
+
+@pytest.mark.parametrize("case", CASES)
+@pytest.mark.parametrize("mode", ["dense", "abs_minus_inf", "rel_lambda0"])
+def test_no_skip_equals_causal_attention(case, mode):
+    B, N, Hq, Hkv, d, Bq, Bk = case
+    Q, K, V = _rand(1, B, N, Hq, Hkv, d)
+    kw = dict(block_q=Bq, block_k=Bk)
+    if mode == "dense":
+        r = oracle_prefill(Q, K, V, mode=GATE_DENSE, **kw)
+    elif mode == "abs_minus_inf":
+        r = oracle_prefill(Q, K, V, mode=GATE_ABSOLUTE, table=_const_table(-math.inf, Hq, 3), **kw)
+    else:
+        r = oracle_prefill(Q, K, V, mode=GATE_RELATIVE, log_lambda=-math.inf, **kw)
+    ref = sdpa_masked(Q, K, V, causal_mask(B, Hq, N))
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=3e-6)
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    np.testing.assert_array_equal(r.kept_counts, np.broadcast_to(noff, r.kept_counts.shape))
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_plus_inf_threshold_is_diagonal_only(case):
+    B, N, Hq, Hkv, d, Bq, Bk = case
+    Q, K, V = _rand(2, B, N, Hq, Hkv, d)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE,
+                       table=_const_table(math.inf, Hq, 2))
+    ref = sdpa_masked(Q, K, V, diagonal_region_mask(B, Hq, N, Bq, Bk))
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=3e-6)
+    assert (r.kept_counts == 0).all()
+
+
+def test_float64_run_matches_library_tightly():
+    Q, K, V = _rand(3, 1, 192, 2, 1, 16)
+    r = oracle_prefill(Q, K, V, block_q=64, block_k=32, mode=GATE_DENSE, dtype=np.float64)
+    ref = sdpa_masked(Q, K, V, causal_mask(1, 2, 192))
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# General thresholds: keep rule against brute force, aggregation against masked attention
+# ---------------------------------------------------------------------------------------------
+def _midpoint_table(bm, Hq, nqb, rng):
+    """Per-(h, i) thresholds placed between two distinct brute-force block maxima, so the
+    keep decision has no near-ties."""
+    T = np.full((1, Hq, nqb), -np.inf, dtype=np.float32)
+    for h in range(Hq):
+        for i in range(nqb):
+            v = np.unique(bm[:, h, i][~np.isnan(bm[:, h, i])])
+            if len(v) >= 2:
+                a = rng.integers(0, len(v) - 1)
+                T[0, h, i] = np.float32(0.5 * (v[a] + v[a + 1]))
+    return T
+
+
+@pytest.mark.parametrize("case", CASES)
+def test_keep_rule_and_renormalisation(case):
+    B, N, Hq, Hkv, d, Bq, Bk = case
+    Q, K, V = _rand(4, B, N, Hq, Hkv, d)
+    bm = brute_block_max(Q, K, Bq, Bk)
+    nqb = -(-N // Bq)
+    T = _midpoint_table(bm[:1], Hq, nqb, np.random.default_rng(5))
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T)
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    exp_keep = np.zeros_like(r.keep)
+    for i in range(nqb):
+        exp_keep[:, :, i, :noff[i]] = bm[:, :, i, :noff[i]] >= T[0][None, :, i, None]
+        n_end = key_block_range(i, N, Bq, Bk)[1]
+        exp_keep[:, :, i, noff[i]:n_end] = True
+        np.testing.assert_allclose(r.stat[:, :, i, :noff[i]], bm[:, :, i, :noff[i]],
+                                   rtol=1e-6, atol=1e-6)
+    np.testing.assert_array_equal(r.keep, exp_keep)
+    np.testing.assert_array_equal(r.kept_counts, exp_keep[..., :].sum(-1) - np.array(
+        [key_block_range(i, N, Bq, Bk)[1] - noff[i] for i in range(nqb)]))
+    ref = sdpa_masked(Q, K, V, block_mask_to_token_mask(r.keep, N, Bq, Bk))
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=3e-6)
+
+
+def test_threshold_reuse_past_calibrated_length():
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 512, 2, 1, 16, 64, 32
+    Q, K, V = _rand(6, B, N, Hq, Hkv, d)
+    bm = brute_block_max(Q, K, Bq, Bk)
+    t_len = 3
+    rng = np.random.default_rng(7)
+    T = np.empty((1, Hq, t_len), np.float32)
+    for h in range(Hq):
+        for c in range(t_len):
+            T[0, h, c] = np.float32(rng.uniform(0.5, 2.5))
+    T[0, :, 0] = -np.inf            # first and last calibrated columns far apart, so a wrong
+    T[0, :, t_len - 1] = np.float32(np.nanmedian(bm))   # column choice past T_len matters
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T)
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    for h in range(Hq):
+        for i in range(N // Bq):
+            thr = T[0, h, min(i, t_len - 1)]
+            assert r.kept_counts[0, h, i] == int((bm[0, h, i, :noff[i]] >= thr).sum())
+    assert (r.kept_counts[0, :, t_len:] < np.array(noff[t_len:])[None, :]).any()
+
+
+def test_budget_slice_selects_table_slice():
+    Q, K, V = _rand(8, 1, 256, 1, 1, 16)
+    T = np.stack([np.full((1, 4), -np.inf), np.full((1, 4), np.inf)]).astype(np.float32)
+    r0 = oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE, table=T,
+                        budget_slice=0)
+    r1 = oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE, table=T,
+                        budget_slice=1)
+    assert list(r0.kept_counts[0, 0]) == [0, 1, 2, 3]
+    assert list(r1.kept_counts[0, 0]) == [0, 0, 0, 0]
+
+
+def test_skipped_values_never_read():
+    # a rejected block loads no V: poisoning the V rows of skipped blocks changes nothing
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 256, 1, 1, 16, 64, 32
+    Q, K, V = _rand(9, B, N, Hq, Hkv, d)
+    bm = brute_block_max(Q, K, Bq, Bk)
+    T = _midpoint_table(bm, Hq, N // Bq, np.random.default_rng(3))
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T)
+    # poison the V rows of every block the last query block skips; its output must not change
+    i = N // Bq - 1
+    Vp = V.copy()
+    n_poisoned = 0
+    for j in range(first_offdiag_blocks(N, Bq, Bk)[i]):
+        if not r.keep[0, 0, i, j]:
+            Vp[0, j * Bk:(j + 1) * Bk] = np.nan
+            n_poisoned += 1
+    assert n_poisoned > 0
+    r2 = oracle_prefill(Q, K, Vp, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T,
+                        query_blocks=[i])
+    np.testing.assert_array_equal(r.out[0, i * Bq:], r2.out[0, i * Bq:])
+    np.testing.assert_array_equal(r.kept_counts[0, 0, i], r2.kept_counts[0, 0, i])
+
+
+def test_gqa_equals_repeated_kv():
+    Q, K, V = _rand(10, 1, 256, 4, 2, 16)
+    T = _const_table(1.0, 4, 4)
+    a = oracle_prefill(Q, K, V, block_q=64, block_k=32, mode=GATE_ABSOLUTE, table=T)
+    b = oracle_prefill(Q, np.repeat(K, 2, axis=2), np.repeat(V, 2, axis=2), block_q=64,
+                       block_k=32, mode=GATE_ABSOLUTE, table=T)
+    np.testing.assert_array_equal(a.out, b.out)
+    np.testing.assert_array_equal(a.kept_counts, b.kept_counts)
+
+
+def test_forced_keep_applies_inside_band_only():
+    Q, K, V = _rand(12, 1, 256, 1, 1, 16)
+    bm = brute_block_max(Q, K, 64, 32)
+    T = np.full((1, 1, 4), np.float32(bm[0, 0, 3, 2]), dtype=np.float32)   # exact tie at (3, 2)
+    base = oracle_prefill(Q, K, V, block_q=64, block_k=32, mode=GATE_ABSOLUTE, table=T)
+    forced = ~base.keep
+    r = oracle_prefill(Q, K, V, block_q=64, block_k=32, mode=GATE_ABSOLUTE, table=T,
+                       forced_keep=forced, band=1e-2)
+    inband = np.abs(base.margin) <= 1e-2
+    np.testing.assert_array_equal(r.keep[inband], forced[inband])
+    outband = ~inband & ~np.isnan(base.margin)
+    np.testing.assert_array_equal(r.keep[outband], base.keep[outband])
+
+
+# ---------------------------------------------------------------------------------------------
+# Relative gate
+# ---------------------------------------------------------------------------------------------
+def _relative_hand_case():
+    """Query block 2 (Bq = Bk = 64, d = 16, scale 1/4): off-diagonal block 0 scores 0 for every
+    pair, block 1 scores -10 for every pair."""
+    N, d = 192, 16
+    Q = np.zeros((1, N, 1, d), np.float32)
+    K = np.zeros((1, N, 1, d), np.float32)
+    V = np.random.default_rng(0).standard_normal((1, N, 1, d)).astype(np.float32)
+    Q[0, 128:, 0, 0] = 4.0
+    K[0, 64:128, 0, 0] = -10.0          # (4 * -10) / 4 = -10
+    K[0, 128:, 0, 0] = 0.0
+    return Q, K, V
+
+
+@pytest.mark.parametrize("lam,kept_block1", [(1e-3, False), (1e-5, True), (0.0, True)])
+def test_relative_gate_hand_case(lam, kept_block1):
+    Q, K, V = _relative_hand_case()
+    ll = math.log(lam) if lam > 0 else -math.inf
+    r = oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_RELATIVE, log_lambda=ll,
+                       scale=0.25)
+    assert r.keep[0, 0, 2, 0]                         # first block: running max is -inf
+    assert r.keep[0, 0, 2, 1] == kept_block1
+    assert r.stat[0, 0, 2, 1] == -10.0
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-3, 1e-2, 1e-1])
+def test_relative_gate_bound_on_dense_weights(lam):
+    # every dense softmax weight inside a skipped block is below lambda
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 512, 2, 1, 16, 64, 32
+    Q, K, V = _rand(13, B, N, Hq, Hkv, d)
+    Q *= 6.0
+    for j in range(1, N // Bk, 2):
+        K[:, j * Bk:(j + 1) * Bk] *= 0.05          # weak key blocks that the gate can drop
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_RELATIVE,
+                       log_lambda=math.log(lam))
+    S = full_scores(Q, K)
+    S = np.where(np.tril(np.ones((N, N), bool)), S, -np.inf)
+    P = np.exp(S - S.max(-1, keepdims=True))
+    P /= P.sum(-1, keepdims=True)
+    n_skipped = 0
+    for h in range(Hq):
+        for i in range(N // Bq):
+            for j in range(first_offdiag_blocks(N, Bq, Bk)[i]):
+                if not r.keep[0, h, i, j]:
+                    n_skipped += 1
+                    assert P[0, h, i * Bq:(i + 1) * Bq, j * Bk:(j + 1) * Bk].max() < lam * (1 + 1e-5)
+    assert n_skipped > 0
+    ref = sdpa_masked(Q, K, V, block_mask_to_token_mask(r.keep, N, Bq, Bk))
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=3e-6)
+
+
+# ---------------------------------------------------------------------------------------------
+# Calibration
+# ---------------------------------------------------------------------------------------------
+def test_kth_highest_hand_values():
+    m = np.array([5.0, 3.0, 3.0, 1.0, 9.0])
+    assert kth_highest(m, 4, 1) == 5.0
+    assert kth_highest(m, 4, 2) == 3.0
+    assert kth_highest(m, 4, 3) == 3.0
+    assert kth_highest(m, 4, 4) == 1.0          # n_off == k: the smallest candidate, not -inf
+    assert kth_highest(m, 4, 5) == -math.inf    # fewer than k candidates
+    assert kth_highest(m, 5, 1) == 9.0
+
+
+def _exact_sample(seed, N=512, Hq=2, Hkv=1, d=32):
+    rng = np.random.default_rng(seed)
+    return (quantized_normal(rng, (1, N, Hq, d)), quantized_normal(rng, (1, N, Hkv, d)),
+            rng.standard_normal((1, N, Hkv, d)).astype(np.float32))
+
+
+@pytest.mark.parametrize("k", [1, 3, 6])
+def test_calibrate_on_one_sample_keeps_exactly_k(k):
+    Bq, Bk, N = 64, 32, 512
+    Q, K, V = _exact_sample(21)
+    bm = brute_block_max(Q, K, Bq, Bk, scale=0.125)
+    T = calibrate([(Q, K)], block_q=Bq, block_k=Bk, budgets=[k], scale=0.125)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T, scale=0.125)
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    for h in range(2):
+        for i in range(N // Bq):
+            vals = bm[0, h, i, :noff[i]]
+            assert len(np.unique(vals)) == len(vals)          # premise: distinct maxima
+            if noff[i] >= k:
+                assert r.kept_counts[0, h, i] == k
+                assert T[0, h, i] == np.sort(vals)[::-1][k - 1]
+            else:
+                assert T[0, h, i] == -np.inf
+                assert r.kept_counts[0, h, i] == noff[i]
+
+
+def test_calibrate_averages_samples():
+    Bq, Bk, N, k = 64, 32, 512, 2
+    s1, s2 = _exact_sample(31), _exact_sample(32)
+    T = calibrate([s1[:2], s2[:2]], block_q=Bq, block_k=Bk, budgets=[k, 5], scale=0.125)
+    noff = first_offdiag_blocks(N, Bq, Bk)
+    b1 = brute_block_max(s1[0], s1[1], Bq, Bk, scale=0.125)
+    b2 = brute_block_max(s2[0], s2[1], Bq, Bk, scale=0.125)
+    for kk, kv in enumerate([k, 5]):
+        for h in range(2):
+            for i in range(N // Bq):
+                if noff[i] < kv:
+                    assert T[kk, h, i] == -np.inf
+                    continue
+                t1 = np.sort(b1[0, h, i, :noff[i]])[::-1][kv - 1]
+                t2 = np.sort(b2[0, h, i, :noff[i]])[::-1][kv - 1]
+                assert T[kk, h, i] == np.float32(0.5 * (t1 + t2))
+
+
+def test_calibrate_batch_entries_are_samples():
+    s1, s2 = _exact_sample(41), _exact_sample(42)
+    Qb = np.concatenate([s1[0], s2[0]])
+    Kb = np.concatenate([s1[1], s2[1]])
+    a = calibrate([(Qb, Kb)], block_q=64, block_k=32, budgets=[3], scale=0.125)
+    b = calibrate([s1[:2], s2[:2]], block_q=64, block_k=32, budgets=[3], scale=0.125)
+    np.testing.assert_array_equal(a, b)
+
+
+def test_predicted_density_closed_form():
+    # sum_i min(n_off(i), k) / sum_i n_off(i) for Bq = 2 Bk: n_off(i) = 2 i
+    for nqb, k in [(128, 32), (256, 16), (256, 64), (256, 256), (1024, 64)]:
+        noff = [key_block_range(i, nqb * 128, 128, 64)[0] for i in range(nqb)]
+        num = sum(min(x, k) for x in noff)
+        den = sum(noff)
+        # closed form: 2 * sum_{i < k/2} i + k * (#i >= k/2) over the triangle sum nqb (nqb - 1)
+        h = min(k // 2, nqb)
+        closed = (h * (h - 1) + k * (nqb - h)) / (nqb * (nqb - 1))
+        assert abs(num / den - closed) < 1e-12
+
+
+def test_oracle_module_header_marks_test_infrastructure():
+    doc = oracle.bsfa_oracle.__doc__
+    assert "TEST INFRASTRUCTURE ONLY" in doc
