@@ -1,0 +1,265 @@
+"""Benchmark: gated prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick]
+
+A step is one bsfa_prefill call over one batch of synthetic input already resident in HBM:
+exact QK^T on every causally visible tile, the gate, online softmax and PV on kept tiles.
+Prints one JSON line. `value` is executed TFLOP/s of the gated call: tile-level FLOPs of QK on
+every visible tile plus PV on every kept or diagonal tile, counted from the kernel's own kept
+counts (2*Bq*Bk*d per tile product), divided by the time of the step. The same line carries
+the dense path of the same kernel (gate compiled out), the zero-skip taxes, the kept fraction,
+the roofline of the prefill kernel (HIP events on the launch stream) and the CPU oracle timed on
+a bounded sample of the same workload.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "gated prefill attn ms + executed TFLOP/s (% MFMA peak) at 32K/128K vs dense"
+PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama_128k")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def block_ranges(N, Bq, Bk=64):
+    """(n_off, n_end) per query block: the same block structure the kernel walks."""
+    out = []
+    for i in range(-(-N // Bq)):
+        n_off = (i * Bq) // Bk
+        n_end = (min((i + 1) * Bq, N) - 1) // Bk + 1
+        out.append((n_off, n_end))
+    return out
+
+
+def executed_flops(kept_counts, N, Bq, d, Bk=64, query_blocks=None):
+    """2*Bq*Bk*d per tile product: QK on every visible tile, PV on kept + diagonal tiles."""
+    import numpy as np
+    kc = np.asarray(kept_counts, dtype=np.int64)        # [B, Hq, nqb]
+    rng = block_ranges(N, Bq, Bk)
+    qbs = range(len(rng)) if query_blocks is None else query_blocks
+    B, Hq = kc.shape[0], kc.shape[1]
+    tiles = 0
+    for i in qbs:
+        n_off, n_end = rng[i]
+        tiles += B * Hq * (n_end + (n_end - n_off)) + int(kc[:, :, i].sum())
+    return 2.0 * Bq * Bk * d * tiles
+
+
+def dense_flops(B, Hq, N, Bq, d, Bk=64):
+    rng = block_ranges(N, Bq, Bk)
+    return 2.0 * Bq * Bk * d * B * Hq * sum(2 * n_end for _, n_end in rng)
+
+
+def predicted_density(N, Bq, k, Bk=64):
+    rng = block_ranges(N, Bq, Bk)
+    den = sum(n_off for n_off, _ in rng)
+    return sum(min(n_off, k) for n_off, _ in rng) / den if den else 1.0
+
+
+class Workload:
+    def __init__(self, name, device):
+        import torch
+        from block_sparse_long_amd import synth
+        from block_sparse_long_amd.table import ThresholdTable
+        self.name = name
+        self.c = c = synth.CONFIGS[name]
+        Q, K, V = synth.make_inputs(name, 0)
+        self.host = synth.to_bf16(Q, K, V)
+        del Q, K, V
+        self.Qd, self.Kd, self.Vd = (x.to(device) for x in self.host)
+        self.O = torch.empty_like(self.Qd)
+        self.N, self.Hq, self.d, self.Bq = c["n"], c["heads_q"], c["d"], c["block_q"]
+        nqb = -(-self.N // self.Bq)
+        self.counts = torch.zeros((1, self.Hq, nqb), dtype=torch.int32, device=device)
+        self.table = None
+        if c["budgets"]:
+            self.table = ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{name}.bin"))
+            self.dtable = self.table.to_device(device)
+        rng = block_ranges(self.N, self.Bq)
+        self.n_off_total = sum(n_off for n_off, _ in rng)
+
+    def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None):
+        from block_sparse_long_amd import _lib
+        _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, gate_mode=mode,
+                          table=table if table is not None else
+                          (self.dtable if mode == "absolute" else None),
+                          budget_slice=budget_slice, log_lambda=log_lambda,
+                          kept_counts=self.counts)
+
+
+def timed(fn, steps, warmup):
+    """(ms per call from HIP events on the launch stream, wall ms per call)."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    return e0.elapsed_time(e1) / steps, wall
+
+
+def run_gate(w, mode, steps, warmup, **kw):
+    import numpy as np
+    import torch
+    ev_ms, wall_ms = timed(lambda: w.call(mode, **kw), steps, warmup)
+    torch.cuda.synchronize()
+    counts = w.counts.cpu().numpy()
+    flops = executed_flops(counts, w.N, w.Bq, w.d)
+    kept = int(counts.sum())
+    return dict(ms=ev_ms, wall_ms=wall_ms, flops=flops, tflops=flops / ev_ms / 1e9,
+                kept_fraction=kept / (w.Hq * w.n_off_total) if w.n_off_total else 1.0,
+                pct_peak=100.0 * flops / ev_ms / 1e9 / PEAK_BF16_TFLOPS)
+
+
+def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
+    """The oracle as it stands, single-threaded BLAS, on a bounded sample of the workload."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    Qh, Kh, Vh = (x.float().numpy() for x in w.host)
+    nqb = -(-w.N // w.Bq)
+    if blocks is None:
+        blocks = sorted({nqb // 4 - 1, nqb // 2 - 1, nqb // 2, 3 * nqb // 4, nqb - 1})
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=64, mode=mode,
+                                  table=None if w.table is None else w.table.T,
+                                  budget_slice=budget_slice, log_lambda=log_lambda,
+                                  query_blocks=blocks)
+        sec = time.perf_counter() - t0
+    flops = executed_flops(np.maximum(r.kept_counts, 0), w.N, w.Bq, w.d, query_blocks=blocks)
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"{w.name}: query blocks {blocks} x all {w.Hq} heads, same inputs and "
+                      f"table, float32 numpy, 1 BLAS thread; executed TFLOP/s of the sample"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported "
+              "(the attention shards by KV head with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from block_sparse_long_amd import _lib
+    _lib.load_library()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    w = Workload(args.workload, dev)
+    k = w.table.budgets[0] if w.table is not None else None
+    mode = "absolute" if w.table is not None else "relative"
+    gate_kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
+
+    gated = run_gate(w, mode, args.steps, args.warmup, **gate_kw)
+    dense = run_gate(w, "dense", args.steps, args.warmup)
+    # zero-skip taxes: the gated instantiations with a gate that never skips
+    ninf = None
+    if w.table is not None:
+        from block_sparse_long_amd.table import ThresholdTable
+        T = np.full_like(w.table.T[:1], -np.inf)
+        ninf = ThresholdTable(T=T, budgets=[0], block_q=w.table.block_q, block_k=64,
+                              head_dim=w.d, softmax_scale=w.table.softmax_scale).to_device(dev)
+        abs_ninf = run_gate(w, "absolute", args.steps, args.warmup, table=ninf)
+    rel_zero = run_gate(w, "relative", args.steps, args.warmup, log_lambda=-math.inf)
+    extras = {
+        "gated_ms": round(gated["ms"], 3), "dense_ms": round(dense["ms"], 3),
+        "speedup_vs_dense": round(dense["ms"] / gated["ms"], 4),
+        "executed_tflops": round(gated["tflops"], 2),
+        "pct_mfma_peak": round(gated["pct_peak"], 2),
+        "dense_tflops": round(dense["tflops"], 2),
+        "dense_pct_mfma_peak": round(dense["pct_peak"], 2),
+        "dense_textbook_tflops": round(4.0 * w.N * w.N / 2 * w.Hq * w.d / dense["ms"] / 1e9, 2),
+        "kept_fraction": round(gated["kept_fraction"], 4),
+        "predicted_density": round(predicted_density(w.N, w.Bq, k), 4) if k else None,
+        "zero_skip_tax_relative": round(rel_zero["ms"] / dense["ms"] - 1, 4),
+    }
+    if w.table is not None:
+        extras["zero_skip_tax_absolute"] = round(abs_ninf["ms"] / dense["ms"] - 1, 4)
+
+    if not args.quick:
+        sweeps = {}
+        del w
+        torch.cuda.empty_cache()
+        w32 = Workload("llama_32k_sweep", dev)
+        d32 = run_gate(w32, "dense", args.steps, args.warmup)
+        rows = {"dense": {"ms": round(d32["ms"], 3), "tflops": round(d32["tflops"], 2)}}
+        for sl, kk in enumerate(w32.table.budgets):
+            r = run_gate(w32, "absolute", args.steps, args.warmup, budget_slice=sl)
+            rows[f"k={kk}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
+                               "pct_mfma_peak": round(r["pct_peak"], 2),
+                               "speedup_vs_dense": round(d32["ms"] / r["ms"], 4),
+                               "kept_fraction": round(r["kept_fraction"], 4),
+                               "predicted_density": round(predicted_density(32768, 128, kk), 4)}
+        sweeps["llama_32k_sweep"] = rows
+        del w32
+        torch.cuda.empty_cache()
+        w64 = Workload("llama_64k_relative", dev)
+        d64 = run_gate(w64, "dense", args.steps, args.warmup)
+        rows = {"dense": {"ms": round(d64["ms"], 3), "tflops": round(d64["tflops"], 2)}}
+        for lam in (0.0, 1e-4, 1e-3, 1e-2):
+            ll = math.log(lam) if lam > 0 else -math.inf
+            r = run_gate(w64, "relative", args.steps, args.warmup, log_lambda=ll)
+            rows[f"lambda={lam:g}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
+                                       "pct_mfma_peak": round(r["pct_peak"], 2),
+                                       "speedup_vs_dense": round(d64["ms"] / r["ms"], 4),
+                                       "kept_fraction": round(r["kept_fraction"], 4)}
+        sweeps["llama_64k_relative"] = rows
+        extras["sweeps"] = sweeps
+        del w64
+        torch.cuda.empty_cache()
+        w = Workload(args.workload, dev)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, mode, **gate_kw)
+
+    c = w.c
+    line = {
+        "metric": METRIC, "value": round(gated["tflops"], 3), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(gated["wall_ms"], 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": 1, "seq_len": w.N,
+                   "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": w.d,
+                   "tile": f"{w.Bq}x64", "gate": mode,
+                   "budget_k": k, "calibrated_len": c["calib_n"] if k else None},
+        "roofline": {"bound": "mfma", "achieved": round(gated["tflops"], 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gated["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "prefill_kernel<128,128,4,gate>",
+                     "flops_per_launch": gated["flops"]},
+        "cpu_baseline": cpu,
+        "extras": extras,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+"""ctypes binding of libbsfa.so (include/bsfa.h). Argument marshalling only.
+
+Torch tensors supply device memory and the current HIP stream; every computation happens in the
+library's kernels. The functions keep the C names. The library is loaded on first use and a
+missing library raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+BSFA_OK = 0
+BSFA_ERR_ARG = 1
+BSFA_ERR_SHAPE = 2
+BSFA_ERR_DTYPE = 3
+BSFA_ERR_ALIGN = 4
+BSFA_ERR_TABLE = 5
+BSFA_ERR_UNSUPPORTED = 6
+BSFA_ERR_HIP = 7
+
+BSFA_GATE_DENSE = 0
+BSFA_GATE_ABSOLUTE = 1
+BSFA_GATE_RELATIVE = 2
+
+BSFA_BF16 = 0
+BSFA_FP32 = 1
+
+GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
+              "relative": BSFA_GATE_RELATIVE}
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
+
+EXPORTED = ("bsfa_prefill", "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error",
+            "bsfa_version")
+
+
+class BsfaProblem(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("seqlen", ctypes.c_int32), ("heads_q", ctypes.c_int32),
+        ("heads_kv", ctypes.c_int32), ("head_dim", ctypes.c_int32), ("block_q", ctypes.c_int32),
+        ("block_k", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class BsfaTable(ctypes.Structure):
+    _fields_ = [
+        ("T", ctypes.c_void_p), ("n_budgets", ctypes.c_int32), ("t_len", ctypes.c_int32),
+        ("heads_q", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class BsfaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"bsfa status {status}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libbsfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with python -m "
+                           "block_sparse_long_amd.build_lib (there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp = ctypes.c_void_p
+    lib.bsfa_prefill.restype = ctypes.c_int32
+    lib.bsfa_prefill.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, ctypes.POINTER(BsfaTable),
+                                 ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp,
+                                 vp]
+    lib.bsfa_calibrate_blockmax.restype = ctypes.c_int32
+    lib.bsfa_calibrate_blockmax.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp,
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp]
+    lib.bsfa_status_string.restype = ctypes.c_char_p
+    lib.bsfa_status_string.argtypes = [ctypes.c_int32]
+    lib.bsfa_last_error.restype = ctypes.c_char_p
+    lib.bsfa_last_error.argtypes = []
+    lib.bsfa_version.restype = ctypes.c_int32
+    lib.bsfa_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def bsfa_status_string(status: int) -> str:
+    return load_library().bsfa_status_string(status).decode()
+
+
+def bsfa_last_error() -> str:
+    return load_library().bsfa_last_error().decode()
+
+
+def bsfa_version() -> int:
+    return load_library().bsfa_version()
+
+
+def _check(status: int) -> None:
+    if status != BSFA_OK:
+        raise BsfaError(status, f"{bsfa_status_string(status)}: {bsfa_last_error()}")
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _strides(t, name: str):
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be [batch, seq, heads, dim]")
+    if t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name}: the head_dim axis must be contiguous")
+    return (t.stride(0), t.stride(1), t.stride(2))
+
+
+def _stream_handle(stream, device) -> int:
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return int(stream.cuda_stream)
+
+
+def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
+                 softmax_scale: float = 0.0) -> BsfaProblem:
+    import torch
+    p = BsfaProblem()
+    p.batch, p.seqlen, p.heads_q, p.head_dim = (int(x) for x in Q.shape)
+    p.heads_kv = int(K.shape[2])
+    p.block_q, p.block_k = int(block_q), int(block_k)
+    p.softmax_scale = float(softmax_scale)
+    dt = {torch.bfloat16: BSFA_BF16, torch.float32: BSFA_FP32}
+    p.in_dtype = dt.get(Q.dtype, -1)
+    p.out_dtype = dt.get(O.dtype, -1) if O is not None else BSFA_BF16
+    p.q_stride[:] = _strides(Q, "Q")
+    p.k_stride[:] = _strides(K, "K")
+    if V is not None:
+        p.v_stride[:] = _strides(V, "V")
+    if O is not None:
+        p.o_stride[:] = _strides(O, "O")
+    return p
+
+
+def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode="dense",
+                 table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
+                 kept_counts=None, kept_total=None, debug_block_stat=None,
+                 softmax_scale: float = 0.0, stream=None, out_dtype=None):
+    """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, N, Hkv, d] bf16 (device).
+
+    O (allocated if None, dtype ``out_dtype`` or bf16), kept_counts (int32 [B, Hq, nqb]),
+    kept_total (int64 [1], read as uint64) and debug_block_stat (fp32 [B, Hq, nqb, nkb]) are
+    written by the kernel on ``stream`` (default: torch's current stream). ``table`` is a
+    block_sparse_long_amd.table.DeviceTable (needed for gate_mode "absolute"). Returns O.
+    """
+    import torch
+    lib = load_library()
+    if O is None:
+        O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
+    mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    p = make_problem(Q, K, V, O, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    tbl = None
+    if table is not None:
+        tbl = table.c_struct()
+    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
+                        ("kept_total", kept_total, torch.int64),
+                        ("debug_block_stat", debug_block_stat, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    st = lib.bsfa_prefill(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
+                          ctypes.byref(tbl) if tbl is not None else None, int(budget_slice),
+                          mode, float(log_lambda), _ptr(O), _ptr(kept_counts), _ptr(kept_total),
+                          _ptr(debug_block_stat), _stream_handle(stream, Q.device))
+    _check(st)
+    return O
+
+
+def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_k: int = 64,
+                            softmax_scale: float = 0.0, stream=None):
+    """k-th highest off-diagonal block max per (budget, b, h, i): fp32 [n_budgets, B, Hq, nqb]."""
+    import torch
+    lib = load_library()
+    B, N, Hq, _ = Q.shape
+    nqb = -(-N // block_q)
+    if kth_out is None:
+        kth_out = torch.empty((len(budgets), B, Hq, nqb), dtype=torch.float32, device=Q.device)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    arr = (ctypes.c_int32 * max(1, len(budgets)))(*[int(k) for k in budgets])
+    st = lib.bsfa_calibrate_blockmax(ctypes.byref(p), _ptr(Q), _ptr(K), arr, len(budgets),
+                                     _ptr(kth_out), _stream_handle(stream, Q.device))
+    _check(st)
+    return kth_out

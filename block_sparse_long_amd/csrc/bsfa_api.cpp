@@ -1,0 +1,243 @@
+// C ABI of libbsfa.so (declared in include/bsfa.h): host-side validation and dispatch.
+//
+// Every check runs on the host before anything is enqueued, so an error status means no GPU
+// work was started and no output was touched. Nothing here synchronises or allocates.
+#include "bsfa.h"
+
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "bsfa_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+bsfa_status fail(bsfa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bsfa_status ok() {
+  g_last_error[0] = '\0';
+  return BSFA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float effective_scale(const bsfa_problem* p) {
+  return p->softmax_scale > 0.f ? p->softmax_scale : 1.f / sqrtf((float)p->head_dim);
+}
+
+// Shape, tile, dtype and stride checks shared by both entry points.
+bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
+  if (!p) return fail(BSFA_ERR_ARG, "problem is NULL");
+  if (p->batch < 0 || p->seqlen < 0)
+    return fail(BSFA_ERR_ARG, "batch (%d) and seqlen (%d) must be >= 0", p->batch, p->seqlen);
+  if (p->heads_q < 1 || p->heads_kv < 1)
+    return fail(BSFA_ERR_ARG, "heads_q (%d) and heads_kv (%d) must be >= 1", p->heads_q,
+                p->heads_kv);
+  if (p->heads_q % p->heads_kv != 0)
+    return fail(BSFA_ERR_SHAPE, "heads_q (%d) is not a multiple of heads_kv (%d)", p->heads_q,
+                p->heads_kv);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(BSFA_ERR_SHAPE, "head_dim %d not supported (64 or 128)", p->head_dim);
+  if (p->block_k != bsfa::kBlockK || (p->block_q != 64 && p->block_q != 128))
+    return fail(BSFA_ERR_SHAPE, "tile %dx%d not supported (64x64 or 128x64)", p->block_q,
+                p->block_k);
+  if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
+    return fail(BSFA_ERR_ARG, "softmax_scale must be finite and >= 0");
+  if (p->in_dtype != BSFA_BF16)
+    return fail(BSFA_ERR_DTYPE, "in_dtype %d not supported (bf16 only)", p->in_dtype);
+  if (need_v_o && p->out_dtype != BSFA_BF16 && p->out_dtype != BSFA_FP32)
+    return fail(BSFA_ERR_DTYPE, "out_dtype %d not supported", p->out_dtype);
+  const int64_t* strides[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+  const char* names[4] = {"q", "k", "v", "o"};
+  const int n_checked = need_v_o ? 4 : 2;
+  for (int t = 0; t < n_checked; ++t) {
+    const int64_t unit = (t == 3 && p->out_dtype == BSFA_FP32) ? 4 : 8;  // elements per 16 B
+    for (int a = 0; a < 3; ++a) {
+      if (strides[t][a] < 0)
+        return fail(BSFA_ERR_ARG, "%s_stride[%d] is negative", names[t], a);
+      if (strides[t][a] % unit != 0)
+        return fail(BSFA_ERR_ALIGN, "%s_stride[%d] = %lld breaks 16-byte row alignment",
+                    names[t], a, (long long)strides[t][a]);
+    }
+  }
+  return BSFA_OK;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+extern "C" {
+
+const char* bsfa_status_string(int32_t s) {
+  switch (s) {
+    case BSFA_OK: return "ok";
+    case BSFA_ERR_ARG: return "invalid argument";
+    case BSFA_ERR_SHAPE: return "unsupported or inconsistent shape";
+    case BSFA_ERR_DTYPE: return "unsupported dtype";
+    case BSFA_ERR_ALIGN: return "misaligned pointer or stride";
+    case BSFA_ERR_TABLE: return "threshold table missing or inconsistent with the problem";
+    case BSFA_ERR_UNSUPPORTED: return "unsupported request";
+    case BSFA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* bsfa_last_error(void) { return g_last_error; }
+
+int32_t bsfa_version(void) { return (1 << 16) | 0; }
+
+bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
+                         const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
+                         float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
+                         float* debug_block_stat, void* stream) {
+  bsfa_status s = check_problem(p, true);
+  if (s != BSFA_OK) return s;
+  if (gate_mode != BSFA_GATE_DENSE && gate_mode != BSFA_GATE_ABSOLUTE &&
+      gate_mode != BSFA_GATE_RELATIVE)
+    return fail(BSFA_ERR_ARG, "gate_mode %d is not a bsfa_gate_mode", gate_mode);
+  if (gate_mode == BSFA_GATE_RELATIVE && (isnan(log_lambda) || log_lambda == INFINITY))
+    return fail(BSFA_ERR_ARG, "log_lambda must be finite or -INFINITY");
+  const float scale = effective_scale(p);
+  if (gate_mode == BSFA_GATE_ABSOLUTE) {
+    if (!table) return fail(BSFA_ERR_TABLE, "ABSOLUTE gate needs a threshold table");
+    if (!table->T) return fail(BSFA_ERR_TABLE, "table->T is NULL");
+    if ((reinterpret_cast<uintptr_t>(table->T) & 3u) != 0)
+      return fail(BSFA_ERR_ALIGN, "table->T is not 4-byte aligned");
+    if (table->n_budgets < 1 || table->t_len < 1)
+      return fail(BSFA_ERR_TABLE, "table has n_budgets %d, t_len %d", table->n_budgets,
+                  table->t_len);
+    if (budget_slice < 0 || budget_slice >= table->n_budgets)
+      return fail(BSFA_ERR_TABLE, "budget_slice %d outside [0, %d)", budget_slice,
+                  table->n_budgets);
+    if (table->heads_q != p->heads_q || table->block_q != p->block_q ||
+        table->block_k != p->block_k || table->head_dim != p->head_dim)
+      return fail(BSFA_ERR_TABLE,
+                  "table calibrated for Hq=%d tile %dx%d d=%d, problem has Hq=%d tile %dx%d d=%d",
+                  table->heads_q, table->block_q, table->block_k, table->head_dim, p->heads_q,
+                  p->block_q, p->block_k, p->head_dim);
+    if (!(fabsf(table->softmax_scale - scale) <= 1e-6f * scale))
+      return fail(BSFA_ERR_TABLE, "table softmax_scale %g differs from the problem's %g",
+                  (double)table->softmax_scale, (double)scale);
+  }
+  const bool empty = p->batch == 0 || p->seqlen == 0;
+  if (!empty) {
+    if (!Q || !K || !V || !O) return fail(BSFA_ERR_ARG, "Q, K, V and O must be non-NULL");
+    if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
+      return fail(BSFA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
+  }
+  if ((kept_counts && (reinterpret_cast<uintptr_t>(kept_counts) & 3u)) ||
+      (kept_total && (reinterpret_cast<uintptr_t>(kept_total) & 7u)) ||
+      (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u)))
+    return fail(BSFA_ERR_ALIGN, "kept_counts, kept_total or debug_block_stat misaligned");
+  const int nqb = ceil_div(p->seqlen, p->block_q);
+  const int nkb = ceil_div(p->seqlen, p->block_k);
+  if ((long long)p->seqlen > (1ll << 30))
+    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d too large", p->seqlen);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (kept_total) {
+    hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(kept_total), st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing kept_total: %s", hipGetErrorString(e));
+  }
+  if (empty) return ok();
+
+  bsfa::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.o = O;
+  a.thr = gate_mode == BSFA_GATE_ABSOLUTE
+              ? table->T + (long long)budget_slice * table->heads_q * table->t_len
+              : nullptr;
+  a.t_len = gate_mode == BSFA_GATE_ABSOLUTE ? table->t_len : 1;
+  a.kept_counts = kept_counts;
+  a.kept_total = reinterpret_cast<unsigned long long*>(kept_total);
+  a.dbg = debug_block_stat;
+  for (int t = 0; t < 3; ++t) {
+    a.qs[t] = p->q_stride[t];
+    a.ks[t] = p->k_stride[t];
+    a.vs[t] = p->v_stride[t];
+    a.os[t] = p->o_stride[t];
+  }
+  a.B = p->batch;
+  a.N = p->seqlen;
+  a.Hq = p->heads_q;
+  a.Hkv = p->heads_kv;
+  a.G = p->heads_q / p->heads_kv;
+  a.nqb = nqb;
+  a.nkb = nkb;
+  const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
+  const int hpw = nw / (p->block_q / 64);
+  a.units = p->batch * p->heads_kv * (a.G / hpw);
+  a.xcd_map = (a.units % 8) == 0;
+  a.scale = scale;
+  a.c_log2 = scale * 1.4426950408889634f;
+  a.log_lambda = log_lambda;
+  a.out_fp32 = p->out_dtype == BSFA_FP32;
+  if ((long long)a.units * nqb > 0x7fffffffll)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+  hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, gate_mode, st);
+  if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
+                                    const int32_t* budgets_host, int32_t n_budgets,
+                                    float* kth_out, void* stream) {
+  bsfa_status s = check_problem(p, false);
+  if (s != BSFA_OK) return s;
+  if (n_budgets < 1 || n_budgets > 16)
+    return fail(BSFA_ERR_ARG, "n_budgets %d outside 1..16", n_budgets);
+  if (!budgets_host) return fail(BSFA_ERR_ARG, "budgets_host is NULL");
+  for (int t = 0; t < n_budgets; ++t)
+    if (budgets_host[t] < 1) return fail(BSFA_ERR_ARG, "budget %d is < 1", budgets_host[t]);
+  const int nkb = ceil_div(p->seqlen, p->block_k);
+  if (nkb > bsfa::kCalibMaxKeyBlocks)
+    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the calibration limit %d", p->seqlen,
+                bsfa::kCalibMaxKeyBlocks * bsfa::kBlockK);
+  const bool empty = p->batch == 0 || p->seqlen == 0;
+  if (empty) return ok();
+  if (!Q || !K || !kth_out) return fail(BSFA_ERR_ARG, "Q, K and kth_out must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(BSFA_ERR_ALIGN, "Q and K must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(kth_out) & 3u) return fail(BSFA_ERR_ALIGN, "kth_out misaligned");
+
+  bsfa::CalibArgs a;
+  memset(&a, 0, sizeof(a));
+  a.q = Q;
+  a.k = K;
+  for (int t = 0; t < 3; ++t) {
+    a.qs[t] = p->q_stride[t];
+    a.ks[t] = p->k_stride[t];
+  }
+  a.B = p->batch;
+  a.N = p->seqlen;
+  a.Hq = p->heads_q;
+  a.Hkv = p->heads_kv;
+  a.G = p->heads_q / p->heads_kv;
+  a.nqb = ceil_div(p->seqlen, p->block_q);
+  a.nkb = nkb;
+  const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
+  const int hpw = nw / (p->block_q / 64);
+  a.units = p->batch * p->heads_kv * (a.G / hpw);
+  a.xcd_map = (a.units % 8) == 0;
+  a.scale = effective_scale(p);
+  a.n_budgets = n_budgets;
+  for (int t = 0; t < n_budgets; ++t) a.budgets[t] = budgets_host[t];
+  a.kth = kth_out;
+  hipError_t e = bsfa::launch_calibrate(a, p->head_dim, p->block_q, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BSFA_ERR_HIP, "calibration launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,54 @@
+// Internal interface between the C ABI (bsfa_api.cpp) and the HIP kernels (bsfa_kernels.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bsfa {
+
+constexpr int kBlockK = 64;          // key tile width (gate tile columns)
+constexpr int kCalibMaxKeyBlocks = 4096;
+
+enum Gate : int { kDense = 0, kAbsolute = 1, kRelative = 2 };
+
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  const float* thr;                // threshold slice [Hq][t_len] (ABSOLUTE) or nullptr
+  int32_t* kept_counts;            // [B][Hq][nqb] or nullptr
+  unsigned long long* kept_total;  // scalar or nullptr
+  float* dbg;                      // [B][Hq][nqb][nkb] or nullptr
+  long long qs[3], ks[3], vs[3], os[3];
+  int B, N, Hq, Hkv, G, nqb, nkb, t_len;
+  int units;                       // B * Hkv * (G / heads per workgroup)
+  int xcd_map;                     // 1: map workgroups so each XCD serves whole KV heads
+  float scale;                     // softmax scale applied to fp32 scores
+  float c_log2;                    // scale * log2(e)
+  float log_lambda;                // RELATIVE threshold
+  int out_fp32;
+};
+
+struct CalibArgs {
+  const void* q;
+  const void* k;
+  long long qs[3], ks[3];
+  int B, N, Hq, Hkv, G, nqb, nkb;
+  int units, xcd_map;
+  float scale;
+  int n_budgets;
+  int budgets[16];
+  float* kth;                      // [n_budgets][B][Hq][nqb]
+};
+
+// Workgroup shape: waves of 64 query rows; a workgroup holds heads_per_wg heads of one KV
+// group times block_q rows. Returns the number of waves (1, 2 or 4), 0 if unsupported.
+int waves_per_workgroup(int block_q, int group);
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
+                          hipStream_t stream);
+hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipStream_t stream);
+hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
+
+}  // namespace bsfa

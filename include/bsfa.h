@@ -1,0 +1,154 @@
+/*
+ * bsfa.h - C ABI of libbsfa.so: exact-score-gated block-sparse causal prefill attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Block Sparse Flash Attention", paper notes, Method):
+ *   For every batch b, query head h and query block i (rows [i*Bq, (i+1)*Bq)), the kernel
+ *   visits the causally visible key blocks j (columns [j*Bk, (j+1)*Bk)) in ascending order and
+ *   computes the exact scaled scores S = Q_i K_j^T * scale of the whole tile (Key Designs 2).
+ *     - Off-diagonal blocks (j < n_off(i) = floor(i*Bq/Bk), wholly before the block's first row)
+ *       are gated. ABSOLUTE: keep iff s_max = max over the tile of S >= T_eff(h, i) (Key Designs
+ *       2, keep-rule equation; ">=" as in the main text). RELATIVE: keep iff some row r of the
+ *       tile has rowmax_j[r] - m[r] >= log_lambda, m the running row max before the block
+ *       ("Skipping attention blocks was the easy part", BLASST blog, section "Vote, then skip").
+ *       DENSE: keep every block (the gate is compiled out).
+ *     - Diagonal-region blocks (n_off(i) <= j < n_end(i)) always run, with the causal mask.
+ *     - A kept block updates the online-softmax state (running max m, sum l, accumulator O)
+ *       and accumulates P V_j; a skipped block loads no V, computes no exponentials and leaves
+ *       m, l and O untouched (Key Designs 3).
+ *     - Output O_i = O / l: attention renormalised over the kept blocks and the diagonal
+ *       region (Overall Architecture; Key Designs 3).
+ *   T_eff(h, i) = T[budget_slice][h][min(i, t_len - 1)]: positions past the calibrated length
+ *   reuse the last calibrated column (Key Designs 1). -INFINITY keeps every block.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers are caller-owned device memory on the current HIP device; the library
+ *     allocates nothing, frees nothing and keeps no state between calls except the thread-local
+ *     error string.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is asynchronous:
+ *     results are valid once the caller has synchronised the stream. The library never
+ *     synchronises.
+ *   - Arguments are validated on the host before anything is enqueued. On any status other
+ *     than BSFA_OK nothing was enqueued and every output is untouched; bsfa_last_error() then
+ *     describes the problem. BSFA_ERR_HIP means the launch itself failed. No C++ exception
+ *     crosses the ABI.
+ *   - Tensors are indexed [batch][token][head][dim] with element strides given per tensor for
+ *     batch, token and head; the dim axis is contiguous. Base pointers and every row
+ *     (batch/token/head offset) must be 16-byte aligned.
+ */
+#ifndef BSFA_H_
+#define BSFA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  BSFA_OK = 0,
+  BSFA_ERR_ARG = 1,          /* NULL pointer, negative size, bad enum value */
+  BSFA_ERR_SHAPE = 2,        /* heads_q % heads_kv != 0, unsupported head_dim or tile */
+  BSFA_ERR_DTYPE = 3,        /* unsupported input or output dtype */
+  BSFA_ERR_ALIGN = 4,        /* pointer or stride breaks the 16-byte row alignment */
+  BSFA_ERR_TABLE = 5,        /* threshold table missing or its header disagrees with the problem */
+  BSFA_ERR_UNSUPPORTED = 6,  /* valid request outside what this build implements */
+  BSFA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
+} bsfa_status;
+
+typedef enum {
+  BSFA_GATE_DENSE = 0,       /* keep every block: the dense path */
+  BSFA_GATE_ABSOLUTE = 1,    /* keep iff s_max >= T_eff(h, i) */
+  BSFA_GATE_RELATIVE = 2     /* keep iff max_r(rowmax_j[r] - m[r]) >= log_lambda */
+} bsfa_gate_mode;
+
+typedef enum { BSFA_BF16 = 0, BSFA_FP32 = 1 } bsfa_dtype;
+
+/* One causal prefill self-attention call (one layer). */
+typedef struct {
+  int32_t batch;             /* B >= 0 */
+  int32_t seqlen;            /* N >= 0 query tokens = key tokens; need not be a tile multiple */
+  int32_t heads_q;           /* Hq >= 1 */
+  int32_t heads_kv;          /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
+  int32_t head_dim;          /* d: 64 or 128 */
+  int32_t block_q;           /* Bq: 64 or 128 (gate tile rows) */
+  int32_t block_k;           /* Bk: 64 (gate tile columns) */
+  float softmax_scale;       /* > 0, or 0 for 1/sqrt(head_dim); applied to fp32 scores */
+  int32_t in_dtype;          /* bsfa_dtype of Q, K, V: BSFA_BF16 */
+  int32_t out_dtype;         /* bsfa_dtype of O: BSFA_BF16 or BSFA_FP32 */
+  int64_t q_stride[3];       /* element strides of Q for batch, token, head */
+  int64_t k_stride[3];       /* element strides of K */
+  int64_t v_stride[3];       /* element strides of V */
+  int64_t o_stride[3];       /* element strides of O */
+} bsfa_problem;
+
+/* One layer's threshold table (the offline calibration artifact), fp32 in device memory.
+ * T holds n_budgets slices, each [heads_q][t_len] row-major; entries may be +-INFINITY.
+ * The header fields record the tile semantics the table was calibrated for and must agree
+ * with the problem: a threshold's meaning changes with the model and the tile shape
+ * ("Block Sparse Flash Attention", Method > Key Designs 1, last paragraph). */
+typedef struct {
+  const float* T;            /* device, 4-byte aligned, n_budgets * heads_q * t_len floats */
+  int32_t n_budgets;         /* >= 1 */
+  int32_t t_len;             /* >= 1 calibrated query blocks; blocks i >= t_len use t_len - 1 */
+  int32_t heads_q;           /* must equal problem heads_q */
+  int32_t block_q;           /* must equal problem block_q */
+  int32_t block_k;           /* must equal problem block_k */
+  int32_t head_dim;          /* must equal problem head_dim */
+  float softmax_scale;       /* must equal the effective scale within 1e-6 relative */
+} bsfa_table;
+
+/* Gated causal prefill attention (the method's hot path).
+ *   p             problem description (host memory, read during the call only)
+ *   Q             device [B][N][Hq][d] bf16;  K, V: device [B][N][Hkv][d] bf16
+ *   table         threshold table; required for ABSOLUTE, ignored otherwise (may be NULL)
+ *   budget_slice  which table slice (0 <= budget_slice < n_budgets) for ABSOLUTE
+ *   gate_mode     bsfa_gate_mode
+ *   log_lambda    RELATIVE only: ln(lambda); -INFINITY (lambda = 0) never skips
+ *   O             device [B][N][Hq][d] in out_dtype, written for every row
+ *   kept_counts   device int32 [B][Hq][ceil(N/Bq)] or NULL: number of kept OFF-diagonal
+ *                 blocks per (b, h, i); the diagonal region is not counted ("Block Sparse
+ *                 Flash Attention", A Worked Example: it does not consume the budget)
+ *   kept_total    device uint64 scalar or NULL: sum of kept_counts (zeroed, then accumulated,
+ *                 on `stream`)
+ *   debug_block_stat  device fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] or NULL: per visible block,
+ *                 the gate statistic in scaled-score units (ABSOLUTE and DENSE: s_max;
+ *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
+ *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
+ *   stream        hipStream_t
+ * Returns BSFA_OK or an error status (see the conventions above). */
+bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
+                         const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
+                         float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
+                         float* debug_block_stat, void* stream);
+
+/* The heavy step of offline threshold calibration ("Block Sparse Flash Attention", Method >
+ * Key Designs 1): for every (b, h, i), the maxima of the scaled scores over each visible
+ * off-diagonal key block j < n_off(i), and for each budget k their k-th highest value
+ * (1-indexed; -INFINITY when n_off(i) < k). Averaging over calibration samples is left to the
+ * caller.
+ *   p             problem description; V strides, o_stride and out_dtype are ignored
+ *   Q, K          as for bsfa_prefill
+ *   budgets_host  host int32 [n_budgets], each >= 1
+ *   n_budgets     1 .. 16
+ *   kth_out       device fp32 [n_budgets][B][Hq][ceil(N/Bq)]
+ *   stream        hipStream_t
+ * This build supports seqlen up to 262144 here (BSFA_ERR_UNSUPPORTED beyond). */
+bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
+                                    const int32_t* budgets_host, int32_t n_budgets,
+                                    float* kth_out, void* stream);
+
+/* Static description of a status code. Never NULL. */
+const char* bsfa_status_string(int32_t status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* bsfa_last_error(void);
+
+/* ABI version: (major << 16) | minor. */
+int32_t bsfa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BSFA_H_ */

@@ -1,0 +1,190 @@
+"""The C ABI without a GPU: libbsfa.so loads, exports every symbol include/bsfa.h declares, and
+rejects invalid calls on the host with the documented status before anything is enqueued.
+
+No call here reaches a kernel launch: every call fails validation first (pointers are never
+dereferenced on the host).
+"""
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_sparse_long_amd import _lib
+from block_sparse_long_amd.table import ThresholdTable
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "bsfa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libbsfa.so not built (python -m block_sparse_long_amd.build_lib)")
+
+FAKE = 0x10000          # 16-byte aligned stand-in address, never dereferenced on these paths
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(bsfa_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(_lib.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load_library()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    for s in range(8):
+        assert _lib.bsfa_status_string(s)
+    assert _lib.bsfa_status_string(99) == "unknown status"
+    assert _lib.bsfa_version() >> 16 == 1
+
+
+def problem(B=1, N=256, Hq=4, Hkv=2, d=128, bq=128, bk=64, out=_lib.BSFA_BF16):
+    p = _lib.BsfaProblem()
+    p.batch, p.seqlen, p.heads_q, p.heads_kv, p.head_dim = B, N, Hq, Hkv, d
+    p.block_q, p.block_k = bq, bk
+    p.softmax_scale = 0.0
+    p.in_dtype, p.out_dtype = _lib.BSFA_BF16, out
+    p.q_stride[:] = (N * Hq * d, Hq * d, d)
+    p.k_stride[:] = (N * Hkv * d, Hkv * d, d)
+    p.v_stride[:] = (N * Hkv * d, Hkv * d, d)
+    p.o_stride[:] = (N * Hq * d, Hq * d, d)
+    return p
+
+
+def table(Hq=4, bq=128, bk=64, d=128, scale=None, n_budgets=2, t_len=2, ptr=FAKE):
+    t = _lib.BsfaTable()
+    t.T = ptr
+    t.n_budgets, t.t_len, t.heads_q, t.block_q, t.block_k, t.head_dim = n_budgets, t_len, Hq, bq, bk, d
+    t.softmax_scale = 1 / math.sqrt(d) if scale is None else scale
+    return t
+
+
+def call_prefill(p, tbl=None, slice_=0, mode=_lib.BSFA_GATE_DENSE, log_lambda=-math.inf,
+                 q=FAKE, k=FAKE, v=FAKE, o=FAKE, counts=None, total=None, dbg=None):
+    lib = _lib.load_library()
+    return lib.bsfa_prefill(ctypes.byref(p), q, k, v, ctypes.byref(tbl) if tbl else None, slice_,
+                            mode, log_lambda, o, counts, total, dbg, None)
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda p: setattr(p, "heads_kv", 3), _lib.BSFA_ERR_SHAPE),
+    (lambda p: setattr(p, "head_dim", 96), _lib.BSFA_ERR_SHAPE),
+    (lambda p: setattr(p, "block_k", 32), _lib.BSFA_ERR_SHAPE),
+    (lambda p: setattr(p, "block_q", 256), _lib.BSFA_ERR_SHAPE),
+    (lambda p: setattr(p, "in_dtype", _lib.BSFA_FP32), _lib.BSFA_ERR_DTYPE),
+    (lambda p: setattr(p, "out_dtype", 7), _lib.BSFA_ERR_DTYPE),
+    (lambda p: setattr(p, "seqlen", -1), _lib.BSFA_ERR_ARG),
+    (lambda p: setattr(p, "heads_q", 0), _lib.BSFA_ERR_ARG),
+    (lambda p: setattr(p, "softmax_scale", -1.0), _lib.BSFA_ERR_ARG),
+    (lambda p: setattr(p, "softmax_scale", float("nan")), _lib.BSFA_ERR_ARG),
+    (lambda p: p.q_stride.__setitem__(1, 100), _lib.BSFA_ERR_ALIGN),
+    (lambda p: p.o_stride.__setitem__(2, -128), _lib.BSFA_ERR_ARG),
+])
+def test_problem_validation(mutate, status):
+    p = problem()
+    mutate(p)
+    assert call_prefill(p) == status
+    assert _lib.bsfa_last_error() != ""
+
+
+def test_fp32_output_needs_only_4_element_alignment():
+    p = problem(out=_lib.BSFA_FP32)
+    p.o_stride[:] = (256 * 4 * 132, 4 * 132, 132)      # 132 floats: 16-byte rows, not 32-byte
+    assert call_prefill(p, o=FAKE + 1) == _lib.BSFA_ERR_ALIGN   # misaligned O base
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_misaligned_or_null_pointers(which):
+    p = problem()
+    assert call_prefill(p, **{which: FAKE + 8}) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, **{which: None}) == _lib.BSFA_ERR_ARG
+
+
+def test_gate_mode_and_lambda_validation():
+    p = problem()
+    assert call_prefill(p, mode=3) == _lib.BSFA_ERR_ARG
+    assert call_prefill(p, mode=_lib.BSFA_GATE_RELATIVE, log_lambda=float("nan"), q=None) == _lib.BSFA_ERR_ARG
+    assert call_prefill(p, mode=_lib.BSFA_GATE_RELATIVE, log_lambda=math.inf, q=None) == _lib.BSFA_ERR_ARG
+
+
+@pytest.mark.parametrize("tbl,slice_", [
+    (None, 0),
+    (table(ptr=None), 0),
+    (table(ptr=FAKE + 2), 0),
+    (table(), 2),
+    (table(), -1),
+    (table(n_budgets=0), 0),
+    (table(t_len=0), 0),
+    (table(Hq=8), 0),
+    (table(bq=64), 0),
+    (table(d=64), 0),
+    (table(scale=0.1), 0),
+])
+def test_table_validation(tbl, slice_):
+    status = call_prefill(problem(), tbl=tbl, slice_=slice_, mode=_lib.BSFA_GATE_ABSOLUTE, q=None)
+    expect = _lib.BSFA_ERR_ALIGN if (tbl is not None and tbl.T == FAKE + 2) else _lib.BSFA_ERR_TABLE
+    assert status == expect
+
+
+def test_table_checked_before_pointers():
+    # the table header is validated against the problem (a threshold is bound to its tile shape)
+    assert call_prefill(problem(), tbl=table(bq=64), mode=_lib.BSFA_GATE_ABSOLUTE,
+                        q=None) == _lib.BSFA_ERR_TABLE
+
+
+def test_misaligned_outputs():
+    p = problem()
+    assert call_prefill(p, counts=FAKE + 2) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, total=FAKE + 4) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, dbg=FAKE + 1) == _lib.BSFA_ERR_ALIGN
+
+
+def call_calib(p, budgets, q=FAKE, k=FAKE, out=FAKE):
+    lib = _lib.load_library()
+    arr = (ctypes.c_int32 * max(1, len(budgets)))(*budgets)
+    return lib.bsfa_calibrate_blockmax(ctypes.byref(p), q, k, arr if budgets is not None else None,
+                                       len(budgets), out, None)
+
+
+def test_calibrate_validation():
+    assert call_calib(problem(), []) == _lib.BSFA_ERR_ARG
+    assert call_calib(problem(), [0]) == _lib.BSFA_ERR_ARG
+    assert call_calib(problem(), list(range(1, 18))) == _lib.BSFA_ERR_ARG
+    assert call_calib(problem(N=262144 + 64), [4]) == _lib.BSFA_ERR_UNSUPPORTED
+    assert call_calib(problem(), [4], q=FAKE + 4) == _lib.BSFA_ERR_ALIGN
+    assert call_calib(problem(), [4], out=None) == _lib.BSFA_ERR_ARG
+    p = problem()
+    p.head_dim = 80
+    assert call_calib(p, [4]) == _lib.BSFA_ERR_SHAPE
+
+
+def test_table_file_round_trip(tmp_path):
+    T = np.array([[[-np.inf, 1.5, 2.25]], [[0.0, np.inf, -3.0]]], dtype=np.float32)
+    t = ThresholdTable(T=T, budgets=[4, 16], block_q=64, block_k=64, head_dim=64,
+                       softmax_scale=0.125, calib_seqlen=192, seeds=[1, 2], generator="x")
+    path = tmp_path / "t.bin"
+    t.save(str(path))
+    u = ThresholdTable.load(str(path))
+    np.testing.assert_array_equal(u.T, T)
+    assert u.budgets == [4, 16] and u.slice_index(16) == 1 and u.t_len == 3 and u.heads_q == 1
+    assert (u.block_q, u.block_k, u.head_dim, u.softmax_scale) == (64, 64, 64, 0.125)
+
+
+def test_stored_tables_load(golden_dir):
+    for f in os.listdir(golden_dir):
+        if f.startswith("thresholds_") and f.endswith(".bin"):
+            t = ThresholdTable.load(os.path.join(golden_dir, f))
+            assert t.T.dtype == np.float32 and len(t.budgets) == t.T.shape[0]
+            # -inf exactly where a query block has fewer than k off-diagonal candidates
+            for kk, k in enumerate(t.budgets):
+                for i in range(t.t_len):
+                    n_off = (i * t.block_q) // t.block_k
+                    assert np.isneginf(t.T[kk, :, i]).all() == (n_off < k)

@@ -1,0 +1,340 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle on the same seeded inputs.
+
+Bar: keep decisions bit-exact outside the 1e-2 near-tie band, kept counts exact, output
+max-abs <= 1e-2 and mean-abs <= 1e-3 (bf16 inputs, float32 oracle). Bitwise identities:
+DENSE == ABSOLUTE(T = -inf) == RELATIVE(lambda = 0); NaN in the V rows of skipped blocks
+changes nothing; back-to-back launches agree bit for bit.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_amd import _lib, synth
+from block_sparse_long_amd.table import ThresholdTable
+from gpu_util import bf16_pair, check_parity, make_table, run_device
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _cuda():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_loaded():
+    _cuda()
+    _lib.load_library()
+
+
+def golden_table(name):
+    return ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{name}.bin"))
+
+
+# ---------------------------------------------------------------------------------------------
+# Tiny single-head workload (1K, d = 64, 64x64 tiles, k = 4 calibrated on seeds 1-4)
+# ---------------------------------------------------------------------------------------------
+@pytest.fixture(scope="module")
+def tiny():
+    Q, K, V = synth.make_inputs("tiny_1k", 0)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    return Qd, Kd, Vd, Qh, Kh, Vh
+
+
+def test_tiny_absolute_k4(tiny):
+    Qd, Kd, Vd, Qh, Kh, Vh = tiny
+    tab = golden_table("tiny_1k")
+    dev = run_device(Qd, Kd, Vd, block_q=64, mode="absolute", table=tab)
+    r = check_parity(dev, Qh, Kh, Vh, block_q=64, mode="absolute", table=tab)
+    assert 0 < dev["total"] < sum(oracle.key_block_range(i, 1024, 64, 64)[0] for i in range(16))
+    print(f"tiny k=4 kept {dev['total']} of 120 off-diagonal blocks")
+
+
+@pytest.mark.parametrize("T,expect", [(-math.inf, "all"), (math.inf, "none")])
+def test_tiny_threshold_limits(tiny, T, expect):
+    Qd, Kd, Vd, Qh, Kh, Vh = tiny
+    tab = make_table(np.full((1, 1, 16), T), 64, 64)
+    dev = run_device(Qd, Kd, Vd, block_q=64, mode="absolute", table=tab)
+    check_parity(dev, Qh, Kh, Vh, block_q=64, mode="absolute", table=tab)
+    assert dev["total"] == (120 if expect == "all" else 0)
+
+
+def test_tiny_dense(tiny):
+    Qd, Kd, Vd, Qh, Kh, Vh = tiny
+    dev = run_device(Qd, Kd, Vd, block_q=64, mode="dense")
+    check_parity(dev, Qh, Kh, Vh, block_q=64, mode="dense")
+
+
+# ---------------------------------------------------------------------------------------------
+# Mid-size cases covering every workgroup shape, ragged tails and GQA
+# ---------------------------------------------------------------------------------------------
+SHAPES = {  # name: (B, N, Hq, Hkv, d, Bq)
+    "llama_like_ragged": (1, 1000, 8, 2, 128, 128),       # 4 waves: 2 heads x 128 rows
+    "d128_bq64_g4": (1, 700, 8, 2, 128, 64),              # 4 waves: 4 heads x 64 rows
+    "d64_bq128_g1": (1, 515, 2, 2, 64, 128),              # 2 waves: 1 head x 128 rows
+    "d64_bq64_g2": (2, 333, 4, 2, 64, 64),                # 2 waves, batch 2
+    "d64_bq64_g1": (1, 200, 1, 1, 64, 64),                # 1 wave
+    "d128_bq64_g1": (1, 130, 2, 2, 128, 64),              # 1 wave, d = 128
+    "g8": (1, 384, 16, 2, 128, 128),                      # G = 8: two workgroups per KV group
+}
+
+
+def _mid_inputs(name, seed):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    if B == 1 and Hq % Hkv == 0 and N > 8:
+        Q, K, V = synth.structured(seed, N, heads_q=Hq, heads_kv=Hkv, d=d, needles=4)
+    else:
+        Q, K, V = synth.uniform_mix(seed, B, N, Hq, Hkv, d)
+        Q = Q * 1.5
+    return Q, K, V
+
+
+@pytest.fixture(scope="module")
+def mid_tables():
+    cache = {}
+
+    def get(name, budgets=(2, 4)):
+        key = (name, tuple(budgets))
+        if key not in cache:
+            B, N, Hq, Hkv, d, Bq = SHAPES[name]
+            samples = []
+            for s in (101, 102):
+                Q, K, _ = _mid_inputs(name, s)
+                _, (Qh, Kh) = bf16_pair(Q, K)
+                samples.append((Qh, Kh))
+            T = oracle.calibrate(samples, block_q=Bq, block_k=64, budgets=list(budgets),
+                                 scale=float(np.float32(1 / math.sqrt(d))))
+            cache[key] = make_table(T, Bq, d, list(budgets))
+        return cache[key]
+    return get
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("mode", ["dense", "absolute", "relative"])
+def test_mid_parity(name, mode, mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, V = _mid_inputs(name, 7)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    kw = {}
+    if mode == "absolute":
+        kw = dict(table=mid_tables(name), budget_slice=1)
+    elif mode == "relative":
+        kw = dict(log_lambda=math.log(1e-3))
+    dev = run_device(Qd, Kd, Vd, block_q=Bq, mode=mode, **kw)
+    check_parity(dev, Qh, Kh, Vh, block_q=Bq, mode=mode, **kw)
+
+
+@pytest.mark.parametrize("lam", [1e-4, 1e-2, 1e-1])
+def test_relative_gate_lambdas(lam):
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    Q, K, V = _mid_inputs("llama_like_ragged", 8)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    dev = run_device(Qd, Kd, Vd, block_q=Bq, mode="relative", log_lambda=math.log(lam))
+    check_parity(dev, Qh, Kh, Vh, block_q=Bq, mode="relative", log_lambda=math.log(lam))
+
+
+def test_budget_slices_switch_per_call(mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    tab = mid_tables("llama_like_ragged", budgets=(1, 2, 4))
+    Q, K, V = _mid_inputs("llama_like_ragged", 9)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    totals = []
+    for sl in range(3):
+        dev = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=sl)
+        check_parity(dev, Qh, Kh, Vh, block_q=Bq, mode="absolute", table=tab, budget_slice=sl)
+        totals.append(dev["total"])
+    assert totals[0] <= totals[1] <= totals[2]
+
+
+# ---------------------------------------------------------------------------------------------
+# Bitwise identities
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["llama_like_ragged", "d64_bq64_g2", "d64_bq64_g1"])
+def test_dense_equals_minus_inf_and_lambda_zero_bitwise(name):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, V = _mid_inputs(name, 10)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    nqb = -(-N // Bq)
+    dense = run_device(Qd, Kd, Vd, block_q=Bq, mode="dense", dbg=False)["O"]
+    dense16 = run_device(Qd, Kd, Vd, block_q=Bq, mode="dense", dbg=False,
+                         out_dtype=torch.bfloat16)["O"]
+    assert torch.equal(dense16, dense.to(torch.bfloat16))     # bf16 out = RNE(fp32 out)
+    tab = make_table(np.full((1, Hq, nqb), -np.inf), Bq, d)
+    absm = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab)
+    rel0 = run_device(Qd, Kd, Vd, block_q=Bq, mode="relative", log_lambda=-math.inf)
+    assert torch.equal(dense, absm["O"])
+    assert torch.equal(dense, rel0["O"])
+    n_off_total = B * Hq * sum(oracle.key_block_range(i, N, Bq, 64)[0] for i in range(nqb))
+    assert absm["total"] == rel0["total"] == n_off_total
+
+
+def test_poisoned_skipped_values_bitwise(mid_tables):
+    # a skipped block loads no V and adds nothing: with NaN in the V rows of key block j0,
+    # every (head, query block) that skips j0 (outside the near-tie band) keeps a
+    # bit-identical output; the rows that keep j0 are not compared
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    tab = mid_tables("llama_like_ragged")
+    Q, K, V = _mid_inputs("llama_like_ragged", 11)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    ref = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=0)
+    G = Hq // Hkv
+    stat = ref["stat"]
+    nqb = stat.shape[2]
+    checked = 0
+    for j0 in (1, 3, 6):
+        g0 = 0
+        Vp = Vd.clone()
+        Vp[:, j0 * 64:(j0 + 1) * 64, g0, :] = float("nan")
+        pois = run_device(Qd, Kd, Vp, block_q=Bq, mode="absolute", table=tab, budget_slice=0)
+        np.testing.assert_array_equal(ref["counts"], pois["counts"])
+        for h in range(g0 * G, (g0 + 1) * G):
+            for i in range(nqb):
+                n_off = oracle.key_block_range(i, N, Bq, 64)[0]
+                thr = tab.T[0][h, min(i, tab.t_len - 1)]
+                if j0 < n_off and stat[0, h, i, j0] < thr - 2e-2:
+                    rows = slice(i * Bq, min((i + 1) * Bq, N))
+                    assert torch.equal(ref["O"][:, rows, h], pois["O"][:, rows, h]), (j0, h, i)
+                    checked += 1
+                elif j0 < n_off and stat[0, h, i, j0] >= thr:
+                    rows = slice(i * Bq, min((i + 1) * Bq, N))
+                    assert torch.isnan(pois["O"][:, rows, h]).any()     # kept: V was read
+    assert checked >= 8
+
+
+def test_back_to_back_launches_bitwise(mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    tab = mid_tables("llama_like_ragged").to_device("cuda")
+    Q, K, V = _mid_inputs("llama_like_ragged", 12)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    outs = [torch.empty_like(Qd) for _ in range(100)]
+    counts = torch.empty((100, B, Hq, -(-N // Bq)), dtype=torch.int32, device="cuda")
+    for t in range(100):
+        _lib.bsfa_prefill(Qd, Kd, Vd, outs[t], block_q=Bq, gate_mode="absolute", table=tab,
+                          budget_slice=t % 2, kept_counts=counts[t])
+    torch.cuda.synchronize()
+    for t in range(2, 100):
+        assert torch.equal(outs[t], outs[t % 2])
+        assert torch.equal(counts[t], counts[t % 2])
+
+
+# ---------------------------------------------------------------------------------------------
+# Layouts, output dtype, empty inputs
+# ---------------------------------------------------------------------------------------------
+def test_head_major_strided_layout_and_fp32_output(mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES["d64_bq64_g2"]
+    Q, K, V = _mid_inputs("d64_bq64_g2", 13)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    # a [B, H, N, d] caller: pass permuted views (token and head strides swap)
+    Qt = Qd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    Kt = Kd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    Vt = Vd.permute(0, 2, 1, 3).contiguous().permute(0, 2, 1, 3)
+    assert Qt.stride(1) == d and not Qt.is_contiguous()
+    tab = mid_tables("d64_bq64_g2")
+    dev = run_device(Qt, Kt, Vt, block_q=Bq, mode="absolute", table=tab, out_dtype=torch.float32)
+    assert dev["O"].dtype == torch.float32
+    check_parity(dev, Qh, Kh, Vh, block_q=Bq, mode="absolute", table=tab)
+    base = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab,
+                      out_dtype=torch.bfloat16)
+    assert torch.equal(base["O"], dev["O"].to(torch.bfloat16))
+
+
+@pytest.mark.parametrize("B,N", [(0, 128), (1, 0)])
+def test_empty_inputs(B, N):
+    Q = torch.zeros((B, N, 2, 64), dtype=torch.bfloat16, device="cuda")
+    K = torch.zeros((B, N, 1, 64), dtype=torch.bfloat16, device="cuda")
+    total = torch.full((1,), 99, dtype=torch.int64, device="cuda")
+    O = _lib.bsfa_prefill(Q, K, K, block_q=64, gate_mode="dense", kept_total=total)
+    torch.cuda.synchronize()
+    assert O.shape == Q.shape and int(total.item()) == 0
+
+
+def test_single_token():
+    Q, K, V = synth.uniform_mix(5, 1, 1, 4, 1, 128)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    dev = run_device(Qd, Kd, Vd, block_q=128, mode="relative", log_lambda=math.log(1e-2))
+    check_parity(dev, Qh, Kh, Vh, block_q=128, mode="relative", log_lambda=math.log(1e-2))
+    np.testing.assert_allclose(dev["O"].float().cpu().numpy()[0, 0, 0], Vh[0, 0, 0], atol=1e-2)
+
+
+# ---------------------------------------------------------------------------------------------
+# Calibration kernel
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", ["llama_like_ragged", "d64_bq64_g2", "g8"])
+def test_calibration_kernel_matches_oracle(name):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, _ = _mid_inputs(name, 14)
+    (Qd, Kd), (Qh, Kh) = bf16_pair(Q, K)
+    budgets = [1, 2, 3, 5, 8]
+    kth = _lib.bsfa_calibrate_blockmax(Qd, Kd, budgets, block_q=Bq)
+    torch.cuda.synchronize()
+    kth = kth.cpu().numpy()
+    sm = oracle.off_diagonal_block_maxima(Qh, Kh, block_q=Bq, block_k=64)
+    for kk, k in enumerate(budgets):
+        for b in range(B):
+            for h in range(Hq):
+                for i in range(sm.shape[2]):
+                    n_off = oracle.key_block_range(i, N, Bq, 64)[0]
+                    ref = oracle.kth_highest(sm[b, h, i], n_off, k)
+                    got = kth[kk, b, h, i]
+                    if math.isinf(ref):
+                        assert got == ref
+                    else:
+                        assert abs(got - ref) <= 1e-3, (k, b, h, i, got, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# Full-size workloads: the whole call on the device, the oracle on sampled query blocks
+# ---------------------------------------------------------------------------------------------
+def _sampled_blocks(nqb, k, extra=()):
+    s = {0, 1, max(0, k // 2 - 1), k // 2, nqb // 4, nqb // 2 - 1, nqb // 2, 3 * nqb // 4, nqb - 1}
+    s.update(extra)
+    return sorted(x for x in s if 0 <= x < nqb)
+
+
+def _full(config, n=None):
+    Q, K, V = synth.make_inputs(config, 0, n=n)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    return Qd, Kd, Vd, Qh, Kh, Vh
+
+
+def _full_check(config, mode, slices=(0,), log_lambdas=(-math.inf,), blocks=None):
+    c = synth.CONFIGS[config]
+    Qd, Kd, Vd, Qh, Kh, Vh = _full(config)
+    nqb = -(-c["n"] // c["block_q"])
+    tab = golden_table(config) if mode == "absolute" else None
+    for sl in slices:
+        for ll in log_lambdas:
+            k = tab.budgets[sl] if tab is not None else 0
+            qbs = blocks if blocks is not None else _sampled_blocks(nqb, k)
+            dev = run_device(Qd, Kd, Vd, block_q=c["block_q"], mode=mode, table=tab,
+                             budget_slice=sl, log_lambda=ll)
+            check_parity(dev, Qh, Kh, Vh, block_q=c["block_q"], mode=mode, table=tab,
+                         budget_slice=sl, log_lambda=ll, query_blocks=qbs)
+            n_off = sum(oracle.key_block_range(i, c["n"], c["block_q"], 64)[0]
+                        for i in range(nqb))
+            print(f"{config} {mode} slice={sl} loglam={ll:.3f}: kept fraction "
+                  f"{dev['total'] / (c['heads_q'] * n_off):.4f}", flush=True)
+
+
+def test_full_llama_16k_k32():
+    _full_check("llama_16k", "absolute")
+
+
+def test_full_llama_32k_budget_sweep():
+    _full_check("llama_32k_sweep", "absolute", slices=(0, 1, 2))
+
+
+def test_full_llama_128k_k64_reuses_last_threshold():
+    # 511 is the last calibrated query block (64K), 512 the first that reuses its threshold
+    _full_check("llama_128k", "absolute", blocks=[0, 31, 32, 511, 512, 1023])
+
+
+def test_full_llama_64k_relative():
+    _full_check("llama_64k_relative", "relative",
+                log_lambdas=(math.log(1e-4), math.log(1e-2)), blocks=[0, 1, 128, 255, 511])
