@@ -26,6 +26,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed fp32 VALU forms stay off: plain float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in VGPRs: the scores feed the softmax VALU directly instead of being
+    # copied out of accumulation registers
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

@@ -41,88 +41,134 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+// O^T += V^T P^T with the accumulator pinned to AGPRs (inline asm): the score MFMAs write
+// VGPRs, which the softmax reads directly, while O, touched only by these MFMAs, the rare
+// rescale and the epilogue, lives in the accumulation registers. The compiler cannot see
+// inside the asm, so the hazards around it are resolved by hand:
+//   * consecutive accumulations into the same full accumulator need no wait states;
+//   * P (SrcB) is written by VALU: pv_operands_ready() puts wait states between the last such
+//     write and the first MFMA, and keep_alive() holds P's registers until the block ends so
+//     no VALU write can land in a register an issued MFMA is still reading;
+//   * VALU access to O after these MFMAs goes through acc_ready(), which waits out the
+//     longest MFMA-result latency first.
+__device__ __forceinline__ void mfma_acc(f32x16& o, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
-// Position of key k (0..63) inside a transposed V row: within each group of 16 keys, the 8
-// keys one lane half feeds to one MFMA k-step (keys 4h..4h+3 and 8+4h..8+4h+3 of the group)
-// become contiguous, matching the order in which the P^T operand holds them.
-__device__ __forceinline__ int vpos(int k) {
-  return (k & ~15) | (((k >> 2) & 1) << 3) | (((k >> 3) & 1) << 2) | (k & 3);
+__device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
+__device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
+
+// max / sum of x over lanes l and l^32 (the two halves holding the same query row)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return fmaxf(bits_f(r[0]), bits_f(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(f_bits(x), f_bits(x), false, false);
+  return bits_f(r[0]) + bits_f(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return bits_f(__builtin_amdgcn_update_dpp(0, f_bits(x), CTRL, 0xf, 0xf, false));
+}
+
+// Wave-uniform max over the 64 lanes: a butterfly within each row of 16 lanes (DPP quad
+// permutes, half-row and row mirrors), then the four row results through readlane.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp<0xB1>(x));     // quad_perm [1,0,3,2]
+  x = fmaxf(x, dpp<0x4E>(x));     // quad_perm [2,3,0,1]
+  x = fmaxf(x, dpp<0x141>(x));    // row_half_mirror
+  x = fmaxf(x, dpp<0x140>(x));    // row_mirror
+  const float r0 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 0));
+  const float r1 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 16));
+  const float r2 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 32));
+  const float r3 = bits_f(__builtin_amdgcn_readlane(f_bits(x), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
 template <int D>
 struct Tile {
-  static constexpr int KSTR = D + 8;        // K tile row stride in LDS (bf16), 16-byte padded
-  static constexpr int VSTR = BK + 8;       // V^T tile row stride in LDS (bf16)
+  static constexpr int CPR = D / 8;         // 16-byte chunks of data per row (16 or 8)
+  static constexpr int STR = D + 8;         // LDS row stride in bf16: one 16-byte pad chunk
+  static constexpr int CPS = CPR + 1;       // chunks per padded row
+  static constexpr int INSTR = 64 * CPS / 64;   // 1 KB loads per 64-row tile (17 or 9)
   static constexpr int KS = D / 16;         // QK k-steps over d
   static constexpr int MD = D / 32;         // PV M-blocks over d
-  static constexpr int CPR = D / 8;         // 16-byte chunks per K/V row
+  static constexpr int ELEMS = 64 * STR;    // bf16 per 64-row tile
 };
 
-// K tile: global [64 keys][D] -> registers -> LDS [key][D] (padded rows).
-template <int D, int NT>
-struct KStage {
-  static constexpr int PER = BK * Tile<D>::CPR / NT;
-  uint4 r[PER];
-  __device__ __forceinline__ void load(const __bf16* base, long long kst, int nvalid, int tid) {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * NT;
-      const int row = c / Tile<D>::CPR, col = c % Tile<D>::CPR;
-      const uint4 x = *reinterpret_cast<const uint4*>(base + min(row, nvalid - 1) * kst + col * 8);
-      r[it] = row < nvalid ? x : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(__bf16* sk, int tid) const {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int c = tid + it * NT;
-      const int row = c / Tile<D>::CPR, col = c % Tile<D>::CPR;
-      *reinterpret_cast<uint4*>(sk + row * Tile<D>::KSTR + col * 8) = r[it];
-    }
-  }
-};
+// LDS tiles hold 64 rows of D bf16 with a 16-byte pad per row: consecutive rows start 4 banks
+// apart, so the rows one MFMA operand read touches spread over the banks, and every fragment
+// address is a per-lane base plus a compile-time offset.
+template <int D>
+__device__ __forceinline__ int elem_off(int r, int c) {
+  return r * Tile<D>::STR + (c << 3);
+}
 
-// V tile: global [64 keys][D] -> registers -> LDS V^T [D][64 permuted keys]. Each work item is
-// a key pair (2kp, 2kp+1) times 8 dims; the pair lands in one 32-bit LDS word per dim.
-template <int D, int NT>
-struct VStage {
-  static constexpr int PER = 32 * Tile<D>::CPR / NT;
-  uint4 a[PER], b[PER];
-  __device__ __forceinline__ void load(const __bf16* base, long long vst, int nvalid, int tid) {
+// Direct global -> LDS copy of a 64-row tile, 1 KB per instruction: lane l of instruction k
+// fills padded chunk q = 64k + l (row q / CPS, column q % CPS), fetching the matching global
+// chunk; pad chunks re-fetch the row's last chunk. Rows at or past `valid` re-read row
+// valid - 1 (their scores are masked and their P weights are zero). Wave w of NW issues
+// instructions k = w + NW*m for a fixed m range, so every wave runs the same straight-line
+// code; instructions past the tile's INSTR land in the spare space of a tile buffer sized by
+// tile_elems<D, NW>() and fetch clamped, valid addresses.
+template <int D, int NW>
+constexpr int tile_instr_per_wave() {
+  return (Tile<D>::INSTR + NW - 1) / NW;
+}
+template <int D, int NW>
+constexpr int tile_elems() {
+  return tile_instr_per_wave<D, NW>() * NW * 512;
+}
+
+template <int D, int NW>
+__device__ __forceinline__ void wg_copy_tile(const __bf16* gbase, long long gst, int valid,
+                                             __bf16* tile, int w, int lane) {
+  constexpr int CPR = Tile<D>::CPR, CPS = Tile<D>::CPS;
 #pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int item = tid + it * NT;
-      const int kp = item & 31, dc = item >> 5;
-      const int k0 = 2 * kp;
-      const uint4 xa = *reinterpret_cast<const uint4*>(base + min(k0, nvalid - 1) * vst + dc * 8);
-      const uint4 xb =
-          *reinterpret_cast<const uint4*>(base + min(k0 + 1, nvalid - 1) * vst + dc * 8);
-      a[it] = k0 < nvalid ? xa : make_uint4(0, 0, 0, 0);
-      b[it] = k0 + 1 < nvalid ? xb : make_uint4(0, 0, 0, 0);
-    }
+  for (int m = 0; m < tile_instr_per_wave<D, NW>(); ++m) {
+    const int k = w + NW * m;
+    const int q = 64 * k + lane;
+    const int r = min(q / CPS, 63), col = min(q % CPS, CPR - 1);
+    const __bf16* src = gbase + (long long)min(r, valid - 1) * gst + col * 8;
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + k * 512),
+                                     16, 0, 0);
   }
-  __device__ __forceinline__ void store(__bf16* sv, int tid) const {
-#pragma unroll
-    for (int it = 0; it < PER; ++it) {
-      const int item = tid + it * NT;
-      const int kp = item & 31, dc = item >> 5;
-      const int pos = vpos(2 * kp);
-      const uint32_t aw[4] = {a[it].x, a[it].y, a[it].z, a[it].w};
-      const uint32_t bw[4] = {b[it].x, b[it].y, b[it].z, b[it].w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t lo = (aw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        const uint32_t hi = (bw[e >> 1] >> (16 * (e & 1))) & 0xffffu;
-        *reinterpret_cast<uint32_t*>(sv + (dc * 8 + e) * Tile<D>::VSTR + pos) = lo | (hi << 16);
-      }
-    }
-  }
-};
+}
+
+// Wait for this wave's outstanding global loads (including those writing LDS directly).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// 16-byte operand: chunk (2 * kstep + half) of row r.
+template <int D>
+__device__ __forceinline__ bf16x8 lds_frag(const __bf16* tile, int r, int c) {
+  return *reinterpret_cast<const bf16x8*>(tile + elem_off<D>(r, c));
+}
+
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+
+// A operand of O^T += V^T P^T for M-block md and key k-step ks2, read from V in natural
+// [key][d] layout with two transposing reads. In each 16-lane group, lane j points at key
+// kseq(j / 4) and the 4 dims 4 * (j % 4) of the group's 16-dim slice; the hardware then hands
+// lane i the dim (slice + i) at keys kseq(0..3). Lane l ends up with d = md*32 + l%32 and keys
+// 16*ks2 + 4h + {0..3} and 16*ks2 + 8 + 4h + {0..3} (h = l/32): the order in which the S^T
+// accumulator, and so P^T, holds them.
+template <int D>
+__device__ __forceinline__ bf16x8 v_frag(const __bf16* sv, int md, int ks2, int lane) {
+  const int grp = lane >> 4, j = lane & 15, hh = lane >> 5;
+  const int d = md * 32 + (grp & 1) * 16 + 4 * (j & 3);
+  const int key0 = 16 * ks2 + 4 * hh + (j >> 2);
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  const int o0 = key0 * Tile<D>::STR + d;
+  const int o1 = o0 + 8 * Tile<D>::STR;
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sv + o0));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sv + o1));
+  bf16x8 r;
+  r[0] = lo[0]; r[1] = lo[1]; r[2] = lo[2]; r[3] = lo[3];
+  r[4] = hi[0]; r[5] = hi[1]; r[6] = hi[2]; r[7] = hi[3];
+  return r;
+}
 
 // S^T[key][row] for one 64-key tile and the wave's 64 rows: s[mb][nb] holds keys
 // mb*32 + 8*(v/4) + 4*(lane/32) + v%4 and row nb*32 + lane%32 in element v. Both operands come
@@ -142,12 +188,10 @@ __device__ __forceinline__ void qk_tile(const __bf16* sk, const __bf16* sq, f32x
     bf16x8 qb[2];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb)
-      qb[nb] = *reinterpret_cast<const bf16x8*>(sq + (nb * 32 + rl) * Tile<D>::KSTR + ks * 16 +
-                                                8 * hh);
+      qb[nb] = lds_frag<D>(sq, nb * 32 + rl, 2 * ks + hh);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          sk + (mb * 32 + rl) * Tile<D>::KSTR + ks * 16 + 8 * hh);
+      const bf16x8 a = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(a, qb[nb], s[mb][nb]);
     }
@@ -169,8 +213,7 @@ __device__ __forceinline__ void qk_tile_regs(const __bf16* sk, const bf16x8 (&qf
   for (int ks = 0; ks < Tile<D>::KS; ++ks) {
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          sk + (mb * 32 + rl) * Tile<D>::KSTR + ks * 16 + 8 * hh);
+      const bf16x8 a = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(a, qf[nb][ks], s[mb][nb]);
     }
@@ -215,88 +258,187 @@ __device__ __forceinline__ void tile_rowmax(f32x16 (&s)[2][2], float (&rmax)[2],
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][nb][v]);
-    rmax[nb] = fmaxf(mx, __shfl_xor(mx, 32));
+    rmax[nb] = half_max(mx);
   }
 }
 
-// Online-softmax update for a kept tile (BLASST blog, "FlashAttention": running max m, sum l,
-// accumulator O, rescale by exp(m_old - m_new)). The exponent reference mref moves only when a
-// row's true max mt exceeds it by more than kLazy in the exp2 domain ("rescale ... when
-// needed", paper notes, Key Designs 3): exponentials stay <= 2^kLazy, O/l is unchanged, and
-// the O rescale (a VALU pass over the accumulators) becomes rare. mt is the exact running max
-// the relative gate compares against. Writes P^T as bf16 MFMA B operands pb[nb][k-step].
+// Online softmax (BLASST blog, "FlashAttention": running max m, sum l, accumulator O, rescale
+// by exp(m_old - m_new)). The exponent reference mref moves only when a row's true max mt
+// exceeds it by more than kLazy in the exp2 domain ("rescale ... when needed", paper notes, Key
+// Designs 3): exponentials stay <= 2^kLazy and O / l is unchanged, while the O rescale (a VALU
+// pass over the accumulators) becomes rare. mt is the exact running max that the relative gate
+// compares against.
 constexpr float kLazy = 8.f;
 
-template <int MD>
-__device__ __forceinline__ void softmax_tile(const f32x16 (&s)[2][2], const float (&rmax)[2],
-                                             float (&mt)[2], float (&mref)[2], float (&l)[2],
-                                             f32x16 (&o)[MD][2], bf16x8 (&pb)[2][4], float c) {
+struct RowState {
+  float mt[2], mref[2], l[2];
+};
+
+// Update the running max for a kept tile. Returns true (wave-uniform) when the reference
+// moved; alpha then holds the factors O and l must be scaled by after the previous PV.
+__device__ __forceinline__ bool softmax_reference(RowState& st, const float (&rmax)[2], float c,
+                                                  float (&alpha)[2]) {
   float mn[2];
   bool move = false;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    mn[nb] = fmaxf(mt[nb], rmax[nb]);
-    mt[nb] = mn[nb];
-    move |= (mn[nb] - mref[nb]) * c > kLazy;    // false for rows that see nothing (-inf - -inf)
+    mn[nb] = fmaxf(st.mt[nb], rmax[nb]);
+    st.mt[nb] = mn[nb];
+    move |= (mn[nb] - st.mref[nb]) * c > kLazy;    // false for rows that see nothing yet
   }
-  if (__any(move)) {
-    float alpha[2];
+  const bool moved = __any(move);
+  if (moved) {
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const float mu = (mn[nb] == kNegInf) ? 0.f : mn[nb];
-      alpha[nb] = __builtin_amdgcn_exp2f((mref[nb] - mu) * c);   // 0 on the first kept block
-      mref[nb] = mu;
-      l[nb] *= alpha[nb];
+      alpha[nb] = __builtin_amdgcn_exp2f((st.mref[nb] - mu) * c);   // 0 on the first block
+      st.mref[nb] = mu;
     }
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[md][nb][v] *= alpha[nb];
   }
-  // l sums exactly the bf16 weights the PV product uses (two per v_dot2 against (1, 1)), so
-  // O / l is a convex combination of V rows even though P is rounded for the MFMA.
+  return moved;
+}
+
+// Wait states between VALU writes of P and the first PV MFMA reading it.
+__device__ __forceinline__ void pv_operands_ready(bf16x8 (&pb)[2][4]) {
+  asm volatile("s_nop 4"
+               : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[0][2]), "+v"(pb[0][3]),
+                 "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pb[1][2]), "+v"(pb[1][3]));
+}
+
+// Keep P's registers allocated until here (the MFMAs issued before may still read them).
+__device__ __forceinline__ void keep_alive(const bf16x8 (&pb)[2][4]) {
+  asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[0][2]), "v"(pb[0][3]), "v"(pb[1][0]),
+               "v"(pb[1][1]), "v"(pb[1][2]), "v"(pb[1][3]));
+}
+
+// Wait out the MFMA result latency before VALU reads or writes of O (and before the next
+// MFMA after a VALU write of O).
+template <int MD>
+__device__ __forceinline__ void acc_ready(f32x16 (&o)[MD][2]);
+
+template <>
+__device__ __forceinline__ void acc_ready<4>(f32x16 (&o)[4][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[2][0]),
+                 "+a"(o[2][1]), "+a"(o[3][0]), "+a"(o[3][1]));
+}
+
+template <>
+__device__ __forceinline__ void acc_ready<2>(f32x16 (&o)[2][2]) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
+               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
+}
+
+// The PV product of the previous kept tile (MFMA, O^T += V^T P^T) interleaved with the
+// exponentials of the current kept tile (VALU): each MFMA is issued next to one element pair
+// of the softmax, so exp2 / convert / sum run while the matrix core is busy. P is rounded to
+// bf16 for the MFMA and l sums exactly those bf16 weights (two per v_dot2 against (1, 1)), so
+// O / l stays a convex combination of V rows.
+template <int D, bool DO_PV, bool DO_EXP>
+__device__ __forceinline__ void pv_exp_block(const __bf16* sv, const bf16x8 (&pbp)[2][4],
+                                             f32x16 (&o)[D / 32][2], const f32x16 (&s)[2][2],
+                                             const float (&off)[2], float c,
+                                             bf16x8 (&pbn)[2][4], float (&sum)[2], int lane) {
+  constexpr int MD = D / 32;
+  constexpr int NMF = MD * 8;                 // PV MFMAs per tile
+  constexpr int PAIRS = 32;                   // softmax element pairs per lane per tile
+  constexpr int SLOTS = NMF > PAIRS ? NMF : PAIRS;
+  const int rl = lane & 31, hh = lane >> 5;
+  bf16x2 ones;
+  ones[0] = (__bf16)1.f;
+  ones[1] = (__bf16)1.f;
+  bf16x8 va;
+  bf16x8 pbl[2][4];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int ks2 = 0; ks2 < 4; ++ks2) pbl[nb][ks2] = pbp[nb][ks2];
+  if (DO_PV) pv_operands_ready(pbl);
+#pragma unroll
+  for (int q = 0; q < SLOTS; ++q) {
+    if (DO_PV && (q * NMF) % SLOTS == 0) {
+      const int mi = q * NMF / SLOTS;
+      const int ks2 = mi / (MD * 2), md = (mi / 2) % MD, nb = mi % 2;
+      if (nb == 0) va = v_frag<D>(sv, md, ks2, lane);
+      mfma_acc(o[md][nb], va, pbl[nb][ks2]);
+    }
+    if (DO_EXP && (q * PAIRS) % SLOTS == 0) {
+      const int pi = q * PAIRS / SLOTS;
+      const int nb = pi / 16, ks2 = (pi / 4) % 4, e = 2 * (pi % 4);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e], c, off[nb]));
+      const float p1 =
+          __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e + 1], c, off[nb]));
+      bf16x2 pr;
+      pr[0] = (__bf16)p0;
+      pr[1] = (__bf16)p1;
+      sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
+      pbn[nb][ks2][e] = pr[0];
+      pbn[nb][ks2][e + 1] = pr[1];
+    }
+  }
+  if (DO_PV) keep_alive(pbl);
+}
+
+// QK^T of the next tile (MFMA, operands from LDS) interleaved with the exponentials of the
+// current kept tile (VALU): one element pair of the softmax next to each of the 32 MFMAs.
+template <int D, bool DO_EXP>
+__device__ __forceinline__ void qk_exp_block(const __bf16* sk, const __bf16* sq,
+                                             f32x16 (&sn)[2][2], const f32x16 (&s)[2][2],
+                                             const float (&off)[2], float c,
+                                             bf16x8 (&pbn)[2][4], float (&sum)[2], int lane) {
+  constexpr int KS = Tile<D>::KS;
+  constexpr int NMF = KS * 4;                 // QK MFMAs per tile
+  constexpr int PAIRS = 32;
+  constexpr int SLOTS = NMF > PAIRS ? NMF : PAIRS;
+  const int rl = lane & 31, hh = lane >> 5;
   bf16x2 ones;
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float off = -mref[nb] * c;
-    float sum = 0.f;
+  for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) {
+    for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e], c, off));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e + 1], c, off));
-        bf16x2 pr;
-        pr[0] = (__bf16)p0;
-        pr[1] = (__bf16)p1;
-        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
-        pb[nb][ks2][e] = pr[0];
-        pb[nb][ks2][e + 1] = pr[1];
+      for (int v = 0; v < 16; ++v) sn[mb][nb][v] = 0.f;
+  bf16x8 qb[2], ka;
+#pragma unroll
+  for (int q = 0; q < SLOTS; ++q) {
+    if ((q * NMF) % SLOTS == 0) {
+      const int mi = q * NMF / SLOTS;
+      const int ks = mi / 4, mb = (mi / 2) % 2, nb = mi % 2;
+      if (mb == 0 && nb == 0) {
+#pragma unroll
+        for (int n2 = 0; n2 < 2; ++n2)
+          qb[n2] = lds_frag<D>(sq, n2 * 32 + rl, 2 * ks + hh);
       }
+      if (nb == 0)
+        ka = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
+      sn[mb][nb] = mfma32(ka, qb[nb], sn[mb][nb]);
     }
-    l[nb] += sum;
+    if (DO_EXP && (q * PAIRS) % SLOTS == 0) {
+      const int pi = q * PAIRS / SLOTS;
+      const int nb = pi / 16, ks2 = (pi / 4) % 4, e = 2 * (pi % 4);
+      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e], c, off[nb]));
+      const float p1 =
+          __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e + 1], c, off[nb]));
+      bf16x2 pr;
+      pr[0] = (__bf16)p0;
+      pr[1] = (__bf16)p1;
+      sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
+      pbn[nb][ks2][e] = pr[0];
+      pbn[nb][ks2][e + 1] = pr[1];
+    }
   }
 }
 
 template <int D>
 __device__ __forceinline__ void pv_tile(const __bf16* sv, const bf16x8 (&pb)[2][4],
                                         f32x16 (&o)[D / 32][2], int lane) {
-  const int rl = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int ks2 = 0; ks2 < 4; ++ks2) {
-#pragma unroll
-    for (int md = 0; md < Tile<D>::MD; ++md) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-          sv + (md * 32 + rl) * Tile<D>::VSTR + 16 * ks2 + 8 * hh);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) o[md][nb] = mfma32(a, pb[nb][ks2], o[md][nb]);
-    }
-  }
+  const f32x16 s0[2][2] = {};
+  const float off[2] = {0.f, 0.f};
+  bf16x8 dummy[2][4];
+  float sum[2] = {0.f, 0.f};
+  pv_exp_block<D, true, false>(sv, pb, o, s0, off, 0.f, dummy, sum, lane);
 }
 
 struct Unit {
@@ -323,20 +465,12 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
   return r;
 }
 
-// The wave's 64 query rows -> LDS [row][D] (padded rows); rows past N are zero.
+// The wave's 64 query rows -> its own LDS tile (swizzled rows; rows past N re-read row N-1,
+// their scores are masked).
 template <int D>
 __device__ __forceinline__ void stage_q(const __bf16* qbase, long long qst, int row0, int N,
                                         __bf16* sq, int lane) {
-  constexpr int CPR = Tile<D>::CPR;
-#pragma unroll
-  for (int it = 0; it < 64 * CPR / 64; ++it) {
-    const int c = lane + it * 64;
-    const int r = c / CPR, col = c % CPR;
-    const int row = row0 + r;
-    const uint4 x = *reinterpret_cast<const uint4*>(qbase + min(row, N - 1) * qst + col * 8);
-    *reinterpret_cast<uint4*>(sq + r * Tile<D>::KSTR + col * 8) =
-        row < N ? x : make_uint4(0, 0, 0, 0);
-  }
+  wg_copy_tile<D, 1>(qbase + (long long)row0 * qst, qst, N - row0, sq, 0, lane);
 }
 
 template <int D, int BQ, int NW, int GATE>
@@ -347,9 +481,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   constexpr int MD = Tile<D>::MD;
   constexpr bool kGated = GATE != kDense;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][64 * Tile<D>::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BK * Tile<D>::KSTR];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][D * Tile<D>::VSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][tile_elems<D, 1>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<D, NW>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][tile_elems<D, NW>()];
   __shared__ float sGate[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -365,6 +499,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   const bool ragged_rows = (i + 1) * BQ > N;
   const bool want_stat = kGated || a.dbg != nullptr;
   const bool head_leader = (rw == 0) && (lane == 0);
+  const float c = a.c_log2;
 
   const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
   const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
@@ -384,8 +519,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   stage_q<D>(Qb, a.qs[1], row0, N, sQ[w], lane);
   const __bf16* sq = sQ[w];
 
-  // mt: true running row max (over kept blocks); mref: exponent reference (lazy)
-  float mt[2] = {kNegInf, kNegInf}, mref[2] = {kNegInf, kNegInf}, l[2] = {0.f, 0.f};
+  RowState st;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    st.mt[nb] = kNegInf;
+    st.mref[nb] = kNegInf;
+    st.l[nb] = 0.f;
+  }
   f32x16 o[MD][2];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
@@ -393,49 +533,48 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
     for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) o[md][nb][v] = 0.f;
-
-  KStage<D, NT> kst;
-  VStage<D, NT> vst;
+  acc_ready<MD>(o);
 
   auto key_valid = [&](int j) { return min(BK, N - j * BK); };
   auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
-  // Gate statistic of this wave for tile j (raw score units; the scale is applied at the
-  // decision): s_max (ABSOLUTE, DENSE, and the diagonal region in every mode) or
-  // max over rows of (rowmax - running max) (RELATIVE, off-diagonal).
+  // Gate statistic of this wave for tile j, in raw score units (the scale is applied at the
+  // decision): s_max for ABSOLUTE and DENSE and for the diagonal region in every mode; for
+  // RELATIVE off-diagonal tiles, max over the wave's rows of (row max - running max).
   auto publish = [&](int j, const float (&rmax)[2]) {
-    float st;
+    float x;
     if (GATE == kRelative && j < n_off) {
-      float x = kNegInf;
+      x = kNegInf;
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         const int row = row0 + nb * 32 + (lane & 31);
-        const float d = rmax[nb] - mt[nb];
-        x = fmaxf(x, row < N ? d : kNegInf);
+        x = fmaxf(x, row < N ? rmax[nb] - st.mt[nb] : kNegInf);
       }
-      st = wave_max(x);
     } else {
-      st = wave_max(fmaxf(rmax[0], rmax[1]));
+      x = fmaxf(rmax[0], rmax[1]);
     }
-    if (lane == 0) sGate[j & 1][w] = st;
+    const float wst = wave_max(x);
+    if (lane == 0) sGate[j & 1][w] = wst;
   };
 
   // ---- prologue: K_0 staged, S_0 computed and published ----
-  kst.load(Kb, a.ks[1], key_valid(0), tid);
-  kst.store(sK[0], tid);
+  wg_copy_tile<D, NW>(Kb, a.ks[1], key_valid(0), sK[0], w, lane);
+  wait_vmem();
   __syncthreads();
-  if (n_end > 1) kst.load(Kb + (long long)BK * a.ks[1], a.ks[1], key_valid(1), tid);
-  f32x16 sc[2][2];
-  float rc[2];
+  if (n_end > 1) wg_copy_tile<D, NW>(Kb + (long long)BK * a.ks[1], a.ks[1], key_valid(1), sK[1], w, lane);
+  f32x16 sc[2][2];   // scores of the tile being processed
+  float rc[2];       // their row maxima
   qk_tile<D>(sK[0], sq, sc, lane);
   tile_rowmax(sc, rc, tile_masked(0), 0, row0, N, lane);
   if (want_stat) publish(0, rc);
-  if (n_end > 1) kst.store(sK[1], tid);
+  wait_vmem();
   __syncthreads();
 
   int kept = 0;
   bool keep_prev = false;
   bf16x8 pbp[2][4];   // P of the previous kept tile, consumed by its PV in this iteration
+  bool pending = false;
+  float pend[2] = {1.f, 1.f};
 
   for (int t = 0; t < n_end; ++t) {
     // ---- decision for tile t (statistics visible since the last barrier) ----
@@ -467,16 +606,61 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
       kept += 1;
     }
 
-    // global loads for V_t (only if some head keeps tile t) and K_{t+2}; they land in LDS at
-    // the end of the iteration
-    if (anyv) vst.load(Vb + (long long)t * BK * a.vs[1], a.vs[1], key_valid(t), tid);
+    // V_t (only if some head of the workgroup keeps tile t) and K_{t+2} go straight from
+    // global memory into LDS; they are waited for at the end of the iteration
+    if (anyv)
+      wg_copy_tile<D, NW>(Vb + (long long)t * BK * a.vs[1], a.vs[1], key_valid(t), sV[t & 1],
+                          w, lane);
     if (t + 2 < n_end)
-      kst.load(Kb + (long long)(t + 2) * BK * a.ks[1], a.ks[1], key_valid(t + 2), tid);
+      wg_copy_tile<D, NW>(Kb + (long long)(t + 2) * BK * a.ks[1], a.ks[1], key_valid(t + 2),
+                          sK[t & 1], w, lane);
 
-    // PV of the previous kept tile (MFMA) next to the exponentials of this one (VALU)
-    if (keep_prev) pv_tile<D>(sV[(t - 1) & 1], pbp, o, lane);
+    // a reference move of the last kept tile rescales O here: after that tile's predecessor
+    // was accumulated (previous iteration) and before its own PV (this iteration)
+    if (pending) {
+      acc_ready<MD>(o);
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) o[md][nb][v] *= pend[nb];
+      acc_ready<MD>(o);
+      pending = false;
+    }
+    // running max and exponent reference of tile t (kept tiles only)
+    float alpha[2] = {1.f, 1.f};
+    bool moved = false;
+    float off[2] = {0.f, 0.f};
+    if (mykeep) {
+      moved = softmax_reference(st, rc, c, alpha);
+      off[0] = -st.mref[0] * c;
+      off[1] = -st.mref[1] * c;
+    }
+    // PV of the previous kept tile with the exponentials of this one interleaved; when this
+    // tile is skipped those exponentials are discarded (VALU work under the PV MFMAs)
     bf16x8 pbn[2][4];
-    if (mykeep) softmax_tile<MD>(sc, rc, mt, mref, l, o, pbn, a.c_log2);
+    float sum[2] = {0.f, 0.f};
+    if (keep_prev)
+      pv_exp_block<D, true, true>(sV[(t - 1) & 1], pbp, o, sc, off, c, pbn, sum, lane);
+    else if (mykeep)
+      pv_exp_block<D, false, true>(sV[(t - 1) & 1], pbp, o, sc, off, c, pbn, sum, lane);
+    if (mykeep) {
+      if (moved) {
+        st.l[0] *= alpha[0];
+        st.l[1] *= alpha[1];
+        pend[0] = alpha[0];
+        pend[1] = alpha[1];
+        pending = true;
+      }
+      st.l[0] += sum[0];
+      st.l[1] += sum[1];
+    }
+    // unconditional: after a skipped tile the next PV is skipped, so pbp is then unused
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 4; ++ks2) pbp[nb][ks2] = pbn[nb][ks2];
 
     // scores of the next tile reuse the registers of this one
     if (t + 1 < n_end) {
@@ -484,26 +668,28 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
       tile_rowmax(sc, rc, tile_masked(t + 1), (t + 1) * BK, row0, N, lane);
       if (want_stat) publish(t + 1, rc);
     }
-    if (anyv) vst.store(sV[t & 1], tid);
-    if (t + 2 < n_end) kst.store(sK[t & 1], tid);
+    wait_vmem();
     __syncthreads();
-
-    if (mykeep) {
+    keep_prev = mykeep;
+  }
+  if (pending) {
+    acc_ready<MD>(o);
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
-        for (int ks2 = 0; ks2 < 4; ++ks2) pbp[nb][ks2] = pbn[nb][ks2];
-    }
-    keep_prev = mykeep;
+        for (int v = 0; v < 16; ++v) o[md][nb][v] *= pend[nb];
+    acc_ready<MD>(o);
   }
   if (keep_prev) pv_tile<D>(sV[(n_end - 1) & 1], pbp, o, lane);
+  acc_ready<MD>(o);
 
   // ---- epilogue: O / l (renormalised over kept + diagonal), kept counts ----
   const int rl = lane & 31, hh = lane >> 5;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
-    const float lt = l[nb] + __shfl_xor(l[nb], 32);
-    const float inv = 1.f / lt;
+    const float inv = 1.f / half_sum(st.l[nb]);
     const int row = row0 + nb * 32 + rl;
     if (row < N) {
       const long long base = b * a.os[0] + (long long)row * a.os[1] + h * a.os[2];
@@ -544,7 +730,7 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
   constexpr int HPW = NW / WPH;
   constexpr int MAXJ = kCalibMaxKeyBlocks;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][BK * Tile<D>::KSTR];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<D, NW>()];
   __shared__ float sW[NW][MAXJ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -563,19 +749,20 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
     const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
     bf16x8 qf[2][D / 16];
     load_q_regs<D>(Qb, a.qs[1], row0, N, qf, lane);
-    KStage<D, NT> kst;
-    kst.load(Kb, a.ks[1], BK, tid);
-    kst.store(sK[0], tid);
+    wg_copy_tile<D, NW>(Kb, a.ks[1], BK, sK[0], w, lane);
+    wait_vmem();
     __syncthreads();
     for (int t = 0; t < n_off; ++t) {
-      if (t + 1 < n_off) kst.load(Kb + (long long)(t + 1) * BK * a.ks[1], a.ks[1], BK, tid);
+      if (t + 1 < n_off)
+        wg_copy_tile<D, NW>(Kb + (long long)(t + 1) * BK * a.ks[1], a.ks[1], BK, sK[(t + 1) & 1],
+                            w, lane);
       f32x16 s[2][2];
       float rmax[2];
       qk_tile_regs<D>(sK[t & 1], qf, s, lane);
       tile_rowmax(s, rmax, ragged_rows, t * BK, row0, N, lane);
       const float st = wave_max(fmaxf(rmax[0], rmax[1]));
       if (lane == 0) sW[w][t] = st * a.scale;
-      if (t + 1 < n_off) kst.store(sK[(t + 1) & 1], tid);
+      wait_vmem();
       __syncthreads();
     }
   }
