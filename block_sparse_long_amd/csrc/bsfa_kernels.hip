@@ -27,6 +27,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace bsfa {
 namespace {
 
@@ -90,44 +92,45 @@ __device__ __forceinline__ float wave_max(float x) {
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;         // 16-byte chunks of data per row (16 or 8)
-  static constexpr int STR = D + 8;         // LDS row stride in bf16: one 16-byte pad chunk
-  static constexpr int CPS = CPR + 1;       // chunks per padded row
-  static constexpr int INSTR = 64 * CPS / 64;   // 1 KB loads per 64-row tile (17 or 9)
+  static constexpr int STR = D + 8;         // Q/K row stride in bf16 (one 16-byte pad chunk)
+  static constexpr int STRV = D + 32;       // V row stride in bf16 (four pad chunks)
   static constexpr int KS = D / 16;         // QK k-steps over d
   static constexpr int MD = D / 32;         // PV M-blocks over d
-  static constexpr int ELEMS = 64 * STR;    // bf16 per 64-row tile
 };
 
-// LDS tiles hold 64 rows of D bf16 with a 16-byte pad per row: consecutive rows start 4 banks
-// apart, so the rows one MFMA operand read touches spread over the banks, and every fragment
-// address is a per-lane base plus a compile-time offset.
+// LDS tiles hold 64 rows of D bf16 plus padding, so that every fragment address is a per-lane
+// base plus a compile-time offset, and the rows one read touches spread over the 64 banks:
+//   * Q and K (row stride D + 8): a 16-byte operand read covers 16 consecutive rows per
+//     16 lanes; rows start 4 banks apart, so the 16 reads tile all 64 banks.
+//   * V (row stride D + 32): a transposing read covers 4 consecutive rows x 64 bytes per 32
+//     lanes; rows start 16 banks apart, so the 4 row segments are disjoint.
 template <int D>
 __device__ __forceinline__ int elem_off(int r, int c) {
   return r * Tile<D>::STR + (c << 3);
 }
 
-// Direct global -> LDS copy of a 64-row tile, 1 KB per instruction: lane l of instruction k
-// fills padded chunk q = 64k + l (row q / CPS, column q % CPS), fetching the matching global
-// chunk; pad chunks re-fetch the row's last chunk. Rows at or past `valid` re-read row
-// valid - 1 (their scores are masked and their P weights are zero). Wave w of NW issues
-// instructions k = w + NW*m for a fixed m range, so every wave runs the same straight-line
-// code; instructions past the tile's INSTR land in the spare space of a tile buffer sized by
-// tile_elems<D, NW>() and fetch clamped, valid addresses.
-template <int D, int NW>
+// Direct global -> LDS copy of a 64-row tile with row stride STRIDE (bf16), 1 KB per
+// instruction: lane l of instruction k fills padded chunk q = 64k + l (row q / CPS, column
+// q % CPS) with the matching global chunk; pad chunks re-fetch the row's last chunk. Rows at or
+// past `valid` re-read row valid - 1 (their scores are masked and their P weights are zero).
+// Wave w of NW issues instructions k = w + NW*m for a fixed m range, so every wave runs the
+// same straight-line code; instructions past the tile's chunk count land in the spare space of
+// a buffer sized by tile_elems<STRIDE, NW>() and fetch clamped, valid addresses.
+template <int STRIDE, int NW>
 constexpr int tile_instr_per_wave() {
-  return (Tile<D>::INSTR + NW - 1) / NW;
+  return (STRIDE / 8 + NW - 1) / NW;       // 64 rows x STRIDE/8 chunks = STRIDE/8 instructions
 }
-template <int D, int NW>
+template <int STRIDE, int NW>
 constexpr int tile_elems() {
-  return tile_instr_per_wave<D, NW>() * NW * 512;
+  return tile_instr_per_wave<STRIDE, NW>() * NW * 512;
 }
 
-template <int D, int NW>
+template <int D, int STRIDE, int NW>
 __device__ __forceinline__ void wg_copy_tile(const __bf16* gbase, long long gst, int valid,
                                              __bf16* tile, int w, int lane) {
-  constexpr int CPR = Tile<D>::CPR, CPS = Tile<D>::CPS;
+  constexpr int CPR = D / 8, CPS = STRIDE / 8;
 #pragma unroll
-  for (int m = 0; m < tile_instr_per_wave<D, NW>(); ++m) {
+  for (int m = 0; m < tile_instr_per_wave<STRIDE, NW>(); ++m) {
     const int k = w + NW * m;
     const int q = 64 * k + lane;
     const int r = min(q / CPS, 63), col = min(q % CPS, CPR - 1);
@@ -135,6 +138,37 @@ __device__ __forceinline__ void wg_copy_tile(const __bf16* gbase, long long gst,
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + k * 512),
                                      16, 0, 0);
   }
+}
+
+// The same copy for a stream of full 64-row tiles with one row stride: the per-lane byte
+// offsets inside a tile are computed once (stream_offsets), so each load of a full tile is a
+// uniform base plus a VGPR offset (stream_issue). Used with 4-wave workgroups; with fewer
+// waves the offsets would cost too many VGPRs and the plain copy is used.
+template <int D, int STRIDE, int NW, int M>
+__device__ __forceinline__ void stream_offsets(unsigned* off, long long gst, int w, int lane) {
+  constexpr int CPR = D / 8, CPS = STRIDE / 8;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int q = 64 * (w + NW * m) + lane;
+    const int r = min(q / CPS, 63), col = min(q % CPS, CPR - 1);
+    off[m] = (unsigned)((r * gst + col * 8) * 2);
+  }
+}
+
+template <int D, int STRIDE, int NW, int M>
+__device__ __forceinline__ void stream_issue(const unsigned* off, const __bf16* gbase,
+                                             long long gst, int valid, __bf16* tile, int w,
+                                             int lane) {
+  if (valid < 64) {
+    wg_copy_tile<D, STRIDE, NW>(gbase, gst, valid, tile, w, lane);
+    return;
+  }
+  const char* b = reinterpret_cast<const char*>(gbase);
+#pragma unroll
+  for (int m = 0; m < M; ++m)
+    __builtin_amdgcn_global_load_lds(b + off[m],
+                                     (__attribute__((address_space(3))) void*)(tile + (w + NW * m) * 512),
+                                     16, 0, 0);
 }
 
 // Wait for this wave's outstanding global loads (including those writing LDS directly).
@@ -160,8 +194,8 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16* sv, int md, int ks2, int 
   const int d = md * 32 + (grp & 1) * 16 + 4 * (j & 3);
   const int key0 = 16 * ks2 + 4 * hh + (j >> 2);
   typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  const int o0 = key0 * Tile<D>::STR + d;
-  const int o1 = o0 + 8 * Tile<D>::STR;
+  const int o0 = key0 * Tile<D>::STRV + d;
+  const int o1 = o0 + 8 * Tile<D>::STRV;
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sv + o0));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(sv + o1));
   bf16x8 r;
@@ -173,28 +207,40 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16* sv, int md, int ks2, int 
 // S^T[key][row] for one 64-key tile and the wave's 64 rows: s[mb][nb] holds keys
 // mb*32 + 8*(v/4) + 4*(lane/32) + v%4 and row nb*32 + lane%32 in element v. Both operands come
 // from LDS: K (A operand) from the shared tile, Q^T (B operand) from the wave's own Q rows.
+// The four fragments of k-step ks+1 are read while the four MFMAs of step ks run; the
+// scheduling fences keep those reads from sinking back next to their use.
 template <int D>
 __device__ __forceinline__ void qk_tile(const __bf16* sk, const __bf16* sq, f32x16 (&s)[2][2],
                                         int lane) {
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[mb][nb][v] = 0.f;
   const int rl = lane & 31, hh = lane >> 5;
+  bf16x8 qb[2][2], ka[2][2];
+  auto load = [&](int ks, int buf) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      qb[buf][n] = lds_frag<D>(sq, n * 32 + rl, 2 * ks + hh);
+      ka[buf][n] = lds_frag<D>(sk, n * 32 + rl, 2 * ks + hh);
+    }
+  };
+  load(0, 0);
 #pragma unroll
   for (int ks = 0; ks < Tile<D>::KS; ++ks) {
-    bf16x8 qb[2];
+    const int buf = ks & 1;
+    if (ks + 1 < Tile<D>::KS) load(ks + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-      qb[nb] = lds_frag<D>(sq, nb * 32 + rl, 2 * ks + hh);
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (ks == 0) {
+          f32x16 z;
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(a, qb[nb], s[mb][nb]);
-    }
+          for (int v = 0; v < 16; ++v) z[v] = 0.f;
+          s[mb][nb] = mfma32(ka[buf][mb], qb[buf][nb], z);
+        } else {
+          s[mb][nb] = mfma32(ka[buf][mb], qb[buf][nb], s[mb][nb]);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -340,95 +386,50 @@ __device__ __forceinline__ void pv_exp_block(const __bf16* sv, const bf16x8 (&pb
                                              const float (&off)[2], float c,
                                              bf16x8 (&pbn)[2][4], float (&sum)[2], int lane) {
   constexpr int MD = D / 32;
-  constexpr int NMF = MD * 8;                 // PV MFMAs per tile
+  constexpr int NSTEP = MD * 4;               // (k-step, M-block) pairs: 2 MFMAs each
   constexpr int PAIRS = 32;                   // softmax element pairs per lane per tile
-  constexpr int SLOTS = NMF > PAIRS ? NMF : PAIRS;
-  const int rl = lane & 31, hh = lane >> 5;
+  constexpr int PPS = PAIRS / NSTEP;          // pairs per step
   bf16x2 ones;
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
-  bf16x8 va;
   bf16x8 pbl[2][4];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb)
 #pragma unroll
     for (int ks2 = 0; ks2 < 4; ++ks2) pbl[nb][ks2] = pbp[nb][ks2];
-  if (DO_PV) pv_operands_ready(pbl);
+  bf16x8 vb[3];
+  if (DO_PV) {
+    pv_operands_ready(pbl);
+    vb[0] = v_frag<D>(sv, 0 % MD, 0 / MD, lane);
+    vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
+  }
 #pragma unroll
-  for (int q = 0; q < SLOTS; ++q) {
-    if (DO_PV && (q * NMF) % SLOTS == 0) {
-      const int mi = q * NMF / SLOTS;
-      const int ks2 = mi / (MD * 2), md = (mi / 2) % MD, nb = mi % 2;
-      if (nb == 0) va = v_frag<D>(sv, md, ks2, lane);
-      mfma_acc(o[md][nb], va, pbl[nb][ks2]);
+  for (int st = 0; st < NSTEP; ++st) {
+    const int ks2 = st / MD, md = st % MD;
+    if (DO_PV) {
+      if (st + 2 < NSTEP) vb[(st + 2) % 3] = v_frag<D>(sv, (st + 2) % MD, (st + 2) / MD, lane);
+      mfma_acc(o[md][0], vb[st % 3], pbl[0][ks2]);
+      mfma_acc(o[md][1], vb[st % 3], pbl[1][ks2]);
     }
-    if (DO_EXP && (q * PAIRS) % SLOTS == 0) {
-      const int pi = q * PAIRS / SLOTS;
-      const int nb = pi / 16, ks2 = (pi / 4) % 4, e = 2 * (pi % 4);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e], c, off[nb]));
-      const float p1 =
-          __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e + 1], c, off[nb]));
-      bf16x2 pr;
-      pr[0] = (__bf16)p0;
-      pr[1] = (__bf16)p1;
-      sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
-      pbn[nb][ks2][e] = pr[0];
-      pbn[nb][ks2][e + 1] = pr[1];
+    if (DO_EXP) {
+#pragma unroll
+      for (int pp = 0; pp < PPS; ++pp) {
+        const int pi = st * PPS + pp;
+        const int nb = pi / 16, k2 = (pi / 4) % 4, e = 2 * (pi % 4);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][nb][(k2 & 1) * 8 + e], c, off[nb]));
+        const float p1 =
+            __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][nb][(k2 & 1) * 8 + e + 1], c, off[nb]));
+        bf16x2 pr;
+        pr[0] = (__bf16)p0;
+        pr[1] = (__bf16)p1;
+        sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
+        pbn[nb][k2][e] = pr[0];
+        pbn[nb][k2][e + 1] = pr[1];
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
   }
   if (DO_PV) keep_alive(pbl);
-}
-
-// QK^T of the next tile (MFMA, operands from LDS) interleaved with the exponentials of the
-// current kept tile (VALU): one element pair of the softmax next to each of the 32 MFMAs.
-template <int D, bool DO_EXP>
-__device__ __forceinline__ void qk_exp_block(const __bf16* sk, const __bf16* sq,
-                                             f32x16 (&sn)[2][2], const f32x16 (&s)[2][2],
-                                             const float (&off)[2], float c,
-                                             bf16x8 (&pbn)[2][4], float (&sum)[2], int lane) {
-  constexpr int KS = Tile<D>::KS;
-  constexpr int NMF = KS * 4;                 // QK MFMAs per tile
-  constexpr int PAIRS = 32;
-  constexpr int SLOTS = NMF > PAIRS ? NMF : PAIRS;
-  const int rl = lane & 31, hh = lane >> 5;
-  bf16x2 ones;
-  ones[0] = (__bf16)1.f;
-  ones[1] = (__bf16)1.f;
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) sn[mb][nb][v] = 0.f;
-  bf16x8 qb[2], ka;
-#pragma unroll
-  for (int q = 0; q < SLOTS; ++q) {
-    if ((q * NMF) % SLOTS == 0) {
-      const int mi = q * NMF / SLOTS;
-      const int ks = mi / 4, mb = (mi / 2) % 2, nb = mi % 2;
-      if (mb == 0 && nb == 0) {
-#pragma unroll
-        for (int n2 = 0; n2 < 2; ++n2)
-          qb[n2] = lds_frag<D>(sq, n2 * 32 + rl, 2 * ks + hh);
-      }
-      if (nb == 0)
-        ka = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
-      sn[mb][nb] = mfma32(ka, qb[nb], sn[mb][nb]);
-    }
-    if (DO_EXP && (q * PAIRS) % SLOTS == 0) {
-      const int pi = q * PAIRS / SLOTS;
-      const int nb = pi / 16, ks2 = (pi / 4) % 4, e = 2 * (pi % 4);
-      const float p0 = __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e], c, off[nb]));
-      const float p1 =
-          __builtin_amdgcn_exp2f(fmaf(s[ks2 >> 1][nb][(ks2 & 1) * 8 + e + 1], c, off[nb]));
-      bf16x2 pr;
-      pr[0] = (__bf16)p0;
-      pr[1] = (__bf16)p1;
-      sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
-      pbn[nb][ks2][e] = pr[0];
-      pbn[nb][ks2][e + 1] = pr[1];
-    }
-  }
 }
 
 template <int D>
@@ -470,7 +471,7 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
 template <int D>
 __device__ __forceinline__ void stage_q(const __bf16* qbase, long long qst, int row0, int N,
                                         __bf16* sq, int lane) {
-  wg_copy_tile<D, 1>(qbase + (long long)row0 * qst, qst, N - row0, sq, 0, lane);
+  wg_copy_tile<D, Tile<D>::STR, 1>(qbase + (long long)row0 * qst, qst, N - row0, sq, 0, lane);
 }
 
 template <int D, int BQ, int NW, int GATE>
@@ -481,12 +482,13 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   constexpr int MD = Tile<D>::MD;
   constexpr bool kGated = GATE != kDense;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][tile_elems<D, 1>()];
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<D, NW>()];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][tile_elems<D, NW>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][tile_elems<Tile<D>::STR, 1>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<Tile<D>::STR, NW>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][tile_elems<Tile<D>::STRV, NW>()];
   __shared__ float sGate[2][NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = tid >> 6;
   const int hw = w / WPH, rw = w % WPH;
   const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
   const int b = un.b, g = un.g, i = un.i;
@@ -536,6 +538,14 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   acc_ready<MD>(o);
 
   auto key_valid = [&](int j) { return min(BK, N - j * BK); };
+  constexpr int MK = tile_instr_per_wave<Tile<D>::STR, NW>();
+  constexpr int MV = tile_instr_per_wave<Tile<D>::STRV, NW>();
+  constexpr bool kStream = NW == 4;
+  unsigned koff[MK], voff[MV];
+  if constexpr (kStream) {
+    stream_offsets<D, Tile<D>::STR, NW, MK>(koff, a.ks[1], w, lane);
+    stream_offsets<D, Tile<D>::STRV, NW, MV>(voff, a.vs[1], w, lane);
+  }
   auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
   // Gate statistic of this wave for tile j, in raw score units (the scale is applied at the
@@ -558,10 +568,10 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   };
 
   // ---- prologue: K_0 staged, S_0 computed and published ----
-  wg_copy_tile<D, NW>(Kb, a.ks[1], key_valid(0), sK[0], w, lane);
+  wg_copy_tile<D, Tile<D>::STR, NW>(Kb, a.ks[1], key_valid(0), sK[0], w, lane);
   wait_vmem();
   __syncthreads();
-  if (n_end > 1) wg_copy_tile<D, NW>(Kb + (long long)BK * a.ks[1], a.ks[1], key_valid(1), sK[1], w, lane);
+  if (n_end > 1) wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)BK * a.ks[1], a.ks[1], key_valid(1), sK[1], w, lane);
   f32x16 sc[2][2];   // scores of the tile being processed
   float rc[2];       // their row maxima
   qk_tile<D>(sK[0], sq, sc, lane);
@@ -572,11 +582,12 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
 
   int kept = 0;
   bool keep_prev = false;
-  bf16x8 pbp[2][4];   // P of the previous kept tile, consumed by its PV in this iteration
   bool pending = false;
   float pend[2] = {1.f, 1.f};
+  bf16x8 pbp[2][4];   // P of the previous kept tile, consumed by its PV in this iteration
 
   for (int t = 0; t < n_end; ++t) {
+    const int par = t & 1;
     // ---- decision for tile t (statistics visible since the last barrier) ----
     const bool diag = t >= n_off;
     bool mykeep = true, anyv = true;
@@ -584,9 +595,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
       float hst[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        float x = sGate[t & 1][hh * WPH];
+        float x = sGate[par][hh * WPH];
 #pragma unroll
-        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sGate[t & 1][hh * WPH + r]);
+        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sGate[par][hh * WPH + r]);
         hst[hh] = x * a.scale;
       }
       if (kGated && !diag) {
@@ -608,12 +619,21 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
 
     // V_t (only if some head of the workgroup keeps tile t) and K_{t+2} go straight from
     // global memory into LDS; they are waited for at the end of the iteration
-    if (anyv)
-      wg_copy_tile<D, NW>(Vb + (long long)t * BK * a.vs[1], a.vs[1], key_valid(t), sV[t & 1],
-                          w, lane);
-    if (t + 2 < n_end)
-      wg_copy_tile<D, NW>(Kb + (long long)(t + 2) * BK * a.ks[1], a.ks[1], key_valid(t + 2),
-                          sK[t & 1], w, lane);
+    if constexpr (kStream) {
+      if (anyv)
+        stream_issue<D, Tile<D>::STRV, NW, MV>(voff, Vb + (long long)t * BK * a.vs[1], a.vs[1],
+                                               key_valid(t), sV[par], w, lane);
+      if (t + 2 < n_end)
+        stream_issue<D, Tile<D>::STR, NW, MK>(koff, Kb + (long long)(t + 2) * BK * a.ks[1],
+                                              a.ks[1], key_valid(t + 2), sK[par], w, lane);
+    } else {
+      if (anyv)
+        wg_copy_tile<D, Tile<D>::STRV, NW>(Vb + (long long)t * BK * a.vs[1], a.vs[1],
+                                           key_valid(t), sV[par], w, lane);
+      if (t + 2 < n_end)
+        wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)(t + 2) * BK * a.ks[1], a.ks[1],
+                                          key_valid(t + 2), sK[par], w, lane);
+    }
 
     // a reference move of the last kept tile rescales O here: after that tile's predecessor
     // was accumulated (previous iteration) and before its own PV (this iteration)
@@ -642,9 +662,9 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
     bf16x8 pbn[2][4];
     float sum[2] = {0.f, 0.f};
     if (keep_prev)
-      pv_exp_block<D, true, true>(sV[(t - 1) & 1], pbp, o, sc, off, c, pbn, sum, lane);
+      pv_exp_block<D, true, true>(sV[1 - par], pbp, o, sc, off, c, pbn, sum, lane);
     else if (mykeep)
-      pv_exp_block<D, false, true>(sV[(t - 1) & 1], pbp, o, sc, off, c, pbn, sum, lane);
+      pv_exp_block<D, false, true>(sV[1 - par], pbp, o, sc, off, c, pbn, sum, lane);
     if (mykeep) {
       if (moved) {
         st.l[0] *= alpha[0];
@@ -664,7 +684,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
 
     // scores of the next tile reuse the registers of this one
     if (t + 1 < n_end) {
-      qk_tile<D>(sK[(t + 1) & 1], sq, sc, lane);
+      qk_tile<D>(sK[1 - par], sq, sc, lane);
       tile_rowmax(sc, rc, tile_masked(t + 1), (t + 1) * BK, row0, N, lane);
       if (want_stat) publish(t + 1, rc);
     }
@@ -730,7 +750,7 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
   constexpr int HPW = NW / WPH;
   constexpr int MAXJ = kCalibMaxKeyBlocks;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<D, NW>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<Tile<D>::STR, NW>()];
   __shared__ float sW[NW][MAXJ];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -749,12 +769,12 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
     const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
     bf16x8 qf[2][D / 16];
     load_q_regs<D>(Qb, a.qs[1], row0, N, qf, lane);
-    wg_copy_tile<D, NW>(Kb, a.ks[1], BK, sK[0], w, lane);
+    wg_copy_tile<D, Tile<D>::STR, NW>(Kb, a.ks[1], BK, sK[0], w, lane);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < n_off; ++t) {
       if (t + 1 < n_off)
-        wg_copy_tile<D, NW>(Kb + (long long)(t + 1) * BK * a.ks[1], a.ks[1], BK, sK[(t + 1) & 1],
+        wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)(t + 1) * BK * a.ks[1], a.ks[1], BK, sK[(t + 1) & 1],
                             w, lane);
       f32x16 s[2][2];
       float rmax[2];
