@@ -253,7 +253,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(gated["tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gated["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<128,128,4,gate>",
+                     "kernel": "prefill_kernel<128,128,8,gate>",
                      "flops_per_launch": gated["flops"]},
         "cpu_baseline": cpu,
         "extras": extras,

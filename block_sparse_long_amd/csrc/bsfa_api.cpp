@@ -69,6 +69,9 @@ bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
                     names[t], a, (long long)strides[t][a]);
     }
   }
+  if (p->k_stride[1] > bsfa::kMaxTokenStride || (need_v_o && p->v_stride[1] > bsfa::kMaxTokenStride))
+    return fail(BSFA_ERR_UNSUPPORTED, "K/V token stride above %lld elements",
+                (long long)bsfa::kMaxTokenStride);
   return BSFA_OK;
 }
 
@@ -178,7 +181,7 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   a.nqb = nqb;
   a.nkb = nkb;
   const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
-  const int hpw = nw / (p->block_q / 64);
+  const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
   a.scale = scale;
@@ -228,7 +231,7 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
   a.nqb = ceil_div(p->seqlen, p->block_q);
   a.nkb = nkb;
   const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
-  const int hpw = nw / (p->block_q / 64);
+  const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
   a.scale = effective_scale(p);

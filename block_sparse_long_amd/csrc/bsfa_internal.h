@@ -42,8 +42,15 @@ struct CalibArgs {
   float* kth;                      // [n_budgets][B][Hq][nqb]
 };
 
-// Workgroup shape: waves of 64 query rows; a workgroup holds heads_per_wg heads of one KV
-// group times block_q rows. Returns the number of waves (1, 2 or 4), 0 if unsupported.
+// Largest K / V token stride (elements): 64 rows of it stay below 4 GB, so tile offsets fit in
+// 32 bits.
+constexpr int64_t kMaxTokenStride = int64_t(1) << 25;
+
+constexpr int kRowsPerWave = 32;
+
+// Workgroup shape: waves of kRowsPerWave query rows; a workgroup holds the waves of 1, 2 or 4
+// query heads of one KV group for one block of block_q rows (at most 8 waves). Returns the
+// number of waves; heads per workgroup = waves / (block_q / kRowsPerWave).
 int waves_per_workgroup(int block_q, int group);
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,

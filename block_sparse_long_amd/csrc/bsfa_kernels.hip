@@ -9,18 +9,22 @@
 // keeps a block iff some row's block max is within ln(lambda) of its running max.
 //
 // Mapping onto CDNA4:
-//   * One wavefront owns 64 query rows of one head. Scores are produced transposed,
-//     S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T resident in VGPRs),
-//     so each lane holds 32 scores of each of its 2 rows: the row max is an in-lane max3 chain
-//     plus one cross-half exchange, and the exponentials stay in the lanes that produced them.
-//   * O^T = V^T P^T: P^T is the MFMA B operand straight from the softmax registers; V^T comes
-//     from LDS, where V tiles are stored transposed with a key permutation that matches the
-//     lane order of P (16 contiguous bytes per operand).
-//   * A workgroup is 4 waves (256 query rows: 2 heads x 128 rows under GQA, or 4 x 64): each
-//     K/V tile is staged in LDS once and read by every wave. K and V are double-buffered.
-//   * QK of tile t+1 is issued before the softmax of tile t, so the gate statistics of tile
-//     t+1 reach LDS before the one barrier of the iteration; V_t is fetched only when some
-//     head of the workgroup keeps tile t, and is written to LDS behind the softmax.
+//   * One wavefront owns 32 query rows of one head, and two wavefronts share each SIMD, so the
+//     exponentials of one issue on the vector ALU while the other's matrix instructions run.
+//     Scores are produced transposed, S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from
+//     LDS, B = Q^T resident in VGPRs): each lane holds 32 scores of its row, so the row max is
+//     an in-lane max chain plus one exchange between the two half-waves, and the exponentials
+//     stay in the lanes that produced them.
+//   * O^T = V^T P^T: P^T is the MFMA B operand straight from the softmax registers; V^T is read
+//     from the natural [key][d] V tile with transposing LDS reads, in the key order in which
+//     the S^T accumulator (and so P^T) holds them.
+//   * A workgroup holds the 32-row waves of one or more query heads of one KV group for one
+//     query block (2 heads x 128 rows = 8 waves for the 128x64 tile under GQA): each K/V tile
+//     is staged in LDS once, by direct global->LDS loads, and read by every wave; K and V are
+//     double-buffered.
+//   * QK of tile t+1 is issued after the softmax of tile t, so the gate statistics of tile t+1
+//     reach LDS before the one barrier of the iteration; V_t is fetched only when some head of
+//     the workgroup keeps tile t.
 //   * Workgroups are ordered heaviest query block first, and (when the unit count allows)
 //     all query blocks of one KV head go to the same XCD so their K/V stream shares its L2.
 #include "bsfa_internal.h"
@@ -33,28 +37,19 @@ namespace bsfa {
 namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
-typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int V>
+using IC = std::integral_constant<int, V>;
 
 constexpr int BK = kBlockK;
 constexpr float kNegInf = -__builtin_huge_valf();
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// O^T += V^T P^T with the accumulator pinned to AGPRs (inline asm): the score MFMAs write
-// VGPRs, which the softmax reads directly, while O, touched only by these MFMAs, the rare
-// rescale and the epilogue, lives in the accumulation registers. The compiler cannot see
-// inside the asm, so the hazards around it are resolved by hand:
-//   * consecutive accumulations into the same full accumulator need no wait states;
-//   * P (SrcB) is written by VALU: pv_operands_ready() puts wait states between the last such
-//     write and the first MFMA, and keep_alive() holds P's registers until the block ends so
-//     no VALU write can land in a register an issued MFMA is still reading;
-//   * VALU access to O after these MFMAs goes through acc_ready(), which waits out the
-//     longest MFMA-result latency first.
-__device__ __forceinline__ void mfma_acc(f32x16& o, const bf16x8& a, const bf16x8& b) {
-  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(o) : "v"(a), "v"(b));
 }
 
 __device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
@@ -89,10 +84,13 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Wait for this wave's outstanding global loads (including those writing LDS directly).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;         // 16-byte chunks of data per row (16 or 8)
-  static constexpr int STR = D + 8;         // Q/K row stride in bf16 (one 16-byte pad chunk)
+  static constexpr int STR = D + 8;         // K row stride in bf16 (one 16-byte pad chunk)
   static constexpr int STRV = D + 32;       // V row stride in bf16 (four pad chunks)
   static constexpr int KS = D / 16;         // QK k-steps over d
   static constexpr int MD = D / 32;         // PV M-blocks over d
@@ -100,87 +98,63 @@ struct Tile {
 
 // LDS tiles hold 64 rows of D bf16 plus padding, so that every fragment address is a per-lane
 // base plus a compile-time offset, and the rows one read touches spread over the 64 banks:
-//   * Q and K (row stride D + 8): a 16-byte operand read covers 16 consecutive rows per
-//     16 lanes; rows start 4 banks apart, so the 16 reads tile all 64 banks.
+//   * K (row stride D + 8): a 16-byte operand read covers 16 consecutive rows per 16 lanes;
+//     rows start 4 banks apart, so the 16 reads tile all 64 banks.
 //   * V (row stride D + 32): a transposing read covers 4 consecutive rows x 64 bytes per 32
 //     lanes; rows start 16 banks apart, so the 4 row segments are disjoint.
-template <int D>
-__device__ __forceinline__ int elem_off(int r, int c) {
-  return r * Tile<D>::STR + (c << 3);
+//
+// Tiles are filled by direct global -> LDS loads, 1 KB per instruction: lane l of instruction k
+// fills padded chunk q = 64k + l (row q / CPS, column q % CPS, CPS = STRIDE / 8 chunks per
+// padded row) with the matching global chunk; pad chunks re-fetch the row's last chunk. A tile
+// is exactly CPS instructions. Rows at or past `valid` re-read row valid - 1 (their scores are
+// masked and their P weights are zero).
+
+// ---------------------------------------------------------------------------------------------
+// Workgroup-wide tile copies. Wave w of NW issues instructions k = w + NW*m.
+// ---------------------------------------------------------------------------------------------
+template <int STRIDE, int NW>
+constexpr int copy_iters() {
+  return (STRIDE / 8 + NW - 1) / NW;
 }
 
-// Direct global -> LDS copy of a 64-row tile with row stride STRIDE (bf16), 1 KB per
-// instruction: lane l of instruction k fills padded chunk q = 64k + l (row q / CPS, column
-// q % CPS) with the matching global chunk; pad chunks re-fetch the row's last chunk. Rows at or
-// past `valid` re-read row valid - 1 (their scores are masked and their P weights are zero).
-// Wave w of NW issues instructions k = w + NW*m for a fixed m range, so every wave runs the
-// same straight-line code; instructions past the tile's chunk count land in the spare space of
-// a buffer sized by tile_elems<STRIDE, NW>() and fetch clamped, valid addresses.
-template <int STRIDE, int NW>
-constexpr int tile_instr_per_wave() {
-  return (STRIDE / 8 + NW - 1) / NW;       // 64 rows x STRIDE/8 chunks = STRIDE/8 instructions
-}
-template <int STRIDE, int NW>
-constexpr int tile_elems() {
-  return tile_instr_per_wave<STRIDE, NW>() * NW * 512;
-}
-
+// Per-lane byte offsets, inside a full tile, of the chunks this wave copies (computed once per
+// workgroup; 32-bit because the host bounds the token stride so that 64 rows stay below 4 GB).
 template <int D, int STRIDE, int NW>
-__device__ __forceinline__ void wg_copy_tile(const __bf16* gbase, long long gst, int valid,
-                                             __bf16* tile, int w, int lane) {
-  constexpr int CPR = D / 8, CPS = STRIDE / 8;
-#pragma unroll
-  for (int m = 0; m < tile_instr_per_wave<STRIDE, NW>(); ++m) {
-    const int k = w + NW * m;
-    const int q = 64 * k + lane;
-    const int r = min(q / CPS, 63), col = min(q % CPS, CPR - 1);
-    const __bf16* src = gbase + (long long)min(r, valid - 1) * gst + col * 8;
-    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)(tile + k * 512),
-                                     16, 0, 0);
-  }
-}
-
-// The same copy for a stream of full 64-row tiles with one row stride: the per-lane byte
-// offsets inside a tile are computed once (stream_offsets), so each load of a full tile is a
-// uniform base plus a VGPR offset (stream_issue). Used with 4-wave workgroups; with fewer
-// waves the offsets would cost too many VGPRs and the plain copy is used.
-template <int D, int STRIDE, int NW, int M>
-__device__ __forceinline__ void stream_offsets(unsigned* off, long long gst, int w, int lane) {
-  constexpr int CPR = D / 8, CPS = STRIDE / 8;
+__device__ __forceinline__ void copy_offsets(unsigned* off, long long gst, int w, int lane) {
+  constexpr int CPR = D / 8, CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
 #pragma unroll
   for (int m = 0; m < M; ++m) {
-    const int q = 64 * (w + NW * m) + lane;
-    const int r = min(q / CPS, 63), col = min(q % CPS, CPR - 1);
-    off[m] = (unsigned)((r * gst + col * 8) * 2);
+    const int q = 64 * min(w + NW * m, CPS - 1) + lane;
+    const int r = q / CPS, col = min(q % CPS, CPR - 1);
+    off[m] = (unsigned)(r * (unsigned)gst + col * 8) * 2u;
   }
 }
 
-template <int D, int STRIDE, int NW, int M>
-__device__ __forceinline__ void stream_issue(const unsigned* off, const __bf16* gbase,
-                                             long long gst, int valid, __bf16* tile, int w,
-                                             int lane) {
-  if (valid < 64) {
-    wg_copy_tile<D, STRIDE, NW>(gbase, gst, valid, tile, w, lane);
-    return;
-  }
-  const char* b = reinterpret_cast<const char*>(gbase);
+// Copy one 64-row tile starting at gbase. For a ragged tile (valid < 64 rows) the chunks of
+// rows at or past `valid` are redirected to row valid - 1.
+template <int D, int STRIDE, int NW>
+__device__ __forceinline__ void copy_tile(const unsigned* off, const __bf16* gbase,
+                                          unsigned row_bytes, int valid, __bf16* tile, int w,
+                                          int lane) {
+  constexpr int CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
+  const char* base = reinterpret_cast<const char*>(gbase);
 #pragma unroll
-  for (int m = 0; m < M; ++m)
-    __builtin_amdgcn_global_load_lds(b + off[m],
-                                     (__attribute__((address_space(3))) void*)(tile + (w + NW * m) * 512),
-                                     16, 0, 0);
+  for (int m = 0; m < M; ++m) {
+    const int k = w + NW * m;
+    if (m + 1 < M || k < CPS) {     // wave-uniform; only the last round can run past the tile
+      unsigned o = off[m];
+      if (valid < 64) {
+        const int r = (64 * k + lane) / CPS;
+        o -= (unsigned)max(r - (valid - 1), 0) * row_bytes;
+      }
+      __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(tile + k * 512), 16, 0, 0);
+    }
+  }
 }
 
-// Wait for this wave's outstanding global loads (including those writing LDS directly).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// 16-byte operand: chunk (2 * kstep + half) of row r.
-template <int D>
-__device__ __forceinline__ bf16x8 lds_frag(const __bf16* tile, int r, int c) {
-  return *reinterpret_cast<const bf16x8*>(tile + elem_off<D>(r, c));
-}
-
-typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+// ---------------------------------------------------------------------------------------------
+// Operand fragments
+// ---------------------------------------------------------------------------------------------
 
 // A operand of O^T += V^T P^T for M-block md and key k-step ks2, read from V in natural
 // [key][d] layout with two transposing reads. In each 16-lane group, lane j points at key
@@ -204,202 +178,116 @@ __device__ __forceinline__ bf16x8 v_frag(const __bf16* sv, int md, int ks2, int 
   return r;
 }
 
-// S^T[key][row] for one 64-key tile and the wave's 64 rows: s[mb][nb] holds keys
-// mb*32 + 8*(v/4) + 4*(lane/32) + v%4 and row nb*32 + lane%32 in element v. Both operands come
-// from LDS: K (A operand) from the shared tile, Q^T (B operand) from the wave's own Q rows.
-// The four fragments of k-step ks+1 are read while the four MFMAs of step ks run; the
-// scheduling fences keep those reads from sinking back next to their use.
+// B operand Q^T of S^T = K Q^T for 32 query rows: lane l holds row row0 + l%32 and dims
+// 16*ks + 8*(l/32) + {0..7} in qf[ks]. Rows past N are zero.
 template <int D>
-__device__ __forceinline__ void qk_tile(const __bf16* sk, const __bf16* sq, f32x16 (&s)[2][2],
-                                        int lane) {
-  const int rl = lane & 31, hh = lane >> 5;
-  bf16x8 qb[2][2], ka[2][2];
-  auto load = [&](int ks, int buf) {
+__device__ __forceinline__ void load_q32(const __bf16* qbase, long long qst, int row0, int N,
+                                         bf16x8 (&qf)[D / 16], int lane) {
+  const int row = row0 + (lane & 31);
+  const __bf16* p = qbase + (long long)min(row, N - 1) * qst + 8 * (lane >> 5);
 #pragma unroll
-    for (int n = 0; n < 2; ++n) {
-      qb[buf][n] = lds_frag<D>(sq, n * 32 + rl, 2 * ks + hh);
-      ka[buf][n] = lds_frag<D>(sk, n * 32 + rl, 2 * ks + hh);
-    }
+  for (int ks = 0; ks < D / 16; ++ks) {
+    const uint4 x = *reinterpret_cast<const uint4*>(p + 16 * ks);
+    qf[ks] = __builtin_bit_cast(bf16x8, row < N ? x : make_uint4(0, 0, 0, 0));
+  }
+}
+
+// S^T[key][row] for one 64-key tile and the wave's 32 rows: s[mb] holds keys
+// mb*32 + 8*(v/4) + 4*(lane/32) + v%4 of row lane%32 in element v. The two K fragments of
+// k-step ks+1 are read while the two MFMAs of step ks run.
+template <int D>
+__device__ __forceinline__ void qk32(const __bf16* sk, const bf16x8 (&qf)[D / 16],
+                                     f32x16 (&s)[2], int lane) {
+  constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR;
+  const __bf16* base = sk + (lane & 31) * STR + 8 * (lane >> 5);
+  bf16x8 ka[2][2];
+  auto load = [&](int ks, int buf) {
+    ka[buf][0] = *reinterpret_cast<const bf16x8*>(base + 16 * ks);
+    ka[buf][1] = *reinterpret_cast<const bf16x8*>(base + 32 * STR + 16 * ks);
   };
   load(0, 0);
 #pragma unroll
-  for (int ks = 0; ks < Tile<D>::KS; ++ks) {
+  for (int ks = 0; ks < KS; ++ks) {
     const int buf = ks & 1;
-    if (ks + 1 < Tile<D>::KS) load(ks + 1, buf ^ 1);
+    if (ks + 1 < KS) load(ks + 1, buf ^ 1);
     __builtin_amdgcn_sched_barrier(0);
+    if (ks == 0) {
+      f32x16 z;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (ks == 0) {
-          f32x16 z;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) z[v] = 0.f;
-          s[mb][nb] = mfma32(ka[buf][mb], qb[buf][nb], z);
-        } else {
-          s[mb][nb] = mfma32(ka[buf][mb], qb[buf][nb], s[mb][nb]);
-        }
-      }
+      for (int v = 0; v < 16; ++v) z[v] = 0.f;
+      s[0] = mfma32(ka[buf][0], qf[ks], z);
+      s[1] = mfma32(ka[buf][1], qf[ks], z);
+    } else {
+      s[0] = mfma32(ka[buf][0], qf[ks], s[0]);
+      s[1] = mfma32(ka[buf][1], qf[ks], s[1]);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Same product with Q^T held in VGPRs (used where registers are plentiful).
-template <int D>
-__device__ __forceinline__ void qk_tile_regs(const __bf16* sk, const bf16x8 (&qf)[2][D / 16],
-                                             f32x16 (&s)[2][2], int lane) {
+// Causal / ragged masking (when `masked`) and the row max over the 64 keys of the tile.
+__device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0, int row, int N,
+                                          int lane) {
+  const int hh = lane >> 5;
+  if (masked) {
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int key = key0 + mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+        if (key > row || row >= N) s[mb][v] = kNegInf;
+      }
+  }
+  float mx = kNegInf;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[mb][nb][v] = 0.f;
-  const int rl = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int ks = 0; ks < Tile<D>::KS; ++ks) {
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const bf16x8 a = lds_frag<D>(sk, mb * 32 + rl, 2 * ks + hh);
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) s[mb][nb] = mfma32(a, qf[nb][ks], s[mb][nb]);
-    }
-  }
-}
-
-template <int D>
-__device__ __forceinline__ void load_q_regs(const __bf16* qbase, long long qst, int row0, int N,
-                                            bf16x8 (&qf)[2][D / 16], int lane) {
-  const int rl = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = row0 + nb * 32 + rl;
-#pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      const uint4 x =
-          *reinterpret_cast<const uint4*>(qbase + min(row, N - 1) * qst + ks * 16 + 8 * hh);
-      const uint4 y = row < N ? x : make_uint4(0, 0, 0, 0);
-      qf[nb][ks] = __builtin_bit_cast(bf16x8, y);
-    }
-  }
-}
-
-// Causal / ragged masking (when `masked`) and the per-row max over the 64 keys of the tile.
-__device__ __forceinline__ void tile_rowmax(f32x16 (&s)[2][2], float (&rmax)[2], bool masked,
-                                            int key0, int row0, int N, int lane) {
-  const int rl = lane & 31, hh = lane >> 5;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int row = row0 + nb * 32 + rl;
-    if (masked) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = key0 + mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-          if (key > row || row >= N) s[mb][nb][v] = kNegInf;
-        }
-    }
-    float mx = kNegInf;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][nb][v]);
-    rmax[nb] = half_max(mx);
-  }
+    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
+  return half_max(mx);
 }
 
 // Online softmax (BLASST blog, "FlashAttention": running max m, sum l, accumulator O, rescale
 // by exp(m_old - m_new)). The exponent reference mref moves only when a row's true max mt
-// exceeds it by more than kLazy in the exp2 domain ("rescale ... when needed", paper notes, Key
-// Designs 3): exponentials stay <= 2^kLazy and O / l is unchanged, while the O rescale (a VALU
-// pass over the accumulators) becomes rare. mt is the exact running max that the relative gate
-// compares against.
+// exceeds it by more than kLazy in the exp2 domain: exponentials stay <= 2^kLazy and O / l is
+// unchanged, while the O rescale (a vector pass over the accumulators) becomes rare. mt is the
+// exact running max that the relative gate compares against.
 constexpr float kLazy = 8.f;
 
 struct RowState {
-  float mt[2], mref[2], l[2];
+  float mt, mref, l;
 };
 
 // Update the running max for a kept tile. Returns true (wave-uniform) when the reference
-// moved; alpha then holds the factors O and l must be scaled by after the previous PV.
-__device__ __forceinline__ bool softmax_reference(RowState& st, const float (&rmax)[2], float c,
-                                                  float (&alpha)[2]) {
-  float mn[2];
-  bool move = false;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    mn[nb] = fmaxf(st.mt[nb], rmax[nb]);
-    st.mt[nb] = mn[nb];
-    move |= (mn[nb] - st.mref[nb]) * c > kLazy;    // false for rows that see nothing yet
-  }
-  const bool moved = __any(move);
+// moved; alpha then holds the factor O and l must be scaled by after the previous PV.
+__device__ __forceinline__ bool update_reference(RowState& st, float rmax, float c,
+                                                 float& alpha) {
+  const float mn = fmaxf(st.mt, rmax);
+  st.mt = mn;
+  const bool moved = __any((mn - st.mref) * c > kLazy);   // false for rows that see nothing yet
   if (moved) {
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const float mu = (mn[nb] == kNegInf) ? 0.f : mn[nb];
-      alpha[nb] = __builtin_amdgcn_exp2f((st.mref[nb] - mu) * c);   // 0 on the first block
-      st.mref[nb] = mu;
-    }
+    const float mu = (mn == kNegInf) ? 0.f : mn;
+    alpha = __builtin_amdgcn_exp2f((st.mref - mu) * c);   // 0 on the first block
+    st.mref = mu;
   }
   return moved;
 }
 
-// Wait states between VALU writes of P and the first PV MFMA reading it.
-__device__ __forceinline__ void pv_operands_ready(bf16x8 (&pb)[2][4]) {
-  asm volatile("s_nop 4"
-               : "+v"(pb[0][0]), "+v"(pb[0][1]), "+v"(pb[0][2]), "+v"(pb[0][3]),
-                 "+v"(pb[1][0]), "+v"(pb[1][1]), "+v"(pb[1][2]), "+v"(pb[1][3]));
-}
-
-// Keep P's registers allocated until here (the MFMAs issued before may still read them).
-__device__ __forceinline__ void keep_alive(const bf16x8 (&pb)[2][4]) {
-  asm volatile("" ::"v"(pb[0][0]), "v"(pb[0][1]), "v"(pb[0][2]), "v"(pb[0][3]), "v"(pb[1][0]),
-               "v"(pb[1][1]), "v"(pb[1][2]), "v"(pb[1][3]));
-}
-
-// Wait out the MFMA result latency before VALU reads or writes of O (and before the next
-// MFMA after a VALU write of O).
-template <int MD>
-__device__ __forceinline__ void acc_ready(f32x16 (&o)[MD][2]);
-
-template <>
-__device__ __forceinline__ void acc_ready<4>(f32x16 (&o)[4][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]), "+a"(o[2][0]),
-                 "+a"(o[2][1]), "+a"(o[3][0]), "+a"(o[3][1]));
-}
-
-template <>
-__device__ __forceinline__ void acc_ready<2>(f32x16 (&o)[2][2]) {
-  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7"
-               : "+a"(o[0][0]), "+a"(o[0][1]), "+a"(o[1][0]), "+a"(o[1][1]));
-}
-
 // The PV product of the previous kept tile (MFMA, O^T += V^T P^T) interleaved with the
-// exponentials of the current kept tile (VALU): each MFMA is issued next to one element pair
-// of the softmax, so exp2 / convert / sum run while the matrix core is busy. P is rounded to
-// bf16 for the MFMA and l sums exactly those bf16 weights (two per v_dot2 against (1, 1)), so
-// O / l stays a convex combination of V rows.
+// exponentials of the current kept tile (VALU): each MFMA is issued next to one or two
+// element pairs of the softmax. P is rounded to bf16 for the MFMA and l sums exactly those
+// bf16 weights (two per v_dot2 against (1, 1)), so O / l stays a convex combination of V rows.
 template <int D, bool DO_PV, bool DO_EXP>
-__device__ __forceinline__ void pv_exp_block(const __bf16* sv, const bf16x8 (&pbp)[2][4],
-                                             f32x16 (&o)[D / 32][2], const f32x16 (&s)[2][2],
-                                             const float (&off)[2], float c,
-                                             bf16x8 (&pbn)[2][4], float (&sum)[2], int lane) {
+__device__ __forceinline__ void pv_exp32(const __bf16* sv, const bf16x8 (&pbp)[4],
+                                         f32x16 (&o)[D / 32], const f32x16 (&s)[2], float off,
+                                         float c, bf16x8 (&pbn)[4], float& sum, int lane) {
   constexpr int MD = D / 32;
-  constexpr int NSTEP = MD * 4;               // (k-step, M-block) pairs: 2 MFMAs each
-  constexpr int PAIRS = 32;                   // softmax element pairs per lane per tile
-  constexpr int PPS = PAIRS / NSTEP;          // pairs per step
+  constexpr int NSTEP = MD * 4;               // (k-step, M-block) pairs, one MFMA each
+  constexpr int PPS = 16 / NSTEP;             // softmax element pairs per step (16 per lane)
   bf16x2 ones;
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
-  bf16x8 pbl[2][4];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int ks2 = 0; ks2 < 4; ++ks2) pbl[nb][ks2] = pbp[nb][ks2];
   bf16x8 vb[3];
   if (DO_PV) {
-    pv_operands_ready(pbl);
     vb[0] = v_frag<D>(sv, 0 % MD, 0 / MD, lane);
     vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
   }
@@ -408,38 +296,25 @@ __device__ __forceinline__ void pv_exp_block(const __bf16* sv, const bf16x8 (&pb
     const int ks2 = st / MD, md = st % MD;
     if (DO_PV) {
       if (st + 2 < NSTEP) vb[(st + 2) % 3] = v_frag<D>(sv, (st + 2) % MD, (st + 2) / MD, lane);
-      mfma_acc(o[md][0], vb[st % 3], pbl[0][ks2]);
-      mfma_acc(o[md][1], vb[st % 3], pbl[1][ks2]);
+      o[md] = mfma32(vb[st % 3], pbp[ks2], o[md]);
     }
     if (DO_EXP) {
 #pragma unroll
       for (int pp = 0; pp < PPS; ++pp) {
         const int pi = st * PPS + pp;
-        const int nb = pi / 16, k2 = (pi / 4) % 4, e = 2 * (pi % 4);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][nb][(k2 & 1) * 8 + e], c, off[nb]));
-        const float p1 =
-            __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][nb][(k2 & 1) * 8 + e + 1], c, off[nb]));
+        const int k2 = pi / 4, e = 2 * (pi % 4);
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e], c, off));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e + 1], c, off));
         bf16x2 pr;
         pr[0] = (__bf16)p0;
         pr[1] = (__bf16)p1;
-        sum[nb] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum[nb], false);
-        pbn[nb][k2][e] = pr[0];
-        pbn[nb][k2][e + 1] = pr[1];
+        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+        pbn[k2][e] = pr[0];
+        pbn[k2][e + 1] = pr[1];
       }
     }
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (DO_PV) keep_alive(pbl);
-}
-
-template <int D>
-__device__ __forceinline__ void pv_tile(const __bf16* sv, const bf16x8 (&pb)[2][4],
-                                        f32x16 (&o)[D / 32][2], int lane) {
-  const f32x16 s0[2][2] = {};
-  const float off[2] = {0.f, 0.f};
-  bf16x8 dummy[2][4];
-  float sum[2] = {0.f, 0.f};
-  pv_exp_block<D, true, false>(sv, pb, o, s0, off, 0.f, dummy, sum, lane);
 }
 
 struct Unit {
@@ -466,25 +341,23 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
   return r;
 }
 
-// The wave's 64 query rows -> its own LDS tile (swizzled rows; rows past N re-read row N-1,
-// their scores are masked).
-template <int D>
-__device__ __forceinline__ void stage_q(const __bf16* qbase, long long qst, int row0, int N,
-                                        __bf16* sq, int lane) {
-  wg_copy_tile<D, Tile<D>::STR, 1>(qbase + (long long)row0 * qst, qst, N - row0, sq, 0, lane);
-}
+// ---------------------------------------------------------------------------------------------
+// Prefill kernel
+// ---------------------------------------------------------------------------------------------
+constexpr int kRows = kRowsPerWave;
 
 template <int D, int BQ, int NW, int GATE>
-__global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
-  constexpr int NT = NW * 64;
-  constexpr int WPH = BQ / 64;             // waves per head
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
+    PrefillArgs a) {
+  constexpr int WPH = BQ / kRows;          // waves per head
   constexpr int HPW = NW / WPH;            // heads per workgroup
-  constexpr int MD = Tile<D>::MD;
+  constexpr int MD = Tile<D>::MD, KS = Tile<D>::KS;
+  constexpr int STR = Tile<D>::STR, STRV = Tile<D>::STRV;
+  constexpr int MK = copy_iters<STR, NW>(), MV = copy_iters<STRV, NW>();
   constexpr bool kGated = GATE != kDense;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sQ[NW][tile_elems<Tile<D>::STR, 1>()];
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<Tile<D>::STR, NW>()];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][tile_elems<Tile<D>::STRV, NW>()];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sV[2][64 * STRV];
   __shared__ float sGate[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -495,7 +368,8 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
   const int N = a.N;
-  const int row0 = i * BQ + rw * 64;
+  const int row0 = i * BQ + rw * kRows;
+  const int row = row0 + (lane & 31);
   const int n_off = (i * BQ) / BK;
   const int n_end = (min((i + 1) * BQ, N) - 1) / BK + 1;
   const bool ragged_rows = (i + 1) * BQ > N;
@@ -506,6 +380,7 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
   const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
   const __bf16* Vb = static_cast<const __bf16*>(a.v) + b * a.vs[0] + g * a.vs[2];
+  const long long kst = a.ks[1], vst = a.vs[1];
 
   float thr[HPW];
 #pragma unroll
@@ -518,86 +393,79 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
       thr[hh] = kNegInf;
   }
 
-  stage_q<D>(Qb, a.qs[1], row0, N, sQ[w], lane);
-  const __bf16* sq = sQ[w];
+  unsigned koff[MK], voff[MV];
+  copy_offsets<D, STR, NW>(koff, kst, w, lane);
+  copy_offsets<D, STRV, NW>(voff, vst, w, lane);
+  auto key_valid = [&](int j) { return min(BK, N - j * BK); };
+  const unsigned krow = (unsigned)kst * 2u, vrow = (unsigned)vst * 2u;
+  auto load_k = [&](int j, __bf16* dst) {
+    copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, key_valid(j), dst, w, lane);
+  };
+  auto load_v = [&](int j, __bf16* dst) {
+    copy_tile<D, STRV, NW>(voff, Vb + (long long)j * BK * vst, vrow, key_valid(j), dst, w, lane);
+  };
+
+  // K_0 first: its copy overlaps the Q fragment loads
+  load_k(0, sK[0]);
+  bf16x8 qf[KS];
+  load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
 
   RowState st;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    st.mt[nb] = kNegInf;
-    st.mref[nb] = kNegInf;
-    st.l[nb] = 0.f;
-  }
-  f32x16 o[MD][2];
+  st.mt = kNegInf;
+  st.mref = kNegInf;
+  st.l = 0.f;
+  f32x16 o[MD];
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[md][nb][v] = 0.f;
-  acc_ready<MD>(o);
+    for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
 
-  auto key_valid = [&](int j) { return min(BK, N - j * BK); };
-  constexpr int MK = tile_instr_per_wave<Tile<D>::STR, NW>();
-  constexpr int MV = tile_instr_per_wave<Tile<D>::STRV, NW>();
-  constexpr bool kStream = NW == 4;
-  unsigned koff[MK], voff[MV];
-  if constexpr (kStream) {
-    stream_offsets<D, Tile<D>::STR, NW, MK>(koff, a.ks[1], w, lane);
-    stream_offsets<D, Tile<D>::STRV, NW, MV>(voff, a.vs[1], w, lane);
-  }
   auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
   // Gate statistic of this wave for tile j, in raw score units (the scale is applied at the
   // decision): s_max for ABSOLUTE and DENSE and for the diagonal region in every mode; for
   // RELATIVE off-diagonal tiles, max over the wave's rows of (row max - running max).
-  auto publish = [&](int j, const float (&rmax)[2]) {
+  auto publish = [&](int j, float rmax, float* slot) {
     float x;
-    if (GATE == kRelative && j < n_off) {
-      x = kNegInf;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int row = row0 + nb * 32 + (lane & 31);
-        x = fmaxf(x, row < N ? rmax[nb] - st.mt[nb] : kNegInf);
-      }
-    } else {
-      x = fmaxf(rmax[0], rmax[1]);
-    }
+    if (GATE == kRelative && j < n_off)
+      x = row < N ? rmax - st.mt : kNegInf;
+    else
+      x = rmax;
     const float wst = wave_max(x);
-    if (lane == 0) sGate[j & 1][w] = wst;
+    if (lane == 0) slot[w] = wst;
   };
 
   // ---- prologue: K_0 staged, S_0 computed and published ----
-  wg_copy_tile<D, Tile<D>::STR, NW>(Kb, a.ks[1], key_valid(0), sK[0], w, lane);
   wait_vmem();
   __syncthreads();
-  if (n_end > 1) wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)BK * a.ks[1], a.ks[1], key_valid(1), sK[1], w, lane);
-  f32x16 sc[2][2];   // scores of the tile being processed
-  float rc[2];       // their row maxima
-  qk_tile<D>(sK[0], sq, sc, lane);
-  tile_rowmax(sc, rc, tile_masked(0), 0, row0, N, lane);
-  if (want_stat) publish(0, rc);
+  if (n_end > 1) load_k(1, sK[1]);
+  f32x16 sc[2];   // scores of the tile being processed
+  float rc;       // their row max
+  qk32<D>(sK[0], qf, sc, lane);
+  rc = rowmax32(sc, tile_masked(0), 0, row, N, lane);
+  if (want_stat) publish(0, rc, sGate[0]);
   wait_vmem();
   __syncthreads();
 
   int kept = 0;
   bool keep_prev = false;
   bool pending = false;
-  float pend[2] = {1.f, 1.f};
-  bf16x8 pbp[2][4];   // P of the previous kept tile, consumed by its PV in this iteration
+  float pend = 1.f;
+  bf16x8 pb[2][4];   // P of the last tiles of each parity; PV of tile t-1 reads pb[(t-1) & 1]
 
-  for (int t = 0; t < n_end; ++t) {
-    const int par = t & 1;
-    // ---- decision for tile t (statistics visible since the last barrier) ----
+  // One iteration: tile t's decision, exponentials and state update, the PV of tile t-1, and
+  // the scores and gate statistic of tile t+1. P = t & 1 picks the LDS and P buffers.
+  auto body = [&](int t, auto par) {
+    constexpr int P = decltype(par)::value;
     const bool diag = t >= n_off;
     bool mykeep = true, anyv = true;
     if (want_stat) {
       float hst[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        float x = sGate[par][hh * WPH];
+        float x = sGate[P][hh * WPH];
 #pragma unroll
-        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sGate[par][hh * WPH + r]);
+        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sGate[P][hh * WPH + r]);
         hst[hh] = x * a.scale;
       }
       if (kGated && !diag) {
@@ -619,119 +487,97 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
 
     // V_t (only if some head of the workgroup keeps tile t) and K_{t+2} go straight from
     // global memory into LDS; they are waited for at the end of the iteration
-    if constexpr (kStream) {
-      if (anyv)
-        stream_issue<D, Tile<D>::STRV, NW, MV>(voff, Vb + (long long)t * BK * a.vs[1], a.vs[1],
-                                               key_valid(t), sV[par], w, lane);
-      if (t + 2 < n_end)
-        stream_issue<D, Tile<D>::STR, NW, MK>(koff, Kb + (long long)(t + 2) * BK * a.ks[1],
-                                              a.ks[1], key_valid(t + 2), sK[par], w, lane);
-    } else {
-      if (anyv)
-        wg_copy_tile<D, Tile<D>::STRV, NW>(Vb + (long long)t * BK * a.vs[1], a.vs[1],
-                                           key_valid(t), sV[par], w, lane);
-      if (t + 2 < n_end)
-        wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)(t + 2) * BK * a.ks[1], a.ks[1],
-                                          key_valid(t + 2), sK[par], w, lane);
-    }
+    if (anyv) load_v(t, sV[P]);
+    if (t + 2 < n_end) load_k(t + 2, sK[P]);
 
     // a reference move of the last kept tile rescales O here: after that tile's predecessor
     // was accumulated (previous iteration) and before its own PV (this iteration)
     if (pending) {
-      acc_ready<MD>(o);
 #pragma unroll
       for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-          for (int v = 0; v < 16; ++v) o[md][nb][v] *= pend[nb];
-      acc_ready<MD>(o);
+        for (int v = 0; v < 16; ++v) o[md][v] *= pend;
       pending = false;
     }
-    // running max and exponent reference of tile t (kept tiles only)
-    float alpha[2] = {1.f, 1.f};
+    float alpha = 1.f, off = 0.f;
     bool moved = false;
-    float off[2] = {0.f, 0.f};
     if (mykeep) {
-      moved = softmax_reference(st, rc, c, alpha);
-      off[0] = -st.mref[0] * c;
-      off[1] = -st.mref[1] * c;
+      moved = update_reference(st, rc, c, alpha);
+      off = -st.mref * c;
     }
-    // PV of the previous kept tile with the exponentials of this one interleaved; when this
-    // tile is skipped those exponentials are discarded (VALU work under the PV MFMAs)
-    bf16x8 pbn[2][4];
-    float sum[2] = {0.f, 0.f};
-    if (keep_prev)
-      pv_exp_block<D, true, true>(sV[1 - par], pbp, o, sc, off, c, pbn, sum, lane);
-    else if (mykeep)
-      pv_exp_block<D, false, true>(sV[1 - par], pbp, o, sc, off, c, pbn, sum, lane);
+    float sum = 0.f;
+    if (keep_prev) {
+      if (mykeep)
+        pv_exp32<D, true, true>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
+      else
+        pv_exp32<D, true, false>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
+    } else if (mykeep) {
+      pv_exp32<D, false, true>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
+    }
     if (mykeep) {
       if (moved) {
-        st.l[0] *= alpha[0];
-        st.l[1] *= alpha[1];
-        pend[0] = alpha[0];
-        pend[1] = alpha[1];
+        st.l *= alpha;
+        pend = alpha;
         pending = true;
       }
-      st.l[0] += sum[0];
-      st.l[1] += sum[1];
+      st.l += sum;
     }
-    // unconditional: after a skipped tile the next PV is skipped, so pbp is then unused
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 4; ++ks2) pbp[nb][ks2] = pbn[nb][ks2];
 
     // scores of the next tile reuse the registers of this one
     if (t + 1 < n_end) {
-      qk_tile<D>(sK[1 - par], sq, sc, lane);
-      tile_rowmax(sc, rc, tile_masked(t + 1), (t + 1) * BK, row0, N, lane);
-      if (want_stat) publish(t + 1, rc);
+      qk32<D>(sK[P ^ 1], qf, sc, lane);
+      rc = rowmax32(sc, tile_masked(t + 1), (t + 1) * BK, row, N, lane);
+      if (want_stat) publish(t + 1, rc, sGate[P ^ 1]);
     }
     wait_vmem();
     __syncthreads();
     keep_prev = mykeep;
+  };
+
+  int t = 0;
+  for (; t + 1 < n_end; t += 2) {
+    body(t, IC<0>{});
+    body(t + 1, IC<1>{});
   }
+  if (t < n_end) body(t, IC<0>{});
+
   if (pending) {
-    acc_ready<MD>(o);
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[md][nb][v] *= pend[nb];
-    acc_ready<MD>(o);
+      for (int v = 0; v < 16; ++v) o[md][v] *= pend;
   }
-  if (keep_prev) pv_tile<D>(sV[(n_end - 1) & 1], pbp, o, lane);
-  acc_ready<MD>(o);
+  if (keep_prev) {   // always: the last tile is diagonal
+    float dsum = 0.f;
+    bf16x8 dummy[4];
+    if ((n_end - 1) & 1)
+      pv_exp32<D, true, false>(sV[1], pb[1], o, sc, 0.f, c, dummy, dsum, lane);
+    else
+      pv_exp32<D, true, false>(sV[0], pb[0], o, sc, 0.f, c, dummy, dsum, lane);
+  }
 
   // ---- epilogue: O / l (renormalised over kept + diagonal), kept counts ----
-  const int rl = lane & 31, hh = lane >> 5;
+  const int hh = lane >> 5;
+  const float inv = 1.f / half_sum(st.l);
+  if (row < N) {
+    const long long base = b * a.os[0] + (long long)row * a.os[1] + h * a.os[2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const float inv = 1.f / half_sum(st.l[nb]);
-    const int row = row0 + nb * 32 + rl;
-    if (row < N) {
-      const long long base = b * a.os[0] + (long long)row * a.os[1] + h * a.os[2];
+    for (int md = 0; md < MD; ++md) {
 #pragma unroll
-      for (int md = 0; md < MD; ++md) {
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int d0 = md * 32 + 8 * q4 + 4 * hh;
-          const float x0 = o[md][nb][4 * q4 + 0] * inv, x1 = o[md][nb][4 * q4 + 1] * inv;
-          const float x2 = o[md][nb][4 * q4 + 2] * inv, x3 = o[md][nb][4 * q4 + 3] * inv;
-          if (a.out_fp32) {
-            *reinterpret_cast<float4*>(static_cast<float*>(a.o) + base + d0) =
-                make_float4(x0, x1, x2, x3);
-          } else {
-            typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
-            bf16x4 y;
-            y[0] = (__bf16)x0;
-            y[1] = (__bf16)x1;
-            y[2] = (__bf16)x2;
-            y[3] = (__bf16)x3;
-            *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + base + d0) = y;
-          }
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int d0 = md * 32 + 8 * q4 + 4 * hh;
+        const float x0 = o[md][4 * q4 + 0] * inv, x1 = o[md][4 * q4 + 1] * inv;
+        const float x2 = o[md][4 * q4 + 2] * inv, x3 = o[md][4 * q4 + 3] * inv;
+        if (a.out_fp32) {
+          *reinterpret_cast<float4*>(static_cast<float*>(a.o) + base + d0) =
+              make_float4(x0, x1, x2, x3);
+        } else {
+          bf16x4 y;
+          y[0] = (__bf16)x0;
+          y[1] = (__bf16)x1;
+          y[2] = (__bf16)x2;
+          y[3] = (__bf16)x3;
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.o) + base + d0) = y;
         }
       }
     }
@@ -742,16 +588,23 @@ __global__ __launch_bounds__(NW * 64, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------------------------
 // Calibration: per (b, h, i) the off-diagonal block maxima, then the k-th highest per budget.
+// Waves of 32 rows as in the prefill kernel, QK only; the per-wave tile maxima collect in LDS.
+// ---------------------------------------------------------------------------------------------
 template <int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void calibrate_kernel(
+    CalibArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int WPH = BQ / 64;
+  constexpr int WPH = BQ / kRows;
   constexpr int HPW = NW / WPH;
   constexpr int MAXJ = kCalibMaxKeyBlocks;
+  constexpr int STR = Tile<D>::STR;
+  constexpr int MK = copy_iters<STR, NW>();
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][tile_elems<Tile<D>::STR, NW>()];
-  __shared__ float sW[NW][MAXJ];
+  __shared__ __attribute__((aligned(16))) __bf16 sK[2][64 * STR];
+  __shared__ float sW[HPW][MAXJ];
+  __shared__ float sPart[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hw = w / WPH, rw = w % WPH;
@@ -760,52 +613,56 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
   const int N = a.N;
-  const int row0 = i * BQ + rw * 64;
+  const int row0 = i * BQ + rw * kRows;
+  const int row = row0 + (lane & 31);
   const int n_off = (i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
 
   if (n_off > 0) {
     const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
     const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
-    bf16x8 qf[2][D / 16];
-    load_q_regs<D>(Qb, a.qs[1], row0, N, qf, lane);
-    wg_copy_tile<D, Tile<D>::STR, NW>(Kb, a.ks[1], BK, sK[0], w, lane);
+    const long long kst = a.ks[1];
+    unsigned koff[MK];
+    copy_offsets<D, STR, NW>(koff, kst, w, lane);
+    bf16x8 qf[D / 16];
+    const unsigned krow = (unsigned)kst * 2u;
+    copy_tile<D, STR, NW>(koff, Kb, krow, BK, sK[0], w, lane);
+    load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < n_off; ++t) {
       if (t + 1 < n_off)
-        wg_copy_tile<D, Tile<D>::STR, NW>(Kb + (long long)(t + 1) * BK * a.ks[1], a.ks[1], BK, sK[(t + 1) & 1],
-                            w, lane);
-      f32x16 s[2][2];
-      float rmax[2];
-      qk_tile_regs<D>(sK[t & 1], qf, s, lane);
-      tile_rowmax(s, rmax, ragged_rows, t * BK, row0, N, lane);
-      const float st = wave_max(fmaxf(rmax[0], rmax[1]));
-      if (lane == 0) sW[w][t] = st * a.scale;
+        copy_tile<D, STR, NW>(koff, Kb + (long long)(t + 1) * BK * kst, krow, BK,
+                              sK[(t + 1) & 1], w, lane);
+      f32x16 s[2];
+      qk32<D>(sK[t & 1], qf, s, lane);
+      const float rmax = rowmax32(s, ragged_rows, t * BK, row, N, lane);
+      const float wst = wave_max(rmax);
+      if (lane == 0) sPart[w] = wst;
       wait_vmem();
+      __syncthreads();
+      if (tid < HPW) {
+        float x = sPart[tid * WPH];
+        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sPart[tid * WPH + r]);
+        sW[tid][t] = x * a.scale;
+      }
       __syncthreads();
     }
   }
-  // merge the waves of each head into the list of its first wave; pad to a power of two
+  // pad each head's list to a power of two with -inf, then an ascending bitonic sort
   int P = 1;
   while (P < n_off) P <<= 1;
   for (int idx = tid; idx < HPW * P; idx += NT) {
     const int hh = idx / P, t = idx % P;
-    float x = kNegInf;
-    if (t < n_off) {
-      x = sW[hh * WPH][t];
-      for (int r = 1; r < WPH; ++r) x = fmaxf(x, sW[hh * WPH + r][t]);
-    }
-    sW[hh * WPH][t] = x;
+    if (t >= n_off) sW[hh][t] = kNegInf;
   }
   __syncthreads();
-  // ascending bitonic sort of each head's list
   for (int k = 2; k <= P; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       for (int idx = tid; idx < HPW * P; idx += NT) {
         const int hh = idx / P, x = idx % P, y = x ^ j;
         if (y > x) {
-          float* L = sW[hh * WPH];
+          float* L = sW[hh];
           const float u = L[x], v = L[y];
           const bool asc = (x & k) == 0;
           if ((u > v) == asc) {
@@ -820,7 +677,7 @@ __global__ __launch_bounds__(NW * 64, 1) void calibrate_kernel(CalibArgs a) {
   if (rw == 0) {
     for (int kk = lane; kk < a.n_budgets; kk += 64) {
       const int kb = a.budgets[kk];
-      const float r = (n_off >= kb) ? sW[w][P - kb] : kNegInf;
+      const float r = (n_off >= kb) ? sW[hw][P - kb] : kNegInf;
       a.kth[(((long long)kk * a.B + b) * a.Hq + h) * a.nqb + i] = r;
     }
   }
@@ -845,32 +702,38 @@ hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t strea
   return hipGetLastError();
 }
 
+// Waves per workgroup: BQ / 32 waves per head times 1, 2 or 4 heads (BQ = 128: 4 or 8 waves;
+// BQ = 64: 2, 4 or 8 waves).
 template <int D, int BQ>
 hipError_t launch_prefill_nw(const PrefillArgs& a, int nw, int gate, hipStream_t stream) {
-  if (BQ == 64 && nw == 1) return launch_prefill_gate<D, BQ, (BQ == 64 ? 1 : 2)>(a, gate, stream);
-  if (nw == 2) return launch_prefill_gate<D, BQ, 2>(a, gate, stream);
-  return launch_prefill_gate<D, BQ, 4>(a, gate, stream);
+  switch (nw) {
+    case 8: return launch_prefill_gate<D, BQ, 8>(a, gate, stream);
+    case 4: return launch_prefill_gate<D, BQ, 4>(a, gate, stream);
+    default: return launch_prefill_gate<D, BQ, BQ / kRows>(a, gate, stream);
+  }
+}
+
+template <int D, int BQ, int NW>
+hipError_t launch_calib_wg(const CalibArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((calibrate_kernel<D, BQ, NW>), dim3(a.units * a.nqb), dim3(NW * 64), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 template <int D, int BQ>
 hipError_t launch_calib_nw(const CalibArgs& a, int nw, hipStream_t stream) {
-  const dim3 grid(a.units * a.nqb);
-  if (BQ == 64 && nw == 1) {
-    constexpr int NW = BQ == 64 ? 1 : 2;
-    hipLaunchKernelGGL((calibrate_kernel<D, BQ, NW>), grid, dim3(NW * 64), 0, stream, a);
-  } else if (nw == 2) {
-    hipLaunchKernelGGL((calibrate_kernel<D, BQ, 2>), grid, dim3(128), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL((calibrate_kernel<D, BQ, 4>), grid, dim3(256), 0, stream, a);
+  switch (nw) {
+    case 8: return launch_calib_wg<D, BQ, 8>(a, stream);
+    case 4: return launch_calib_wg<D, BQ, 4>(a, stream);
+    default: return launch_calib_wg<D, BQ, BQ / kRows>(a, stream);
   }
-  return hipGetLastError();
 }
 
 }  // namespace
 
 int waves_per_workgroup(int block_q, int group) {
-  const int wph = block_q / 64;
-  int hpw = 4 / wph;
+  const int wph = block_q / kRows;
+  int hpw = 8 / wph;
   while (hpw > 1 && group % hpw != 0) hpw >>= 1;
   return hpw * wph;
 }

@@ -75,12 +75,12 @@ def test_tiny_dense(tiny):
 # Mid-size cases covering every workgroup shape, ragged tails and GQA
 # ---------------------------------------------------------------------------------------------
 SHAPES = {  # name: (B, N, Hq, Hkv, d, Bq)
-    "llama_like_ragged": (1, 1000, 8, 2, 128, 128),       # 4 waves: 2 heads x 128 rows
-    "d128_bq64_g4": (1, 700, 8, 2, 128, 64),              # 4 waves: 4 heads x 64 rows
-    "d64_bq128_g1": (1, 515, 2, 2, 64, 128),              # 2 waves: 1 head x 128 rows
-    "d64_bq64_g2": (2, 333, 4, 2, 64, 64),                # 2 waves, batch 2
-    "d64_bq64_g1": (1, 200, 1, 1, 64, 64),                # 1 wave
-    "d128_bq64_g1": (1, 130, 2, 2, 128, 64),              # 1 wave, d = 128
+    "llama_like_ragged": (1, 1000, 8, 2, 128, 128),       # 8 waves: 2 heads x 128 rows
+    "d128_bq64_g4": (1, 700, 8, 2, 128, 64),              # 8 waves: 4 heads x 64 rows
+    "d64_bq128_g1": (1, 515, 2, 2, 64, 128),              # 4 waves: 1 head x 128 rows
+    "d64_bq64_g2": (2, 333, 4, 2, 64, 64),                # 4 waves: 2 heads, batch 2
+    "d64_bq64_g1": (1, 200, 1, 1, 64, 64),                # 2 waves
+    "d128_bq64_g1": (1, 130, 2, 2, 128, 64),              # 2 waves, d = 128
     "g8": (1, 384, 16, 2, 128, 128),                      # G = 8: two workgroups per KV group
 }
 
