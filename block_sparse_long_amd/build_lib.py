@@ -52,12 +52,14 @@ def build(isa_dir: str | None = None, verbose: bool = False) -> str:
     def compile_one(src: str) -> str:
         obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
         cmd = [hipcc, *FLAGS, "-x", "hip", "-c", src, "-o", obj]
-        if isa_dir:
-            os.makedirs(isa_dir, exist_ok=True)
-            cmd += ["--save-temps"]
-        r = subprocess.run(cmd, cwd=isa_dir or BUILD_DIR, capture_output=True, text=True)
+        r = subprocess.run(cmd, cwd=BUILD_DIR, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
+        if isa_dir and src.endswith(".hip"):
+            os.makedirs(isa_dir, exist_ok=True)
+            asm = os.path.join(isa_dir, os.path.basename(src)[:-4] + "-gfx950.s")
+            subprocess.run([hipcc, *FLAGS, "-x", "hip", "--offload-device-only", "-S",
+                            src, "-o", asm], check=True, capture_output=True)
         if verbose and r.stderr.strip():
             print(r.stderr, file=sys.stderr)
         return obj

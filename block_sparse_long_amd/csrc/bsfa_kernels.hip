@@ -45,6 +45,15 @@ typedef __attribute__((address_space(3))) void lds_void;
 template <int V>
 using IC = std::integral_constant<int, V>;
 
+// Calls f(IC<i>{}) for i = I .. E-1 (compile-time loop index).
+template <int I, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < E) {
+    f(IC<I>{});
+    static_for<I + 1, E>(f);
+  }
+}
+
 constexpr int BK = kBlockK;
 constexpr float kNegInf = -__builtin_huge_valf();
 
@@ -54,6 +63,14 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 __device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float, x); }
 __device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
+
+// max(a, b, c) as one v_max3_f32 without the operand canonicalisation that fmaxf implies in
+// IEEE mode (scores are finite or -inf here, never NaN).
+__device__ __forceinline__ float max3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 
 // max / sum of x over lanes l and l^32 (the two halves holding the same query row)
 __device__ __forceinline__ float half_max(float x) {
@@ -130,26 +147,57 @@ __device__ __forceinline__ void copy_offsets(unsigned* off, long long gst, int w
   }
 }
 
-// Copy one 64-row tile starting at gbase. For a ragged tile (valid < 64 rows) the chunks of
-// rows at or past `valid` are redirected to row valid - 1.
+// One direct global -> LDS copy instruction (16 bytes per lane, lane l to LDS lds + 16 l),
+// issued through inline asm: the compiler then does not track it, and in particular does not
+// make later LDS reads (of other buffers) wait for it; whoever reads the destination waits
+// for it with wait_vmem() before a barrier. gbase and lds are wave-uniform, voff per lane.
+// M0 (the LDS destination) is saved and restored around the copy.
+__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
+  const unsigned glo = __builtin_amdgcn_readfirstlane((unsigned)g);
+  const unsigned ghi = __builtin_amdgcn_readfirstlane((unsigned)(g >> 32));
+  const unsigned long long gs = ((unsigned long long)ghi << 32) | glo;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gs), "s"(m0)
+      : "memory");
+}
+
+// Round m of a tile copy: instruction k = w + NW*m of the tile, if it exists (wave-uniform;
+// only the last round can run past the tile). For a ragged tile (valid < 64 rows) the chunks
+// of rows at or past `valid` are redirected to row valid - 1.
+template <int D, int STRIDE, int NW>
+__device__ __forceinline__ void copy_round(int m, const unsigned* off, const __bf16* gbase,
+                                           unsigned row_bytes, int valid, __bf16* tile, int w,
+                                           int lane) {
+  constexpr int CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
+  const int k = w + NW * m;
+  if (m + 1 < M || k < CPS) {
+    unsigned o = off[m];
+    if (valid < 64) {
+      const int r = (64 * k + lane) / CPS;
+      o -= (unsigned)max(r - (valid - 1), 0) * row_bytes;
+    }
+    dma16(gbase, o, tile + k * 512);
+  }
+}
+
+// Copy one 64-row tile starting at gbase (all rounds).
 template <int D, int STRIDE, int NW>
 __device__ __forceinline__ void copy_tile(const unsigned* off, const __bf16* gbase,
                                           unsigned row_bytes, int valid, __bf16* tile, int w,
                                           int lane) {
-  constexpr int CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
-  const char* base = reinterpret_cast<const char*>(gbase);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int k = w + NW * m;
-    if (m + 1 < M || k < CPS) {     // wave-uniform; only the last round can run past the tile
-      unsigned o = off[m];
-      if (valid < 64) {
-        const int r = (64 * k + lane) / CPS;
-        o -= (unsigned)max(r - (valid - 1), 0) * row_bytes;
-      }
-      __builtin_amdgcn_global_load_lds(base + o, (lds_void*)(tile + k * 512), 16, 0, 0);
-    }
-  }
+  for (int m = 0; m < copy_iters<STRIDE, NW>(); ++m)
+    copy_round<D, STRIDE, NW>(m, off, gbase, row_bytes, valid, tile, w, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -242,7 +290,7 @@ __device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0,
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[mb][v]);
+    for (int v = 0; v < 16; v += 2) mx = max3(mx, s[mb][v], s[mb][v + 1]);
   return half_max(mx);
 }
 
@@ -272,49 +320,149 @@ __device__ __forceinline__ bool update_reference(RowState& st, float rmax, float
   return moved;
 }
 
-// The PV product of the previous kept tile (MFMA, O^T += V^T P^T) interleaved with the
-// exponentials of the current kept tile (VALU): each MFMA is issued next to one or two
-// element pairs of the softmax. P is rounded to bf16 for the MFMA and l sums exactly those
-// bf16 weights (two per v_dot2 against (1, 1)), so O / l stays a convex combination of V rows.
-template <int D, bool DO_PV, bool DO_EXP>
-__device__ __forceinline__ void pv_exp32(const __bf16* sv, const bf16x8 (&pbp)[4],
-                                         f32x16 (&o)[D / 32], const f32x16 (&s)[2], float off,
-                                         float c, bf16x8 (&pbn)[4], float& sum, int lane) {
-  constexpr int MD = D / 32;
-  constexpr int NSTEP = MD * 4;               // (k-step, M-block) pairs, one MFMA each
-  constexpr int PPS = 16 / NSTEP;             // softmax element pairs per step (16 per lane)
-  bf16x2 ones;
+// One pair of P entries of the current tile: exponentials of the scaled scores against the
+// exponent reference (off = -mref * c), rounded to bf16 for the PV MFMA, and their sum added to
+// the row sum; l sums exactly the bf16 weights the MFMA uses (two per v_dot2 against (1, 1)),
+// so O / l stays a convex combination of V rows. Pair p covers P^T elements 2(p%4), 2(p%4)+1
+// of k-step p/4, i.e. scores s[p/8][8 ((p/4) % 2) + 2(p%4) + {0, 1}].
+__device__ __forceinline__ void exp_pair(int p, const f32x16 (&s)[2], float off, float c,
+                                         bf16x8 (&pbn)[4], float& sum) {
+  const int k2 = p / 4, e = 2 * (p % 4);
+  const float p0 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e], c, off));
+  const float p1 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e + 1], c, off));
+  bf16x2 pr, ones;
+  pr[0] = (__bf16)p0;
+  pr[1] = (__bf16)p1;
   ones[0] = (__bf16)1.f;
   ones[1] = (__bf16)1.f;
-  bf16x8 vb[3];
-  if (DO_PV) {
-    vb[0] = v_frag<D>(sv, 0 % MD, 0 / MD, lane);
-    vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
-  }
-#pragma unroll
-  for (int st = 0; st < NSTEP; ++st) {
-    const int ks2 = st / MD, md = st % MD;
-    if (DO_PV) {
-      if (st + 2 < NSTEP) vb[(st + 2) % 3] = v_frag<D>(sv, (st + 2) % MD, (st + 2) / MD, lane);
+  sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
+  pbn[k2][e] = pr[0];
+  pbn[k2][e + 1] = pr[1];
+}
+
+constexpr int kPairs = 16;        // P pairs per lane per tile (32 rows x 64 keys / 64 lanes / 2)
+constexpr int kPairsQK = 8;       // of which issued under the QK MFMAs; the rest under PV
+
+// Copies issued next to the MFMAs of an iteration: V_t (once the decision is known, if some
+// head of the workgroup keeps tile t) during the PV phase and K_{t+2} during the QK phase.
+struct Copies {
+  const unsigned* koff;
+  const unsigned* voff;
+  const __bf16* kg;          // K_{t+2} (global) or nullptr
+  const __bf16* vg;          // V_t (global)
+  __bf16* kt;                // LDS destinations
+  __bf16* vt;
+  unsigned krow, vrow;
+  int kvalid, vvalid;
+  int w, lane;
+};
+
+// Steps [FIRST, LAST) of the PV product of the previous kept tile (O^T += V^T P^T, one MFMA per
+// (k-step, M-block); fragments issued two steps ahead into vb, the first two by pv_prefetch)
+// with, next to the MFMAs, exponential pairs 0 .. kPairsQK-1 of the current tile (do_exp) and
+// the V_t copy rounds (vload), both spread over steps DEC .. NSTEP-1.
+template <int D>
+__device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], int lane) {
+  constexpr int MD = D / 32;
+  vb[0] = v_frag<D>(sv, 0, 0, lane);
+  vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
+}
+
+template <int D, int NW, int FIRST, int LAST, int DEC>
+__device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, const __bf16* sv,
+                                         const bf16x8 (&pbp)[4], f32x16 (&o)[D / 32],
+                                         bf16x8 (&vb)[3], const f32x16 (&sc)[2], float off,
+                                         float c, bf16x8 (&pbn)[4], float& sum,
+                                         const Copies& cp, int lane) {
+  constexpr int MD = D / 32;
+  constexpr int NSTEP = MD * 4;
+  constexpr int MV = copy_iters<Tile<D>::STRV, NW>();
+  constexpr int NE = NSTEP - DEC > 0 ? NSTEP - DEC : 1;
+  static_for<FIRST, LAST>([&](auto stc) {
+    constexpr int st = decltype(stc)::value;
+    constexpr int ks2 = st / MD, md = st % MD;
+    if (do_pv) {
+      if constexpr (st + 2 < NSTEP)
+        vb[(st + 2) % 3] = v_frag<D>(sv, (st + 2) % MD, (st + 2) / MD, lane);
       o[md] = mfma32(vb[st % 3], pbp[ks2], o[md]);
     }
-    if (DO_EXP) {
+    if (vload) {
 #pragma unroll
-      for (int pp = 0; pp < PPS; ++pp) {
-        const int pi = st * PPS + pp;
-        const int k2 = pi / 4, e = 2 * (pi % 4);
-        const float p0 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e], c, off));
-        const float p1 = __builtin_amdgcn_exp2f(fmaf(s[k2 >> 1][(k2 & 1) * 8 + e + 1], c, off));
-        bf16x2 pr;
-        pr[0] = (__bf16)p0;
-        pr[1] = (__bf16)p1;
-        sum = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, sum, false);
-        pbn[k2][e] = pr[0];
-        pbn[k2][e + 1] = pr[1];
-      }
+      for (int r = 0; r < MV; ++r)
+        if (DEC + r * NE / MV == st)
+          copy_round<D, Tile<D>::STRV, NW>(r, cp.voff, cp.vg, cp.vrow, cp.vvalid, cp.vt, cp.w,
+                                           cp.lane);
+    }
+    if (do_exp && st >= DEC) {
+#pragma unroll
+      for (int pi = (st - DEC) * kPairsQK / NE; pi < (st - DEC + 1) * kPairsQK / NE; ++pi)
+        exp_pair(pi, sc, off, c, pbn, sum);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+}
+
+// S^T = K Q^T for the next tile, M-block outer (step st: block st / KS, k-step st % KS), each
+// step reading the next step's K fragment. Next to the MFMAs: the K_{t+2} copy rounds, the
+// remaining exponential pairs of the current tile (do_exp), and, during the second M-block,
+// the in-lane max over the first block's 16 scores (into mx).
+template <int D, int NW>
+__device__ __forceinline__ void qk_phase(bool do_exp, const __bf16* kbase,
+                                         const bf16x8 (&qf)[D / 16],
+                                         f32x16 (&sn)[2], const f32x16 (&sc)[2], float off,
+                                         float c, bf16x8 (&pbn)[4], float& sum,
+                                         const Copies& cp, float& mx) {
+  constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR, NST = 2 * KS;
+  constexpr int MK = copy_iters<Tile<D>::STR, NW>();
+  constexpr int NP = kPairs - kPairsQK;
+  bf16x8 ka[2];
+  ka[0] = *reinterpret_cast<const bf16x8*>(kbase);
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    const int mb = st / KS, ks = st % KS;
+    const int buf = st & 1;
+    if (st + 1 < NST) {
+      const int mb1 = (st + 1) / KS, ks1 = (st + 1) % KS;
+      ka[buf ^ 1] = *reinterpret_cast<const bf16x8*>(kbase + mb1 * 32 * STR + 16 * ks1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (ks == 0) {
+      f32x16 z;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) z[v] = 0.f;
+      sn[mb] = mfma32(ka[buf], qf[0], z);
+    } else {
+      sn[mb] = mfma32(ka[buf], qf[ks], sn[mb]);
+    }
+#pragma unroll
+    for (int r = 0; r < MK; ++r)
+      if (r * NST / MK == st && cp.kg)
+        copy_round<D, Tile<D>::STR, NW>(r, cp.koff, cp.kg, cp.krow, cp.kvalid, cp.kt, cp.w,
+                                        cp.lane);
+    if (do_exp) {
+#pragma unroll
+      for (int pi = kPairsQK + st * NP / NST; pi < kPairsQK + (st + 1) * NP / NST; ++pi)
+        exp_pair(pi, sc, off, c, pbn, sum);
+    }
+    if (mb == 1) {
+#pragma unroll
+      for (int e = ks * 16 / KS; e < (ks + 1) * 16 / KS; e += 2)
+        mx = max3(mx, sn[0][e], sn[0][e + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+}
+
+// Causal / ragged mask of a score tile (diagonal-region and ragged tiles only).
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int row, int N, int lane) {
+  const int hh = lane >> 5;
+#pragma unroll
+  for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = key0 + mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
+      if (key > row || row >= N) s[mb][v] = kNegInf;
+    }
 }
 
 struct Unit {
@@ -356,12 +504,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int MK = copy_iters<STR, NW>(), MV = copy_iters<STRV, NW>();
   constexpr bool kGated = GATE != kDense;
 
-  __shared__ __attribute__((aligned(16))) __bf16 sK[2][64 * STR];
-  __shared__ __attribute__((aligned(16))) __bf16 sV[2][64 * STRV];
-  __shared__ float sGate[2][NW];
+  // Separate objects per buffer: the compiler then sees that a direct copy into one buffer
+  // cannot alias reads of the other and does not wait for the copy before those reads.
+  __shared__ __attribute__((aligned(16))) __bf16 sK0[64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sK1[64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sV0[64 * STRV];
+  __shared__ __attribute__((aligned(16))) __bf16 sV1[64 * STRV];
+  __shared__ __attribute__((aligned(16))) float sGate[2][NW * kRows];   // per-row gate statistics
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
   const int hw = w / WPH, rw = w % WPH;
   const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
   const int b = un.b, g = un.g, i = un.i;
@@ -406,7 +558,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   };
 
   // K_0 first: its copy overlaps the Q fragment loads
-  load_k(0, sK[0]);
+  load_k(0, sK0);
   bf16x8 qf[KS];
   load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
 
@@ -422,113 +574,145 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
-  // Gate statistic of this wave for tile j, in raw score units (the scale is applied at the
-  // decision): s_max for ABSOLUTE and DENSE and for the diagonal region in every mode; for
-  // RELATIVE off-diagonal tiles, max over the wave's rows of (row max - running max).
+  // Gate statistic of each row of this wave for tile j, in raw score units (the scale is applied
+  // at the decision): the row max for ABSOLUTE and DENSE and for the diagonal region in every
+  // mode; for RELATIVE off-diagonal tiles, row max - running max (-inf for rows past N). Lanes
+  // l and l + 32 hold the same row and store the same value.
   auto publish = [&](int j, float rmax, float* slot) {
     float x;
     if (GATE == kRelative && j < n_off)
       x = row < N ? rmax - st.mt : kNegInf;
     else
       x = rmax;
-    const float wst = wave_max(x);
-    if (lane == 0) slot[w] = wst;
+    slot[w * kRows + (lane & 31)] = x;
   };
 
   // ---- prologue: K_0 staged, S_0 computed and published ----
   wait_vmem();
   __syncthreads();
-  if (n_end > 1) load_k(1, sK[1]);
-  f32x16 sc[2];   // scores of the tile being processed
-  float rc;       // their row max
-  qk32<D>(sK[0], qf, sc, lane);
-  rc = rowmax32(sc, tile_masked(0), 0, row, N, lane);
+  if (n_end > 1) load_k(1, sK1);
+  f32x16 sb[2][2];     // scores of the last tiles of each parity
+  float rc;            // row max of the newest scores
+  qk32<D>(sK0, qf, sb[0], lane);
+  rc = rowmax32(sb[0], tile_masked(0), 0, row, N, lane);
   if (want_stat) publish(0, rc, sGate[0]);
   wait_vmem();
   __syncthreads();
 
   int kept = 0;
   bool keep_prev = false;
-  bool pending = false;
-  float pend = 1.f;
-  bf16x8 pb[2][4];   // P of the last tiles of each parity; PV of tile t-1 reads pb[(t-1) & 1]
+  bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of tile t-1 reads pb[(t-1) & 1]
+  const int kfo = (lane & 31) * STR + 8 * (lane >> 5);
+  constexpr int NSTEP = 4 * MD;               // PV MFMA steps
+  constexpr int DEC = 2;                      // PV steps issued before the tile-t decision
+  constexpr int GV = WPH * kRows / 64;        // statistics per lane per head
 
-  // One iteration: tile t's decision, exponentials and state update, the PV of tile t-1, and
-  // the scores and gate statistic of tile t+1. P = t & 1 picks the LDS and P buffers.
+  Copies cp;
+  cp.koff = koff;
+  cp.voff = voff;
+  cp.krow = krow;
+  cp.vrow = vrow;
+  cp.w = w;
+  cp.lane = lane;
+
+  // One iteration over key tile t (P = t & 1 picks the LDS, P and score buffers):
+  //   PV phase: the PV product of tile t-1 (if kept); next to its first MFMAs the per-row
+  //     statistics of tile t are read and put to the vote (keep iff some row's statistic, times
+  //     the scale, reaches the threshold: the block-max rule), then V_t is copied (if some head
+  //     of the workgroup keeps t) and half of tile t's exponentials run;
+  //   QK phase: scores of tile t+1, next to which K_{t+2} is copied and the other half of the
+  //     exponentials and the first half of t+1's row max run; then t+1's statistics are
+  //     published and the one barrier makes them and both copies visible.
+  // The last iteration computes scores of a tile t+1 past the end from stale LDS and discards
+  // them, which keeps the loop body free of branches around the MFMAs.
   auto body = [&](int t, auto par) {
     constexpr int P = decltype(par)::value;
     const bool diag = t >= n_off;
+    float gv[HPW][GV];
+    if (want_stat) {
+#pragma unroll
+      for (int hh = 0; hh < HPW; ++hh)
+#pragma unroll
+        for (int k = 0; k < GV; ++k) gv[hh][k] = sGate[P][hh * WPH * kRows + 64 * k + lane];
+    }
+    cp.kg = (t + 2 < n_end) ? Kb + (long long)(t + 2) * BK * kst : nullptr;
+    cp.kt = P ? sK1 : sK0;
+    cp.kvalid = key_valid(t + 2);
+    cp.vg = Vb + (long long)t * BK * vst;
+    cp.vt = P ? sV1 : sV0;
+    cp.vvalid = key_valid(t);
+    const __bf16* const sv = P ? sV0 : sV1;     // V_{t-1}
+    bf16x8 vb[3];
+    float sum = 0.f;
+    if (keep_prev) pv_prefetch<D>(sv, vb, lane);
+    pv_steps<D, NW, 0, DEC, DEC>(keep_prev, false, false, sv, pb[P ^ 1], o, vb, sb[P], 0.f, c,
+                                 pb[P], sum, cp, lane);
+
     bool mykeep = true, anyv = true;
     if (want_stat) {
-      float hst[HPW];
+      float hv[HPW];
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        float x = sGate[P][hh * WPH];
+        float x = gv[hh][0];
 #pragma unroll
-        for (int r = 1; r < WPH; ++r) x = fmaxf(x, sGate[P][hh * WPH + r]);
-        hst[hh] = x * a.scale;
+        for (int k = 1; k < GV; ++k) x = fmaxf(x, gv[hh][k]);
+        hv[hh] = x * a.scale;
       }
       if (kGated && !diag) {
         anyv = false;
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
-          const bool k = hst[hh] >= thr[hh];
+          const bool k = __any(hv[hh] >= thr[hh]);
           anyv |= k;
           if (hh == hw) mykeep = k;
         }
       }
-      if (head_leader) {
-        if (!diag) kept += mykeep ? 1 : 0;
-        if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + t] = hst[hw];
+      if (a.dbg) {
+        float x = hv[0];
+#pragma unroll
+        for (int hh = 1; hh < HPW; ++hh) x = hh == hw ? hv[hh] : x;
+        x = wave_max(x);
+        if (head_leader) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + t] = x;
       }
-    } else if (head_leader && !diag) {
-      kept += 1;
     }
+    if (head_leader && !diag) kept += mykeep ? 1 : 0;
 
-    // V_t (only if some head of the workgroup keeps tile t) and K_{t+2} go straight from
-    // global memory into LDS; they are waited for at the end of the iteration
-    if (anyv) load_v(t, sV[P]);
-    if (t + 2 < n_end) load_k(t + 2, sK[P]);
-
-    // a reference move of the last kept tile rescales O here: after that tile's predecessor
-    // was accumulated (previous iteration) and before its own PV (this iteration)
-    if (pending) {
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[md][v] *= pend;
-      pending = false;
-    }
     float alpha = 1.f, off = 0.f;
     bool moved = false;
     if (mykeep) {
       moved = update_reference(st, rc, c, alpha);
       off = -st.mref * c;
     }
-    float sum = 0.f;
-    if (keep_prev) {
-      if (mykeep)
-        pv_exp32<D, true, true>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
-      else
-        pv_exp32<D, true, false>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
-    } else if (mykeep) {
-      pv_exp32<D, false, true>(sV[P ^ 1], pb[P ^ 1], o, sc, off, c, pb[P], sum, lane);
-    }
-    if (mykeep) {
-      if (moved) {
-        st.l *= alpha;
-        pend = alpha;
-        pending = true;
-      }
-      st.l += sum;
+    // rest of PV(t-1) with the first half of tile t's exponentials and the V_t copy
+    pv_steps<D, NW, DEC, NSTEP, DEC>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P], off,
+                                     c, pb[P], sum, cp, lane);
+    // P(t-1) is dead from here on (the next write of its buffer precedes the next read)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm("" : "=v"(pb[P ^ 1][k]));
+    // a reference move at tile t rescales O after PV(t-1) and before PV(t)
+    if (moved) {
+#pragma unroll
+      for (int md = 0; md < MD; ++md)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+      st.l *= alpha;
     }
 
-    // scores of the next tile reuse the registers of this one
-    if (t + 1 < n_end) {
-      qk32<D>(sK[P ^ 1], qf, sc, lane);
-      rc = rowmax32(sc, tile_masked(t + 1), (t + 1) * BK, row, N, lane);
-      if (want_stat) publish(t + 1, rc, sGate[P ^ 1]);
+    // scores of tile t+1 with the second half of tile t's exponentials and the K_{t+2} copy
+    const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K_{t+1}
+    float mx = kNegInf;
+    qk_phase<D, NW>(mykeep, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, cp, mx);
+    if (mykeep) st.l += sum;
+    if (tile_masked(t + 1)) {
+      mask_tile(sb[P ^ 1], (t + 1) * BK, row, N, lane);
+      mx = kNegInf;
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][0][v], sb[P ^ 1][0][v + 1]);
     }
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1]);
+    rc = half_max(mx);
+    if (want_stat) publish(t + 1, rc, sGate[P ^ 1]);
     wait_vmem();
     __syncthreads();
     keep_prev = mykeep;
@@ -541,19 +725,18 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
   if (t < n_end) body(t, IC<0>{});
 
-  if (pending) {
-#pragma unroll
-    for (int md = 0; md < MD; ++md)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) o[md][v] *= pend;
-  }
   if (keep_prev) {   // always: the last tile is diagonal
     float dsum = 0.f;
-    bf16x8 dummy[4];
-    if ((n_end - 1) & 1)
-      pv_exp32<D, true, false>(sV[1], pb[1], o, sc, 0.f, c, dummy, dsum, lane);
+    bf16x8 dummy[4], vb[3];
+    const int L = (n_end - 1) & 1;
+    const __bf16* const sv = L ? sV1 : sV0;
+    pv_prefetch<D>(sv, vb, lane);
+    if (L)
+      pv_steps<D, NW, 0, NSTEP, NSTEP>(true, false, false, sv, pb[1], o, vb, sb[0], 0.f, c,
+                                       dummy, dsum, cp, lane);
     else
-      pv_exp32<D, true, false>(sV[0], pb[0], o, sc, 0.f, c, dummy, dsum, lane);
+      pv_steps<D, NW, 0, NSTEP, NSTEP>(true, false, false, sv, pb[0], o, vb, sb[0], 0.f, c,
+                                       dummy, dsum, cp, lane);
   }
 
   // ---- epilogue: O / l (renormalised over kept + diagonal), kept counts ----
@@ -606,7 +789,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ float sW[HPW][MAXJ];
   __shared__ float sPart[NW];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = w / WPH, rw = w % WPH;
   const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
   const int b = un.b, g = un.g, i = un.i;
