@@ -65,11 +65,18 @@ __device__ __forceinline__ float bits_f(int x) { return __builtin_bit_cast(float
 __device__ __forceinline__ int f_bits(float x) { return __builtin_bit_cast(int, x); }
 
 // max(a, b, c) as one v_max3_f32 without the operand canonicalisation that fmaxf implies in
-// IEEE mode (scores are finite or -inf here, never NaN).
+// IEEE mode (scores are finite or -inf here, never NaN). The compiler cannot see into the asm,
+// so it cannot insert the wait states the hardware needs between an MFMA writing a VGPR and a
+// vector instruction reading it: a block of MFMA results is first read by a compiler-visible
+// instruction (first_max(), which the compiler delays as far as the hazard requires), and the
+// asm reads of the block follow it in the dependency chain.
 __device__ __forceinline__ float max3(float a, float b, float c) {
   float r;
   asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
   return r;
+}
+__device__ __forceinline__ float first_max(float acc, float a, float b) {
+  return fmaxf(acc, fmaxf(a, b));
 }
 
 // max / sum of x over lanes l and l^32 (the two halves holding the same query row)
@@ -151,7 +158,10 @@ __device__ __forceinline__ void copy_offsets(unsigned* off, long long gst, int w
 // issued through inline asm: the compiler then does not track it, and in particular does not
 // make later LDS reads (of other buffers) wait for it; whoever reads the destination waits
 // for it with wait_vmem() before a barrier. gbase and lds are wave-uniform, voff per lane.
-// M0 (the LDS destination) is saved and restored around the copy.
+// M0 (the LDS destination) is saved and restored around the copy. The scalar operands may have
+// just been written by v_readfirstlane, and a memory instruction reading an SGPR written by a
+// vector instruction needs 5 wait states; the asm supplies them itself (the compiler cannot
+// see the read): two moves plus s_nop 2.
 __device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
   typedef __attribute__((address_space(3))) const char lds_char;
   const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
@@ -163,7 +173,7 @@ __device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const vo
   asm volatile(
       "s_mov_b32 %0, m0\n\t"
       "s_mov_b32 m0, %3\n\t"
-      "s_nop 0\n\t"
+      "s_nop 2\n\t"
       "global_load_lds_dwordx4 %1, %2\n\t"
       "s_mov_b32 m0, %0"
       : "=&s"(saved)
@@ -290,7 +300,8 @@ __device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0,
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) mx = max3(mx, s[mb][v], s[mb][v + 1]);
+    for (int v = 0; v < 16; v += 2)
+      mx = (v == 0) ? first_max(mx, s[mb][v], s[mb][v + 1]) : max3(mx, s[mb][v], s[mb][v + 1]);
   return half_max(mx);
 }
 
@@ -343,24 +354,10 @@ __device__ __forceinline__ void exp_pair(int p, const f32x16 (&s)[2], float off,
 constexpr int kPairs = 16;        // P pairs per lane per tile (32 rows x 64 keys / 64 lanes / 2)
 constexpr int kPairsQK = 8;       // of which issued under the QK MFMAs; the rest under PV
 
-// Copies issued next to the MFMAs of an iteration: V_t (once the decision is known, if some
-// head of the workgroup keeps tile t) during the PV phase and K_{t+2} during the QK phase.
-struct Copies {
-  const unsigned* koff;
-  const unsigned* voff;
-  const __bf16* kg;          // K_{t+2} (global) or nullptr
-  const __bf16* vg;          // V_t (global)
-  __bf16* kt;                // LDS destinations
-  __bf16* vt;
-  unsigned krow, vrow;
-  int kvalid, vvalid;
-  int w, lane;
-};
-
 // Steps [FIRST, LAST) of the PV product of the previous kept tile (O^T += V^T P^T, one MFMA per
-// (k-step, M-block); fragments issued two steps ahead into vb, the first two by pv_prefetch)
+// (k-step, M-block); fragments read two steps ahead into vb, the first two by pv_prefetch)
 // with, next to the MFMAs, exponential pairs 0 .. kPairsQK-1 of the current tile (do_exp) and
-// the V_t copy rounds (vload), both spread over steps DEC .. NSTEP-1.
+// the MV rounds of the V_t copy (vload, copy_v(r)), both spread over steps DEC .. NSTEP-1.
 template <int D>
 __device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], int lane) {
   constexpr int MD = D / 32;
@@ -368,15 +365,14 @@ __device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], i
   vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
 }
 
-template <int D, int NW, int FIRST, int LAST, int DEC>
+template <int D, int FIRST, int LAST, int DEC, int MV, typename CopyV>
 __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, const __bf16* sv,
                                          const bf16x8 (&pbp)[4], f32x16 (&o)[D / 32],
                                          bf16x8 (&vb)[3], const f32x16 (&sc)[2], float off,
-                                         float c, bf16x8 (&pbn)[4], float& sum,
-                                         const Copies& cp, int lane) {
+                                         float c, bf16x8 (&pbn)[4], float& sum, int lane,
+                                         CopyV&& copy_v) {
   constexpr int MD = D / 32;
   constexpr int NSTEP = MD * 4;
-  constexpr int MV = copy_iters<Tile<D>::STRV, NW>();
   constexpr int NE = NSTEP - DEC > 0 ? NSTEP - DEC : 1;
   static_for<FIRST, LAST>([&](auto stc) {
     constexpr int st = decltype(stc)::value;
@@ -389,9 +385,7 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
     if (vload) {
 #pragma unroll
       for (int r = 0; r < MV; ++r)
-        if (DEC + r * NE / MV == st)
-          copy_round<D, Tile<D>::STRV, NW>(r, cp.voff, cp.vg, cp.vrow, cp.vvalid, cp.vt, cp.w,
-                                           cp.lane);
+        if (DEC + r * NE / MV == st) copy_v(r);
     }
     if (do_exp && st >= DEC) {
 #pragma unroll
@@ -403,17 +397,17 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
 }
 
 // S^T = K Q^T for the next tile, M-block outer (step st: block st / KS, k-step st % KS), each
-// step reading the next step's K fragment. Next to the MFMAs: the K_{t+2} copy rounds, the
-// remaining exponential pairs of the current tile (do_exp), and, during the second M-block,
-// the in-lane max over the first block's 16 scores (into mx).
-template <int D, int NW>
-__device__ __forceinline__ void qk_phase(bool do_exp, const __bf16* kbase,
+// step reading the next step's K fragment. Next to the MFMAs: the MK rounds of the K_{t+2}
+// copy (kload, copy_k(r)) on the first steps, the remaining exponential pairs of the current
+// tile (do_exp) and, during the second M-block, the in-lane max over the first block's 16
+// scores (into mx).
+template <int D, int MK, typename CopyK>
+__device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* kbase,
                                          const bf16x8 (&qf)[D / 16],
                                          f32x16 (&sn)[2], const f32x16 (&sc)[2], float off,
-                                         float c, bf16x8 (&pbn)[4], float& sum,
-                                         const Copies& cp, float& mx) {
+                                         float c, bf16x8 (&pbn)[4], float& sum, float& mx,
+                                         CopyK&& copy_k) {
   constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR, NST = 2 * KS;
-  constexpr int MK = copy_iters<Tile<D>::STR, NW>();
   constexpr int NP = kPairs - kPairsQK;
   bf16x8 ka[2];
   ka[0] = *reinterpret_cast<const bf16x8*>(kbase);
@@ -434,11 +428,11 @@ __device__ __forceinline__ void qk_phase(bool do_exp, const __bf16* kbase,
     } else {
       sn[mb] = mfma32(ka[buf], qf[ks], sn[mb]);
     }
+    if (kload) {
 #pragma unroll
-    for (int r = 0; r < MK; ++r)
-      if (r * NST / MK == st && cp.kg)
-        copy_round<D, Tile<D>::STR, NW>(r, cp.koff, cp.kg, cp.krow, cp.kvalid, cp.kt, cp.w,
-                                        cp.lane);
+      for (int r = 0; r < MK; ++r)
+        if (r * (NST / 2) / MK == st) copy_k(r);
+    }
     if (do_exp) {
 #pragma unroll
       for (int pi = kPairsQK + st * NP / NST; pi < kPairsQK + (st + 1) * NP / NST; ++pi)
@@ -447,7 +441,7 @@ __device__ __forceinline__ void qk_phase(bool do_exp, const __bf16* kbase,
     if (mb == 1) {
 #pragma unroll
       for (int e = ks * 16 / KS; e < (ks + 1) * 16 / KS; e += 2)
-        mx = max3(mx, sn[0][e], sn[0][e + 1]);
+        mx = e == 0 ? first_max(mx, sn[0][e], sn[0][e + 1]) : max3(mx, sn[0][e], sn[0][e + 1]);
     }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -553,9 +547,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto load_k = [&](int j, __bf16* dst) {
     copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, key_valid(j), dst, w, lane);
   };
-  auto load_v = [&](int j, __bf16* dst) {
-    copy_tile<D, STRV, NW>(voff, Vb + (long long)j * BK * vst, vrow, key_valid(j), dst, w, lane);
-  };
 
   // K_0 first: its copy overlaps the Q fragment loads
   load_k(0, sK0);
@@ -606,22 +597,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int NSTEP = 4 * MD;               // PV MFMA steps
   constexpr int DEC = 2;                      // PV steps issued before the tile-t decision
   constexpr int GV = WPH * kRows / 64;        // statistics per lane per head
-
-  Copies cp;
-  cp.koff = koff;
-  cp.voff = voff;
-  cp.krow = krow;
-  cp.vrow = vrow;
-  cp.w = w;
-  cp.lane = lane;
+  constexpr int MKR = copy_iters<STR, NW>(), MVR = copy_iters<STRV, NW>();
 
   // One iteration over key tile t (P = t & 1 picks the LDS, P and score buffers):
   //   PV phase: the PV product of tile t-1 (if kept); next to its first MFMAs the per-row
   //     statistics of tile t are read and put to the vote (keep iff some row's statistic, times
-  //     the scale, reaches the threshold: the block-max rule), then V_t is copied (if some head
-  //     of the workgroup keeps t) and half of tile t's exponentials run;
-  //   QK phase: scores of tile t+1, next to which K_{t+2} is copied and the other half of the
-  //     exponentials and the first half of t+1's row max run; then t+1's statistics are
+  //     the scale, reaches the threshold: the block-max rule); after it the V_t copy (if some
+  //     head of the workgroup keeps t) and half of tile t's exponentials run next to the MFMAs;
+  //   QK phase: scores of tile t+1 with the K_{t+2} copy, the other half of the exponentials
+  //     and the first half of t+1's row max next to the MFMAs; then t+1's statistics are
   //     published and the one barrier makes them and both copies visible.
   // The last iteration computes scores of a tile t+1 past the end from stale LDS and discards
   // them, which keeps the loop body free of branches around the MFMAs.
@@ -631,22 +615,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float gv[HPW][GV];
     if (want_stat) {
 #pragma unroll
-      for (int hh = 0; hh < HPW; ++hh)
-#pragma unroll
-        for (int k = 0; k < GV; ++k) gv[hh][k] = sGate[P][hh * WPH * kRows + 64 * k + lane];
+      for (int hh = 0; hh < HPW; ++hh) {
+        const float* g = sGate[P] + hh * WPH * kRows + GV * lane;
+        if constexpr (GV == 2) {
+          const float2 x = *reinterpret_cast<const float2*>(g);
+          gv[hh][0] = x.x;
+          gv[hh][GV - 1] = x.y;
+        } else {
+          gv[hh][0] = g[0];
+        }
+      }
     }
-    cp.kg = (t + 2 < n_end) ? Kb + (long long)(t + 2) * BK * kst : nullptr;
-    cp.kt = P ? sK1 : sK0;
-    cp.kvalid = key_valid(t + 2);
-    cp.vg = Vb + (long long)t * BK * vst;
-    cp.vt = P ? sV1 : sV0;
-    cp.vvalid = key_valid(t);
+    const bool kload = t + 2 < n_end;
+    const __bf16* const kg = Kb + (long long)(t + 2) * BK * kst;
+    const __bf16* const vg = Vb + (long long)t * BK * vst;
+    auto copy_k = [&](int r) {
+      copy_round<D, STR, NW>(r, koff, kg, krow, key_valid(t + 2), P ? sK1 : sK0, w, lane);
+    };
+    auto copy_v = [&](int r) {
+      copy_round<D, STRV, NW>(r, voff, vg, vrow, key_valid(t), P ? sV1 : sV0, w, lane);
+    };
     const __bf16* const sv = P ? sV0 : sV1;     // V_{t-1}
     bf16x8 vb[3];
     float sum = 0.f;
-    if (keep_prev) pv_prefetch<D>(sv, vb, lane);
-    pv_steps<D, NW, 0, DEC, DEC>(keep_prev, false, false, sv, pb[P ^ 1], o, vb, sb[P], 0.f, c,
-                                 pb[P], sum, cp, lane);
+    if (keep_prev) {
+      pv_prefetch<D>(sv, vb, lane);
+      pv_steps<D, 0, DEC, DEC, MVR>(true, false, false, sv, pb[P ^ 1], o, vb, sb[P], 0.f, c,
+                                    pb[P], sum, lane, copy_v);
+    }
 
     bool mykeep = true, anyv = true;
     if (want_stat) {
@@ -683,9 +679,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       moved = update_reference(st, rc, c, alpha);
       off = -st.mref * c;
     }
-    // rest of PV(t-1) with the first half of tile t's exponentials and the V_t copy
-    pv_steps<D, NW, DEC, NSTEP, DEC>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P], off,
-                                     c, pb[P], sum, cp, lane);
+    // rest of PV(t-1) with the first half of tile t's exponentials and the V_t copy (skipped
+    // as a whole when there is none of the three)
+    if (keep_prev || anyv)
+      pv_steps<D, DEC, NSTEP, DEC, MVR>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P],
+                                        off, c, pb[P], sum, lane, copy_v);
     // P(t-1) is dead from here on (the next write of its buffer precedes the next read)
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm("" : "=v"(pb[P ^ 1][k]));
@@ -698,10 +696,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st.l *= alpha;
     }
 
-    // scores of tile t+1 with the second half of tile t's exponentials and the K_{t+2} copy
+    // scores of tile t+1 with the second half of tile t's exponentials
     const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K_{t+1}
     float mx = kNegInf;
-    qk_phase<D, NW>(mykeep, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, cp, mx);
+    qk_phase<D, MKR>(mykeep, kload, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
     if (mykeep) st.l += sum;
     if (tile_masked(t + 1)) {
       mask_tile(sb[P ^ 1], (t + 1) * BK, row, N, lane);
@@ -710,7 +708,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][0][v], sb[P ^ 1][0][v + 1]);
     }
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1]);
+    for (int v = 0; v < 16; v += 2)
+      mx = v == 0 ? first_max(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1])
+                  : max3(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1]);
     rc = half_max(mx);
     if (want_stat) publish(t + 1, rc, sGate[P ^ 1]);
     wait_vmem();
@@ -732,11 +732,11 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const __bf16* const sv = L ? sV1 : sV0;
     pv_prefetch<D>(sv, vb, lane);
     if (L)
-      pv_steps<D, NW, 0, NSTEP, NSTEP>(true, false, false, sv, pb[1], o, vb, sb[0], 0.f, c,
-                                       dummy, dsum, cp, lane);
+      pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sv, pb[1], o, vb, sb[0], 0.f, c,
+                                      dummy, dsum, lane, [](int) {});
     else
-      pv_steps<D, NW, 0, NSTEP, NSTEP>(true, false, false, sv, pb[0], o, vb, sb[0], 0.f, c,
-                                       dummy, dsum, cp, lane);
+      pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sv, pb[0], o, vb, sb[0], 0.f, c,
+                                      dummy, dsum, lane, [](int) {});
   }
 
   // ---- epilogue: O / l (renormalised over kept + diagonal), kept counts ----
@@ -917,7 +917,7 @@ hipError_t launch_calib_nw(const CalibArgs& a, int nw, hipStream_t stream) {
 
 int waves_per_workgroup(int block_q, int group) {
   const int wph = block_q / kRows;
-  int hpw = 8 / wph;
+  int hpw = 4 / wph;
   while (hpw > 1 && group % hpw != 0) hpw >>= 1;
   return hpw * wph;
 }
