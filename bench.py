@@ -1,6 +1,7 @@
 """Benchmark: gated prefill attention on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick]
+    python bench.py --profile-once     # one 1 GiB copy + one gated call, for counter runs
 
 A step is one bsfa_prefill call over one batch of synthetic input already resident in HBM:
 exact QK^T on every causally visible tile, the gate, online softmax and PV on kept tiles.
@@ -9,8 +10,11 @@ every visible tile plus PV on every kept or diagonal tile, counted from the kern
 counts (2*Bq*Bk*d per tile product), divided by the time of the step. The same line carries
 the dense path of the same kernel (gate compiled out), the zero-skip taxes, the kept fraction,
 the roofline of the prefill kernel (HIP events on the launch stream) and the CPU oracle timed on
-a bounded sample of the same workload.
+a bounded sample of the same workload. roofline.traffic is the HBM bytes per launch that
+rocprofv3 counters measured for the current kernel source (profiles/traffic_<workload>.json,
+FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy); it is null when the kernel source changed.
 """
+import hashlib
 import argparse
 import json
 import math
@@ -35,7 +39,51 @@ def parse():
     ap.add_argument("--workload", default="llama_128k")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--profile-once", action="store_true",
+                    help="run a 1 GiB device copy and one gated call, then exit (counter runs)")
     return ap.parse_args()
+
+
+KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_long_amd", "csrc", "bsfa_kernels.hip")
+COPY_BYTES = 1 << 30
+
+
+def kernel_source_sha256():
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the gated call from the committed counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    return rec["hbm_bytes_per_launch"]
+
+
+def profile_once(args):
+    """The command the counter summaries are taken from: a plain 1 GiB device copy (the
+    scale reference for FETCH_SIZE / WRITE_SIZE), then one gated call of the workload."""
+    import torch
+    from block_sparse_long_amd import _lib
+    _lib.load_library()
+    dev = torch.device("cuda:0")
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    w = Workload(args.workload, dev)
+    mode = "absolute" if w.table is not None else "relative"
+    kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
+    w.call(mode, **kw)
+    torch.cuda.synchronize()
+    print(json.dumps({"profile_once": args.workload, "copy_bytes": COPY_BYTES,
+                      "kernel_source_sha256": kernel_source_sha256()}), flush=True)
 
 
 def block_ranges(N, Bq, Bk=64):
@@ -95,13 +143,19 @@ class Workload:
         rng = block_ranges(self.N, self.Bq)
         self.n_off_total = sum(n_off for n_off, _ in rng)
 
-    def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None):
+    def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None, workspace=None):
+        import torch
         from block_sparse_long_amd import _lib
+        if workspace is None and mode == "absolute":
+            if getattr(self, "workspace", None) is None:
+                n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq)
+                self.workspace = torch.empty(n, dtype=torch.uint8, device=self.Qd.device)
+            workspace = self.workspace
         _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, gate_mode=mode,
                           table=table if table is not None else
                           (self.dtable if mode == "absolute" else None),
                           budget_slice=budget_slice, log_lambda=log_lambda,
-                          kept_counts=self.counts)
+                          kept_counts=self.counts, workspace=workspace)
 
 
 def timed(fn, steps, warmup):
@@ -165,6 +219,9 @@ def main():
               "(the attention shards by KV head with no exchange; see the design notes)",
               file=sys.stderr)
         sys.exit(2)
+    if args.profile_once:
+        profile_once(args)
+        return
     import numpy as np
     import torch
     from block_sparse_long_amd import _lib
@@ -252,8 +309,9 @@ def main():
                    "budget_k": k, "calibrated_len": c["calib_n"] if k else None},
         "roofline": {"bound": "mfma", "achieved": round(gated["tflops"], 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gated["tflops"] / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                     "kernel": "prefill_kernel<128,128,8,gate>",
+                     "frac": round(gated["tflops"] / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload),
+                     "kernel": "prefill_kernel<128,128,4,gate>",
                      "flops_per_launch": gated["flops"]},
         "cpu_baseline": cpu,
         "extras": extras,

@@ -31,8 +31,8 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
 
-EXPORTED = ("bsfa_prefill", "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error",
-            "bsfa_version")
+EXPORTED = ("bsfa_prefill", "bsfa_prefill_workspace_bytes", "bsfa_calibrate_blockmax",
+            "bsfa_status_string", "bsfa_last_error", "bsfa_version")
 
 
 class BsfaProblem(ctypes.Structure):
@@ -76,7 +76,9 @@ def load_library(path: str = LIB_PATH):
     lib.bsfa_prefill.restype = ctypes.c_int32
     lib.bsfa_prefill.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, ctypes.POINTER(BsfaTable),
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp,
-                                 vp]
+                                 vp, ctypes.c_uint64, vp]
+    lib.bsfa_prefill_workspace_bytes.restype = ctypes.c_uint64
+    lib.bsfa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem), ctypes.c_int32]
     lib.bsfa_calibrate_blockmax.restype = ctypes.c_int32
     lib.bsfa_calibrate_blockmax.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp]
@@ -149,13 +151,15 @@ def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
 def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode="dense",
                  table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
                  kept_counts=None, kept_total=None, debug_block_stat=None,
-                 softmax_scale: float = 0.0, stream=None, out_dtype=None):
+                 softmax_scale: float = 0.0, stream=None, out_dtype=None, workspace=None):
     """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, N, Hkv, d] bf16 (device).
 
     O (allocated if None, dtype ``out_dtype`` or bf16), kept_counts (int32 [B, Hq, nqb]),
     kept_total (int64 [1], read as uint64) and debug_block_stat (fp32 [B, Hq, nqb, nkb]) are
     written by the kernel on ``stream`` (default: torch's current stream). ``table`` is a
-    block_sparse_long_amd.table.DeviceTable (needed for gate_mode "absolute"). Returns O.
+    block_sparse_long_amd.table.DeviceTable (needed for gate_mode "absolute"). ``workspace`` is a
+    device uint8 tensor of at least bsfa_prefill_workspace_bytes bytes for the absolute gate's
+    keep masks; None allocates one, and an empty tensor asks for the path without it. Returns O.
     """
     import torch
     lib = load_library()
@@ -171,10 +175,18 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                         ("debug_block_stat", debug_block_stat, torch.float32)):
         if t is not None and (t.dtype != dt or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if workspace is None:
+        nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is not None and workspace.numel() == 0:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.bsfa_prefill(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
                           ctypes.byref(tbl) if tbl is not None else None, int(budget_slice),
                           mode, float(log_lambda), _ptr(O), _ptr(kept_counts), _ptr(kept_total),
-                          _ptr(debug_block_stat), _stream_handle(stream, Q.device))
+                          _ptr(debug_block_stat), _ptr(workspace), ctypes.c_uint64(ws_bytes),
+                          _stream_handle(stream, Q.device))
     _check(st)
     return O
 
@@ -194,3 +206,11 @@ def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_
                                      _ptr(kth_out), _stream_handle(stream, Q.device))
     _check(st)
     return kth_out
+
+
+def bsfa_prefill_workspace_bytes(Q, K, *, block_q: int, block_k: int = 64,
+                                 gate_mode="absolute") -> int:
+    """Bytes of workspace bsfa_prefill can use for this problem and gate mode (0: none)."""
+    mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k)
+    return int(load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))

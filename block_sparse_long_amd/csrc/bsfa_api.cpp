@@ -97,12 +97,22 @@ const char* bsfa_status_string(int32_t s) {
 
 const char* bsfa_last_error(void) { return g_last_error; }
 
-int32_t bsfa_version(void) { return (1 << 16) | 0; }
+int32_t bsfa_version(void) { return (1 << 16) | 1; }
+
+uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) {
+  if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
+      p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
+    return 0;
+  const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
+  const uint64_t words = ceil_div(ceil_div(p->seqlen, p->block_k), 64);
+  return (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
+}
 
 bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
                          const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
                          float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
-                         float* debug_block_stat, void* stream) {
+                         float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
+                         void* stream) {
   bsfa_status s = check_problem(p, true);
   if (s != BSFA_OK) return s;
   if (gate_mode != BSFA_GATE_DENSE && gate_mode != BSFA_GATE_ABSOLUTE &&
@@ -138,6 +148,8 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
       return fail(BSFA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
   }
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 7u))
+    return fail(BSFA_ERR_ALIGN, "workspace is not 8-byte aligned");
   if ((kept_counts && (reinterpret_cast<uintptr_t>(kept_counts) & 3u)) ||
       (kept_total && (reinterpret_cast<uintptr_t>(kept_total) & 7u)) ||
       (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u)))
@@ -146,6 +158,14 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   const int nkb = ceil_div(p->seqlen, p->block_k);
   if ((long long)p->seqlen > (1ll << 30))
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d too large", p->seqlen);
+  if (gate_mode == BSFA_GATE_ABSOLUTE && nkb > bsfa::kMaxGateTiles)
+    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the absolute-gate limit %d", p->seqlen,
+                bsfa::kMaxGateTiles * bsfa::kBlockK);
+  const uint64_t ws_need = bsfa_prefill_workspace_bytes(p, gate_mode);
+  const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty;
+  if (use_masks && workspace_bytes < ws_need)
+    return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
+                (unsigned long long)workspace_bytes, (unsigned long long)ws_need);
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (kept_total) {
@@ -180,7 +200,7 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   a.G = p->heads_q / p->heads_kv;
   a.nqb = nqb;
   a.nkb = nkb;
-  const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
+  const int nw = bsfa::prefill_waves_per_workgroup(p->block_q, a.G, gate_mode);
   const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
@@ -190,6 +210,19 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   a.out_fp32 = p->out_dtype == BSFA_FP32;
   if ((long long)a.units * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+  // ABSOLUTE with a workspace: the gate sweep decides every block first (its own launch, so
+  // that all workgroups stream K in step), then the prefill kernel runs over the kept ones
+  a.keep_mask = nullptr;
+  a.mask_words = ceil_div(nkb, 64);
+  if (use_masks) {
+    a.keep_mask = static_cast<unsigned long long*>(workspace);
+    bsfa::PrefillArgs sw = a;
+    const int shpw = bsfa::gate_sweep_heads(p->block_q, a.G);
+    sw.units = p->batch * p->heads_kv * (a.G / shpw);
+    sw.xcd_map = (sw.units % 8) == 0;
+    hipError_t e = bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
+  }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, gate_mode, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();

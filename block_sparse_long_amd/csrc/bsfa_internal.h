@@ -28,6 +28,10 @@ struct PrefillArgs {
   float c_log2;                    // scale * log2(e)
   float log_lambda;                // RELATIVE threshold
   int out_fp32;
+  // ABSOLUTE: keep bitmasks from the gate sweep, [B][Hq][nqb][mask_words] (bit j of word
+  // j / 64: off-diagonal tile j kept), or nullptr to find them inside the prefill kernel
+  unsigned long long* keep_mask;
+  int mask_words;
 };
 
 struct CalibArgs {
@@ -53,9 +57,22 @@ constexpr int kRowsPerWave = 32;
 // number of waves; heads per workgroup = waves / (block_q / kRowsPerWave).
 int waves_per_workgroup(int block_q, int group);
 
+// The prefill kernel's workgroup: as above, except that the absolute gate runs one head per
+// workgroup (its keep decisions are made per head before the softmax pass).
+int prefill_waves_per_workgroup(int block_q, int group, int gate);
+
+// Largest number of off-diagonal key tiles per query block under the absolute gate (the
+// keep bitmask lives in LDS): 32768 tiles of 64 keys.
+constexpr int kMaxGateTiles = 32768;
+
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
                           hipStream_t stream);
 hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipStream_t stream);
+// The gate sweep for the absolute gate: fills a.keep_mask (and the off-diagonal entries of
+// a.dbg). a.units must describe launch_gate_sweep's own workgroups (gate_sweep_heads()).
+hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream);
+// Heads per workgroup of the gate sweep.
+int gate_sweep_heads(int block_q, int group);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 
 }  // namespace bsfa

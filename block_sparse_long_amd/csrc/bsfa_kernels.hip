@@ -78,6 +78,25 @@ __device__ __forceinline__ float max3(float a, float b, float c) {
 __device__ __forceinline__ float first_max(float acc, float a, float b) {
   return fmaxf(acc, fmaxf(a, b));
 }
+// max3 that is ordered after `dep` (an unused input), for asm reads of a block of MFMA results
+// that do not otherwise depend on its compiler-visible first read.
+__device__ __forceinline__ float max3_after(float a, float b, float c, float dep) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c), "v"(dep));
+  return r;
+}
+
+// max over the 16 scores of one MFMA result block and acc, as a shallow tree (the reduction
+// ends the iteration's critical path).
+__device__ __forceinline__ float block_max(float acc, const f32x16& s) {
+  const float a = first_max(acc, s[0], s[1]);
+  const float m1 = max3_after(s[2], s[3], s[4], a);
+  const float m2 = max3_after(s[5], s[6], s[7], a);
+  const float m3 = max3_after(s[8], s[9], s[10], a);
+  const float m4 = max3_after(s[11], s[12], s[13], a);
+  const float m5 = max3_after(s[14], s[15], s[15], a);
+  return max3(max3(a, m1, m2), max3(m3, m4, m5), m5);
+}
 
 // max / sum of x over lanes l and l^32 (the two halves holding the same query row)
 __device__ __forceinline__ float half_max(float x) {
@@ -488,6 +507,8 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
 // ---------------------------------------------------------------------------------------------
 constexpr int kRows = kRowsPerWave;
 
+constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
+
 template <int D, int BQ, int NW, int GATE>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     PrefillArgs a) {
@@ -496,7 +517,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr int MD = Tile<D>::MD, KS = Tile<D>::KS;
   constexpr int STR = Tile<D>::STR, STRV = Tile<D>::STRV;
   constexpr int MK = copy_iters<STR, NW>(), MV = copy_iters<STRV, NW>();
-  constexpr bool kGated = GATE != kDense;
+  // ABSOLUTE: the gate of a block depends only on its own maximum, so all off-diagonal
+  // maxima are found first (pass 1, scores only) and the softmax then runs over the kept
+  // tiles and the diagonal region (pass 2). RELATIVE decides tile by tile inside the loop.
+  constexpr bool kTwoPass = GATE == kAbsolute;
+  constexpr bool kLoopGate = GATE == kRelative;
+  static_assert(!kTwoPass || HPW == 1, "the absolute gate runs one head per workgroup");
 
   // Separate objects per buffer: the compiler then sees that a direct copy into one buffer
   // cannot alias reads of the other and does not wait for the copy before those reads.
@@ -505,6 +531,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) __bf16 sV0[64 * STRV];
   __shared__ __attribute__((aligned(16))) __bf16 sV1[64 * STRV];
   __shared__ __attribute__((aligned(16))) float sGate[2][NW * kRows];   // per-row gate statistics
+  __shared__ unsigned long long sMask[kTwoPass ? kMaskWords : 1];       // kept off-diagonal tiles
+  __shared__ float sStage[2][NW][2];                                     // pass 1 wave maxima
+  __shared__ int sKept;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
@@ -519,7 +548,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int n_off = (i * BQ) / BK;
   const int n_end = (min((i + 1) * BQ, N) - 1) / BK + 1;
   const bool ragged_rows = (i + 1) * BQ > N;
-  const bool want_stat = kGated || a.dbg != nullptr;
+  const bool want_stat = kLoopGate || a.dbg != nullptr;
   const bool head_leader = (rw == 0) && (lane == 0);
   const float c = a.c_log2;
 
@@ -548,10 +577,103 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, key_valid(j), dst, w, lane);
   };
 
-  // K_0 first: its copy overlaps the Q fragment loads
-  load_k(0, sK0);
   bf16x8 qf[KS];
   load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
+  auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
+
+  // ---- pass 1 (absolute gate): maxima of all off-diagonal tiles, two tiles per barrier ----
+  // A threshold of -inf keeps every block, so no maxima are needed then (unless they are
+  // dumped), and the sequence below is simply every tile.
+  int kept = 0, kept_all = 0;
+  const bool have_mask = kTwoPass && a.keep_mask != nullptr;
+  const bool two_pass = kTwoPass && n_off > 0 && (thr[0] != kNegInf || a.dbg != nullptr);
+  if (two_pass && have_mask) {
+    // the gate sweep already decided: copy this (b, h, i)'s mask into LDS and count it
+    const int nw64 = (n_off + 63) >> 6;
+    const unsigned long long* gm =
+        a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) * a.mask_words;
+    for (int x = tid; x < nw64; x += NW * 64) sMask[x] = gm[x];
+    __syncthreads();
+    if (w == 0 && lane == 0) {
+      for (int x = 0; x < nw64; ++x) kept += __builtin_popcountll(sMask[x]);
+      sKept = kept;
+    }
+    __syncthreads();
+    kept_all = sKept;
+  } else if (two_pass) {
+    // four K tiles in flight: the K buffers and the (not yet used) V buffers
+    auto kbuf = [&](int x) { return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sV0 : sV1; };
+    const int nw64 = (n_off + 63) >> 6;
+    for (int x = tid; x < nw64; x += NW * 64) sMask[x] = 0ull;
+    const int ng = (n_off + 1) >> 1;
+    auto load_group = [&](int gg, int p) {
+      load_k(2 * gg, kbuf(2 * p));
+      if (2 * gg + 1 < n_off) load_k(2 * gg + 1, kbuf(2 * p + 1));
+    };
+    // wave 0, lane 0: the block maxima of group gg (the waves' partial maxima in slot p) against
+    // the threshold; kept tiles set their bit
+    auto combine = [&](int gg, int p) {
+      if (w == 0 && lane == 0) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const int j = 2 * gg + k;
+          if (j < n_off) {
+            float x = sStage[p][0][k];
+#pragma unroll
+            for (int r = 1; r < NW; ++r) x = fmaxf(x, sStage[p][r][k]);
+            const float sm = x * a.scale;
+            if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
+            if (sm >= thr[0]) {
+              sMask[j >> 6] |= 1ull << (j & 63);
+              ++kept;
+            }
+          }
+        }
+      }
+    };
+    load_group(0, 0);
+    wait_vmem();
+    __syncthreads();
+    for (int gg = 0; gg < ng; ++gg) {
+      const int p = gg & 1;
+      if (gg + 1 < ng) load_group(gg + 1, p ^ 1);
+      f32x16 s2[2][2];
+      qk32<D>(kbuf(2 * p), qf, s2[0], lane);
+      const float m0 = rowmax32(s2[0], ragged_rows, 2 * gg * BK, row, N, lane);
+      float m1 = kNegInf;
+      if (2 * gg + 1 < n_off) {
+        qk32<D>(kbuf(2 * p + 1), qf, s2[1], lane);
+        m1 = rowmax32(s2[1], ragged_rows, (2 * gg + 1) * BK, row, N, lane);
+      }
+      const float w0 = wave_max(m0), w1 = wave_max(m1);
+      if (lane == 0) {
+        sStage[p][w][0] = w0;
+        sStage[p][w][1] = w1;
+      }
+      if (gg > 0) combine(gg - 1, p ^ 1);
+      wait_vmem();
+      __syncthreads();
+    }
+    combine(ng - 1, (ng - 1) & 1);
+    if (w == 0 && lane == 0) sKept = kept;
+    __syncthreads();
+    kept_all = sKept;
+  } else if (kTwoPass || GATE == kDense) {
+    kept = n_off;
+  }
+  // The tile after j in the sequence the softmax walks: with the pass-1 mask, the next kept
+  // off-diagonal tile and then the diagonal region; otherwise every tile.
+  auto next_tile = [&](int j) -> int {
+    ++j;
+    if (!two_pass || j >= n_off) return j;
+    int wi = j >> 6;
+    unsigned long long bits = sMask[wi] & (~0ull << (j & 63));
+    while (bits == 0ull) {
+      if (++wi << 6 >= n_off) return n_off;
+      bits = sMask[wi];
+    }
+    return min((wi << 6) + (int)__builtin_ctzll(bits), n_off);
+  };
 
   RowState st;
   st.mt = kNegInf;
@@ -562,8 +684,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int v = 0; v < 16; ++v) o[md][v] = 0.f;
-
-  auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
   // Gate statistic of each row of this wave for tile j, in raw score units (the scale is applied
   // at the decision): the row max for ABSOLUTE and DENSE and for the diagonal region in every
@@ -578,64 +698,68 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     slot[w * kRows + (lane & 31)] = x;
   };
 
-  // ---- prologue: K_0 staged, S_0 computed and published ----
+  // ---- prologue: the first two tiles of the sequence staged, scores of the first published ----
+  int t = next_tile(-1);
+  int t1 = next_tile(t);
+  load_k(t, sK0);
   wait_vmem();
   __syncthreads();
-  if (n_end > 1) load_k(1, sK1);
+  if (t1 < n_end) load_k(t1, sK1);
   f32x16 sb[2][2];     // scores of the last tiles of each parity
   float rc;            // row max of the newest scores
   qk32<D>(sK0, qf, sb[0], lane);
-  rc = rowmax32(sb[0], tile_masked(0), 0, row, N, lane);
-  if (want_stat) publish(0, rc, sGate[0]);
+  rc = rowmax32(sb[0], tile_masked(t), t * BK, row, N, lane);
+  if (want_stat) publish(t, rc, sGate[0]);
   wait_vmem();
   __syncthreads();
 
-  int kept = 0;
   bool keep_prev = false;
-  bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of tile t-1 reads pb[(t-1) & 1]
+  bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of the previous tile reads pb[P ^ 1]
   const int kfo = (lane & 31) * STR + 8 * (lane >> 5);
   constexpr int NSTEP = 4 * MD;               // PV MFMA steps
   constexpr int DEC = 2;                      // PV steps issued before the tile-t decision
   constexpr int GV = WPH * kRows / 64;        // statistics per lane per head
   constexpr int MKR = copy_iters<STR, NW>(), MVR = copy_iters<STRV, NW>();
 
-  // One iteration over key tile t (P = t & 1 picks the LDS, P and score buffers):
-  //   PV phase: the PV product of tile t-1 (if kept); next to its first MFMAs the per-row
-  //     statistics of tile t are read and put to the vote (keep iff some row's statistic, times
-  //     the scale, reaches the threshold: the block-max rule); after it the V_t copy (if some
-  //     head of the workgroup keeps t) and half of tile t's exponentials run next to the MFMAs;
-  //   QK phase: scores of tile t+1 with the K_{t+2} copy, the other half of the exponentials
-  //     and the first half of t+1's row max next to the MFMAs; then t+1's statistics are
-  //     published and the one barrier makes them and both copies visible.
-  // The last iteration computes scores of a tile t+1 past the end from stale LDS and discards
-  // them, which keeps the loop body free of branches around the MFMAs.
-  auto body = [&](int t, auto par) {
+  // One iteration over sequence position u (P = u & 1 picks the LDS, P and score buffers) with
+  // tile t and the next two tiles t1, t2 of the sequence:
+  //   PV phase: the PV product of the previous tile (if kept); for the relative gate, next to
+  //     its first MFMAs the per-row statistics of tile t are read and put to the vote (keep iff
+  //     some row's statistic reaches ln(lambda)); then the V_t copy (if some head of the
+  //     workgroup keeps t) and half of tile t's exponentials run next to the MFMAs;
+  //   QK phase: scores of tile t1 with the K_{t2} copy, the other half of the exponentials and
+  //     the first half of t1's row max next to the MFMAs; then t1's statistics are published
+  //     and the one barrier makes them and both copies visible.
+  // The last iteration computes scores of a tile past the end from stale LDS and discards them,
+  // which keeps the loop body free of branches around the MFMAs.
+  auto body = [&](auto par) {
     constexpr int P = decltype(par)::value;
+    const int t2 = next_tile(t1);
     const bool diag = t >= n_off;
     float gv[HPW][GV];
     if (want_stat) {
 #pragma unroll
       for (int hh = 0; hh < HPW; ++hh) {
-        const float* g = sGate[P] + hh * WPH * kRows + GV * lane;
+        const float* gp = sGate[P] + hh * WPH * kRows + GV * lane;
         if constexpr (GV == 2) {
-          const float2 x = *reinterpret_cast<const float2*>(g);
+          const float2 x = *reinterpret_cast<const float2*>(gp);
           gv[hh][0] = x.x;
           gv[hh][GV - 1] = x.y;
         } else {
-          gv[hh][0] = g[0];
+          gv[hh][0] = gp[0];
         }
       }
     }
-    const bool kload = t + 2 < n_end;
-    const __bf16* const kg = Kb + (long long)(t + 2) * BK * kst;
+    const bool kload = t2 < n_end;
+    const __bf16* const kg = Kb + (long long)t2 * BK * kst;
     const __bf16* const vg = Vb + (long long)t * BK * vst;
     auto copy_k = [&](int r) {
-      copy_round<D, STR, NW>(r, koff, kg, krow, key_valid(t + 2), P ? sK1 : sK0, w, lane);
+      copy_round<D, STR, NW>(r, koff, kg, krow, key_valid(t2), P ? sK1 : sK0, w, lane);
     };
     auto copy_v = [&](int r) {
       copy_round<D, STRV, NW>(r, voff, vg, vrow, key_valid(t), P ? sV1 : sV0, w, lane);
     };
-    const __bf16* const sv = P ? sV0 : sV1;     // V_{t-1}
+    const __bf16* const sv = P ? sV0 : sV1;     // V of the previous tile
     bf16x8 vb[3];
     float sum = 0.f;
     if (keep_prev) {
@@ -654,7 +778,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int k = 1; k < GV; ++k) x = fmaxf(x, gv[hh][k]);
         hv[hh] = x * a.scale;
       }
-      if (kGated && !diag) {
+      if (kLoopGate && !diag) {
         anyv = false;
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
@@ -671,7 +795,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (head_leader) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + t] = x;
       }
     }
-    if (head_leader && !diag) kept += mykeep ? 1 : 0;
+    if (kLoopGate && head_leader && !diag) kept += mykeep ? 1 : 0;
 
     float alpha = 1.f, off = 0.f;
     bool moved = false;
@@ -679,15 +803,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       moved = update_reference(st, rc, c, alpha);
       off = -st.mref * c;
     }
-    // rest of PV(t-1) with the first half of tile t's exponentials and the V_t copy (skipped
-    // as a whole when there is none of the three)
+    // rest of PV of the previous tile with the first half of tile t's exponentials and the V_t
+    // copy (skipped as a whole when there is none of the three)
     if (keep_prev || anyv)
       pv_steps<D, DEC, NSTEP, DEC, MVR>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P],
                                         off, c, pb[P], sum, lane, copy_v);
-    // P(t-1) is dead from here on (the next write of its buffer precedes the next read)
+    // the previous P is dead from here on (the next write of its buffer precedes the next read)
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm("" : "=v"(pb[P ^ 1][k]));
-    // a reference move at tile t rescales O after PV(t-1) and before PV(t)
+    // a reference move at tile t rescales O after the previous PV and before PV of tile t
     if (moved) {
 #pragma unroll
       for (int md = 0; md < MD; ++md)
@@ -696,42 +820,44 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st.l *= alpha;
     }
 
-    // scores of tile t+1 with the second half of tile t's exponentials
-    const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K_{t+1}
+    // scores of tile t1 with the second half of tile t's exponentials
+    const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K of t1
     float mx = kNegInf;
     qk_phase<D, MKR>(mykeep, kload, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
     if (mykeep) st.l += sum;
-    if (tile_masked(t + 1)) {
-      mask_tile(sb[P ^ 1], (t + 1) * BK, row, N, lane);
+    if (tile_masked(t1)) {
+      mask_tile(sb[P ^ 1], t1 * BK, row, N, lane);
       mx = kNegInf;
 #pragma unroll
       for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][0][v], sb[P ^ 1][0][v + 1]);
     }
-#pragma unroll
-    for (int v = 0; v < 16; v += 2)
-      mx = v == 0 ? first_max(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1])
-                  : max3(mx, sb[P ^ 1][1][v], sb[P ^ 1][1][v + 1]);
+    mx = block_max(mx, sb[P ^ 1][1]);
     rc = half_max(mx);
-    if (want_stat) publish(t + 1, rc, sGate[P ^ 1]);
+    if (want_stat) publish(t1, rc, sGate[P ^ 1]);
     wait_vmem();
     __syncthreads();
     keep_prev = mykeep;
+    t = t1;
+    t1 = t2;
   };
 
-  int t = 0;
-  for (; t + 1 < n_end; t += 2) {
-    body(t, IC<0>{});
-    body(t + 1, IC<1>{});
+  // sequence length: the kept off-diagonal tiles (all of them without the pass-1 mask) and the
+  // diagonal region
+  const int n_seq = (two_pass ? kept_all : n_off) + (n_end - n_off);
+  int u = 0;
+  for (; u + 1 < n_seq; u += 2) {
+    body(IC<0>{});
+    body(IC<1>{});
   }
-  if (t < n_end) body(t, IC<0>{});
+  if (u < n_seq) body(IC<0>{});
+  const int last = (n_seq - 1) & 1;   // parity of the last sequence position
 
   if (keep_prev) {   // always: the last tile is diagonal
     float dsum = 0.f;
     bf16x8 dummy[4], vb[3];
-    const int L = (n_end - 1) & 1;
-    const __bf16* const sv = L ? sV1 : sV0;
+    const __bf16* const sv = last ? sV1 : sV0;
     pv_prefetch<D>(sv, vb, lane);
-    if (L)
+    if (last)
       pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sv, pb[1], o, vb, sb[0], 0.f, c,
                                       dummy, dsum, lane, [](int) {});
     else
@@ -768,6 +894,120 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (head_leader) {
     if (a.kept_counts) a.kept_counts[((long long)b * a.Hq + h) * a.nqb + i] = kept;
     if (a.kept_total) atomicAdd(a.kept_total, (unsigned long long)kept);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Gate sweep (absolute gate; launched before the prefill kernel): for every (b, h, i) the
+// maxima of all off-diagonal tiles, two tiles per barrier, compared with T_eff(h, i); kept
+// tiles set their bit in the keep mask. Every workgroup does the same work per tile, so the
+// workgroups that share a KV head stream its K tiles in step and mostly from L2; the
+// workgroup's heads share each staged K tile.
+// ---------------------------------------------------------------------------------------------
+template <int D, int BQ, int NW>
+__global__ __launch_bounds__(NW * 64) void gate_sweep_kernel(PrefillArgs a) {
+  constexpr int WPH = BQ / kRows;
+  constexpr int HPW = NW / WPH;
+  constexpr int STR = Tile<D>::STR, KS = Tile<D>::KS;
+  constexpr int MK = copy_iters<STR, NW>();
+
+  __shared__ __attribute__((aligned(16))) __bf16 sKa[64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sKb[64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sKc[64 * STR];
+  __shared__ __attribute__((aligned(16))) __bf16 sKd[64 * STR];
+  __shared__ unsigned long long sM[HPW][kMaskWords];
+  __shared__ float sStage[2][NW][2];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = w / WPH, rw = w % WPH;
+  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
+  const int b = un.b, g = un.g, i = un.i;
+  const int h0 = g * a.G + un.hg * HPW;
+  const int h = h0 + hw;
+  const int N = a.N;
+  const int row0 = i * BQ + rw * kRows;
+  const int row = row0 + (lane & 31);
+  const int n_off = (i * BQ) / BK;
+  const bool ragged_rows = (i + 1) * BQ > N;
+  if (n_off == 0) return;   // uniform: nothing off-diagonal to decide
+
+  const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
+  const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
+  const long long kst = a.ks[1];
+  const unsigned krow = (unsigned)kst * 2u;
+  unsigned koff[MK];
+  copy_offsets<D, STR, NW>(koff, kst, w, lane);
+  auto load_k = [&](int j, __bf16* dst) {
+    copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, BK, dst, w, lane);
+  };
+  auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : x == 2 ? sKc : sKd; };
+  const float thr = a.thr[h * a.t_len + min(i, a.t_len - 1)];
+  // heads whose threshold is -inf keep everything without a mask (the softmax kernel does not
+  // read one then), so a workgroup of only such heads has nothing to decide unless the maxima
+  // are dumped
+  bool all_keep = a.dbg == nullptr;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)] == kNegInf;
+  if (all_keep) return;
+
+  const int nw64 = (n_off + 63) >> 6;
+  for (int x = tid; x < HPW * nw64; x += NW * 64) sM[x / nw64][x % nw64] = 0ull;
+  const int ng = (n_off + 1) >> 1;
+  auto load_group = [&](int gg, int p) {
+    load_k(2 * gg, kbuf(2 * p));
+    if (2 * gg + 1 < n_off) load_k(2 * gg + 1, kbuf(2 * p + 1));
+  };
+  // the first wave of each head, lane 0: block maxima of group gg (partial maxima of the
+  // head's waves in slot p) against the head's threshold
+  auto combine = [&](int gg, int p) {
+    if (rw == 0 && lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = 2 * gg + k;
+        if (j < n_off) {
+          float x = sStage[p][hw * WPH][k];
+#pragma unroll
+          for (int r = 1; r < WPH; ++r) x = fmaxf(x, sStage[p][hw * WPH + r][k]);
+          const float sm = x * a.scale;
+          if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
+          if (sm >= thr) sM[hw][j >> 6] |= 1ull << (j & 63);
+        }
+      }
+    }
+  };
+
+  load_group(0, 0);
+  bf16x8 qf[KS];
+  load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
+  wait_vmem();
+  __syncthreads();
+  for (int gg = 0; gg < ng; ++gg) {
+    const int p = gg & 1;
+    if (gg + 1 < ng) load_group(gg + 1, p ^ 1);
+    f32x16 s0[2], s1[2];
+    qk32<D>(kbuf(2 * p), qf, s0, lane);
+    const float m0 = rowmax32(s0, ragged_rows, 2 * gg * BK, row, N, lane);
+    float m1 = kNegInf;
+    if (2 * gg + 1 < n_off) {
+      qk32<D>(kbuf(2 * p + 1), qf, s1, lane);
+      m1 = rowmax32(s1, ragged_rows, (2 * gg + 1) * BK, row, N, lane);
+    }
+    const float w0 = wave_max(m0), w1 = wave_max(m1);
+    if (lane == 0) {
+      sStage[p][w][0] = w0;
+      sStage[p][w][1] = w1;
+    }
+    if (gg > 0) combine(gg - 1, p ^ 1);
+    wait_vmem();
+    __syncthreads();
+  }
+  combine(ng - 1, (ng - 1) & 1);
+  __syncthreads();
+  for (int x = tid; x < HPW * nw64; x += NW * 64) {
+    const int hh = x / nw64, wi = x % nw64;
+    a.keep_mask[(((long long)b * a.Hq + h0 + hh) * a.nqb + i) * a.mask_words + wi] = sM[hh][wi];
   }
 }
 
@@ -877,7 +1117,10 @@ hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t strea
       hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kDense>), grid, block, 0, stream, a);
       break;
     case kAbsolute:
-      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute>), grid, block, 0, stream, a);
+      if constexpr (NW == BQ / kRows)   // one head per workgroup
+        hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute>), grid, block, 0, stream, a);
+      else
+        return hipErrorInvalidConfiguration;
       break;
     default:
       hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kRelative>), grid, block, 0, stream, a);
@@ -913,7 +1156,32 @@ hipError_t launch_calib_nw(const CalibArgs& a, int nw, hipStream_t stream) {
   }
 }
 
+template <int D, int BQ>
+hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
+  constexpr int WPH = BQ / kRows;
+  const dim3 grid(a.units * a.nqb);
+  if (hpw == 2 && WPH * 2 <= 8)
+    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, WPH * 2>), grid, dim3(WPH * 128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, WPH>), grid, dim3(WPH * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+int gate_sweep_heads(int block_q, int group) {
+  (void)block_q;
+  return group % 2 == 0 ? 2 : 1;
+}
+
+hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream) {
+  const int hpw = gate_sweep_heads(block_q, a.G);
+  if (head_dim == 128)
+    return block_q == 128 ? launch_sweep_hpw<128, 128>(a, hpw, stream)
+                          : launch_sweep_hpw<128, 64>(a, hpw, stream);
+  return block_q == 128 ? launch_sweep_hpw<64, 128>(a, hpw, stream)
+                        : launch_sweep_hpw<64, 64>(a, hpw, stream);
+}
 
 int waves_per_workgroup(int block_q, int group) {
   const int wph = block_q / kRows;
@@ -922,9 +1190,13 @@ int waves_per_workgroup(int block_q, int group) {
   return hpw * wph;
 }
 
+int prefill_waves_per_workgroup(int block_q, int group, int gate) {
+  return gate == kAbsolute ? block_q / kRows : waves_per_workgroup(block_q, group);
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
                           hipStream_t stream) {
-  const int nw = waves_per_workgroup(block_q, a.G);
+  const int nw = prefill_waves_per_workgroup(block_q, a.G, gate);
   if (head_dim == 128) {
     return block_q == 128 ? launch_prefill_nw<128, 128>(a, nw, gate, stream)
                           : launch_prefill_nw<128, 64>(a, nw, gate, stream);

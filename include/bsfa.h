@@ -98,6 +98,11 @@ typedef struct {
   float softmax_scale;       /* must equal the effective scale within 1e-6 relative */
 } bsfa_table;
 
+/* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
+ * ABSOLUTE, one keep bitmask per (b, h, i), B * Hq * ceil(N/Bq) * ceil(ceil(N/Bk)/64) uint64
+ * words. */
+uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
+
 /* Gated causal prefill attention (the method's hot path).
  *   p             problem description (host memory, read during the call only)
  *   Q             device [B][N][Hq][d] bf16;  K, V: device [B][N][Hkv][d] bf16
@@ -115,12 +120,21 @@ typedef struct {
  *                 the gate statistic in scaled-score units (ABSOLUTE and DENSE: s_max;
  *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
  *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
+ *   workspace     device, 8-byte aligned, or NULL; caller-owned scratch of workspace_bytes
+ *                 (its contents on return are unspecified). For ABSOLUTE with a workspace of
+ *                 at least bsfa_prefill_workspace_bytes(p, gate_mode) bytes, the keep
+ *                 decisions of all blocks are made in a separate launch first (scores only),
+ *                 and the softmax launch then walks the kept blocks; without one, both happen
+ *                 in one launch. The results are the same. A non-NULL workspace that is too
+ *                 small is an error (BSFA_ERR_ARG).
  *   stream        hipStream_t
+ * The absolute gate supports seqlen up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
  * Returns BSFA_OK or an error status (see the conventions above). */
 bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
                          const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
                          float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
-                         float* debug_block_stat, void* stream);
+                         float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
+                         void* stream);
 
 /* The heavy step of offline threshold calibration ("Block Sparse Flash Attention", Method >
  * Key Designs 1): for every (b, h, i), the maxima of the scaled scores over each visible

@@ -30,7 +30,8 @@ def bf16_pair(*xs):
 
 
 def run_device(Qd, Kd, Vd, *, block_q, mode, table=None, budget_slice=0,
-               log_lambda=-math.inf, out_dtype=torch.float32, dbg=True, O=None):
+               log_lambda=-math.inf, out_dtype=torch.float32, dbg=True, O=None,
+               workspace=None):
     B, N, Hq, _ = Qd.shape
     nqb, nkb = -(-N // block_q), -(-N // 64)
     counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
@@ -39,7 +40,8 @@ def run_device(Qd, Kd, Vd, *, block_q, mode, table=None, budget_slice=0,
     dtab = table.to_device("cuda") if table is not None else None
     O = _lib.bsfa_prefill(Qd, Kd, Vd, O, block_q=block_q, gate_mode=mode, table=dtab,
                           budget_slice=budget_slice, log_lambda=log_lambda, kept_counts=counts,
-                          kept_total=total, debug_block_stat=stat, out_dtype=out_dtype)
+                          kept_total=total, debug_block_stat=stat, out_dtype=out_dtype,
+                          workspace=workspace)
     torch.cuda.synchronize()
     return dict(O=O, counts=counts.cpu().numpy(), total=int(total.item()),
                 stat=None if stat is None else stat.cpu().numpy())

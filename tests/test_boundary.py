@@ -68,10 +68,11 @@ def table(Hq=4, bq=128, bk=64, d=128, scale=None, n_budgets=2, t_len=2, ptr=FAKE
 
 
 def call_prefill(p, tbl=None, slice_=0, mode=_lib.BSFA_GATE_DENSE, log_lambda=-math.inf,
-                 q=FAKE, k=FAKE, v=FAKE, o=FAKE, counts=None, total=None, dbg=None):
+                 q=FAKE, k=FAKE, v=FAKE, o=FAKE, counts=None, total=None, dbg=None, ws=None,
+                 ws_bytes=0):
     lib = _lib.load_library()
     return lib.bsfa_prefill(ctypes.byref(p), q, k, v, ctypes.byref(tbl) if tbl else None, slice_,
-                            mode, log_lambda, o, counts, total, dbg, None)
+                            mode, log_lambda, o, counts, total, dbg, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("mutate,status", [
@@ -145,6 +146,32 @@ def test_misaligned_outputs():
     assert call_prefill(p, counts=FAKE + 2) == _lib.BSFA_ERR_ALIGN
     assert call_prefill(p, total=FAKE + 4) == _lib.BSFA_ERR_ALIGN
     assert call_prefill(p, dbg=FAKE + 1) == _lib.BSFA_ERR_ALIGN
+
+
+def test_workspace_size_and_validation():
+    lib = _lib.load_library()
+    p = problem()
+    N, bq, bk = p.seqlen, p.block_q, p.block_k
+    words = -(-(-(-N // bk)) // 64)
+    need = p.batch * p.heads_q * (-(-N // bq)) * words * 8
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == need
+    for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+    assert lib.bsfa_prefill_workspace_bytes(None, _lib.BSFA_GATE_ABSOLUTE) == 0
+    # 65 key tiles need two mask words per query block
+    p2 = problem(N=65 * 64)
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p2), _lib.BSFA_GATE_ABSOLUTE) == \
+        p2.batch * p2.heads_q * (-(-p2.seqlen // p2.block_q)) * 2 * 8
+    abs_call = dict(tbl=table(t_len=-(-N // bq)), mode=_lib.BSFA_GATE_ABSOLUTE)
+    assert call_prefill(p, ws=FAKE + 4, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, ws=FAKE, ws_bytes=need - 8, **abs_call) == _lib.BSFA_ERR_ARG
+    assert "workspace" in _lib.bsfa_last_error()
+
+
+def test_absolute_gate_length_limit():
+    p = problem(N=2097152 + 64)
+    st = call_prefill(p, tbl=table(t_len=1), mode=_lib.BSFA_GATE_ABSOLUTE)
+    assert st == _lib.BSFA_ERR_UNSUPPORTED
 
 
 def call_calib(p, budgets, q=FAKE, k=FAKE, out=FAKE):

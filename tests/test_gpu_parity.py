@@ -75,13 +75,13 @@ def test_tiny_dense(tiny):
 # Mid-size cases covering every workgroup shape, ragged tails and GQA
 # ---------------------------------------------------------------------------------------------
 SHAPES = {  # name: (B, N, Hq, Hkv, d, Bq)
-    "llama_like_ragged": (1, 1000, 8, 2, 128, 128),       # 8 waves: 2 heads x 128 rows
-    "d128_bq64_g4": (1, 700, 8, 2, 128, 64),              # 8 waves: 4 heads x 64 rows
+    "llama_like_ragged": (1, 1000, 8, 2, 128, 128),       # 4 waves: 1 head x 128 rows
+    "d128_bq64_g4": (1, 700, 8, 2, 128, 64),              # 4 waves: 2 heads x 64 rows
     "d64_bq128_g1": (1, 515, 2, 2, 64, 128),              # 4 waves: 1 head x 128 rows
     "d64_bq64_g2": (2, 333, 4, 2, 64, 64),                # 4 waves: 2 heads, batch 2
-    "d64_bq64_g1": (1, 200, 1, 1, 64, 64),                # 2 waves
+    "d64_bq64_g1": (1, 200, 1, 1, 64, 64),                # 2 waves: 1 head x 64 rows
     "d128_bq64_g1": (1, 130, 2, 2, 128, 64),              # 2 waves, d = 128
-    "g8": (1, 384, 16, 2, 128, 128),                      # G = 8: two workgroups per KV group
+    "g8": (1, 384, 16, 2, 128, 128),                      # G = 8: 8 workgroups per KV group
 }
 
 
@@ -205,6 +205,30 @@ def test_poisoned_skipped_values_bitwise(mid_tables):
                     rows = slice(i * Bq, min((i + 1) * Bq, N))
                     assert torch.isnan(pois["O"][:, rows, h]).any()     # kept: V was read
     assert checked >= 8
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("dbg", [True, False])
+def test_absolute_gate_sweep_and_single_launch_agree_bitwise(name, dbg, mid_tables):
+    # with a workspace the keep masks come from the separate gate sweep, without one from the
+    # softmax kernel's own first pass: same decisions, same output bits
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    tab = mid_tables(name)
+    Q, K, V = _mid_inputs(name, 14)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    need = _lib.bsfa_prefill_workspace_bytes(Qd, Kd, block_q=Bq)
+    ws = torch.full((need + 64,), 0xA5, dtype=torch.uint8, device="cuda")   # stale contents
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    for sl in (0, 1):
+        a = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=sl,
+                       dbg=dbg, workspace=ws)
+        b = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=sl,
+                       dbg=dbg, workspace=none)
+        assert torch.equal(a["O"], b["O"])
+        np.testing.assert_array_equal(a["counts"], b["counts"])
+        assert a["total"] == b["total"]
+        if dbg:
+            np.testing.assert_array_equal(a["stat"], b["stat"])
 
 
 def test_back_to_back_launches_bitwise(mid_tables):
