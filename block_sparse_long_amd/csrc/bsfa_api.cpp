@@ -222,6 +222,9 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
     sw.xcd_map = (sw.units % 8) == 0;
     hipError_t e = bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
+    // the walk over kept tiles is as long as the head keeps: spread every KV head over all
+    // XCDs, turning the assignment once per set of query blocks in flight together
+    if (a.xcd_map) a.xcd_rot = a.units < bsfa::kResidentWorkgroups ? bsfa::kResidentWorkgroups / a.units : 1;
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, gate_mode, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -23,7 +23,9 @@ struct PrefillArgs {
   long long qs[3], ks[3], vs[3], os[3];
   int B, N, Hq, Hkv, G, nqb, nkb, t_len;
   int units;                       // B * Hkv * (G / heads per workgroup)
-  int xcd_map;                     // 1: map workgroups so each XCD serves whole KV heads
+  int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads)
+  int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
+                                   // blocks (0: never)
   float scale;                     // softmax scale applied to fp32 scores
   float c_log2;                    // scale * log2(e)
   float log_lambda;                // RELATIVE threshold
@@ -39,7 +41,7 @@ struct CalibArgs {
   const void* k;
   long long qs[3], ks[3];
   int B, N, Hq, Hkv, G, nqb, nkb;
-  int units, xcd_map;
+  int units, xcd_map, xcd_rot;
   float scale;
   int n_budgets;
   int budgets[16];
@@ -60,6 +62,9 @@ int waves_per_workgroup(int block_q, int group);
 // The prefill kernel's workgroup: as above, except that the absolute gate runs one head per
 // workgroup (its keep decisions are made per head before the softmax pass).
 int prefill_waves_per_workgroup(int block_q, int group, int gate);
+
+// Workgroups of the prefill kernel resident on the whole chip at once (256 CUs, two each).
+constexpr int kResidentWorkgroups = 512;
 
 // Largest number of off-diagonal key tiles per query block under the absolute gate (the
 // keep bitmask lives in LDS): 32768 tiles of 64 keys.

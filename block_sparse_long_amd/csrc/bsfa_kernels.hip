@@ -482,13 +482,20 @@ struct Unit {
   int b, g, hg, i;
 };
 
+// Workgroup L -> (batch, KV head, head group, query block). Query blocks go from the last
+// (longest) to the first. Consecutive workgroups land on the 8 XCDs in turn (L mod 8); with
+// xcd_map the unit index is chosen so that XCD x serves fixed units (for B * Hkv = 8: KV head
+// x), which keeps each XCD's L2 on one K/V stream when the workgroups sweep it in step. A
+// nonzero xcd_rot turns that assignment by one every xcd_rot query blocks (about the number
+// in flight at once), so that over the launch every XCD serves every KV head equally often:
+// for walks whose length differs between heads, the XCDs then finish together.
 __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, int Hkv,
-                                            int xcd_map) {
+                                            int xcd_map, int xcd_rot) {
   int i, u;
   if (xcd_map) {
     const int x = L & 7, s = L >> 3, upx = units >> 3;
     i = nqb - 1 - s / upx;
-    u = (s % upx) * 8 + x;
+    u = (s % upx) * 8 + (xcd_rot ? ((x + (nqb - 1 - i) / xcd_rot) & 7) : x);
   } else {
     i = nqb - 1 - L / units;
     u = L % units;
@@ -538,7 +545,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
+  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
@@ -921,7 +928,7 @@ __global__ __launch_bounds__(NW * 64) void gate_sweep_kernel(PrefillArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
+  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
@@ -1032,7 +1039,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map);
+  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
