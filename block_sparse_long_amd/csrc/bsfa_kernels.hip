@@ -909,12 +909,70 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // maxima of all off-diagonal tiles, two tiles per barrier, compared with T_eff(h, i); kept
 // tiles set their bit in the keep mask. Every workgroup does the same work per tile, so the
 // workgroups that share a KV head stream its K tiles in step and mostly from L2; the
-// workgroup's heads share each staged K tile.
+// workgroup's heads share each staged K tile. With no softmax state to hold, a wave takes 64
+// query rows: each K fragment read from LDS feeds two MFMAs, which halves the LDS reads per
+// product (32-row waves read K from LDS as fast as the MFMAs consume it).
 // ---------------------------------------------------------------------------------------------
-template <int D, int BQ, int NW>
-__global__ __launch_bounds__(NW * 64) void gate_sweep_kernel(PrefillArgs a) {
-  constexpr int WPH = BQ / kRows;
-  constexpr int HPW = NW / WPH;
+
+// S^T for one 64-key tile and 64 query rows (two 32-row halves rb): s[rb][mb] as in qk32 for
+// rows row0 + 32 rb. Same k-step order as qk32, so every score is bitwise the same.
+template <int D>
+__device__ __forceinline__ void qk64(const __bf16* sk, const bf16x8 (&qf)[2][D / 16],
+                                     f32x16 (&s)[2][2], int lane) {
+  constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR;
+  const __bf16* base = sk + (lane & 31) * STR + 8 * (lane >> 5);
+  bf16x8 ka[2][2];
+  auto load = [&](int ks, int buf) {
+    ka[buf][0] = *reinterpret_cast<const bf16x8*>(base + 16 * ks);
+    ka[buf][1] = *reinterpret_cast<const bf16x8*>(base + 32 * STR + 16 * ks);
+  };
+  load(0, 0);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int buf = ks & 1;
+    if (ks + 1 < KS) load(ks + 1, buf ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        if (ks == 0) {
+          f32x16 z;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) z[v] = 0.f;
+          s[rb][mb] = mfma32(ka[buf][mb], qf[rb][ks], z);
+        } else {
+          s[rb][mb] = mfma32(ka[buf][mb], qf[rb][ks], s[rb][mb]);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// This lane's max over a fully visible tile's scores for the wave's 64 rows; rows at or past
+// N (the last query block only) do not count.
+__device__ __forceinline__ float tile_max64(f32x16 (&s)[2][2], bool ragged, int row0, int N,
+                                            int lane) {
+  if (ragged) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+      if (row0 + 32 * rb + (lane & 31) >= N)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) s[rb][mb][v] = kNegInf;
+  }
+  float mx = block_max(kNegInf, s[0][0]);
+  mx = block_max(mx, s[0][1]);
+  mx = block_max(mx, s[1][0]);
+  return block_max(mx, s[1][1]);
+}
+
+template <int D, int BQ, int HPW>
+__global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gate_sweep_kernel(PrefillArgs a) {
+  constexpr int WPH = BQ / 64;             // waves per head
+  constexpr int NW = HPW * WPH;
   constexpr int STR = Tile<D>::STR, KS = Tile<D>::KS;
   constexpr int MK = copy_iters<STR, NW>();
 
@@ -933,8 +991,7 @@ __global__ __launch_bounds__(NW * 64) void gate_sweep_kernel(PrefillArgs a) {
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
   const int N = a.N;
-  const int row0 = i * BQ + rw * kRows;
-  const int row = row0 + (lane & 31);
+  const int row0 = i * BQ + rw * 64;
   const int n_off = (i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
   if (n_off == 0) return;   // uniform: nothing off-diagonal to decide
@@ -986,20 +1043,21 @@ __global__ __launch_bounds__(NW * 64) void gate_sweep_kernel(PrefillArgs a) {
   };
 
   load_group(0, 0);
-  bf16x8 qf[KS];
-  load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
+  bf16x8 qf[2][KS];
+  load_q32<D>(Qb, a.qs[1], row0, N, qf[0], lane);
+  load_q32<D>(Qb, a.qs[1], row0 + 32, N, qf[1], lane);
   wait_vmem();
   __syncthreads();
   for (int gg = 0; gg < ng; ++gg) {
     const int p = gg & 1;
     if (gg + 1 < ng) load_group(gg + 1, p ^ 1);
-    f32x16 s0[2], s1[2];
-    qk32<D>(kbuf(2 * p), qf, s0, lane);
-    const float m0 = rowmax32(s0, ragged_rows, 2 * gg * BK, row, N, lane);
+    f32x16 s0[2][2], s1[2][2];
+    qk64<D>(kbuf(2 * p), qf, s0, lane);
+    const float m0 = tile_max64(s0, ragged_rows, row0, N, lane);
     float m1 = kNegInf;
     if (2 * gg + 1 < n_off) {
-      qk32<D>(kbuf(2 * p + 1), qf, s1, lane);
-      m1 = rowmax32(s1, ragged_rows, (2 * gg + 1) * BK, row, N, lane);
+      qk64<D>(kbuf(2 * p + 1), qf, s1, lane);
+      m1 = tile_max64(s1, ragged_rows, row0, N, lane);
     }
     const float w0 = wave_max(m0), w1 = wave_max(m1);
     if (lane == 0) {
@@ -1165,12 +1223,12 @@ hipError_t launch_calib_nw(const CalibArgs& a, int nw, hipStream_t stream) {
 
 template <int D, int BQ>
 hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
-  constexpr int WPH = BQ / kRows;
+  constexpr int WPH = BQ / 64;
   const dim3 grid(a.units * a.nqb);
-  if (hpw == 2 && WPH * 2 <= 8)
-    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, WPH * 2>), grid, dim3(WPH * 128), 0, stream, a);
+  if (hpw == 2)
+    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2>), grid, dim3(WPH * 128), 0, stream, a);
   else
-    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, WPH>), grid, dim3(WPH * 64), 0, stream, a);
+    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1>), grid, dim3(WPH * 64), 0, stream, a);
   return hipGetLastError();
 }
 
