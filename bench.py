@@ -2,6 +2,7 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--quick]
     python bench.py --profile-once     # one 1 GiB copy + one gated call, for counter runs
+    python bench.py --counters FETCH_DIR WRITE_DIR   # counter runs -> profiles/traffic_*.json
 
 A step is one bsfa_prefill call over one batch of synthetic input already resident in HBM:
 exact QK^T on every causally visible tile, the gate, online softmax and PV on kept tiles.
@@ -9,10 +10,13 @@ Prints one JSON line. `value` is executed TFLOP/s of the gated call: tile-level 
 every visible tile plus PV on every kept or diagonal tile, counted from the kernel's own kept
 counts (2*Bq*Bk*d per tile product), divided by the time of the step. The same line carries
 the dense path of the same kernel (gate compiled out), the zero-skip taxes, the kept fraction,
-the roofline of the prefill kernel (HIP events on the launch stream) and the CPU oracle timed on
-a bounded sample of the same workload. roofline.traffic is the HBM bytes per launch that
-rocprofv3 counters measured for the current kernel source (profiles/traffic_<workload>.json,
-FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy); it is null when the kernel source changed.
+the roofline of the call's dominant kernel and the CPU oracle timed on a bounded sample of the
+same workload. Under the absolute gate the call is two launches: the gate sweep (QK on every
+off-diagonal tile, timed on its own through bsfa_gate_masks with HIP events on the launch
+stream) and the softmax walk over the kept tiles (the rest of the call). roofline.traffic is
+the HBM bytes per launch that rocprofv3 counters measured for that kernel on the current kernel
+source (profiles/traffic_<workload>.json, FETCH_SIZE + WRITE_SIZE scaled by a 1 GiB copy); it
+is null when the kernel source changed.
 """
 import hashlib
 import argparse
@@ -41,6 +45,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 1 GiB device copy and one gated call, then exit (counter runs)")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc runs of --profile-once (FETCH_SIZE, "
+                         "WRITE_SIZE) into profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -53,9 +60,9 @@ def kernel_source_sha256():
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the gated call from the committed counter summary, if it was
-    taken on the current kernel source; else None."""
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` (a name prefix) from the committed counter summary, if
+    it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
         return None
@@ -63,7 +70,67 @@ def measured_traffic(workload):
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_sha256():
         return None
-    return rec["hbm_bytes_per_launch"]
+    for k, v in rec.get("kernels", {}).items():
+        if k.startswith(kernel):
+            return v["hbm_bytes_per_launch"]
+    return None
+
+
+def summarise_counters(args):
+    """FETCH_SIZE / WRITE_SIZE per dispatch of the prefill-path kernels, each scaled by what the
+    same counter reads for the 1 GiB device copy of --profile-once (a plain copy reads and
+    writes exactly COPY_BYTES), written to profiles/traffic_<workload>.json."""
+    import csv
+    import glob
+    import re
+
+    def per_dispatch(d, counter):
+        rows = {}
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        if not files:
+            sys.exit(f"no counter_collection.csv under {d}")
+        with open(max(files, key=os.path.getmtime)) as fh:   # the newest run only
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+                rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
+        return rows
+
+    fetch, write = per_dispatch(args.counters[0], "FETCH_SIZE"), per_dispatch(args.counters[1],
+                                                                              "WRITE_SIZE")
+    def copy_kib(rows):
+        v = [x for (_, n), x in rows.items() if "copyBuffer" in n]
+        return max(v) if v else None
+    fk, wk = copy_kib(fetch), copy_kib(write)
+    if not fk or not wk:
+        sys.exit("no 1 GiB copy dispatch found in the counter runs")
+    f_scale, w_scale = COPY_BYTES / (fk * 1024.0), COPY_BYTES / (wk * 1024.0)
+    kernels = {}
+    for rows, tag, sc in ((fetch, "fetch", f_scale), (write, "write", w_scale)):
+        for (_, name), kib in rows.items():
+            m = re.search(r"bsfa::\(anonymous namespace\)::(\w+<[^>]*>)", name)
+            if not m:
+                continue
+            k = kernels.setdefault(m.group(1), {})
+            k[f"{tag}_size_kib"] = kib
+            k[f"{tag}_bytes"] = kib * 1024.0 * sc
+    for k in kernels.values():
+        k["hbm_bytes_per_launch"] = k.get("fetch_bytes", 0.0) + k.get("write_bytes", 0.0)
+    rec = {"workload": args.workload, "kernel_source_sha256": kernel_source_sha256(),
+           "copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
+           "copy_fetch_kib": fk, "copy_write_kib": wk, "kernels": kernels,
+           "commands": ["cd /tmp && export TMPDIR=/tmp",
+                        "rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -- python3 "
+                        "<repo>/bench.py --profile-once --workload " + args.workload,
+                        "rocprofv3 --pmc WRITE_SIZE -d <write_dir> -- python3 "
+                        "<repo>/bench.py --profile-once --workload " + args.workload,
+                        "python3 bench.py --counters <fetch_dir> <write_dir> --workload "
+                        + args.workload]}
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec, indent=1))
 
 
 def profile_once(args):
@@ -176,6 +243,25 @@ def timed(fn, steps, warmup):
     return e0.elapsed_time(e1) / steps, wall
 
 
+def sweep_flops(w):
+    """QK on every off-diagonal tile of every (b, h, i): the gate sweep's work."""
+    return 2.0 * w.Bq * 64 * w.d * w.Hq * w.n_off_total
+
+
+def run_sweep(w, steps, warmup):
+    """The gate sweep on its own (bsfa_gate_masks), timed like a step."""
+    import torch
+    from block_sparse_long_amd import _lib
+    if getattr(w, "masks", None) is None:
+        nqb, nkb = -(-w.N // w.Bq), -(-w.N // 64)
+        w.masks = torch.empty((1, w.Hq, nqb, -(-nkb // 64)), dtype=torch.int64,
+                              device=w.Qd.device)
+    ev_ms, wall_ms = timed(lambda: _lib.bsfa_gate_masks(w.Qd, w.Kd, w.dtable, 0, w.masks,
+                                                        block_q=w.Bq), steps, warmup)
+    fl = sweep_flops(w)
+    return dict(ms=ev_ms, wall_ms=wall_ms, flops=fl, tflops=fl / ev_ms / 1e9)
+
+
 def run_gate(w, mode, steps, warmup, **kw):
     import numpy as np
     import torch
@@ -184,7 +270,7 @@ def run_gate(w, mode, steps, warmup, **kw):
     counts = w.counts.cpu().numpy()
     flops = executed_flops(counts, w.N, w.Bq, w.d)
     kept = int(counts.sum())
-    return dict(ms=ev_ms, wall_ms=wall_ms, flops=flops, tflops=flops / ev_ms / 1e9,
+    return dict(ms=ev_ms, wall_ms=wall_ms, flops=flops, tflops=flops / ev_ms / 1e9, kept=kept,
                 kept_fraction=kept / (w.Hq * w.n_off_total) if w.n_off_total else 1.0,
                 pct_peak=100.0 * flops / ev_ms / 1e9 / PEAK_BF16_TFLOPS)
 
@@ -222,6 +308,9 @@ def main():
     if args.profile_once:
         profile_once(args)
         return
+    if args.counters:
+        summarise_counters(args)
+        return
     import numpy as np
     import torch
     from block_sparse_long_amd import _lib
@@ -235,6 +324,7 @@ def main():
     gate_kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
 
     gated = run_gate(w, mode, args.steps, args.warmup, **gate_kw)
+    sweep = run_sweep(w, args.steps, args.warmup) if mode == "absolute" else None
     dense = run_gate(w, "dense", args.steps, args.warmup)
     # zero-skip taxes: the gated instantiations with a gate that never skips
     ninf = None
@@ -259,6 +349,26 @@ def main():
     }
     if w.table is not None:
         extras["zero_skip_tax_absolute"] = round(abs_ninf["ms"] / dense["ms"] - 1, 4)
+    # the call's launches: under the absolute gate the sweep, then the walk over kept tiles
+    # (QK again and PV on every kept and diagonal tile)
+    walk_tiles = gated["kept"] + w.Hq * sum(
+        n_end - n_off for n_off, n_end in block_ranges(w.N, w.Bq))
+    walk_flops = 2 * 2.0 * w.Bq * 64 * w.d * walk_tiles
+    if sweep is not None:
+        walk_ms = gated["ms"] - sweep["ms"]
+        extras["launches"] = {
+            "gate_sweep": {"ms": round(sweep["ms"], 3), "tflops": round(sweep["tflops"], 2),
+                           "flops": sweep["flops"]},
+            "softmax_walk": {"ms": round(walk_ms, 3), "flops": walk_flops,
+                             "tflops": round(walk_flops / walk_ms / 1e9, 2)}}
+        if sweep["ms"] >= walk_ms:
+            dom = dict(kernel="gate_sweep_kernel<128, 128, 2>", ms=sweep["ms"],
+                       flops=sweep["flops"])
+        else:
+            dom = dict(kernel="prefill_kernel<128, 128, 4, 1>", ms=walk_ms, flops=walk_flops)
+    else:
+        dom = dict(kernel=f"prefill_kernel<128, 128, 4, {2 if mode == 'relative' else 0}>",
+                   ms=gated["ms"], flops=gated["flops"])
 
     if not args.quick:
         sweeps = {}
@@ -307,12 +417,12 @@ def main():
                    "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": w.d,
                    "tile": f"{w.Bq}x64", "gate": mode,
                    "budget_k": k, "calibrated_len": c["calib_n"] if k else None},
-        "roofline": {"bound": "mfma", "achieved": round(gated["tflops"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(dom["flops"] / dom["ms"] / 1e9, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gated["tflops"] / PEAK_BF16_TFLOPS, 4),
-                     "traffic": measured_traffic(args.workload),
-                     "kernel": "prefill_kernel<128,128,4,gate>",
-                     "flops_per_launch": gated["flops"]},
+                     "frac": round(dom["flops"] / dom["ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(args.workload, dom["kernel"]),
+                     "kernel": dom["kernel"], "ms_per_launch": round(dom["ms"], 3),
+                     "flops_per_launch": dom["flops"]},
         "cpu_baseline": cpu,
         "extras": extras,
     }

@@ -31,8 +31,8 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
 
-EXPORTED = ("bsfa_prefill", "bsfa_prefill_workspace_bytes", "bsfa_calibrate_blockmax",
-            "bsfa_status_string", "bsfa_last_error", "bsfa_version")
+EXPORTED = ("bsfa_prefill", "bsfa_prefill_workspace_bytes", "bsfa_gate_masks",
+            "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error", "bsfa_version")
 
 
 class BsfaProblem(ctypes.Structure):
@@ -79,6 +79,9 @@ def load_library(path: str = LIB_PATH):
                                  vp, ctypes.c_uint64, vp]
     lib.bsfa_prefill_workspace_bytes.restype = ctypes.c_uint64
     lib.bsfa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem), ctypes.c_int32]
+    lib.bsfa_gate_masks.restype = ctypes.c_int32
+    lib.bsfa_gate_masks.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, ctypes.POINTER(BsfaTable),
+                                    ctypes.c_int32, vp, ctypes.c_uint64, vp, vp]
     lib.bsfa_calibrate_blockmax.restype = ctypes.c_int32
     lib.bsfa_calibrate_blockmax.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp]
@@ -189,6 +192,32 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                           _stream_handle(stream, Q.device))
     _check(st)
     return O
+
+
+def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block_q: int,
+                    block_k: int = 64, debug_block_stat=None, softmax_scale: float = 0.0,
+                    stream=None):
+    """Keep bitmasks of the absolute gate: int64 [B, Hq, nqb, W] (bit j % 64 of word j // 64 set
+    iff off-diagonal key block j is kept); allocated if None. Returns keep_mask."""
+    import torch
+    lib = load_library()
+    B, N, Hq, _ = Q.shape
+    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    if keep_mask is None:
+        keep_mask = torch.empty((B, Hq, nqb, -(-nkb // 64)), dtype=torch.int64, device=Q.device)
+    if not keep_mask.is_contiguous() or keep_mask.element_size() != 8:
+        raise ValueError("keep_mask must be a contiguous 8-byte-element tensor")
+    if debug_block_stat is not None and (debug_block_stat.dtype != torch.float32
+                                         or not debug_block_stat.is_contiguous()):
+        raise ValueError("debug_block_stat must be a contiguous float32 tensor")
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    tbl = table.c_struct()
+    st = lib.bsfa_gate_masks(ctypes.byref(p), _ptr(Q), _ptr(K), ctypes.byref(tbl),
+                             int(budget_slice), _ptr(keep_mask),
+                             ctypes.c_uint64(keep_mask.numel() * 8), _ptr(debug_block_stat),
+                             _stream_handle(stream, Q.device))
+    _check(st)
+    return keep_mask
 
 
 def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_k: int = 64,

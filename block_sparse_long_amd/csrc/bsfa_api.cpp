@@ -77,6 +77,73 @@ bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+// The threshold table against the problem: present, aligned, bound to the same heads, tile,
+// head_dim and scale, and the budget slice in range.
+bsfa_status check_table(const bsfa_problem* p, const bsfa_table* table, int32_t budget_slice) {
+  const float scale = effective_scale(p);
+  if (!table) return fail(BSFA_ERR_TABLE, "ABSOLUTE gate needs a threshold table");
+  if (!table->T) return fail(BSFA_ERR_TABLE, "table->T is NULL");
+  if ((reinterpret_cast<uintptr_t>(table->T) & 3u) != 0)
+    return fail(BSFA_ERR_ALIGN, "table->T is not 4-byte aligned");
+  if (table->n_budgets < 1 || table->t_len < 1)
+    return fail(BSFA_ERR_TABLE, "table has n_budgets %d, t_len %d", table->n_budgets,
+                table->t_len);
+  if (budget_slice < 0 || budget_slice >= table->n_budgets)
+    return fail(BSFA_ERR_TABLE, "budget_slice %d outside [0, %d)", budget_slice,
+                table->n_budgets);
+  if (table->heads_q != p->heads_q || table->block_q != p->block_q ||
+      table->block_k != p->block_k || table->head_dim != p->head_dim)
+    return fail(BSFA_ERR_TABLE,
+                "table calibrated for Hq=%d tile %dx%d d=%d, problem has Hq=%d tile %dx%d d=%d",
+                table->heads_q, table->block_q, table->block_k, table->head_dim, p->heads_q,
+                p->block_q, p->block_k, p->head_dim);
+  if (!(fabsf(table->softmax_scale - scale) <= 1e-6f * scale))
+    return fail(BSFA_ERR_TABLE, "table softmax_scale %g differs from the problem's %g",
+                (double)table->softmax_scale, (double)scale);
+  return BSFA_OK;
+}
+
+// Kernel arguments common to the prefill kernel and the gate sweep.
+bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K, const void* V,
+                            const bsfa_table* table, int32_t budget_slice, int32_t gate_mode) {
+  bsfa::PrefillArgs a;
+  memset(&a, 0, sizeof(a));
+  const float scale = effective_scale(p);
+  a.q = Q;
+  a.k = K;
+  a.v = V;
+  a.thr = gate_mode == BSFA_GATE_ABSOLUTE
+              ? table->T + (long long)budget_slice * table->heads_q * table->t_len
+              : nullptr;
+  a.t_len = gate_mode == BSFA_GATE_ABSOLUTE ? table->t_len : 1;
+  for (int t = 0; t < 3; ++t) {
+    a.qs[t] = p->q_stride[t];
+    a.ks[t] = p->k_stride[t];
+    a.vs[t] = p->v_stride[t];
+    a.os[t] = p->o_stride[t];
+  }
+  a.B = p->batch;
+  a.N = p->seqlen;
+  a.Hq = p->heads_q;
+  a.Hkv = p->heads_kv;
+  a.G = p->heads_q / p->heads_kv;
+  a.nqb = ceil_div(p->seqlen, p->block_q);
+  a.nkb = ceil_div(p->seqlen, p->block_k);
+  a.scale = scale;
+  a.c_log2 = scale * 1.4426950408889634f;
+  a.mask_words = ceil_div(a.nkb, 64);
+  return a;
+}
+
+// The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i).
+hipError_t launch_sweep(bsfa::PrefillArgs sw, const bsfa_problem* p, hipStream_t st) {
+  const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G);
+  sw.units = p->batch * p->heads_kv * (sw.G / shpw);
+  sw.xcd_map = (sw.units % 8) == 0;
+  sw.xcd_rot = 0;
+  return bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
+}
+
 }  // namespace
 
 extern "C" {
@@ -120,27 +187,9 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
     return fail(BSFA_ERR_ARG, "gate_mode %d is not a bsfa_gate_mode", gate_mode);
   if (gate_mode == BSFA_GATE_RELATIVE && (isnan(log_lambda) || log_lambda == INFINITY))
     return fail(BSFA_ERR_ARG, "log_lambda must be finite or -INFINITY");
-  const float scale = effective_scale(p);
   if (gate_mode == BSFA_GATE_ABSOLUTE) {
-    if (!table) return fail(BSFA_ERR_TABLE, "ABSOLUTE gate needs a threshold table");
-    if (!table->T) return fail(BSFA_ERR_TABLE, "table->T is NULL");
-    if ((reinterpret_cast<uintptr_t>(table->T) & 3u) != 0)
-      return fail(BSFA_ERR_ALIGN, "table->T is not 4-byte aligned");
-    if (table->n_budgets < 1 || table->t_len < 1)
-      return fail(BSFA_ERR_TABLE, "table has n_budgets %d, t_len %d", table->n_budgets,
-                  table->t_len);
-    if (budget_slice < 0 || budget_slice >= table->n_budgets)
-      return fail(BSFA_ERR_TABLE, "budget_slice %d outside [0, %d)", budget_slice,
-                  table->n_budgets);
-    if (table->heads_q != p->heads_q || table->block_q != p->block_q ||
-        table->block_k != p->block_k || table->head_dim != p->head_dim)
-      return fail(BSFA_ERR_TABLE,
-                  "table calibrated for Hq=%d tile %dx%d d=%d, problem has Hq=%d tile %dx%d d=%d",
-                  table->heads_q, table->block_q, table->block_k, table->head_dim, p->heads_q,
-                  p->block_q, p->block_k, p->head_dim);
-    if (!(fabsf(table->softmax_scale - scale) <= 1e-6f * scale))
-      return fail(BSFA_ERR_TABLE, "table softmax_scale %g differs from the problem's %g",
-                  (double)table->softmax_scale, (double)scale);
+    s = check_table(p, table, budget_slice);
+    if (s != BSFA_OK) return s;
   }
   const bool empty = p->batch == 0 || p->seqlen == 0;
   if (!empty) {
@@ -161,6 +210,8 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   if (gate_mode == BSFA_GATE_ABSOLUTE && nkb > bsfa::kMaxGateTiles)
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the absolute-gate limit %d", p->seqlen,
                 bsfa::kMaxGateTiles * bsfa::kBlockK);
+  if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   const uint64_t ws_need = bsfa_prefill_workspace_bytes(p, gate_mode);
   const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty;
   if (use_masks && workspace_bytes < ws_need)
@@ -174,60 +225,65 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   }
   if (empty) return ok();
 
-  bsfa::PrefillArgs a;
-  memset(&a, 0, sizeof(a));
-  a.q = Q;
-  a.k = K;
-  a.v = V;
+  bsfa::PrefillArgs a = base_args(p, Q, K, V, table, budget_slice, gate_mode);
   a.o = O;
-  a.thr = gate_mode == BSFA_GATE_ABSOLUTE
-              ? table->T + (long long)budget_slice * table->heads_q * table->t_len
-              : nullptr;
-  a.t_len = gate_mode == BSFA_GATE_ABSOLUTE ? table->t_len : 1;
   a.kept_counts = kept_counts;
   a.kept_total = reinterpret_cast<unsigned long long*>(kept_total);
   a.dbg = debug_block_stat;
-  for (int t = 0; t < 3; ++t) {
-    a.qs[t] = p->q_stride[t];
-    a.ks[t] = p->k_stride[t];
-    a.vs[t] = p->v_stride[t];
-    a.os[t] = p->o_stride[t];
-  }
-  a.B = p->batch;
-  a.N = p->seqlen;
-  a.Hq = p->heads_q;
-  a.Hkv = p->heads_kv;
-  a.G = p->heads_q / p->heads_kv;
-  a.nqb = nqb;
-  a.nkb = nkb;
   const int nw = bsfa::prefill_waves_per_workgroup(p->block_q, a.G, gate_mode);
   const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
-  a.scale = scale;
-  a.c_log2 = scale * 1.4426950408889634f;
   a.log_lambda = log_lambda;
   a.out_fp32 = p->out_dtype == BSFA_FP32;
-  if ((long long)a.units * nqb > 0x7fffffffll)
-    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   // ABSOLUTE with a workspace: the gate sweep decides every block first (its own launch, so
   // that all workgroups stream K in step), then the prefill kernel runs over the kept ones
-  a.keep_mask = nullptr;
-  a.mask_words = ceil_div(nkb, 64);
   if (use_masks) {
     a.keep_mask = static_cast<unsigned long long*>(workspace);
-    bsfa::PrefillArgs sw = a;
-    const int shpw = bsfa::gate_sweep_heads(p->block_q, a.G);
-    sw.units = p->batch * p->heads_kv * (a.G / shpw);
-    sw.xcd_map = (sw.units % 8) == 0;
-    hipError_t e = bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
+    hipError_t e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
     // the walk over kept tiles is as long as the head keeps: spread every KV head over all
     // XCDs, turning the assignment once per set of query blocks in flight together
-    if (a.xcd_map) a.xcd_rot = a.units < bsfa::kResidentWorkgroups ? bsfa::kResidentWorkgroups / a.units : 1;
+    if (a.xcd_map)
+      a.xcd_rot = a.units < bsfa::kResidentWorkgroups ? bsfa::kResidentWorkgroups / a.units : 1;
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, gate_mode, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
+                            const bsfa_table* table, int32_t budget_slice, uint64_t* keep_mask,
+                            uint64_t mask_bytes, float* debug_block_stat, void* stream) {
+  bsfa_status s = check_problem(p, false);
+  if (s != BSFA_OK) return s;
+  s = check_table(p, table, budget_slice);
+  if (s != BSFA_OK) return s;
+  const bool empty = p->batch == 0 || p->seqlen == 0;
+  if (empty) return ok();
+  if (!Q || !K || !keep_mask) return fail(BSFA_ERR_ARG, "Q, K and keep_mask must be non-NULL");
+  if (!aligned16(Q) || !aligned16(K)) return fail(BSFA_ERR_ALIGN, "Q and K must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(keep_mask) & 7u)
+    return fail(BSFA_ERR_ALIGN, "keep_mask is not 8-byte aligned");
+  if (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u))
+    return fail(BSFA_ERR_ALIGN, "debug_block_stat misaligned");
+  const int nqb = ceil_div(p->seqlen, p->block_q);
+  const int nkb = ceil_div(p->seqlen, p->block_k);
+  if (nkb > bsfa::kMaxGateTiles)
+    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the absolute-gate limit %d", p->seqlen,
+                bsfa::kMaxGateTiles * bsfa::kBlockK);
+  if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
+    return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
+  const uint64_t need = bsfa_prefill_workspace_bytes(p, BSFA_GATE_ABSOLUTE);
+  if (mask_bytes < need)
+    return fail(BSFA_ERR_ARG, "mask_bytes %llu below the required %llu",
+                (unsigned long long)mask_bytes, (unsigned long long)need);
+  bsfa::PrefillArgs a = base_args(p, Q, K, nullptr, table, budget_slice, BSFA_GATE_ABSOLUTE);
+  a.keep_mask = reinterpret_cast<unsigned long long*>(keep_mask);
+  a.dbg = debug_block_stat;
+  a.full_masks = 1;
+  hipError_t e = launch_sweep(a, p, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
   return ok();
 }
 

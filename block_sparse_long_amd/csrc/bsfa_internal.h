@@ -34,6 +34,7 @@ struct PrefillArgs {
   // j / 64: off-diagonal tile j kept), or nullptr to find them inside the prefill kernel
   unsigned long long* keep_mask;
   int mask_words;
+  int full_masks;                  // gate sweep: write every mask word of every (b, h, i)
 };
 
 struct CalibArgs {

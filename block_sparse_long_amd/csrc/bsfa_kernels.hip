@@ -994,7 +994,14 @@ void gate_sweep_kernel(PrefillArgs a) {
   const int row0 = i * BQ + rw * 64;
   const int n_off = (i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
-  if (n_off == 0) return;   // uniform: nothing off-diagonal to decide
+  // words of each head's mask this workgroup writes: those covering the off-diagonal tiles, or
+  // with full_masks every word (zero past the off-diagonal tiles)
+  const int nwr = a.full_masks ? a.mask_words : (n_off + 63) >> 6;
+  if (n_off == 0) {         // uniform: nothing off-diagonal to decide
+    for (int x = tid; x < HPW * nwr; x += NW * 64)
+      a.keep_mask[(((long long)b * a.Hq + h0 + x / nwr) * a.nqb + i) * a.mask_words + x % nwr] = 0ull;
+    return;
+  }
 
   const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
   const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
@@ -1010,14 +1017,13 @@ void gate_sweep_kernel(PrefillArgs a) {
   // heads whose threshold is -inf keep everything without a mask (the softmax kernel does not
   // read one then), so a workgroup of only such heads has nothing to decide unless the maxima
   // are dumped
-  bool all_keep = a.dbg == nullptr;
+  bool all_keep = a.dbg == nullptr && !a.full_masks;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
     all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)] == kNegInf;
   if (all_keep) return;
 
-  const int nw64 = (n_off + 63) >> 6;
-  for (int x = tid; x < HPW * nw64; x += NW * 64) sM[x / nw64][x % nw64] = 0ull;
+  for (int x = tid; x < HPW * nwr; x += NW * 64) sM[x / nwr][x % nwr] = 0ull;
   const int ng = (n_off + 1) >> 1;
   auto load_group = [&](int gg, int p) {
     load_k(2 * gg, kbuf(2 * p));
@@ -1070,8 +1076,8 @@ void gate_sweep_kernel(PrefillArgs a) {
   }
   combine(ng - 1, (ng - 1) & 1);
   __syncthreads();
-  for (int x = tid; x < HPW * nw64; x += NW * 64) {
-    const int hh = x / nw64, wi = x % nw64;
+  for (int x = tid; x < HPW * nwr; x += NW * 64) {
+    const int hh = x / nwr, wi = x % nwr;
     a.keep_mask[(((long long)b * a.Hq + h0 + hh) * a.nqb + i) * a.mask_words + wi] = sM[hh][wi];
   }
 }

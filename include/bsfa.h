@@ -136,6 +136,24 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
                          float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
                          void* stream);
 
+/* The absolute gate's keep decisions alone ("Block Sparse Flash Attention", Method: a block
+ * is kept when its exact maximum scaled score reaches the threshold T[layer, head, query
+ * block]). For every (b, h, i) the exact scores of all off-diagonal blocks j < n_off(i) are
+ * computed (no softmax, no V) and bit j % 64 of keep_mask[b][h][i][j / 64] is set iff
+ * s_max(i, j) >= T_eff(h, i); the diagonal region is not part of the mask (it is always kept).
+ *   p, Q, K, table, budget_slice   as for bsfa_prefill with gate_mode ABSOLUTE (V, O unused)
+ *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(N/Bk)/64), 8-byte
+ *                 aligned; every word is written (bits at or past n_off(i) are zero)
+ *   mask_bytes    size of keep_mask; at least bsfa_prefill_workspace_bytes(p, ABSOLUTE)
+ *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
+ *   stream        hipStream_t
+ * This is the first of the two launches bsfa_prefill makes when given a workspace; on its own
+ * it serves inspection and density monitoring. Same limits and errors as bsfa_prefill
+ * (BSFA_ERR_ARG for a NULL or too small keep_mask). */
+bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
+                            const bsfa_table* table, int32_t budget_slice, uint64_t* keep_mask,
+                            uint64_t mask_bytes, float* debug_block_stat, void* stream);
+
 /* The heavy step of offline threshold calibration ("Block Sparse Flash Attention", Method >
  * Key Designs 1): for every (b, h, i), the maxima of the scaled scores over each visible
  * off-diagonal key block j < n_off(i), and for each budget k their k-th highest value

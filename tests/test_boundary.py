@@ -168,6 +168,31 @@ def test_workspace_size_and_validation():
     assert "workspace" in _lib.bsfa_last_error()
 
 
+def call_masks(p, tbl, slice_=0, q=FAKE, k=FAKE, mask=FAKE, mask_bytes=1 << 20, dbg=None):
+    lib = _lib.load_library()
+    return lib.bsfa_gate_masks(ctypes.byref(p), q, k, ctypes.byref(tbl) if tbl else None, slice_,
+                               mask, mask_bytes, dbg, None)
+
+
+def test_gate_masks_validation():
+    p = problem()
+    need = _lib.load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p),
+                                                            _lib.BSFA_GATE_ABSOLUTE)
+    assert call_masks(p, None) == _lib.BSFA_ERR_TABLE
+    assert call_masks(p, table(bq=64)) == _lib.BSFA_ERR_TABLE
+    assert call_masks(p, table(), slice_=2) == _lib.BSFA_ERR_TABLE
+    assert call_masks(p, table(), mask=None) == _lib.BSFA_ERR_ARG
+    assert call_masks(p, table(), q=None) == _lib.BSFA_ERR_ARG
+    assert call_masks(p, table(), mask=FAKE + 4) == _lib.BSFA_ERR_ALIGN
+    assert call_masks(p, table(), k=FAKE + 8) == _lib.BSFA_ERR_ALIGN
+    assert call_masks(p, table(), dbg=FAKE + 2) == _lib.BSFA_ERR_ALIGN
+    assert call_masks(p, table(), mask_bytes=need - 8) == _lib.BSFA_ERR_ARG
+    assert call_masks(problem(N=2097152 + 64), table(t_len=1)) == _lib.BSFA_ERR_UNSUPPORTED
+    q = problem()
+    q.head_dim = 96
+    assert call_masks(q, table()) == _lib.BSFA_ERR_SHAPE
+
+
 def test_absolute_gate_length_limit():
     p = problem(N=2097152 + 64)
     st = call_prefill(p, tbl=table(t_len=1), mode=_lib.BSFA_GATE_ABSOLUTE)

@@ -15,7 +15,7 @@ import torch
 import oracle
 from block_sparse_long_amd import _lib, synth
 from block_sparse_long_amd.table import ThresholdTable
-from gpu_util import bf16_pair, check_parity, make_table, run_device
+from gpu_util import BAND, bf16_pair, check_parity, make_table, run_device
 
 pytestmark = pytest.mark.gpu
 
@@ -229,6 +229,64 @@ def test_absolute_gate_sweep_and_single_launch_agree_bitwise(name, dbg, mid_tabl
         assert a["total"] == b["total"]
         if dbg:
             np.testing.assert_array_equal(a["stat"], b["stat"])
+
+
+def _unpack_masks(mask, nkb):
+    m = np.ascontiguousarray(mask.cpu().numpy()).view(np.uint8)
+    bits = np.unpackbits(m, axis=-1, bitorder="little").astype(bool)
+    return bits[..., :nkb], bits[..., nkb:]
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_gate_masks_match_oracle_decisions(name, mid_tables):
+    # the keep decisions alone: the mask bits are the device's own fp32 comparison of its dumped
+    # maxima with the threshold, the oracle's outside the near-tie band, and zero elsewhere
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    tab = mid_tables(name)
+    dtab = tab.to_device("cuda")
+    Q, K, V = _mid_inputs(name, 15)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    nqb, nkb = -(-N // Bq), -(-N // 64)
+    W = -(-nkb // 64)
+    for sl in (0, 1):
+        mask = torch.full((B, Hq, nqb, W), -0x5A5A5A5A5A5A5A5B, dtype=torch.int64, device="cuda")
+        stat = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32, device="cuda")
+        _lib.bsfa_gate_masks(Qd, Kd, dtab, sl, mask, block_q=Bq, debug_block_stat=stat)
+        torch.cuda.synchronize()
+        bits, pad = _unpack_masks(mask, nkb)
+        assert not pad.any()
+        st = stat.cpu().numpy()
+        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=Bq, block_k=64, mode="absolute",
+                                  table=tab.T, budget_slice=sl)
+        for i in range(nqb):
+            n_off = oracle.key_block_range(i, N, Bq, 64)[0]
+            assert not bits[:, :, i, n_off:].any()
+            thr = tab.T[sl][:, min(i, tab.t_len - 1)].astype(np.float32)
+            dev = st[:, :, i, :n_off] >= thr[None, :, None]
+            np.testing.assert_array_equal(bits[:, :, i, :n_off], dev)
+            mg = r.margin[:, :, i, :n_off]
+            outside = np.abs(mg) > BAND
+            np.testing.assert_array_equal(bits[:, :, i, :n_off][outside],
+                                          r.keep[:, :, i, :n_off][outside])
+            fin = np.isfinite(r.stat[:, :, i, :n_off])
+            np.testing.assert_allclose(st[:, :, i, :n_off][fin], r.stat[:, :, i, :n_off][fin],
+                                       rtol=1e-5, atol=2e-3)
+
+
+def test_gate_masks_minus_inf_keeps_all_and_writes_every_word():
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    Q, K, V = _mid_inputs("llama_like_ragged", 16)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    nqb, nkb = -(-N // Bq), -(-N // 64)
+    tab = make_table(np.full((1, Hq, nqb), -np.inf), Bq, d).to_device("cuda")
+    mask = torch.full((B, Hq, nqb, -(-nkb // 64)), -1, dtype=torch.int64, device="cuda")
+    _lib.bsfa_gate_masks(Qd, Kd, tab, 0, mask, block_q=Bq)
+    torch.cuda.synchronize()
+    bits, pad = _unpack_masks(mask, nkb)
+    assert not pad.any()
+    for i in range(nqb):
+        n_off = oracle.key_block_range(i, N, Bq, 64)[0]
+        assert bits[:, :, i, :n_off].all() and not bits[:, :, i, n_off:].any()
 
 
 def test_back_to_back_launches_bitwise(mid_tables):
