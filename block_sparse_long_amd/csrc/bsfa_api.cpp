@@ -230,7 +230,10 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   a.kept_counts = kept_counts;
   a.kept_total = reinterpret_cast<unsigned long long*>(kept_total);
   a.dbg = debug_block_stat;
-  const int nw = bsfa::prefill_waves_per_workgroup(p->block_q, a.G, gate_mode);
+  // the kernel instantiation: the absolute gate walks the sweep's masks, or without a
+  // workspace decides every block inside the softmax loop
+  const int kgate = gate_mode == BSFA_GATE_ABSOLUTE && !use_masks ? bsfa::kAbsVote : gate_mode;
+  const int nw = bsfa::prefill_waves_per_workgroup(p->block_q, a.G, kgate);
   const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
@@ -247,7 +250,7 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
     if (a.xcd_map)
       a.xcd_rot = a.units < bsfa::kResidentWorkgroups ? bsfa::kResidentWorkgroups / a.units : 1;
   }
-  hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, gate_mode, st);
+  hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
 }

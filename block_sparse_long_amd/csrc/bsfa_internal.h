@@ -9,7 +9,9 @@ namespace bsfa {
 constexpr int kBlockK = 64;          // key tile width (gate tile columns)
 constexpr int kCalibMaxKeyBlocks = 4096;
 
-enum Gate : int { kDense = 0, kAbsolute = 1, kRelative = 2 };
+// Prefill kernel instantiations: the public gate modes, plus the absolute gate decided inside
+// the softmax loop (kAbsVote, used when no keep masks are given).
+enum Gate : int { kDense = 0, kAbsolute = 1, kRelative = 2, kAbsVote = 3 };
 
 struct PrefillArgs {
   const void* q;

@@ -527,9 +527,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // ABSOLUTE: the gate of a block depends only on its own maximum, so all off-diagonal
   // maxima are found first (pass 1, scores only) and the softmax then runs over the kept
   // tiles and the diagonal region (pass 2). RELATIVE decides tile by tile inside the loop.
-  constexpr bool kTwoPass = GATE == kAbsolute;
-  constexpr bool kLoopGate = GATE == kRelative;
-  static_assert(!kTwoPass || HPW == 1, "the absolute gate runs one head per workgroup");
+  constexpr bool kAbs = GATE == kAbsolute;          // walks the gate sweep's keep masks
+  constexpr bool kThr = kAbs || GATE == kAbsVote;    // thresholds from the table
+  static_assert(!kThr || HPW == 1, "the absolute gate runs one head per workgroup");
 
   // Separate objects per buffer: the compiler then sees that a direct copy into one buffer
   // cannot alias reads of the other and does not wait for the copy before those reads.
@@ -538,8 +538,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) __bf16 sV0[64 * STRV];
   __shared__ __attribute__((aligned(16))) __bf16 sV1[64 * STRV];
   __shared__ __attribute__((aligned(16))) float sGate[2][NW * kRows];   // per-row gate statistics
-  __shared__ unsigned long long sMask[kTwoPass ? kMaskWords : 1];       // kept off-diagonal tiles
-  __shared__ float sStage[2][NW][2];                                     // pass 1 wave maxima
+  __shared__ unsigned long long sMask[kAbs ? kMaskWords : 1];           // kept off-diagonal tiles
   __shared__ int sKept;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -555,7 +554,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int n_off = (i * BQ) / BK;
   const int n_end = (min((i + 1) * BQ, N) - 1) / BK + 1;
   const bool ragged_rows = (i + 1) * BQ > N;
-  const bool want_stat = kLoopGate || a.dbg != nullptr;
   const bool head_leader = (rw == 0) && (lane == 0);
   const float c = a.c_log2;
 
@@ -567,13 +565,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float thr[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    if (GATE == kAbsolute)
+    if (kThr)
       thr[hh] = a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)];
     else if (GATE == kRelative)
       thr[hh] = a.log_lambda;
     else
       thr[hh] = kNegInf;
   }
+  // How the absolute gate decides: kAbsolute walks only the kept tiles of the gate sweep's
+  // keep mask (two_pass); kAbsVote decides each tile in the loop like the relative gate
+  // (loop_gate, a vote of the rows on s_max >= T). A threshold of -inf keeps every block, so
+  // nothing needs deciding then (unless the maxima are dumped).
+  const bool decide = kThr && n_off > 0 && (thr[0] != kNegInf || a.dbg != nullptr);
+  const bool two_pass = kAbs && decide;
+  const bool loop_gate = GATE == kRelative || (GATE == kAbsVote && decide);
+  const bool want_stat = loop_gate || a.dbg != nullptr;
 
   unsigned koff[MK], voff[MV];
   copy_offsets<D, STR, NW>(koff, kst, w, lane);
@@ -588,14 +594,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
   auto tile_masked = [&](int j) { return j >= n_off || ragged_rows; };
 
-  // ---- pass 1 (absolute gate): maxima of all off-diagonal tiles, two tiles per barrier ----
-  // A threshold of -inf keeps every block, so no maxima are needed then (unless they are
-  // dumped), and the sequence below is simply every tile.
+  // ---- the gate sweep's keep mask of this (b, h, i), staged in LDS and counted ----
   int kept = 0, kept_all = 0;
-  const bool have_mask = kTwoPass && a.keep_mask != nullptr;
-  const bool two_pass = kTwoPass && n_off > 0 && (thr[0] != kNegInf || a.dbg != nullptr);
-  if (two_pass && have_mask) {
-    // the gate sweep already decided: copy this (b, h, i)'s mask into LDS and count it
+  if (two_pass) {
     const int nw64 = (n_off + 63) >> 6;
     const unsigned long long* gm =
         a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) * a.mask_words;
@@ -607,66 +608,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     __syncthreads();
     kept_all = sKept;
-  } else if (two_pass) {
-    // four K tiles in flight: the K buffers and the (not yet used) V buffers
-    auto kbuf = [&](int x) { return x == 0 ? sK0 : x == 1 ? sK1 : x == 2 ? sV0 : sV1; };
-    const int nw64 = (n_off + 63) >> 6;
-    for (int x = tid; x < nw64; x += NW * 64) sMask[x] = 0ull;
-    const int ng = (n_off + 1) >> 1;
-    auto load_group = [&](int gg, int p) {
-      load_k(2 * gg, kbuf(2 * p));
-      if (2 * gg + 1 < n_off) load_k(2 * gg + 1, kbuf(2 * p + 1));
-    };
-    // wave 0, lane 0: the block maxima of group gg (the waves' partial maxima in slot p) against
-    // the threshold; kept tiles set their bit
-    auto combine = [&](int gg, int p) {
-      if (w == 0 && lane == 0) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const int j = 2 * gg + k;
-          if (j < n_off) {
-            float x = sStage[p][0][k];
-#pragma unroll
-            for (int r = 1; r < NW; ++r) x = fmaxf(x, sStage[p][r][k]);
-            const float sm = x * a.scale;
-            if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
-            if (sm >= thr[0]) {
-              sMask[j >> 6] |= 1ull << (j & 63);
-              ++kept;
-            }
-          }
-        }
-      }
-    };
-    load_group(0, 0);
-    wait_vmem();
-    __syncthreads();
-    for (int gg = 0; gg < ng; ++gg) {
-      const int p = gg & 1;
-      if (gg + 1 < ng) load_group(gg + 1, p ^ 1);
-      f32x16 s2[2][2];
-      qk32<D>(kbuf(2 * p), qf, s2[0], lane);
-      const float m0 = rowmax32(s2[0], ragged_rows, 2 * gg * BK, row, N, lane);
-      float m1 = kNegInf;
-      if (2 * gg + 1 < n_off) {
-        qk32<D>(kbuf(2 * p + 1), qf, s2[1], lane);
-        m1 = rowmax32(s2[1], ragged_rows, (2 * gg + 1) * BK, row, N, lane);
-      }
-      const float w0 = wave_max(m0), w1 = wave_max(m1);
-      if (lane == 0) {
-        sStage[p][w][0] = w0;
-        sStage[p][w][1] = w1;
-      }
-      if (gg > 0) combine(gg - 1, p ^ 1);
-      wait_vmem();
-      __syncthreads();
-    }
-    combine(ng - 1, (ng - 1) & 1);
-    if (w == 0 && lane == 0) sKept = kept;
-    __syncthreads();
-    kept_all = sKept;
-  } else if (kTwoPass || GATE == kDense) {
-    kept = n_off;
+  } else if (!loop_gate) {
+    kept = n_off;   // dense, or an absolute threshold of -inf: every block kept
   }
   // The tile after j in the sequence the softmax walks: with the pass-1 mask, the next kept
   // off-diagonal tile and then the diagonal region; otherwise every tile.
@@ -785,7 +728,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         for (int k = 1; k < GV; ++k) x = fmaxf(x, gv[hh][k]);
         hv[hh] = x * a.scale;
       }
-      if (kLoopGate && !diag) {
+      if (loop_gate && !diag) {
         anyv = false;
 #pragma unroll
         for (int hh = 0; hh < HPW; ++hh) {
@@ -802,7 +745,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         if (head_leader) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + t] = x;
       }
     }
-    if (kLoopGate && head_leader && !diag) kept += mykeep ? 1 : 0;
+    if (loop_gate && head_leader && !diag) kept += mykeep ? 1 : 0;
 
     float alpha = 1.f, off = 0.f;
     bool moved = false;
@@ -1188,10 +1131,15 @@ hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t strea
       hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kDense>), grid, block, 0, stream, a);
       break;
     case kAbsolute:
-      if constexpr (NW == BQ / kRows)   // one head per workgroup
-        hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute>), grid, block, 0, stream, a);
-      else
+    case kAbsVote:
+      if constexpr (NW == BQ / kRows) {   // one head per workgroup
+        if (gate == kAbsolute)
+          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute>), grid, block, 0, stream, a);
+        else
+          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsVote>), grid, block, 0, stream, a);
+      } else {
         return hipErrorInvalidConfiguration;
+      }
       break;
     default:
       hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kRelative>), grid, block, 0, stream, a);
@@ -1262,7 +1210,8 @@ int waves_per_workgroup(int block_q, int group) {
 }
 
 int prefill_waves_per_workgroup(int block_q, int group, int gate) {
-  return gate == kAbsolute ? block_q / kRows : waves_per_workgroup(block_q, group);
+  return gate == kAbsolute || gate == kAbsVote ? block_q / kRows
+                                               : waves_per_workgroup(block_q, group);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
