@@ -384,12 +384,15 @@ __device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], i
   vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
 }
 
-template <int D, int FIRST, int LAST, int DEC, int MV, typename CopyV>
+// ALL = true: the caller has established do_pv, do_exp and vload, so the steps are straight-line
+// code with no per-step branches (the common case: nothing skipped).
+template <int D, int FIRST, int LAST, int DEC, int MV, bool ALL = false, typename CopyV>
 __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, const __bf16* sv,
                                          const bf16x8 (&pbp)[4], f32x16 (&o)[D / 32],
                                          bf16x8 (&vb)[3], const f32x16 (&sc)[2], float off,
                                          float c, bf16x8 (&pbn)[4], float& sum, int lane,
                                          CopyV&& copy_v) {
+  if constexpr (ALL) do_pv = do_exp = vload = true;
   constexpr int MD = D / 32;
   constexpr int NSTEP = MD * 4;
   constexpr int NE = NSTEP - DEC > 0 ? NSTEP - DEC : 1;
@@ -420,12 +423,14 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
 // copy (kload, copy_k(r)) on the first steps, the remaining exponential pairs of the current
 // tile (do_exp) and, during the second M-block, the in-lane max over the first block's 16
 // scores (into mx).
-template <int D, int MK, typename CopyK>
+// ALL = true: do_exp and kload are established by the caller (straight-line steps).
+template <int D, int MK, bool ALL = false, typename CopyK>
 __device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* kbase,
                                          const bf16x8 (&qf)[D / 16],
                                          f32x16 (&sn)[2], const f32x16 (&sc)[2], float off,
                                          float c, bf16x8 (&pbn)[4], float& sum, float& mx,
                                          CopyK&& copy_k) {
+  if constexpr (ALL) do_exp = kload = true;
   constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR, NST = 2 * KS;
   constexpr int NP = kPairs - kPairsQK;
   bf16x8 ka[2];
@@ -755,7 +760,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // rest of PV of the previous tile with the first half of tile t's exponentials and the V_t
     // copy (skipped as a whole when there is none of the three)
-    if (keep_prev || anyv)
+    // straight-line steps when everything runs (in the voting kernels a second copy of the
+    // phase costs more registers than the branches it saves)
+    constexpr bool kFast = GATE == kDense || GATE == kAbsolute;
+    if (kFast && keep_prev && mykeep && anyv)
+      pv_steps<D, DEC, NSTEP, DEC, MVR, true>(true, true, true, sv, pb[P ^ 1], o, vb, sb[P],
+                                              off, c, pb[P], sum, lane, copy_v);
+    else if (keep_prev || anyv)
       pv_steps<D, DEC, NSTEP, DEC, MVR>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P],
                                         off, c, pb[P], sum, lane, copy_v);
     // the previous P is dead from here on (the next write of its buffer precedes the next read)
@@ -773,7 +784,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // scores of tile t1 with the second half of tile t's exponentials
     const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K of t1
     float mx = kNegInf;
-    qk_phase<D, MKR>(mykeep, kload, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
+    if (kFast && mykeep && kload)
+      qk_phase<D, MKR, true>(true, true, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
+    else
+      qk_phase<D, MKR>(mykeep, kload, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
     if (mykeep) st.l += sum;
     if (tile_masked(t1)) {
       mask_tile(sb[P ^ 1], t1 * BK, row, N, lane);
