@@ -384,15 +384,24 @@ __device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], i
   vb[1] = v_frag<D>(sv, 1 % MD, 1 / MD, lane);
 }
 
-// ALL = true: the caller has established do_pv, do_exp and vload, so the steps are straight-line
-// code with no per-step branches (the common case: nothing skipped).
-template <int D, int FIRST, int LAST, int DEC, int MV, bool ALL = false, typename CopyV>
+// How a step sequence treats each of its optional parts: kNever (compiled out), kFlag (a
+// wave-uniform run-time flag tested at every step) or kAlways (straight-line code). Per-step
+// tests cost a compare and a branch each; the common cases are compiled without them.
+enum PartMode : int { kNever = 0, kFlag = 1, kAlways = 2 };
+__device__ __forceinline__ bool part_on(int mode, bool flag) {
+  return mode == kAlways || (mode == kFlag && flag);
+}
+
+template <int D, int FIRST, int LAST, int DEC, int MV, int PVM = kFlag, int EXM = kFlag,
+          int VLM = kFlag, typename CopyV>
 __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, const __bf16* sv,
                                          const bf16x8 (&pbp)[4], f32x16 (&o)[D / 32],
                                          bf16x8 (&vb)[3], const f32x16 (&sc)[2], float off,
                                          float c, bf16x8 (&pbn)[4], float& sum, int lane,
                                          CopyV&& copy_v) {
-  if constexpr (ALL) do_pv = do_exp = vload = true;
+  do_pv = part_on(PVM, do_pv);
+  do_exp = part_on(EXM, do_exp);
+  vload = part_on(VLM, vload);
   constexpr int MD = D / 32;
   constexpr int NSTEP = MD * 4;
   constexpr int NE = NSTEP - DEC > 0 ? NSTEP - DEC : 1;
@@ -423,14 +432,14 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
 // copy (kload, copy_k(r)) on the first steps, the remaining exponential pairs of the current
 // tile (do_exp) and, during the second M-block, the in-lane max over the first block's 16
 // scores (into mx).
-// ALL = true: do_exp and kload are established by the caller (straight-line steps).
-template <int D, int MK, bool ALL = false, typename CopyK>
+template <int D, int MK, int EXM = kFlag, int KLM = kFlag, typename CopyK>
 __device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* kbase,
                                          const bf16x8 (&qf)[D / 16],
                                          f32x16 (&sn)[2], const f32x16 (&sc)[2], float off,
                                          float c, bf16x8 (&pbn)[4], float& sum, float& mx,
                                          CopyK&& copy_k) {
-  if constexpr (ALL) do_exp = kload = true;
+  do_exp = part_on(EXM, do_exp);
+  kload = part_on(KLM, kload);
   constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR, NST = 2 * KS;
   constexpr int NP = kPairs - kPairsQK;
   bf16x8 ka[2];
@@ -760,15 +769,28 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     // rest of PV of the previous tile with the first half of tile t's exponentials and the V_t
     // copy (skipped as a whole when there is none of the three)
-    // straight-line steps when everything runs (in the voting kernels a second copy of the
-    // phase costs more registers than the branches it saves)
-    constexpr bool kFast = GATE == kDense || GATE == kAbsolute;
-    if (kFast && keep_prev && mykeep && anyv)
-      pv_steps<D, DEC, NSTEP, DEC, MVR, true>(true, true, true, sv, pb[P ^ 1], o, vb, sb[P],
-                                              off, c, pb[P], sum, lane, copy_v);
-    else if (keep_prev || anyv)
-      pv_steps<D, DEC, NSTEP, DEC, MVR>(keep_prev, mykeep, anyv, sv, pb[P ^ 1], o, vb, sb[P],
-                                        off, c, pb[P], sum, lane, copy_v);
+    // Step sequences without per-step tests wherever possible. Dense and the mask walk keep
+    // every tile they visit: one straight-line form (and a flagged one for the first tile).
+    // The voting kernels take the PV test out of the steps (a form with and one without the
+    // MFMAs) and compute the exponentials of every tile: those of a skipped tile are never
+    // used, which costs less than a test per step (and a second full copy of the phase costs
+    // more registers than the tests it saves).
+    constexpr bool kVote = GATE == kRelative || GATE == kAbsVote;
+    if constexpr (!kVote) {
+      if (keep_prev)
+        pv_steps<D, DEC, NSTEP, DEC, MVR, kAlways, kAlways, kAlways>(
+            true, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+      else
+        pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kAlways>(
+            false, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+    } else {
+      if (keep_prev)
+        pv_steps<D, DEC, NSTEP, DEC, MVR, kAlways, kAlways, kFlag>(
+            true, true, anyv, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+      else
+        pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kFlag>(
+            false, true, anyv, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+    }
     // the previous P is dead from here on (the next write of its buffer precedes the next read)
 #pragma unroll
     for (int k = 0; k < 4; ++k) asm("" : "=v"(pb[P ^ 1][k]));
@@ -784,10 +806,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // scores of tile t1 with the second half of tile t's exponentials
     const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K of t1
     float mx = kNegInf;
-    if (kFast && mykeep && kload)
-      qk_phase<D, MKR, true>(true, true, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
+    if (kload)
+      qk_phase<D, MKR, kAlways, kAlways>(true, true, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P],
+                                         sum, mx, copy_k);
     else
-      qk_phase<D, MKR>(mykeep, kload, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P], sum, mx, copy_k);
+      qk_phase<D, MKR, kAlways, kNever>(true, false, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P],
+                                        sum, mx, copy_k);
     if (mykeep) st.l += sum;
     if (tile_masked(t1)) {
       mask_tile(sb[P ^ 1], t1 * BK, row, N, lane);
