@@ -245,10 +245,9 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
     a.keep_mask = static_cast<unsigned long long*>(workspace);
     hipError_t e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
-    // the walk over kept tiles is as long as the head keeps: spread every KV head over all
-    // XCDs, turning the assignment once per set of query blocks in flight together
-    if (a.xcd_map)
-      a.xcd_rot = a.units < bsfa::kResidentWorkgroups ? bsfa::kResidentWorkgroups / a.units : 1;
+    // the walk over kept tiles: one KV head at a time on all XCDs (its K/V stays in the
+    // last-level cache, and walks whose lengths differ between heads spread over every XCD)
+    a.xcd_map = -1;
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

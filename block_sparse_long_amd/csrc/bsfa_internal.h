@@ -25,7 +25,8 @@ struct PrefillArgs {
   long long qs[3], ks[3], vs[3], os[3];
   int B, N, Hq, Hkv, G, nqb, nkb, t_len;
   int units;                       // B * Hkv * (G / heads per workgroup)
-  int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads)
+  int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads);
+                                   // -1: KV-head-major order over all XCDs
   int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
                                    // blocks (0: never)
   float scale;                     // softmax scale applied to fp32 scores

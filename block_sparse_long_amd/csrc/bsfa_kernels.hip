@@ -506,6 +506,20 @@ struct Unit {
 __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, int Hkv,
                                             int xcd_map, int xcd_rot) {
   int i, u;
+  if (xcd_map < 0) {
+    // KV-head-major: every (batch, KV head) in turn, its query blocks from the last, its head
+    // groups innermost. Consecutive workgroups still go to the 8 XCDs in turn, so all XCDs
+    // work on the same KV head at a time and its K/V (64 MB at 128K, d = 128) stays in the
+    // last-level cache for every XCD's walk.
+    const int upg = units / (B * Hkv);
+    const int bh = L / (nqb * upg), rem = L % (nqb * upg);
+    Unit r;
+    r.b = bh / Hkv;
+    r.g = bh % Hkv;
+    r.i = nqb - 1 - rem / upg;
+    r.hg = rem % upg;
+    return r;
+  }
   if (xcd_map) {
     const int x = L & 7, s = L >> 3, upx = units >> 3;
     i = nqb - 1 - s / upx;
