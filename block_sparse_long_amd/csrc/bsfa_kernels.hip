@@ -130,6 +130,13 @@ __device__ __forceinline__ float wave_max(float x) {
 // Wait for this wave's outstanding global loads (including those writing LDS directly).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Wait until at most N of this wave's global loads are outstanding (they complete in order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_n() {
+  static_assert(N >= 0 && N < 64, "vmcnt field");   // bits 3:0 and 15:14
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
 template <int D>
 struct Tile {
   static constexpr int CPR = D / 8;         // 16-byte chunks of data per row (16 or 8)
@@ -964,19 +971,18 @@ __device__ __forceinline__ float tile_max64(f32x16 (&s)[2][2], bool ragged, int 
 }
 
 template <int D, int BQ, int HPW>
-__global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gate_sweep_kernel(PrefillArgs a) {
   constexpr int WPH = BQ / 64;             // waves per head
   constexpr int NW = HPW * WPH;
   constexpr int STR = Tile<D>::STR, KS = Tile<D>::KS;
-  constexpr int MK = copy_iters<STR, NW>();
+  constexpr int MK = copy_iters<STR, NW>(), CPS = STR / 8;
 
+  // three K tiles: tile j is read from buffer j % 3 while tiles j + 1 and j + 2 are in flight
   __shared__ __attribute__((aligned(16))) __bf16 sKa[64 * STR];
   __shared__ __attribute__((aligned(16))) __bf16 sKb[64 * STR];
   __shared__ __attribute__((aligned(16))) __bf16 sKc[64 * STR];
-  __shared__ __attribute__((aligned(16))) __bf16 sKd[64 * STR];
-  __shared__ unsigned long long sM[HPW][kMaskWords];
-  __shared__ float sStage[2][NW][2];
+  __shared__ float sStage[2][NW];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -989,12 +995,17 @@ void gate_sweep_kernel(PrefillArgs a) {
   const int row0 = i * BQ + rw * 64;
   const int n_off = (i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
-  // words of each head's mask this workgroup writes: those covering the off-diagonal tiles, or
-  // with full_masks every word (zero past the off-diagonal tiles)
-  const int nwr = a.full_masks ? a.mask_words : (n_off + 63) >> 6;
+  const bool leader = rw == 0 && lane == 0;   // one lane per head: its decisions and mask words
+  unsigned long long* const mask = a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) *
+                                                     a.mask_words;
+  // with full_masks every word of every head is written (zero past the off-diagonal tiles)
+  const int nw64 = (n_off + 63) >> 6;
+  auto zero_tail = [&]() {
+    if (a.full_masks && leader)
+      for (int x = nw64; x < a.mask_words; ++x) mask[x] = 0ull;
+  };
   if (n_off == 0) {         // uniform: nothing off-diagonal to decide
-    for (int x = tid; x < HPW * nwr; x += NW * 64)
-      a.keep_mask[(((long long)b * a.Hq + h0 + x / nwr) * a.nqb + i) * a.mask_words + x % nwr] = 0ull;
+    zero_tail();
     return;
   }
 
@@ -1007,7 +1018,7 @@ void gate_sweep_kernel(PrefillArgs a) {
   auto load_k = [&](int j, __bf16* dst) {
     copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, BK, dst, w, lane);
   };
-  auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : x == 2 ? sKc : sKd; };
+  auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
   const float thr = a.thr[h * a.t_len + min(i, a.t_len - 1)];
   // heads whose threshold is -inf keep everything without a mask (the softmax kernel does not
   // read one then), so a workgroup of only such heads has nothing to decide unless the maxima
@@ -1018,63 +1029,56 @@ void gate_sweep_kernel(PrefillArgs a) {
     all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)] == kNegInf;
   if (all_keep) return;
 
-  for (int x = tid; x < HPW * nwr; x += NW * 64) sM[x / nwr][x % nwr] = 0ull;
-  const int ng = (n_off + 1) >> 1;
-  auto load_group = [&](int gg, int p) {
-    load_k(2 * gg, kbuf(2 * p));
-    if (2 * gg + 1 < n_off) load_k(2 * gg + 1, kbuf(2 * p + 1));
+  // The copy instructions one tile takes from this wave (the last round only on some waves):
+  // waiting until that many remain outstanding leaves the newest tile in flight.
+  const bool last_round = w + NW * (MK - 1) < CPS;
+  auto wait_all_but_newest_tile = [&]() {
+    if (last_round)
+      wait_vmem_n<MK>();
+    else
+      wait_vmem_n<MK - 1>();
   };
-  // the first wave of each head, lane 0: block maxima of group gg (partial maxima of the
-  // head's waves in slot p) against the head's threshold
-  auto combine = [&](int gg, int p) {
-    if (rw == 0 && lane == 0) {
+  // leader of head hw: decision for tile j from the head's waves' maxima in slot j & 1; each
+  // completed mask word goes out at once
+  unsigned long long word = 0ull;
+  auto combine = [&](int j) {
+    if (leader) {
+      float x = sStage[j & 1][hw * WPH];
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int j = 2 * gg + k;
-        if (j < n_off) {
-          float x = sStage[p][hw * WPH][k];
-#pragma unroll
-          for (int r = 1; r < WPH; ++r) x = fmaxf(x, sStage[p][hw * WPH + r][k]);
-          const float sm = x * a.scale;
-          if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
-          if (sm >= thr) sM[hw][j >> 6] |= 1ull << (j & 63);
-        }
+      for (int r = 1; r < WPH; ++r) x = fmaxf(x, sStage[j & 1][hw * WPH + r]);
+      const float sm = x * a.scale;
+      if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
+      if (sm >= thr) word |= 1ull << (j & 63);
+      if ((j & 63) == 63 || j == n_off - 1) {
+        mask[j >> 6] = word;
+        word = 0ull;
       }
     }
   };
 
-  load_group(0, 0);
+  load_k(0, sKa);
+  if (n_off > 1) load_k(1, sKb);
   bf16x8 qf[2][KS];
   load_q32<D>(Qb, a.qs[1], row0, N, qf[0], lane);
   load_q32<D>(Qb, a.qs[1], row0 + 32, N, qf[1], lane);
   wait_vmem();
   __syncthreads();
-  for (int gg = 0; gg < ng; ++gg) {
-    const int p = gg & 1;
-    if (gg + 1 < ng) load_group(gg + 1, p ^ 1);
-    f32x16 s0[2][2], s1[2][2];
-    qk64<D>(kbuf(2 * p), qf, s0, lane);
-    const float m0 = tile_max64(s0, ragged_rows, row0, N, lane);
-    float m1 = kNegInf;
-    if (2 * gg + 1 < n_off) {
-      qk64<D>(kbuf(2 * p + 1), qf, s1, lane);
-      m1 = tile_max64(s1, ragged_rows, row0, N, lane);
-    }
-    const float w0 = wave_max(m0), w1 = wave_max(m1);
-    if (lane == 0) {
-      sStage[p][w][0] = w0;
-      sStage[p][w][1] = w1;
-    }
-    if (gg > 0) combine(gg - 1, p ^ 1);
-    wait_vmem();
+  for (int j = 0; j < n_off; ++j) {
+    if (j + 2 < n_off) load_k(j + 2, kbuf((j + 2) % 3));   // the buffer tile j - 1 used
+    f32x16 s[2][2];
+    qk64<D>(kbuf(j % 3), qf, s, lane);
+    const float m = wave_max(tile_max64(s, ragged_rows, row0, N, lane));
+    if (lane == 0) sStage[j & 1][w] = m;
+    if (j > 0) combine(j - 1);
+    // tile j + 1 must have landed before the barrier; tile j + 2 may stay in flight
+    if (j + 2 < n_off)
+      wait_all_but_newest_tile();
+    else
+      wait_vmem();
     __syncthreads();
   }
-  combine(ng - 1, (ng - 1) & 1);
-  __syncthreads();
-  for (int x = tid; x < HPW * nwr; x += NW * 64) {
-    const int hh = x / nwr, wi = x % nwr;
-    a.keep_mask[(((long long)b * a.Hq + h0 + hh) * a.nqb + i) * a.mask_words + wi] = sM[hh][wi];
-  }
+  combine(n_off - 1);
+  zero_tail();
 }
 
 // ---------------------------------------------------------------------------------------------
