@@ -36,6 +36,11 @@ Readings taken where the pages are silent or ambiguous (each is listed in the de
   * The relative gate compares max over the tile's rows of (row max of the block - running row
     max before the block) with ln(lambda); lambda = 0 means never skip.
   * Rows past the end of a ragged last block do not exist (blocks are clipped to N).
+  * Chunked prefill: a chunk of N_q query rows follows a prefix of P = N_k - N_q keys (its rows
+    sit at absolute positions P .. N_k - 1). Query block i then starts at absolute row
+    P + i*Bq, the causal mask and n_off / n_end use absolute positions, and the absolute gate
+    reads the threshold column of the absolute query block P/Bq + i, which needs P to be a
+    multiple of Bq (thresholds are bound to the calibration's tile grid).
 
 Pins (tests that tie each function to something other than itself) are in
 tests/test_oracle_pins.py; every public function here is pinned.
@@ -58,8 +63,10 @@ def num_blocks(n: int, block: int) -> int:
     return (n + block - 1) // block
 
 
-def key_block_range(i: int, n: int, block_q: int, block_k: int) -> tuple[int, int]:
-    """(n_off, n_end) for query block i of a length-n causal prefill.
+def key_block_range(i: int, n: int, block_q: int, block_k: int,
+                    prefix: int = 0) -> tuple[int, int]:
+    """(n_off, n_end) for query block i of a causal prefill of n query rows that follow
+    ``prefix`` earlier keys (rows at absolute positions prefix .. prefix + n - 1).
 
     Key blocks j < n_off lie wholly before the query block's first row, so every pair in them is
     visible: these are the off-diagonal candidates the gate acts on. Blocks n_off <= j < n_end
@@ -67,8 +74,8 @@ def key_block_range(i: int, n: int, block_q: int, block_k: int) -> tuple[int, in
     past n_end are invisible to every row of the block. ("Block Sparse Flash Attention",
     Method > Key Designs 2, on the causal diagonal region and on unequal tile shapes.)
     """
-    n_off = (i * block_q) // block_k
-    last_row = min((i + 1) * block_q, n) - 1
+    n_off = (prefix + i * block_q) // block_k
+    last_row = prefix + min((i + 1) * block_q, n) - 1
     n_end = last_row // block_k + 1
     return n_off, n_end
 
@@ -85,9 +92,9 @@ def effective_threshold(table: np.ndarray, budget_slice: int, h: int, i: int) ->
 
 @dataclass
 class OracleResult:
-    out: np.ndarray          # [B, N, Hq, d]; NaN rows for query blocks not computed
+    out: np.ndarray          # [B, Nq, Hq, d]; NaN rows for query blocks not computed
     kept_counts: np.ndarray  # [B, Hq, nqb] int64, kept OFF-diagonal blocks; -1 if not computed
-    stat: np.ndarray         # [B, Hq, nqb, nkb] gate statistic per visible block; NaN elsewhere
+    stat: np.ndarray         # [B, Hq, nqb, nkb] (nkb over Nk) gate statistic per visible block
     keep: np.ndarray         # [B, Hq, nqb, nkb] bool; True for kept blocks and the diagonal region
     margin: np.ndarray       # [B, Hq, nqb, nkb] stat - threshold (off-diagonal only); NaN elsewhere
 
@@ -99,7 +106,9 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                    query_blocks=None, dtype=np.float32) -> OracleResult:
     """Gated causal prefill attention, one (b, h, i) work unit at a time.
 
-    Q: [B, N, Hq, d]; K, V: [B, N, Hkv, d] with Hq % Hkv == 0.
+    Q: [B, Nq, Hq, d]; K, V: [B, Nk, Hkv, d] with Nk >= Nq and Hq % Hkv == 0. The query rows
+    are the last Nq positions of the sequence (a chunk after a prefix of P = Nk - Nq keys; P = 0
+    is a whole prefill).
     mode: "dense" (keep everything), "absolute" (keep iff s_max >= T_eff(h, i) from ``table``
     [n_budgets][Hq][T_len] at ``budget_slice``) or "relative" (keep iff
     max_r(rowmax_j[r] - m[r]) >= log_lambda).
@@ -113,14 +122,17 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     K = np.asarray(K, dtype=dtype)
     V = np.asarray(V, dtype=dtype)
     B, N, Hq, d = Q.shape
-    Hkv = K.shape[2]
-    if K.shape != (B, N, Hkv, d) or V.shape != K.shape or Hq % Hkv != 0:
+    Hkv, Nk = K.shape[2], K.shape[1]
+    if K.shape != (B, Nk, Hkv, d) or V.shape != K.shape or Hq % Hkv != 0 or Nk < N:
         raise ValueError("shape mismatch")
+    P = Nk - N                                               # keys before the chunk
     if mode == GATE_ABSOLUTE and table is None:
         raise ValueError("absolute gate needs a threshold table")
+    if mode == GATE_ABSOLUTE and P % block_q != 0:
+        raise ValueError("the absolute gate needs the prefix to be a multiple of block_q")
     G = Hq // Hkv
     sc = dtype(1.0 / math.sqrt(d) if scale is None else scale)
-    nqb, nkb = num_blocks(N, block_q), num_blocks(N, block_k)
+    nqb, nkb = num_blocks(N, block_q), num_blocks(Nk, block_k)
     blocks = range(nqb) if query_blocks is None else sorted(set(int(x) for x in query_blocks))
 
     out = np.full((B, N, Hq, d), np.nan, dtype=dtype)
@@ -141,17 +153,18 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                     m = np.full(R, -np.inf, dtype=dtype)
                     l = np.zeros(R, dtype=dtype)
                     o = np.zeros((R, d), dtype=dtype)
-                    n_off, n_end = key_block_range(i, N, block_q, block_k)
-                    te = (effective_threshold(table, budget_slice, h, i)
+                    n_off, n_end = key_block_range(i, N, block_q, block_k, P)
+                    # thresholds belong to the absolute query block
+                    te = (effective_threshold(table, budget_slice, h, P // block_q + i)
                           if mode == GATE_ABSOLUTE else None)
                     kept = 0
                     for j in range(n_end):                    # ascending; diagonal region last
-                        c0, c1 = j * block_k, min((j + 1) * block_k, N)
+                        c0, c1 = j * block_k, min((j + 1) * block_k, Nk)
                         # exact scaled pre-softmax scores of the whole tile (keep-rule equation)
                         s = (q @ K[b, c0:c1, g, :].T) * sc
                         if j >= n_off:
                             # causal diagonal region: mask future keys, always aggregated
-                            rows = np.arange(r0, r1)[:, None]
+                            rows = P + np.arange(r0, r1)[:, None]     # absolute positions
                             cols = np.arange(c0, c1)[None, :]
                             s = np.where(cols > rows, dtype(-np.inf), s)
                             stat[b, h, i, j] = float(s.max())

@@ -401,3 +401,75 @@ def test_predicted_density_closed_form():
 def test_oracle_module_header_marks_test_infrastructure():
     doc = oracle.bsfa_oracle.__doc__
     assert "TEST INFRASTRUCTURE ONLY" in doc
+
+
+# ---------------------------------------------------------------------------------------------
+# Chunked prefill: a chunk of query rows after a prefix of keys
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("Nq,P,Bq,Bk", [(256, 128, 64, 64), (300, 256, 128, 64), (200, 70, 64, 64),
+                                        (129, 1, 128, 64), (64, 1000, 64, 32)])
+def test_block_ranges_with_prefix_match_brute_force(Nq, P, Bq, Bk):
+    Nk = Nq + P
+    nkb = -(-Nk // Bk)
+    for i in range(-(-Nq // Bq)):
+        n_off, n_end = key_block_range(i, Nq, Bq, Bk, P)
+        first, last = P + i * Bq, P + min((i + 1) * Bq, Nq) - 1     # absolute rows
+        # blocks whose every key precedes the first row, and blocks holding a visible key
+        assert n_off == sum(1 for j in range(nkb) if min((j + 1) * Bk, Nk) - 1 < first)
+        assert n_end == sum(1 for j in range(nkb) if j * Bk <= last)
+
+
+@pytest.mark.parametrize("B,Nq,P,Hq,Hkv,d,Bq,Bk", [(1, 200, 128, 2, 1, 16, 64, 64),
+                                                   (2, 130, 70, 4, 2, 8, 128, 64),
+                                                   (1, 64, 333, 2, 2, 16, 64, 32)])
+def test_prefix_dense_equals_masked_attention(B, Nq, P, Hq, Hkv, d, Bq, Bk):
+    # any prefix (aligned to the tiles or not): row r of the chunk sees keys 0 .. P + r
+    rng = np.random.default_rng(31)
+    Q = rng.standard_normal((B, Nq, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((B, Nq + P, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, Nq + P, Hkv, d)).astype(np.float32)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_DENSE)
+    mask = np.arange(Nq + P)[None, :] <= (P + np.arange(Nq))[:, None]
+    ref = sdpa_masked(Q, K, V, np.broadcast_to(mask, (B, Hq, Nq, Nq + P)).copy())
+    np.testing.assert_allclose(r.out, ref, rtol=0, atol=3e-6)
+    for i in range(-(-Nq // Bq)):
+        assert (r.kept_counts[:, :, i] == key_block_range(i, Nq, Bq, Bk, P)[0]).all()
+
+
+@pytest.mark.parametrize("mode", ["dense", "absolute", "relative"])
+@pytest.mark.parametrize("P", [128, 256])
+def test_chunk_equals_rows_of_full_prefill(mode, P):
+    # with the prefix on the query-block grid, every query block of the chunk sees the same
+    # keys, thresholds and traversal as the same block of the whole prefill: identical results
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 512, 4, 2, 16, 64, 64
+    Q, K, V = _rand(32, B, N, Hq, Hkv, d)
+    Q = Q * 2.0
+    nqb = N // Bq
+    kw = dict(block_q=Bq, block_k=Bk, mode=mode)
+    if mode == "absolute":
+        rng = np.random.default_rng(5)
+        kw["table"] = _midpoint_table(brute_block_max(Q, K, Bq, Bk), Hq, nqb, rng)
+    elif mode == "relative":
+        # keys after the first block weaker, so that later blocks trail the running max
+        K = K.copy()
+        K[:, 64:] *= 0.3
+        kw["log_lambda"] = math.log(0.3)
+    full = oracle_prefill(Q, K, V, **kw)
+    chunk = oracle_prefill(Q[:, P:], K, V, **kw)
+    i0 = P // Bq
+    np.testing.assert_array_equal(chunk.out, full.out[:, P:])
+    np.testing.assert_array_equal(chunk.kept_counts, full.kept_counts[:, :, i0:])
+    np.testing.assert_array_equal(chunk.keep, full.keep[:, :, i0:])
+    np.testing.assert_array_equal(np.isnan(chunk.stat), np.isnan(full.stat[:, :, i0:]))
+    fin = ~np.isnan(chunk.stat)
+    np.testing.assert_array_equal(chunk.stat[fin], full.stat[:, :, i0:][fin])
+    if mode != "dense":
+        assert 0 < chunk.kept_counts.sum() < sum(key_block_range(i, N - P, Bq, Bk, P)[0]
+                                                 for i in range(nqb - i0)) * B * Hq
+
+
+def test_absolute_gate_rejects_prefix_off_the_block_grid():
+    Q, K, V = _rand(33, 1, 192, 1, 1, 8)
+    with pytest.raises(ValueError):
+        oracle_prefill(Q[:, 100:], K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE,
+                       table=_const_table(0.0, 1, 3))
