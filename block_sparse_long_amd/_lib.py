@@ -43,6 +43,7 @@ class BsfaProblem(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+        ("kv_seqlen", ctypes.c_int32),
     ]
 
 
@@ -137,6 +138,8 @@ def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
     p = BsfaProblem()
     p.batch, p.seqlen, p.heads_q, p.head_dim = (int(x) for x in Q.shape)
     p.heads_kv = int(K.shape[2])
+    # K and V may hold more positions than Q: the query rows are their last seqlen positions
+    p.kv_seqlen = int(K.shape[1]) if K.shape[1] != Q.shape[1] else 0
     p.block_q, p.block_k = int(block_q), int(block_k)
     p.softmax_scale = float(softmax_scale)
     dt = {torch.bfloat16: BSFA_BF16, torch.float32: BSFA_FP32}
@@ -155,7 +158,8 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                  table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
                  kept_counts=None, kept_total=None, debug_block_stat=None,
                  softmax_scale: float = 0.0, stream=None, out_dtype=None, workspace=None):
-    """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, N, Hkv, d] bf16 (device).
+    """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, Nk, Hkv, d] bf16 (device),
+    Nk >= N (Nk > N: a chunk of N query rows after Nk - N cached keys).
 
     O (allocated if None, dtype ``out_dtype`` or bf16), kept_counts (int32 [B, Hq, nqb]),
     kept_total (int64 [1], read as uint64) and debug_block_stat (fp32 [B, Hq, nqb, nkb]) are
@@ -202,7 +206,7 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
     import torch
     lib = load_library()
     B, N, Hq, _ = Q.shape
-    nqb, nkb = -(-N // block_q), -(-N // block_k)
+    nqb, nkb = -(-N // block_q), -(-int(K.shape[1]) // block_k)
     if keep_mask is None:
         keep_mask = torch.empty((B, Hq, nqb, -(-nkb // 64)), dtype=torch.int64, device=Q.device)
     if not keep_mask.is_contiguous() or keep_mask.element_size() != 8:

@@ -42,6 +42,9 @@ bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
   if (p->heads_q < 1 || p->heads_kv < 1)
     return fail(BSFA_ERR_ARG, "heads_q (%d) and heads_kv (%d) must be >= 1", p->heads_q,
                 p->heads_kv);
+  if (p->kv_seqlen != 0 && p->kv_seqlen < p->seqlen)
+    return fail(BSFA_ERR_ARG, "kv_seqlen (%d) must be 0 or >= seqlen (%d)", p->kv_seqlen,
+                p->seqlen);
   if (p->heads_q % p->heads_kv != 0)
     return fail(BSFA_ERR_SHAPE, "heads_q (%d) is not a multiple of heads_kv (%d)", p->heads_q,
                 p->heads_kv);
@@ -76,6 +79,9 @@ bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Key tokens: the query rows are the last seqlen of kv_seqlen positions (0: a whole prefill).
+int key_len(const bsfa_problem* p) { return p->kv_seqlen > 0 ? p->kv_seqlen : p->seqlen; }
 
 // The threshold table against the problem: present, aligned, bound to the same heads, tile,
 // head_dim and scale, and the budget slice in range.
@@ -124,11 +130,13 @@ bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K,
   }
   a.B = p->batch;
   a.N = p->seqlen;
+  a.Nk = key_len(p);
+  a.P = a.Nk - a.N;
   a.Hq = p->heads_q;
   a.Hkv = p->heads_kv;
   a.G = p->heads_q / p->heads_kv;
   a.nqb = ceil_div(p->seqlen, p->block_q);
-  a.nkb = ceil_div(p->seqlen, p->block_k);
+  a.nkb = ceil_div(a.Nk, p->block_k);
   a.scale = scale;
   a.c_log2 = scale * 1.4426950408889634f;
   a.mask_words = ceil_div(a.nkb, 64);
@@ -171,7 +179,7 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
     return 0;
   const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
-  const uint64_t words = ceil_div(ceil_div(p->seqlen, p->block_k), 64);
+  const uint64_t words = ceil_div(ceil_div(key_len(p), p->block_k), 64);
   return (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
 }
 
@@ -204,12 +212,16 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
       (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u)))
     return fail(BSFA_ERR_ALIGN, "kept_counts, kept_total or debug_block_stat misaligned");
   const int nqb = ceil_div(p->seqlen, p->block_q);
-  const int nkb = ceil_div(p->seqlen, p->block_k);
-  if ((long long)p->seqlen > (1ll << 30))
-    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d too large", p->seqlen);
+  const int nkb = ceil_div(key_len(p), p->block_k);
+  if ((long long)key_len(p) > (1ll << 30))
+    return fail(BSFA_ERR_UNSUPPORTED, "kv_seqlen %d too large", key_len(p));
   if (gate_mode == BSFA_GATE_ABSOLUTE && nkb > bsfa::kMaxGateTiles)
-    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the absolute-gate limit %d", p->seqlen,
+    return fail(BSFA_ERR_UNSUPPORTED, "%d keys above the absolute-gate limit %d", key_len(p),
                 bsfa::kMaxGateTiles * bsfa::kBlockK);
+  if (gate_mode == BSFA_GATE_ABSOLUTE && (key_len(p) - p->seqlen) % p->block_q != 0)
+    return fail(BSFA_ERR_SHAPE, "the absolute gate needs the prefix (%d keys) to be a multiple "
+                "of block_q (%d): thresholds are indexed by absolute query block",
+                key_len(p) - p->seqlen, p->block_q);
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   const uint64_t ws_need = bsfa_prefill_workspace_bytes(p, gate_mode);
@@ -270,10 +282,14 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
   if (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u))
     return fail(BSFA_ERR_ALIGN, "debug_block_stat misaligned");
   const int nqb = ceil_div(p->seqlen, p->block_q);
-  const int nkb = ceil_div(p->seqlen, p->block_k);
+  const int nkb = ceil_div(key_len(p), p->block_k);
   if (nkb > bsfa::kMaxGateTiles)
-    return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the absolute-gate limit %d", p->seqlen,
+    return fail(BSFA_ERR_UNSUPPORTED, "%d keys above the absolute-gate limit %d", key_len(p),
                 bsfa::kMaxGateTiles * bsfa::kBlockK);
+  if ((key_len(p) - p->seqlen) % p->block_q != 0)
+    return fail(BSFA_ERR_SHAPE, "the absolute gate needs the prefix (%d keys) to be a multiple "
+                "of block_q (%d): thresholds are indexed by absolute query block",
+                key_len(p) - p->seqlen, p->block_q);
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   const uint64_t need = bsfa_prefill_workspace_bytes(p, BSFA_GATE_ABSOLUTE);
@@ -299,6 +315,8 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
   if (!budgets_host) return fail(BSFA_ERR_ARG, "budgets_host is NULL");
   for (int t = 0; t < n_budgets; ++t)
     if (budgets_host[t] < 1) return fail(BSFA_ERR_ARG, "budget %d is < 1", budgets_host[t]);
+  if (key_len(p) != p->seqlen)
+    return fail(BSFA_ERR_UNSUPPORTED, "calibration takes whole sequences (kv_seqlen 0 or seqlen)");
   const int nkb = ceil_div(p->seqlen, p->block_k);
   if (nkb > bsfa::kCalibMaxKeyBlocks)
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the calibration limit %d", p->seqlen,

@@ -24,6 +24,7 @@ struct PrefillArgs {
   float* dbg;                      // [B][Hq][nqb][nkb] or nullptr
   long long qs[3], ks[3], vs[3], os[3];
   int B, N, Hq, Hkv, G, nqb, nkb, t_len;
+  int Nk, P;                       // key tokens and the prefix before the query rows (Nk - N)
   int units;                       // B * Hkv * (G / heads per workgroup)
   int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads);
                                    // -1: KV-head-major order over all XCDs

@@ -310,8 +310,10 @@ __device__ __forceinline__ void qk32(const __bf16* sk, const bf16x8 (&qf)[D / 16
 }
 
 // Causal / ragged masking (when `masked`) and the row max over the 64 keys of the tile.
-__device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0, int row, int N,
-                                          int lane) {
+// arow: the lane's query row as an absolute position (the causal compare); rvalid: the row
+// exists (rows past the end of a ragged last block do not).
+__device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0, int arow,
+                                          bool rvalid, int lane) {
   const int hh = lane >> 5;
   if (masked) {
 #pragma unroll
@@ -319,7 +321,7 @@ __device__ __forceinline__ float rowmax32(f32x16 (&s)[2], bool masked, int key0,
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int key = key0 + mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-        if (key > row || row >= N) s[mb][v] = kNegInf;
+        if (key > arow || !rvalid) s[mb][v] = kNegInf;
       }
   }
   float mx = kNegInf;
@@ -487,15 +489,17 @@ __device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* 
   }
 }
 
-// Causal / ragged mask of a score tile (diagonal-region and ragged tiles only).
-__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int row, int N, int lane) {
+// Causal / ragged mask of a score tile (diagonal-region and ragged tiles only); arow and rvalid
+// as for rowmax32.
+__device__ __forceinline__ void mask_tile(f32x16 (&s)[2], int key0, int arow, bool rvalid,
+                                          int lane) {
   const int hh = lane >> 5;
 #pragma unroll
   for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = key0 + mb * 32 + 8 * (v >> 2) + 4 * hh + (v & 3);
-      if (key > row || row >= N) s[mb][v] = kNegInf;
+      if (key > arow || !rvalid) s[mb][v] = kNegInf;
     }
 }
 
@@ -583,11 +587,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
-  const int N = a.N;
+  // N query rows at absolute positions pre .. pre + N - 1 against Nk = pre + N keys (a chunk
+  // after a prefix of cached keys; pre = 0 for a whole prefill)
+  const int N = a.N, Nk = a.Nk, pre = a.P;
   const int row0 = i * BQ + rw * kRows;
   const int row = row0 + (lane & 31);
-  const int n_off = (i * BQ) / BK;
-  const int n_end = (min((i + 1) * BQ, N) - 1) / BK + 1;
+  const int arow = pre + row;
+  const bool rvalid = row < N;
+  const int n_off = (pre + i * BQ) / BK;
+  const int n_end = (pre + min((i + 1) * BQ, N) - 1) / BK + 1;
   const bool ragged_rows = (i + 1) * BQ > N;
   const bool head_leader = (rw == 0) && (lane == 0);
   const float c = a.c_log2;
@@ -600,8 +608,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   float thr[HPW];
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh) {
-    if (kThr)
-      thr[hh] = a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)];
+    if (kThr)   // the absolute query block's column (pre is a multiple of BQ here)
+      thr[hh] = a.thr[(h0 + hh) * a.t_len + min(pre / BQ + i, a.t_len - 1)];
     else if (GATE == kRelative)
       thr[hh] = a.log_lambda;
     else
@@ -619,7 +627,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   unsigned koff[MK], voff[MV];
   copy_offsets<D, STR, NW>(koff, kst, w, lane);
   copy_offsets<D, STRV, NW>(voff, vst, w, lane);
-  auto key_valid = [&](int j) { return min(BK, N - j * BK); };
+  auto key_valid = [&](int j) { return min(BK, Nk - j * BK); };
   const unsigned krow = (unsigned)kst * 2u, vrow = (unsigned)vst * 2u;
   auto load_k = [&](int j, __bf16* dst) {
     copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, key_valid(j), dst, w, lane);
@@ -677,7 +685,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto publish = [&](int j, float rmax, float* slot) {
     float x;
     if (GATE == kRelative && j < n_off)
-      x = row < N ? rmax - st.mt : kNegInf;
+      x = rvalid ? rmax - st.mt : kNegInf;
     else
       x = rmax;
     slot[w * kRows + (lane & 31)] = x;
@@ -693,7 +701,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   f32x16 sb[2][2];     // scores of the last tiles of each parity
   float rc;            // row max of the newest scores
   qk32<D>(sK0, qf, sb[0], lane);
-  rc = rowmax32(sb[0], tile_masked(t), t * BK, row, N, lane);
+  rc = rowmax32(sb[0], tile_masked(t), t * BK, arow, rvalid, lane);
   if (want_stat) publish(t, rc, sGate[0]);
   wait_vmem();
   __syncthreads();
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                         sum, mx, copy_k);
     if (mykeep) st.l += sum;
     if (tile_masked(t1)) {
-      mask_tile(sb[P ^ 1], t1 * BK, row, N, lane);
+      mask_tile(sb[P ^ 1], t1 * BK, arow, rvalid, lane);
       mx = kNegInf;
 #pragma unroll
       for (int v = 0; v < 16; v += 2) mx = max3(mx, sb[P ^ 1][0][v], sb[P ^ 1][0][v + 1]);
@@ -991,9 +999,9 @@ void gate_sweep_kernel(PrefillArgs a) {
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
-  const int N = a.N;
+  const int N = a.N, pre = a.P;   // query rows at absolute positions pre .. (see prefill_kernel)
   const int row0 = i * BQ + rw * 64;
-  const int n_off = (i * BQ) / BK;
+  const int n_off = (pre + i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
   const bool leader = rw == 0 && lane == 0;   // one lane per head: its decisions and mask words
   unsigned long long* const mask = a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) *
@@ -1019,14 +1027,15 @@ void gate_sweep_kernel(PrefillArgs a) {
     copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, BK, dst, w, lane);
   };
   auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
-  const float thr = a.thr[h * a.t_len + min(i, a.t_len - 1)];
+  const int tcol = min(pre / BQ + i, a.t_len - 1);   // the absolute query block's threshold
+  const float thr = a.thr[h * a.t_len + tcol];
   // heads whose threshold is -inf keep everything without a mask (the softmax kernel does not
   // read one then), so a workgroup of only such heads has nothing to decide unless the maxima
   // are dumped
   bool all_keep = a.dbg == nullptr && !a.full_masks;
 #pragma unroll
   for (int hh = 0; hh < HPW; ++hh)
-    all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + min(i, a.t_len - 1)] == kNegInf;
+    all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + tcol] == kNegInf;
   if (all_keep) return;
 
   // The copy instructions one tile takes from this wave (the last round only on some waves):
@@ -1130,7 +1139,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                               sK[(t + 1) & 1], w, lane);
       f32x16 s[2];
       qk32<D>(sK[t & 1], qf, s, lane);
-      const float rmax = rowmax32(s, ragged_rows, t * BK, row, N, lane);
+      const float rmax = rowmax32(s, ragged_rows, t * BK, row, row < N, lane);
       const float wst = wave_max(rmax);
       if (lane == 0) sPart[w] = wst;
       wait_vmem();

@@ -3,23 +3,27 @@
  * AMD Instinct MI355X (gfx950).
  *
  * The operation ("Block Sparse Flash Attention", paper notes, Method):
- *   For every batch b, query head h and query block i (rows [i*Bq, (i+1)*Bq)), the kernel
- *   visits the causally visible key blocks j (columns [j*Bk, (j+1)*Bk)) in ascending order and
- *   computes the exact scaled scores S = Q_i K_j^T * scale of the whole tile (Key Designs 2).
- *     - Off-diagonal blocks (j < n_off(i) = floor(i*Bq/Bk), wholly before the block's first row)
- *       are gated. ABSOLUTE: keep iff s_max = max over the tile of S >= T_eff(h, i) (Key Designs
+ *   For every batch b, query head h and query block i (query rows [i*Bq, (i+1)*Bq), at
+ *   absolute positions P + i*Bq .. with P = kv_seqlen - seqlen, 0 for a whole prefill), the
+ *   kernel visits the causally visible key blocks j (columns [j*Bk, (j+1)*Bk)) in ascending
+ *   order and computes the exact scaled scores S = Q_i K_j^T * scale of the whole tile (Key
+ *   Designs 2).
+ *     - Off-diagonal blocks (j < n_off(i) = floor((P + i*Bq)/Bk), wholly before the block's
+ *       first row) are gated. ABSOLUTE: keep iff s_max = max over the tile of S >= T_eff(h, i) (Key Designs
  *       2, keep-rule equation; ">=" as in the main text). RELATIVE: keep iff some row r of the
  *       tile has rowmax_j[r] - m[r] >= log_lambda, m the running row max before the block
  *       ("Skipping attention blocks was the easy part", BLASST blog, section "Vote, then skip").
  *       DENSE: keep every block (the gate is compiled out).
  *     - Diagonal-region blocks (n_off(i) <= j < n_end(i)) always run, with the causal mask.
  *     - A kept block updates the online-softmax state (running max m, sum l, accumulator O)
- *       and accumulates P V_j; a skipped block loads no V, computes no exponentials and leaves
- *       m, l and O untouched (Key Designs 3).
+ *       and accumulates P V_j; a skipped block loads no V, adds nothing and leaves m, l and O
+ *       untouched (Key Designs 3). (Where the decision is voted inside the softmax loop, a
+ *       skipped tile's exponentials may be evaluated and discarded; results are unaffected.)
  *     - Output O_i = O / l: attention renormalised over the kept blocks and the diagonal
  *       region (Overall Architecture; Key Designs 3).
- *   T_eff(h, i) = T[budget_slice][h][min(i, t_len - 1)]: positions past the calibrated length
- *   reuse the last calibrated column (Key Designs 1). -INFINITY keeps every block.
+ *   T_eff(h, i) = T[budget_slice][h][min(P/Bq + i, t_len - 1)] (the absolute query block):
+ *   positions past the calibrated length reuse the last calibrated column (Key Designs 1).
+ *   -INFINITY keeps every block.
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned device memory on the current HIP device; the library
@@ -67,7 +71,7 @@ typedef enum { BSFA_BF16 = 0, BSFA_FP32 = 1 } bsfa_dtype;
 /* One causal prefill self-attention call (one layer). */
 typedef struct {
   int32_t batch;             /* B >= 0 */
-  int32_t seqlen;            /* N >= 0 query tokens = key tokens; need not be a tile multiple */
+  int32_t seqlen;            /* N >= 0 query tokens; need not be a tile multiple */
   int32_t heads_q;           /* Hq >= 1 */
   int32_t heads_kv;          /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
   int32_t head_dim;          /* d: 64 or 128 */
@@ -80,6 +84,13 @@ typedef struct {
   int64_t k_stride[3];       /* element strides of K */
   int64_t v_stride[3];       /* element strides of V */
   int64_t o_stride[3];       /* element strides of O */
+  int32_t kv_seqlen;         /* key tokens Nk: 0 means N (a whole prefill); otherwise Nk >= N and
+                              * the N query tokens are the last N of the Nk positions (a chunk
+                              * after a prefix of P = Nk - N cached keys). Query block i then
+                              * starts at absolute row P + i*Bq: the causal mask, the off-diagonal
+                              * range and the threshold column (P/Bq + i) use absolute positions,
+                              * and the absolute gate needs P % Bq == 0 (thresholds live on the
+                              * calibration's tile grid). K and V hold Nk rows. */
 } bsfa_problem;
 
 /* One layer's threshold table (the offline calibration artifact), fp32 in device memory.
@@ -99,13 +110,13 @@ typedef struct {
 } bsfa_table;
 
 /* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
- * ABSOLUTE, one keep bitmask per (b, h, i), B * Hq * ceil(N/Bq) * ceil(ceil(N/Bk)/64) uint64
+ * ABSOLUTE, one keep bitmask per (b, h, i), B * Hq * ceil(N/Bq) * ceil(ceil(Nk/Bk)/64) uint64
  * words. */
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
 
 /* Gated causal prefill attention (the method's hot path).
  *   p             problem description (host memory, read during the call only)
- *   Q             device [B][N][Hq][d] bf16;  K, V: device [B][N][Hkv][d] bf16
+ *   Q             device [B][N][Hq][d] bf16;  K, V: device [B][Nk][Hkv][d] bf16
  *   table         threshold table; required for ABSOLUTE, ignored otherwise (may be NULL)
  *   budget_slice  which table slice (0 <= budget_slice < n_budgets) for ABSOLUTE
  *   gate_mode     bsfa_gate_mode
@@ -116,7 +127,7 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 Flash Attention", A Worked Example: it does not consume the budget)
  *   kept_total    device uint64 scalar or NULL: sum of kept_counts (zeroed, then accumulated,
  *                 on `stream`)
- *   debug_block_stat  device fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] or NULL: per visible block,
+ *   debug_block_stat  device fp32 [B][Hq][ceil(N/Bq)][ceil(Nk/Bk)] or NULL: per visible block,
  *                 the gate statistic in scaled-score units (ABSOLUTE and DENSE: s_max;
  *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
  *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
@@ -128,7 +139,7 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 in one launch. The results are the same. A non-NULL workspace that is too
  *                 small is an error (BSFA_ERR_ARG).
  *   stream        hipStream_t
- * The absolute gate supports seqlen up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
+ * The absolute gate supports Nk up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
  * Returns BSFA_OK or an error status (see the conventions above). */
 bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
                          const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
@@ -142,7 +153,7 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
  * computed (no softmax, no V) and bit j % 64 of keep_mask[b][h][i][j / 64] is set iff
  * s_max(i, j) >= T_eff(h, i); the diagonal region is not part of the mask (it is always kept).
  *   p, Q, K, table, budget_slice   as for bsfa_prefill with gate_mode ABSOLUTE (V, O unused)
- *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(N/Bk)/64), 8-byte
+ *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(Nk/Bk)/64), 8-byte
  *                 aligned; every word is written (bits at or past n_off(i) are zero)
  *   mask_bytes    size of keep_mask; at least bsfa_prefill_workspace_bytes(p, ABSOLUTE)
  *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
@@ -165,7 +176,8 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
  *   n_budgets     1 .. 16
  *   kth_out       device fp32 [n_budgets][B][Hq][ceil(N/Bq)]
  *   stream        hipStream_t
- * This build supports seqlen up to 262144 here (BSFA_ERR_UNSUPPORTED beyond). */
+ * This build supports seqlen up to 262144 here, whole sequences only (kv_seqlen 0 or equal to
+ * seqlen; BSFA_ERR_UNSUPPORTED otherwise). */
 bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
                                     const int32_t* budgets_host, int32_t n_budgets,
                                     float* kth_out, void* stream);

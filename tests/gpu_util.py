@@ -33,7 +33,7 @@ def run_device(Qd, Kd, Vd, *, block_q, mode, table=None, budget_slice=0,
                log_lambda=-math.inf, out_dtype=torch.float32, dbg=True, O=None,
                workspace=None):
     B, N, Hq, _ = Qd.shape
-    nqb, nkb = -(-N // block_q), -(-N // 64)
+    nqb, nkb = -(-N // block_q), -(-int(Kd.shape[1]) // 64)
     counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
     total = torch.zeros(1, dtype=torch.int64, device="cuda")
     stat = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32, device="cuda") if dbg else None
@@ -54,7 +54,8 @@ def make_table(T, block_q, d, budgets=None):
                           softmax_scale=float(np.float32(1 / math.sqrt(d))))
 
 
-def device_keep(dev, *, N, block_q, mode, table=None, budget_slice=0, log_lambda=-math.inf):
+def device_keep(dev, *, N, block_q, mode, table=None, budget_slice=0, log_lambda=-math.inf,
+                prefix=0):
     """The device's keep decisions, recomputed from its dumped statistic with the same fp32
     comparison the kernel makes. Returns (keep [B, Hq, nqb, nkb], offdiag mask)."""
     stat = dev["stat"]
@@ -62,13 +63,14 @@ def device_keep(dev, *, N, block_q, mode, table=None, budget_slice=0, log_lambda
     keep = np.zeros(stat.shape, bool)
     off = np.zeros(stat.shape, bool)
     for i in range(nqb):
-        n_off, n_end = oracle.key_block_range(i, N, block_q, 64)
+        n_off, n_end = oracle.key_block_range(i, N, block_q, 64, prefix)
         off[:, :, i, :n_off] = True
         keep[:, :, i, n_off:n_end] = True
         if mode == "dense":
             keep[:, :, i, :n_off] = True
         elif mode == "absolute":
-            thr = table.T[budget_slice][:, min(i, table.t_len - 1)].astype(np.float32)
+            col = min(prefix // block_q + i, table.t_len - 1)
+            thr = table.T[budget_slice][:, col].astype(np.float32)
             keep[:, :, i, :n_off] = stat[:, :, i, :n_off] >= thr[None, :, None]
         else:
             keep[:, :, i, :n_off] = stat[:, :, i, :n_off] >= np.float32(log_lambda)
@@ -79,8 +81,9 @@ def check_parity(dev, Qh, Kh, Vh, *, block_q, mode, table=None, budget_slice=0,
                  log_lambda=-math.inf, query_blocks=None, stat_atol=2e-3):
     """Compare one device run with the oracle; returns the oracle result."""
     N = Qh.shape[1]
+    prefix = Kh.shape[1] - N
     keep_dev, off = device_keep(dev, N=N, block_q=block_q, mode=mode, table=table,
-                                budget_slice=budget_slice, log_lambda=log_lambda)
+                                budget_slice=budget_slice, log_lambda=log_lambda, prefix=prefix)
     # kept counts are the number of kept off-diagonal blocks, and the total their sum
     counts_from_stat = (keep_dev & off).sum(-1)
     np.testing.assert_array_equal(dev["counts"], counts_from_stat)

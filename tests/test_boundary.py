@@ -193,6 +193,29 @@ def test_gate_masks_validation():
     assert call_masks(q, table()) == _lib.BSFA_ERR_SHAPE
 
 
+def test_kv_seqlen_validation():
+    lib = _lib.load_library()
+    p = problem()
+    p.kv_seqlen = p.seqlen - 1
+    assert call_prefill(p) == _lib.BSFA_ERR_ARG
+    p.kv_seqlen = -5
+    assert call_prefill(p) == _lib.BSFA_ERR_ARG
+    # the absolute gate reads thresholds by absolute query block: the prefix sits on the grid
+    p.kv_seqlen = p.seqlen + 64
+    abs_call = dict(tbl=table(t_len=4), mode=_lib.BSFA_GATE_ABSOLUTE)
+    assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_SHAPE
+    assert call_masks(p, table(t_len=4)) == _lib.BSFA_ERR_SHAPE
+    # calibration takes whole sequences
+    arr = (ctypes.c_int32 * 1)(4)
+    assert lib.bsfa_calibrate_blockmax(ctypes.byref(p), FAKE, FAKE, arr, 1, FAKE, None) == \
+        _lib.BSFA_ERR_UNSUPPORTED
+    # the masks cover the keys: 65 key tiles after a prefix need two words per query block
+    p.kv_seqlen = 65 * 64
+    p.seqlen = 128
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == \
+        p.batch * p.heads_q * 1 * 2 * 8
+
+
 def test_absolute_gate_length_limit():
     p = problem(N=2097152 + 64)
     st = call_prefill(p, tbl=table(t_len=1), mode=_lib.BSFA_GATE_ABSOLUTE)

@@ -289,6 +289,65 @@ def test_gate_masks_minus_inf_keeps_all_and_writes_every_word():
         assert bits[:, :, i, :n_off].all() and not bits[:, :, i, n_off:].any()
 
 
+# ---------------------------------------------------------------------------------------------
+# Chunked prefill: query rows after a prefix of cached keys (K and V longer than Q)
+# ---------------------------------------------------------------------------------------------
+PREFIX_CASES = [   # (shape, prefix, modes)
+    ("llama_like_ragged", 256, ("dense", "absolute", "relative")),   # aligned to Bq = 128
+    ("llama_like_ragged", 100, ("dense", "relative")),               # off the tile grid
+    ("d64_bq64_g2", 128, ("dense", "absolute", "relative")),          # batch 2, Bq = 64
+    ("d128_bq64_g4", 64, ("absolute",)),
+    ("g8", 256, ("absolute", "relative")),
+]
+
+
+@pytest.mark.parametrize("name,prefix,modes", PREFIX_CASES)
+def test_prefix_parity(name, prefix, modes, mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, V = _mid_inputs(name, 17)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q[:, prefix:].contiguous(), K, V)
+    for mode in modes:
+        kw = {}
+        if mode == "absolute":
+            kw = dict(table=mid_tables(name), budget_slice=1)
+        elif mode == "relative":
+            kw = dict(log_lambda=math.log(1e-3))
+        dev = run_device(Qd, Kd, Vd, block_q=Bq, mode=mode, **kw)
+        check_parity(dev, Qh, Kh, Vh, block_q=Bq, mode=mode, **kw)
+
+
+@pytest.mark.parametrize("name,prefix", [("llama_like_ragged", 256), ("llama_like_ragged", 640),
+                                         ("d64_bq64_g2", 192), ("g8", 128)])
+def test_chunks_equal_rows_of_the_whole_call_bitwise(name, prefix, mid_tables):
+    # a chunk on the query-block grid computes every query block exactly as the whole call does
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    tab = mid_tables(name)
+    Q, K, V = _mid_inputs(name, 18)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    Qc = Qd[:, prefix:].contiguous()
+    i0 = prefix // Bq
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    for mode, kw in (("dense", {}), ("relative", dict(log_lambda=math.log(1e-3))),
+                     ("absolute", dict(table=tab, budget_slice=1)),
+                     ("absolute", dict(table=tab, budget_slice=0, workspace=none))):
+        full = run_device(Qd, Kd, Vd, block_q=Bq, mode=mode, **kw)
+        part = run_device(Qc, Kd, Vd, block_q=Bq, mode=mode, **kw)
+        assert torch.equal(part["O"], full["O"][:, prefix:]), mode
+        np.testing.assert_array_equal(part["counts"], full["counts"][:, :, i0:])
+        np.testing.assert_array_equal(part["stat"], full["stat"][:, :, i0:])
+
+
+def test_gate_masks_with_prefix_match_the_whole_call(mid_tables):
+    B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
+    tab = mid_tables("llama_like_ragged").to_device("cuda")
+    Q, K, V = _mid_inputs("llama_like_ragged", 19)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    full = _lib.bsfa_gate_masks(Qd, Kd, tab, 1, block_q=Bq)
+    part = _lib.bsfa_gate_masks(Qd[:, 384:].contiguous(), Kd, tab, 1, block_q=Bq)
+    torch.cuda.synchronize()
+    assert torch.equal(part, full[:, :, 3:])
+
+
 def test_back_to_back_launches_bitwise(mid_tables):
     B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
     tab = mid_tables("llama_like_ragged").to_device("cuda")
