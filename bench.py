@@ -262,6 +262,39 @@ def run_sweep(w, steps, warmup):
     return dict(ms=ev_ms, wall_ms=wall_ms, flops=fl, tflops=fl / ev_ms / 1e9)
 
 
+def run_chunked(w, chunk, steps, warmup, budget_slice=0):
+    """Chunked prefill of the workload under the absolute gate: the query rows in chunks of
+    `chunk`, chunk c against the K/V prefix of every earlier position (kv_seqlen), one call per
+    chunk. A step is all chunks; executed FLOPs come from each chunk's kept counts."""
+    import numpy as np
+    import torch
+    from block_sparse_long_amd import _lib
+    n_chunks = -(-w.N // chunk)
+    spans = [(c * chunk, min((c + 1) * chunk, w.N)) for c in range(n_chunks)]
+    counts = [torch.zeros((1, w.Hq, -(-(r1 - r0) // w.Bq)), dtype=torch.int32,
+                          device=w.Qd.device) for r0, r1 in spans]
+    ws = torch.empty(_lib.bsfa_prefill_workspace_bytes(w.Qd, w.Kd, block_q=w.Bq),
+                     dtype=torch.uint8, device=w.Qd.device)
+
+    def step():
+        for (r0, r1), kc in zip(spans, counts):
+            _lib.bsfa_prefill(w.Qd[:, r0:r1], w.Kd[:, :r1], w.Vd[:, :r1], w.O[:, r0:r1],
+                              block_q=w.Bq, gate_mode="absolute", table=w.dtable,
+                              budget_slice=budget_slice, kept_counts=kc, workspace=ws)
+    ev_ms, wall_ms = timed(step, steps, warmup)
+    torch.cuda.synchronize()
+    tiles = kept = 0
+    for (r0, r1), kc in zip(spans, counts):
+        kc = kc.cpu().numpy()
+        kept += int(kc.sum())
+        for i in range(kc.shape[2]):
+            n_end = (r0 + min((i + 1) * w.Bq, r1 - r0) - 1) // 64 + 1
+            n_off = (r0 + i * w.Bq) // 64
+            tiles += w.Hq * (n_end + (n_end - n_off)) + int(kc[:, :, i].sum())
+    flops = 2.0 * w.Bq * 64 * w.d * tiles
+    return dict(ms=ev_ms, chunks=n_chunks, flops=flops, tflops=flops / ev_ms / 1e9, kept=kept)
+
+
 def run_gate(w, mode, steps, warmup, **kw):
     import numpy as np
     import torch
@@ -370,6 +403,13 @@ def main():
         dom = dict(kernel=f"prefill_kernel<128, 128, 4, {2 if mode == 'relative' else 0}>",
                    ms=gated["ms"], flops=gated["flops"])
 
+    if not args.quick and w.table is not None:
+        # chunked prefill of the same sequence (chunks of 16K after their KV prefix)
+        ch = run_chunked(w, 16384, args.steps, args.warmup)
+        extras["chunked_16k"] = {"ms": round(ch["ms"], 3), "chunks": ch["chunks"],
+                                 "tflops": round(ch["tflops"], 2),
+                                 "kept_blocks": ch["kept"], "kept_blocks_whole_call": gated["kept"],
+                                 "vs_whole_call": round(ch["ms"] / gated["ms"], 4)}
     if not args.quick:
         sweeps = {}
         del w
