@@ -31,8 +31,9 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
 
-EXPORTED = ("bsfa_prefill", "bsfa_prefill_workspace_bytes", "bsfa_gate_masks",
-            "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error", "bsfa_version")
+EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_workspace_bytes",
+            "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error",
+            "bsfa_version")
 
 
 class BsfaProblem(ctypes.Structure):
@@ -78,6 +79,10 @@ def load_library(path: str = LIB_PATH):
     lib.bsfa_prefill.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, ctypes.POINTER(BsfaTable),
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp,
                                  vp, ctypes.c_uint64, vp]
+    lib.bsfa_prefill_varlen.restype = ctypes.c_int32
+    lib.bsfa_prefill_varlen.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, vp, vp,
+                                        ctypes.POINTER(BsfaTable), ctypes.c_int32, ctypes.c_int32,
+                                        ctypes.c_float, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
     lib.bsfa_prefill_workspace_bytes.restype = ctypes.c_uint64
     lib.bsfa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem), ctypes.c_int32]
     lib.bsfa_gate_masks.restype = ctypes.c_int32
@@ -194,6 +199,59 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                           mode, float(log_lambda), _ptr(O), _ptr(kept_counts), _ptr(kept_total),
                           _ptr(debug_block_stat), _ptr(workspace), ctypes.c_uint64(ws_bytes),
                           _stream_handle(stream, Q.device))
+    _check(st)
+    return O
+
+
+def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
+                        max_seqlen_k: int, O=None, *, block_q: int, block_k: int = 64,
+                        gate_mode="dense", table=None, budget_slice: int = 0,
+                        log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
+                        debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
+                        out_dtype=None, workspace=None):
+    """bsfa_prefill over sequences packed along the token axis. Q: [total_q, Hq, d] bf16;
+    K, V: [total_k, Hkv, d] bf16; cu_seqlens_q / cu_seqlens_k: device int32 [B + 1] token
+    offsets. Per-sequence outputs are padded to the longest sequence. Returns O."""
+    import torch
+    lib = load_library()
+    if Q.dim() != 3 or K.dim() != 3 or V.dim() != 3:
+        raise ValueError("Q, K and V must be [tokens, heads, dim]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or not t.is_contiguous() or t.dim() != 1:
+            raise ValueError(f"{name} must be a contiguous int32 vector")
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel():
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must have the same length")
+    if O is None:
+        O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
+    mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    # the per-token views as [1, tokens, heads, dim] give the token and head strides
+    p = make_problem(Q[None], K[None], V[None], O[None], block_q=block_q, block_k=block_k,
+                     softmax_scale=softmax_scale)
+    p.batch = cu_seqlens_q.numel() - 1
+    p.seqlen = int(max_seqlen_q)
+    p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
+    for st in (p.q_stride, p.k_stride, p.v_stride, p.o_stride):
+        st[0] = 0
+    tbl = table.c_struct() if table is not None else None
+    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
+                        ("kept_total", kept_total, torch.int64),
+                        ("debug_block_stat", debug_block_stat, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if workspace is None:
+        nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is not None and workspace.numel() == 0:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.bsfa_prefill_varlen(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_q),
+                                 _ptr(cu_seqlens_k),
+                                 ctypes.byref(tbl) if tbl is not None else None,
+                                 int(budget_slice), mode, float(log_lambda), _ptr(O),
+                                 _ptr(kept_counts), _ptr(kept_total), _ptr(debug_block_stat),
+                                 _ptr(workspace), ctypes.c_uint64(ws_bytes),
+                                 _stream_handle(stream, Q.device))
     _check(st)
     return O
 

@@ -183,11 +183,16 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
   return (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
 }
 
-bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
-                         const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
-                         float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
-                         float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
-                         void* stream) {
+}  // extern "C"
+
+namespace {
+
+// bsfa_prefill and bsfa_prefill_varlen: cu_q / cu_k are NULL for a fixed-length batch.
+bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, const void* V,
+                         const int32_t* cu_q, const int32_t* cu_k, const bsfa_table* table,
+                         int32_t budget_slice, int32_t gate_mode, float log_lambda, void* O,
+                         int32_t* kept_counts, uint64_t* kept_total, float* debug_block_stat,
+                         void* workspace, uint64_t workspace_bytes, void* stream) {
   bsfa_status s = check_problem(p, true);
   if (s != BSFA_OK) return s;
   if (gate_mode != BSFA_GATE_DENSE && gate_mode != BSFA_GATE_ABSOLUTE &&
@@ -201,6 +206,8 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   }
   const bool empty = p->batch == 0 || p->seqlen == 0;
   if (!empty) {
+    if (cu_q && ((reinterpret_cast<uintptr_t>(cu_q) | reinterpret_cast<uintptr_t>(cu_k)) & 3u))
+      return fail(BSFA_ERR_ALIGN, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
     if (!Q || !K || !V || !O) return fail(BSFA_ERR_ARG, "Q, K, V and O must be non-NULL");
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
       return fail(BSFA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
@@ -239,6 +246,8 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
 
   bsfa::PrefillArgs a = base_args(p, Q, K, V, table, budget_slice, gate_mode);
   a.o = O;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
   a.kept_counts = kept_counts;
   a.kept_total = reinterpret_cast<unsigned long long*>(kept_total);
   a.dbg = debug_block_stat;
@@ -264,6 +273,35 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, const void* V,
+                         const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
+                         float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
+                         float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
+                         void* stream) {
+  return prefill_impl(p, Q, K, V, nullptr, nullptr, table, budget_slice, gate_mode, log_lambda,
+                      O, kept_counts, kept_total, debug_block_stat, workspace, workspace_bytes,
+                      stream);
+}
+
+bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void* K,
+                                const void* V, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const bsfa_table* table,
+                                int32_t budget_slice, int32_t gate_mode, float log_lambda, void* O,
+                                int32_t* kept_counts, uint64_t* kept_total,
+                                float* debug_block_stat, void* workspace,
+                                uint64_t workspace_bytes, void* stream) {
+  if (!p) return fail(BSFA_ERR_ARG, "problem is NULL");
+  if (p->batch > 0 && p->seqlen > 0 && (!cu_seqlens_q || !cu_seqlens_k))
+    return fail(BSFA_ERR_ARG, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
+  return prefill_impl(p, Q, K, V, cu_seqlens_q, cu_seqlens_k, table, budget_slice, gate_mode,
+                      log_lambda, O, kept_counts, kept_total, debug_block_stat, workspace,
+                      workspace_bytes, stream);
 }
 
 bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,

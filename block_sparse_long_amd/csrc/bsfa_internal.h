@@ -25,6 +25,10 @@ struct PrefillArgs {
   long long qs[3], ks[3], vs[3], os[3];
   int B, N, Hq, Hkv, G, nqb, nkb, t_len;
   int Nk, P;                       // key tokens and the prefix before the query rows (Nk - N)
+  // variable-length batches: token offsets of each sequence's queries and keys [B + 1] (the
+  // sequences packed along the token axis; N, Nk are then the longest), or nullptr
+  const int* cu_q;
+  const int* cu_k;
   int units;                       // B * Hkv * (G / heads per workgroup)
   int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads);
                                    // -1: KV-head-major order over all XCDs

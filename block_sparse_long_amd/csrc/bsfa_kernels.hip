@@ -507,6 +507,37 @@ struct Unit {
   int b, g, hg, i;
 };
 
+// The sequence a workgroup works on: its query rows N, key tokens Nk, the prefix pre = Nk - N
+// (query row r sits at absolute position pre + r) and the element offsets of its first token in
+// Q, K, V and O. A fixed-length batch strides by the batch axis; a variable-length batch packs
+// its sequences along the token axis, with their token offsets in cu_q / cu_k.
+struct Seq {
+  int N, Nk, pre;
+  long long q, k, v, o;
+};
+
+__device__ __forceinline__ Seq seq_of(const PrefillArgs& a, int b) {
+  Seq s;
+  if (a.cu_q) {
+    const int q0 = a.cu_q[b], k0 = a.cu_k[b];
+    s.N = a.cu_q[b + 1] - q0;
+    s.Nk = a.cu_k[b + 1] - k0;
+    s.q = (long long)q0 * a.qs[1];
+    s.o = (long long)q0 * a.os[1];
+    s.k = (long long)k0 * a.ks[1];
+    s.v = (long long)k0 * a.vs[1];
+  } else {
+    s.N = a.N;
+    s.Nk = a.Nk;
+    s.q = b * a.qs[0];
+    s.o = b * a.os[0];
+    s.k = b * a.ks[0];
+    s.v = b * a.vs[0];
+  }
+  s.pre = s.Nk - s.N;
+  return s;
+}
+
 // Workgroup L -> (batch, KV head, head group, query block). Query blocks go from the last
 // (longest) to the first. Consecutive workgroups land on the 8 XCDs in turn (L mod 8); with
 // xcd_map the unit index is chosen so that XCD x serves fixed units (for B * Hkv = 8: KV head
@@ -589,7 +620,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int h = h0 + hw;
   // N query rows at absolute positions pre .. pre + N - 1 against Nk = pre + N keys (a chunk
   // after a prefix of cached keys; pre = 0 for a whole prefill)
-  const int N = a.N, Nk = a.Nk, pre = a.P;
+  const Seq sq = seq_of(a, b);
+  if (i * BQ >= sq.N) return;   // uniform: past this sequence's query blocks (variable length)
+  const int N = sq.N, Nk = sq.Nk, pre = sq.pre;
   const int row0 = i * BQ + rw * kRows;
   const int row = row0 + (lane & 31);
   const int arow = pre + row;
@@ -600,9 +633,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const bool head_leader = (rw == 0) && (lane == 0);
   const float c = a.c_log2;
 
-  const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
-  const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
-  const __bf16* Vb = static_cast<const __bf16*>(a.v) + b * a.vs[0] + g * a.vs[2];
+  const __bf16* Qb = static_cast<const __bf16*>(a.q) + sq.q + h * a.qs[2];
+  const __bf16* Kb = static_cast<const __bf16*>(a.k) + sq.k + g * a.ks[2];
+  const __bf16* Vb = static_cast<const __bf16*>(a.v) + sq.v + g * a.vs[2];
   const long long kst = a.ks[1], vst = a.vs[1];
 
   float thr[HPW];
@@ -886,7 +919,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   const int hh = lane >> 5;
   const float inv = 1.f / half_sum(st.l);
   if (row < N) {
-    const long long base = b * a.os[0] + (long long)row * a.os[1] + h * a.os[2];
+    const long long base = sq.o + (long long)row * a.os[1] + h * a.os[2];
 #pragma unroll
     for (int md = 0; md < MD; ++md) {
 #pragma unroll
@@ -999,7 +1032,9 @@ void gate_sweep_kernel(PrefillArgs a) {
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
-  const int N = a.N, pre = a.P;   // query rows at absolute positions pre .. (see prefill_kernel)
+  const Seq sq = seq_of(a, b);   // query rows at absolute positions pre .. (see prefill_kernel)
+  if (i * BQ >= sq.N) return;     // uniform: past this sequence's query blocks (variable length)
+  const int N = sq.N, pre = sq.pre;
   const int row0 = i * BQ + rw * 64;
   const int n_off = (pre + i * BQ) / BK;
   const bool ragged_rows = (i + 1) * BQ > N;
@@ -1017,8 +1052,8 @@ void gate_sweep_kernel(PrefillArgs a) {
     return;
   }
 
-  const __bf16* Qb = static_cast<const __bf16*>(a.q) + b * a.qs[0] + h * a.qs[2];
-  const __bf16* Kb = static_cast<const __bf16*>(a.k) + b * a.ks[0] + g * a.ks[2];
+  const __bf16* Qb = static_cast<const __bf16*>(a.q) + sq.q + h * a.qs[2];
+  const __bf16* Kb = static_cast<const __bf16*>(a.k) + sq.k + g * a.ks[2];
   const long long kst = a.ks[1];
   const unsigned krow = (unsigned)kst * 2u;
   unsigned koff[MK];

@@ -147,6 +147,33 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
                          float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
                          void* stream);
 
+/* bsfa_prefill over a batch of sequences of different lengths, packed along the token axis
+ * (the interface of variable-length attention kernels; "FlashPrefill V2: Block-Sparse Prefill
+ * Attention for Long-Context LLM Serving" names varlen scheduling, chunked prefill and
+ * continuous batching as what a serving stack needs from a prefill backend). Sequence b owns
+ * query tokens [cu_seqlens_q[b], cu_seqlens_q[b+1]) of Q and O and key tokens
+ * [cu_seqlens_k[b], cu_seqlens_k[b+1]) of K and V; its Nq_b queries are the last Nq_b of its
+ * Nk_b >= Nq_b key positions (a prefix of P_b = Nk_b - Nq_b cached keys, 0 for a whole prefill).
+ *   p             batch = number of sequences; seqlen = max_b Nq_b; kv_seqlen = max_b Nk_b (0:
+ *                 seqlen); the token and head strides apply, the batch strides are unused
+ *   Q, O          device [total_q][Hq][d];  K, V: device [total_k][Hkv][d]
+ *   cu_seqlens_q, cu_seqlens_k  device int32 [batch + 1], 4-byte aligned, starting at 0,
+ *                 nondecreasing, with Nq_b <= seqlen, Nk_b <= kv_seqlen and Nk_b >= Nq_b (the
+ *                 caller guarantees these; they are read on the device only)
+ *   kept_counts, debug_block_stat, workspace   as for bsfa_prefill, padded to the longest
+ *                 sequence ([batch][Hq][ceil(seqlen/Bq)] ...); entries of query blocks past a
+ *                 sequence's end are not written
+ *   the rest      as for bsfa_prefill. Under ABSOLUTE each P_b must be a multiple of Bq
+ *                 (otherwise the threshold column is floor(P_b/Bq) + i).
+ * The results for each sequence are those of bsfa_prefill on that sequence alone. */
+bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void* K,
+                                const void* V, const int32_t* cu_seqlens_q,
+                                const int32_t* cu_seqlens_k, const bsfa_table* table,
+                                int32_t budget_slice, int32_t gate_mode, float log_lambda, void* O,
+                                int32_t* kept_counts, uint64_t* kept_total,
+                                float* debug_block_stat, void* workspace,
+                                uint64_t workspace_bytes, void* stream);
+
 /* The absolute gate's keep decisions alone ("Block Sparse Flash Attention", Method: a block
  * is kept when its exact maximum scaled score reaches the threshold T[layer, head, query
  * block]). For every (b, h, i) the exact scores of all off-diagonal blocks j < n_off(i) are

@@ -201,6 +201,48 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     return OracleResult(out, kept_counts, stat, keep_mask, margin)
 
 
+def oracle_prefill_varlen(Q, K, V, cu_q, cu_k, *, block_q: int, block_k: int, mode: str,
+                          **kw) -> OracleResult:
+    """oracle_prefill for sequences packed along the token axis.
+
+    Q: [total_q, Hq, d]; K, V: [total_k, Hkv, d]; sequence b owns query tokens
+    cu_q[b] .. cu_q[b+1] and key tokens cu_k[b] .. cu_k[b+1] (its queries are the last of its
+    key positions). Each sequence is computed on its own; the per-block results are padded to
+    the longest sequence (NaN / -1 / False past a sequence's blocks). ``out`` is
+    [total_q, Hq, d].
+    """
+    cu_q = [int(x) for x in cu_q]
+    cu_k = [int(x) for x in cu_k]
+    B = len(cu_q) - 1
+    Q = np.asarray(Q)
+    Hq, d = Q.shape[1], Q.shape[2]
+    nq = [cu_q[b + 1] - cu_q[b] for b in range(B)]
+    nk = [cu_k[b + 1] - cu_k[b] for b in range(B)]
+    nqb = num_blocks(max(nq + [0]), block_q)
+    nkb = num_blocks(max(nk + [0]), block_k)
+    dtype = kw.get("dtype", np.float32)
+    out = np.full((cu_q[-1], Hq, d), np.nan, dtype=dtype)
+    kept_counts = np.full((B, Hq, nqb), -1, dtype=np.int64)
+    stat = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
+    keep = np.zeros((B, Hq, nqb, nkb), dtype=bool)
+    margin = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
+    forced = kw.pop("forced_keep", None)
+    for b in range(B):
+        if nq[b] == 0:
+            continue
+        r = oracle_prefill(Q[None, cu_q[b]:cu_q[b + 1]], np.asarray(K)[None, cu_k[b]:cu_k[b + 1]],
+                           np.asarray(V)[None, cu_k[b]:cu_k[b + 1]], block_q=block_q,
+                           block_k=block_k, mode=mode,
+                           forced_keep=None if forced is None else forced[b:b + 1], **kw)
+        qb, kb = r.kept_counts.shape[2], r.stat.shape[3]
+        out[cu_q[b]:cu_q[b + 1]] = r.out[0]
+        kept_counts[b, :, :qb] = r.kept_counts[0]
+        stat[b, :, :qb, :kb] = r.stat[0]
+        keep[b, :, :qb, :kb] = r.keep[0]
+        margin[b, :, :qb, :kb] = r.margin[0]
+    return OracleResult(out, kept_counts, stat, keep, margin)
+
+
 def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float | None = None,
                               dtype=np.float32) -> np.ndarray:
     """s_max[b, h, i, j] for every off-diagonal block j < n_off(i); NaN elsewhere.

@@ -216,6 +216,21 @@ def test_kv_seqlen_validation():
         p.batch * p.heads_q * 1 * 2 * 8
 
 
+def test_varlen_validation():
+    lib = _lib.load_library()
+    p = problem()
+
+    def call(cu_q=FAKE, cu_k=FAKE, **kw):
+        return lib.bsfa_prefill_varlen(ctypes.byref(p), FAKE, FAKE, FAKE, cu_q, cu_k, None, 0,
+                                       _lib.BSFA_GATE_DENSE, -math.inf, FAKE, None, None, None,
+                                       None, 0, None)
+    assert call(cu_q=None) == _lib.BSFA_ERR_ARG
+    assert call(cu_k=None) == _lib.BSFA_ERR_ARG
+    assert call(cu_q=FAKE + 2) == _lib.BSFA_ERR_ALIGN
+    assert lib.bsfa_prefill_varlen(None, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, 0, -math.inf,
+                                   FAKE, None, None, None, None, 0, None) == _lib.BSFA_ERR_ARG
+
+
 def test_absolute_gate_length_limit():
     p = problem(N=2097152 + 64)
     st = call_prefill(p, tbl=table(t_len=1), mode=_lib.BSFA_GATE_ABSOLUTE)

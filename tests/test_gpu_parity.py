@@ -348,6 +348,83 @@ def test_gate_masks_with_prefix_match_the_whole_call(mid_tables):
     assert torch.equal(part, full[:, :, 3:])
 
 
+# ---------------------------------------------------------------------------------------------
+# Variable-length batches
+# ---------------------------------------------------------------------------------------------
+def _varlen_batch(seed, Hq, Hkv, d, nq, nk):
+    """Packed sequences of the given query / key lengths (key length >= query length)."""
+    g = torch.Generator().manual_seed(seed)
+    cu_q = np.cumsum([0] + nq).astype(np.int32)
+    cu_k = np.cumsum([0] + nk).astype(np.int32)
+    Q = torch.randn(int(cu_q[-1]), Hq, d, generator=g) * 1.5
+    K = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
+    V = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
+    return Q, K, V, cu_q, cu_k
+
+
+VARLEN = [   # Hq, Hkv, d, Bq, query lengths, key lengths
+    (8, 2, 128, 128, [1000, 0, 300, 64, 517], [1000, 0, 556, 64, 773]),
+    (4, 2, 64, 64, [200, 333, 64], [328, 333, 192]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN)
+@pytest.mark.parametrize("mode", ["dense", "absolute", "relative"])
+def test_varlen_equals_one_call_per_sequence_bitwise(case, mode):
+    Hq, Hkv, d, Bq, nq, nk = case
+    Q, K, V, cu_q, cu_k = _varlen_batch(20, Hq, Hkv, d, nq, nk)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    B, nqb_max, nkb_max = len(nq), -(-max(nq) // Bq), -(-max(nk) // 64)
+    kw = {}
+    if mode == "absolute":
+        T = np.random.default_rng(3).uniform(-1.0, 3.0, (2, Hq, nqb_max + 8)).astype(np.float32)
+        kw = dict(table=make_table(T, Bq, d).to_device("cuda"), budget_slice=1)
+    elif mode == "relative":
+        kw = dict(log_lambda=math.log(1e-2))
+    counts = torch.full((B, Hq, nqb_max), -7, dtype=torch.int32, device="cuda")
+    stat = torch.full((B, Hq, nqb_max, nkb_max), float("nan"), device="cuda")
+    O = _lib.bsfa_prefill_varlen(Qd, Kd, Vd, torch.tensor(cu_q, device="cuda"),
+                                 torch.tensor(cu_k, device="cuda"), max(nq), max(nk),
+                                 block_q=Bq, gate_mode=mode, kept_counts=counts,
+                                 debug_block_stat=stat, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    for b in range(B):
+        if nq[b] == 0:
+            assert (counts[b] == -7).all()
+            continue
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        c1 = torch.zeros((1, Hq, -(-nq[b] // Bq)), dtype=torch.int32, device="cuda")
+        s1 = torch.full((1, Hq, -(-nq[b] // Bq), -(-nk[b] // 64)), float("nan"), device="cuda")
+        O1 = _lib.bsfa_prefill(Qd[None, q0:q1], Kd[None, k0:k1], Vd[None, k0:k1], block_q=Bq,
+                               gate_mode=mode, kept_counts=c1, debug_block_stat=s1,
+                               out_dtype=torch.float32, **kw)
+        torch.cuda.synchronize()
+        one = dict(O=O1, counts=c1.cpu().numpy(), stat=s1.cpu().numpy())
+        assert torch.equal(O[q0:q1], one["O"][0]), b
+        qb, kb = one["counts"].shape[2], one["stat"].shape[3]
+        np.testing.assert_array_equal(counts[b, :, :qb].cpu().numpy(), one["counts"][0])
+        assert (counts[b, :, qb:] == -7).all()
+        np.testing.assert_array_equal(stat[b, :, :qb, :kb].cpu().numpy(), one["stat"][0])
+
+
+@pytest.mark.parametrize("case", VARLEN)
+def test_varlen_parity_with_oracle(case):
+    # the packed addressing and the per-sequence prefixes against the oracle (dense: no gate
+    # decisions, whose near-ties the per-sequence tests cover)
+    Hq, Hkv, d, Bq, nq, nk = case
+    Q, K, V, cu_q, cu_k = _varlen_batch(21, Hq, Hkv, d, nq, nk)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    O = _lib.bsfa_prefill_varlen(Qd, Kd, Vd, torch.tensor(cu_q, device="cuda"),
+                                 torch.tensor(cu_k, device="cuda"), max(nq), max(nk),
+                                 block_q=Bq, gate_mode="dense", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    r = oracle.oracle_prefill_varlen(Qh, Kh, Vh, cu_q, cu_k, block_q=Bq, block_k=64,
+                                     mode="dense")
+    err = np.abs(O.cpu().numpy() - r.out)
+    assert np.isfinite(O.cpu().numpy()).all()
+    assert err.max() <= 1e-2 and err.mean() <= 1e-3, (err.max(), err.mean())
+
+
 def test_back_to_back_launches_bitwise(mid_tables):
     B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
     tab = mid_tables("llama_like_ragged").to_device("cuda")

@@ -473,3 +473,55 @@ def test_absolute_gate_rejects_prefix_off_the_block_grid():
     with pytest.raises(ValueError):
         oracle_prefill(Q[:, 100:], K, V, block_q=64, block_k=64, mode=GATE_ABSOLUTE,
                        table=_const_table(0.0, 1, 3))
+
+
+# ---------------------------------------------------------------------------------------------
+# Variable-length batches (sequences packed along the token axis)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", ["dense", "absolute", "relative"])
+def test_varlen_of_equal_sequences_equals_the_batch(mode):
+    # packing a batch of equal-length sequences changes nothing
+    B, N, Hq, Hkv, d, Bq, Bk = 3, 192, 2, 1, 16, 64, 64
+    Q, K, V = _rand(34, B, N, Hq, Hkv, d)
+    kw = dict(block_q=Bq, block_k=Bk, mode=mode)
+    if mode == "absolute":
+        kw["table"] = _midpoint_table(brute_block_max(Q, K, Bq, Bk), Hq, N // Bq,
+                                      np.random.default_rng(6))
+    elif mode == "relative":
+        kw["log_lambda"] = math.log(0.3)
+    batch = oracle_prefill(Q, K, V, **kw)
+    cu = [0, N, 2 * N, 3 * N]
+    var = oracle.oracle_prefill_varlen(Q.reshape(B * N, Hq, d), K.reshape(B * N, Hkv, d),
+                                       V.reshape(B * N, Hkv, d), cu, cu, **kw)
+    np.testing.assert_array_equal(var.out, batch.out.reshape(B * N, Hq, d))
+    np.testing.assert_array_equal(var.kept_counts, batch.kept_counts)
+    np.testing.assert_array_equal(var.keep, batch.keep)
+
+
+def test_varlen_mixed_lengths_and_prefixes():
+    # sequences of different lengths, one with a prefix, one empty: each equals its own call,
+    # and the padding past each sequence's blocks stays unwritten
+    rng = np.random.default_rng(35)
+    Hq, Hkv, d, Bq, Bk = 2, 1, 8, 64, 64
+    nq, nk = [100, 0, 256, 64], [100, 0, 384, 64]
+    cu_q, cu_k = np.cumsum([0] + nq), np.cumsum([0] + nk)
+    Q = rng.standard_normal((cu_q[-1], Hq, d)).astype(np.float32)
+    K = rng.standard_normal((cu_k[-1], Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((cu_k[-1], Hkv, d)).astype(np.float32)
+    r = oracle.oracle_prefill_varlen(Q, K, V, cu_q, cu_k, block_q=Bq, block_k=Bk, mode="dense")
+    for b in range(4):
+        if nq[b] == 0:
+            assert (r.kept_counts[b] == -1).all()
+            continue
+        one = oracle_prefill(Q[None, cu_q[b]:cu_q[b + 1]], K[None, cu_k[b]:cu_k[b + 1]],
+                             V[None, cu_k[b]:cu_k[b + 1]], block_q=Bq, block_k=Bk, mode="dense")
+        np.testing.assert_array_equal(r.out[cu_q[b]:cu_q[b + 1]], one.out[0])
+        qb = one.kept_counts.shape[2]
+        np.testing.assert_array_equal(r.kept_counts[b, :, :qb], one.kept_counts[0])
+        assert (r.kept_counts[b, :, qb:] == -1).all()
+    # and the prefixed sequence is plain masked attention over its keys
+    b = 2
+    mask = np.arange(nk[b])[None, :] <= (nk[b] - nq[b] + np.arange(nq[b]))[:, None]
+    ref = sdpa_masked(Q[None, cu_q[b]:cu_q[b + 1]], K[None, cu_k[b]:cu_k[b + 1]],
+                      V[None, cu_k[b]:cu_k[b + 1]], np.broadcast_to(mask, (1, Hq) + mask.shape).copy())
+    np.testing.assert_allclose(r.out[None, cu_q[b]:cu_q[b + 1]], ref, rtol=0, atol=3e-6)
