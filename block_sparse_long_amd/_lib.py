@@ -260,13 +260,15 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
                     block_k: int = 64, debug_block_stat=None, softmax_scale: float = 0.0,
                     stream=None):
     """Keep bitmasks of the absolute gate: int64 [B, Hq, nqb, W] (bit j % 64 of word j // 64 set
-    iff off-diagonal key block j is kept); allocated if None. Returns keep_mask."""
+    iff off-diagonal 64-key tile j is kept; a kept 128-key block sets both of its tiles);
+    allocated if None. Returns keep_mask."""
     import torch
     lib = load_library()
     B, N, Hq, _ = Q.shape
-    nqb, nkb = -(-N // block_q), -(-int(K.shape[1]) // block_k)
+    nqb, ntile = -(-N // block_q), -(-int(K.shape[1]) // 64)   # one bit per 64-key tile
     if keep_mask is None:
-        keep_mask = torch.empty((B, Hq, nqb, -(-nkb // 64)), dtype=torch.int64, device=Q.device)
+        keep_mask = torch.empty((B, Hq, nqb, -(-ntile // 64)), dtype=torch.int64,
+                                device=Q.device)
     if not keep_mask.is_contiguous() or keep_mask.element_size() != 8:
         raise ValueError("keep_mask must be a contiguous 8-byte-element tensor")
     if debug_block_stat is not None and (debug_block_stat.dtype != torch.float32

@@ -50,9 +50,11 @@ bsfa_status check_problem(const bsfa_problem* p, bool need_v_o) {
                 p->heads_kv);
   if (p->head_dim != 64 && p->head_dim != 128)
     return fail(BSFA_ERR_SHAPE, "head_dim %d not supported (64 or 128)", p->head_dim);
-  if (p->block_k != bsfa::kBlockK || (p->block_q != 64 && p->block_q != 128))
-    return fail(BSFA_ERR_SHAPE, "tile %dx%d not supported (64x64 or 128x64)", p->block_q,
-                p->block_k);
+  const bool tile_ok = (p->block_k == bsfa::kBlockK && (p->block_q == 64 || p->block_q == 128)) ||
+                       (p->block_k == 2 * bsfa::kBlockK && p->block_q == 128);
+  if (!tile_ok)
+    return fail(BSFA_ERR_SHAPE, "tile %dx%d not supported (64x64, 128x64 or 128x128)",
+                p->block_q, p->block_k);
   if (!(p->softmax_scale >= 0.f) || isinf(p->softmax_scale))
     return fail(BSFA_ERR_ARG, "softmax_scale must be finite and >= 0");
   if (p->in_dtype != BSFA_BF16)
@@ -137,9 +139,10 @@ bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K,
   a.G = p->heads_q / p->heads_kv;
   a.nqb = ceil_div(p->seqlen, p->block_q);
   a.nkb = ceil_div(a.Nk, p->block_k);
+  a.kpb = p->block_k / bsfa::kBlockK;
   a.scale = scale;
   a.c_log2 = scale * 1.4426950408889634f;
-  a.mask_words = ceil_div(a.nkb, 64);
+  a.mask_words = ceil_div(ceil_div(a.Nk, bsfa::kBlockK), 64);
   return a;
 }
 
@@ -178,8 +181,9 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
   if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
     return 0;
+  // one bit per 64-key tile (a gate block of 128 keys sets two)
   const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
-  const uint64_t words = ceil_div(ceil_div(key_len(p), p->block_k), 64);
+  const uint64_t words = ceil_div(ceil_div(key_len(p), bsfa::kBlockK), 64);
   return (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
 }
 
@@ -204,6 +208,18 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     s = check_table(p, table, budget_slice);
     if (s != BSFA_OK) return s;
   }
+  if (p->block_k != bsfa::kBlockK) {
+    // 128-key gate blocks are decided by the gate sweep; a vote inside the softmax loop, which
+    // walks 64-key tiles, is not built for them
+    if (gate_mode == BSFA_GATE_RELATIVE)
+      return fail(BSFA_ERR_UNSUPPORTED, "the relative gate takes 64-key blocks");
+    if (gate_mode == BSFA_GATE_ABSOLUTE && !workspace)
+      return fail(BSFA_ERR_UNSUPPORTED,
+                  "128-key blocks under the absolute gate need a workspace (the gate sweep)");
+    if (debug_block_stat)
+      return fail(BSFA_ERR_UNSUPPORTED,
+                  "128-key blocks: the block statistics come from bsfa_gate_masks");
+  }
   const bool empty = p->batch == 0 || p->seqlen == 0;
   if (!empty) {
     if (cu_q && ((reinterpret_cast<uintptr_t>(cu_q) | reinterpret_cast<uintptr_t>(cu_k)) & 3u))
@@ -219,7 +235,7 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
       (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u)))
     return fail(BSFA_ERR_ALIGN, "kept_counts, kept_total or debug_block_stat misaligned");
   const int nqb = ceil_div(p->seqlen, p->block_q);
-  const int nkb = ceil_div(key_len(p), p->block_k);
+  const int nkb = ceil_div(key_len(p), bsfa::kBlockK);
   if ((long long)key_len(p) > (1ll << 30))
     return fail(BSFA_ERR_UNSUPPORTED, "kv_seqlen %d too large", key_len(p));
   if (gate_mode == BSFA_GATE_ABSOLUTE && nkb > bsfa::kMaxGateTiles)
@@ -320,7 +336,7 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
   if (debug_block_stat && (reinterpret_cast<uintptr_t>(debug_block_stat) & 3u))
     return fail(BSFA_ERR_ALIGN, "debug_block_stat misaligned");
   const int nqb = ceil_div(p->seqlen, p->block_q);
-  const int nkb = ceil_div(key_len(p), p->block_k);
+  const int nkb = ceil_div(key_len(p), bsfa::kBlockK);
   if (nkb > bsfa::kMaxGateTiles)
     return fail(BSFA_ERR_UNSUPPORTED, "%d keys above the absolute-gate limit %d", key_len(p),
                 bsfa::kMaxGateTiles * bsfa::kBlockK);
@@ -355,7 +371,7 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
     if (budgets_host[t] < 1) return fail(BSFA_ERR_ARG, "budget %d is < 1", budgets_host[t]);
   if (key_len(p) != p->seqlen)
     return fail(BSFA_ERR_UNSUPPORTED, "calibration takes whole sequences (kv_seqlen 0 or seqlen)");
-  const int nkb = ceil_div(p->seqlen, p->block_k);
+  const int nkb = ceil_div(p->seqlen, bsfa::kBlockK);   // 64-key tiles
   if (nkb > bsfa::kCalibMaxKeyBlocks)
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the calibration limit %d", p->seqlen,
                 bsfa::kCalibMaxKeyBlocks * bsfa::kBlockK);
@@ -380,6 +396,7 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
   a.G = p->heads_q / p->heads_kv;
   a.nqb = ceil_div(p->seqlen, p->block_q);
   a.nkb = nkb;
+  a.kpb = p->block_k / bsfa::kBlockK;
   const int nw = bsfa::waves_per_workgroup(p->block_q, a.G);
   const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);

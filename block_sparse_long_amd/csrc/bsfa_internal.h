@@ -43,6 +43,10 @@ struct PrefillArgs {
   unsigned long long* keep_mask;
   int mask_words;
   int full_masks;                  // gate sweep: write every mask word of every (b, h, i)
+  // 64-key tiles per gate block (block_k / 64: 1, or 2 for 128-key blocks). Loads and loop
+  // iterations stay at 64 keys; decisions, kept counts and the statistic dump are per block,
+  // and a kept block sets the mask bits of all its tiles. nkb counts gate blocks.
+  int kpb;
 };
 
 struct CalibArgs {
@@ -52,6 +56,7 @@ struct CalibArgs {
   int B, N, Hq, Hkv, G, nqb, nkb;
   int units, xcd_map, xcd_rot;
   float scale;
+  int kpb;                         // 64-key tiles per gate block
   int n_budgets;
   int budgets[16];
   float* kth;                      // [n_budgets][B][Hq][nqb]

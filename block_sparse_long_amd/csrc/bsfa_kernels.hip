@@ -681,11 +681,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (w == 0 && lane == 0) {
       for (int x = 0; x < nw64; ++x) kept += __builtin_popcountll(sMask[x]);
       sKept = kept;
+      kept /= a.kpb;          // kept gate blocks (a kept block sets all its tiles' bits)
     }
     __syncthreads();
     kept_all = sKept;
   } else if (!loop_gate) {
-    kept = n_off;   // dense, or an absolute threshold of -inf: every block kept
+    // dense, or an absolute threshold of -inf: every off-diagonal gate block kept
+    kept = (pre + i * BQ) / (BK * a.kpb);
   }
   // The tile after j in the sequence the softmax walks: with the pass-1 mask, the next kept
   // off-diagonal tile and then the diagonal region; otherwise every tile.
@@ -1084,15 +1086,22 @@ void gate_sweep_kernel(PrefillArgs a) {
   };
   // leader of head hw: decision for tile j from the head's waves' maxima in slot j & 1; each
   // completed mask word goes out at once
+  // (with 128-key gate blocks, a block is decided on its second tile from both tiles' maxima
+  // and keeps both bits; n_off is a whole number of blocks then, since BQ = 128)
   unsigned long long word = 0ull;
+  float xblk = kNegInf;
   auto combine = [&](int j) {
     if (leader) {
       float x = sStage[j & 1][hw * WPH];
 #pragma unroll
       for (int r = 1; r < WPH; ++r) x = fmaxf(x, sStage[j & 1][hw * WPH + r]);
-      const float sm = x * a.scale;
-      if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + j] = sm;
-      if (sm >= thr) word |= 1ull << (j & 63);
+      xblk = (j % a.kpb == 0) ? x : fmaxf(xblk, x);
+      if (j % a.kpb == a.kpb - 1) {
+        const int jb = j / a.kpb;
+        const float sm = xblk * a.scale;
+        if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + jb] = sm;
+        if (sm >= thr) word |= (a.kpb == 2 ? 3ull : 1ull) << ((j + 1 - a.kpb) & 63);
+      }
       if ((j & 63) == 63 || j == n_off - 1) {
         mask[j >> 6] = word;
         word = 0ull;
@@ -1179,20 +1188,23 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       if (lane == 0) sPart[w] = wst;
       wait_vmem();
       __syncthreads();
-      if (tid < HPW) {
+      if (tid < HPW) {   // the candidate of gate block t / kpb: max over its tiles
         float x = sPart[tid * WPH];
         for (int r = 1; r < WPH; ++r) x = fmaxf(x, sPart[tid * WPH + r]);
-        sW[tid][t] = x * a.scale;
+        x *= a.scale;
+        sW[tid][t / a.kpb] = (t % a.kpb == 0) ? x : fmaxf(sW[tid][t / a.kpb], x);
       }
       __syncthreads();
     }
   }
-  // pad each head's list to a power of two with -inf, then an ascending bitonic sort
+  // pad each head's list of gate-block candidates to a power of two with -inf, then an
+  // ascending bitonic sort
+  const int n_cand = n_off / a.kpb;
   int P = 1;
-  while (P < n_off) P <<= 1;
+  while (P < n_cand) P <<= 1;
   for (int idx = tid; idx < HPW * P; idx += NT) {
     const int hh = idx / P, t = idx % P;
-    if (t >= n_off) sW[hh][t] = kNegInf;
+    if (t >= n_cand) sW[hh][t] = kNegInf;
   }
   __syncthreads();
   for (int k = 2; k <= P; k <<= 1) {
@@ -1215,7 +1227,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   if (rw == 0) {
     for (int kk = lane; kk < a.n_budgets; kk += 64) {
       const int kb = a.budgets[kk];
-      const float r = (n_off >= kb) ? sW[hw][P - kb] : kNegInf;
+      const float r = (n_cand >= kb) ? sW[hw][P - kb] : kNegInf;
       a.kth[(((long long)kk * a.B + b) * a.Hq + h) * a.nqb + i] = r;
     }
   }

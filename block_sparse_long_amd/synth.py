@@ -144,6 +144,10 @@ CONFIGS = {
     "llama_32k_sweep": dict(kind="structured", n=32768, heads_q=32, heads_kv=8, d=128,
                             block_q=128, block_k=64, budgets=[16, 64, 256], calib_n=32768,
                             calib_seeds=list(range(1, 9))),
+    # the 32K sweep with 128-key tiles: the same key budgets (8, 32, 128 blocks of 128 keys)
+    "llama_32k_bk128": dict(kind="structured", n=32768, heads_q=32, heads_kv=8, d=128,
+                            block_q=128, block_k=128, budgets=[8, 32, 128], calib_n=32768,
+                            calib_seeds=list(range(1, 9))),
     "llama_128k": dict(kind="structured", n=131072, heads_q=32, heads_kv=8, d=128, block_q=128,
                        block_k=64, budgets=[64], calib_n=65536, calib_seeds=list(range(1, 9))),
     "llama_64k_relative": dict(kind="structured", n=65536, heads_q=32, heads_kv=8, d=128,

@@ -76,7 +76,13 @@ typedef struct {
   int32_t heads_kv;          /* Hkv >= 1, Hq % Hkv == 0; query head h reads KV head h / (Hq/Hkv) */
   int32_t head_dim;          /* d: 64 or 128 */
   int32_t block_q;           /* Bq: 64 or 128 (gate tile rows) */
-  int32_t block_k;           /* Bk: 64 (gate tile columns) */
+  int32_t block_k;           /* Bk: 64, or 128 with Bq = 128 (gate tile columns). 128-key blocks
+                              * (the notes re-tile for other hardware and recalibrate, "Block
+                              * Sparse Flash Attention", Loss & Training) are decided by the gate
+                              * sweep: DENSE, and ABSOLUTE with a workspace; RELATIVE, ABSOLUTE
+                              * without a workspace and bsfa_prefill's debug_block_stat return
+                              * BSFA_ERR_UNSUPPORTED for them. Loads and loop steps stay at 64
+                              * keys; decisions, kept counts and block statistics are per block. */
   float softmax_scale;       /* > 0, or 0 for 1/sqrt(head_dim); applied to fp32 scores */
   int32_t in_dtype;          /* bsfa_dtype of Q, K, V: BSFA_BF16 */
   int32_t out_dtype;         /* bsfa_dtype of O: BSFA_BF16 or BSFA_FP32 */
@@ -110,8 +116,8 @@ typedef struct {
 } bsfa_table;
 
 /* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
- * ABSOLUTE, one keep bitmask per (b, h, i), B * Hq * ceil(N/Bq) * ceil(ceil(Nk/Bk)/64) uint64
- * words. */
+ * ABSOLUTE, one keep bitmask per (b, h, i) with one bit per 64-key tile,
+ * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words. */
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
 
 /* Gated causal prefill attention (the method's hot path).
@@ -180,8 +186,9 @@ bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void
  * computed (no softmax, no V) and bit j % 64 of keep_mask[b][h][i][j / 64] is set iff
  * s_max(i, j) >= T_eff(h, i); the diagonal region is not part of the mask (it is always kept).
  *   p, Q, K, table, budget_slice   as for bsfa_prefill with gate_mode ABSOLUTE (V, O unused)
- *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(Nk/Bk)/64), 8-byte
- *                 aligned; every word is written (bits at or past n_off(i) are zero)
+ *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(Nk/64)/64), 8-byte
+ *                 aligned, one bit per 64-key tile (a kept 128-key block sets both of its
+ *                 tiles); every word is written (bits past the off-diagonal tiles are zero)
  *   mask_bytes    size of keep_mask; at least bsfa_prefill_workspace_bytes(p, ABSOLUTE)
  *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
  *   stream        hipStream_t

@@ -47,10 +47,10 @@ def run_device(Qd, Kd, Vd, *, block_q, mode, table=None, budget_slice=0,
                 stat=None if stat is None else stat.cpu().numpy())
 
 
-def make_table(T, block_q, d, budgets=None):
+def make_table(T, block_q, d, budgets=None, block_k=64):
     T = np.asarray(T, np.float32)
     return ThresholdTable(T=T, budgets=budgets or list(range(1, T.shape[0] + 1)),
-                          block_q=block_q, block_k=64, head_dim=d,
+                          block_q=block_q, block_k=block_k, head_dim=d,
                           softmax_scale=float(np.float32(1 / math.sqrt(d))))
 
 

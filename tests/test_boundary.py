@@ -231,6 +231,23 @@ def test_varlen_validation():
                                    FAKE, None, None, None, None, 0, None) == _lib.BSFA_ERR_ARG
 
 
+def test_wide_key_blocks():
+    # 128 x 128 tiles: dense and the absolute gate's two launches; the votes inside the loop
+    # and the per-tile statistic dump are not built for them
+    p = problem(bk=128)
+    assert call_prefill(p, mode=_lib.BSFA_GATE_RELATIVE, q=None) == _lib.BSFA_ERR_UNSUPPORTED
+    abs_call = dict(tbl=table(bk=128), mode=_lib.BSFA_GATE_ABSOLUTE)
+    assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_UNSUPPORTED          # no workspace
+    assert call_prefill(p, dbg=FAKE, ws=FAKE, ws_bytes=1 << 20, **abs_call) == \
+        _lib.BSFA_ERR_UNSUPPORTED
+    assert call_prefill(problem(bq=64, bk=128)) == _lib.BSFA_ERR_SHAPE
+    # the workspace keeps one bit per 64-key tile
+    lib = _lib.load_library()
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(problem(N=65 * 64, bk=128)),
+                                            _lib.BSFA_GATE_ABSOLUTE) == \
+        lib.bsfa_prefill_workspace_bytes(ctypes.byref(problem(N=65 * 64)), _lib.BSFA_GATE_ABSOLUTE)
+
+
 def test_absolute_gate_length_limit():
     p = problem(N=2097152 + 64)
     st = call_prefill(p, tbl=table(t_len=1), mode=_lib.BSFA_GATE_ABSOLUTE)

@@ -15,7 +15,7 @@ import torch
 import oracle
 from block_sparse_long_amd import _lib, synth
 from block_sparse_long_amd.table import ThresholdTable
-from gpu_util import BAND, bf16_pair, check_parity, make_table, run_device
+from gpu_util import BAND, MAX_ABS, MEAN_ABS, bf16_pair, check_parity, make_table, run_device
 
 pytestmark = pytest.mark.gpu
 
@@ -504,6 +504,106 @@ def test_calibration_kernel_matches_oracle(name):
                         assert got == ref
                     else:
                         assert abs(got - ref) <= 1e-3, (k, b, h, i, got, ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# 128-key gate blocks (128 x 128 tiles): decided by the gate sweep
+# ---------------------------------------------------------------------------------------------
+BK128 = ["llama_like_ragged", "g8", "d64_bq128_g1"]
+
+
+def _bk128_table(name, budgets=(1, 2)):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    samples = []
+    for s_ in (101, 102):
+        Q, K, _ = _mid_inputs(name, s_)
+        _, (Qh, Kh) = bf16_pair(Q, K)
+        samples.append((Qh, Kh))
+    T = oracle.calibrate(samples, block_q=Bq, block_k=128, budgets=list(budgets),
+                         scale=float(np.float32(1 / math.sqrt(d))))
+    return make_table(T, Bq, d, list(budgets), block_k=128)
+
+
+@pytest.mark.parametrize("name", BK128)
+def test_bk128_gate_masks_and_prefill_match_oracle(name):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    tab = _bk128_table(name)
+    dtab = tab.to_device("cuda")
+    Q, K, V = _mid_inputs(name, 22)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    nqb, nkb, ntile = -(-N // Bq), -(-N // 128), -(-N // 64)
+    for sl in (0, 1):
+        mask = torch.full((B, Hq, nqb, -(-ntile // 64)), -1, dtype=torch.int64, device="cuda")
+        stat = torch.full((B, Hq, nqb, nkb), float("nan"), device="cuda")
+        _lib.bsfa_gate_masks(Qd, Kd, dtab, sl, mask, block_q=Bq, block_k=128,
+                             debug_block_stat=stat)
+        counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
+        O = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, block_k=128, gate_mode="absolute",
+                              table=dtab, budget_slice=sl, kept_counts=counts,
+                              out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        m = np.ascontiguousarray(mask.cpu().numpy()).view(np.uint8)
+        bits = np.unpackbits(m, axis=-1, bitorder="little").astype(bool)[..., :ntile]
+        st = stat.cpu().numpy()
+        # a block's two tiles carry one decision: the device's fp32 comparison of its maximum
+        keep_dev = np.zeros((B, Hq, nqb, nkb), bool)
+        for i in range(nqb):
+            n_off = oracle.key_block_range(i, N, Bq, 128)[0]
+            thr = tab.T[sl][:, min(i, tab.t_len - 1)].astype(np.float32)
+            kb = st[:, :, i, :n_off] >= thr[None, :, None]
+            np.testing.assert_array_equal(bits[:, :, i, 0:2 * n_off:2], kb)
+            np.testing.assert_array_equal(bits[:, :, i, 1:2 * n_off:2], kb)
+            assert not bits[:, :, i, 2 * n_off:].any()
+            keep_dev[:, :, i, :n_off] = kb
+        np.testing.assert_array_equal(counts.cpu().numpy(), keep_dev.sum(-1))
+        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=Bq, block_k=128, mode="absolute",
+                                  table=tab.T, budget_slice=sl, forced_keep=keep_dev, band=BAND)
+        for i in range(nqb):
+            n_off = oracle.key_block_range(i, N, Bq, 128)[0]
+            mg = r.margin[:, :, i, :n_off]
+            out = np.abs(mg) > BAND
+            np.testing.assert_array_equal(r.keep[:, :, i, :n_off][out], keep_dev[:, :, i, :n_off][out])
+            fin = np.isfinite(r.stat[:, :, i, :n_off])
+            np.testing.assert_allclose(st[:, :, i, :n_off][fin], r.stat[:, :, i, :n_off][fin],
+                                       rtol=1e-5, atol=2e-3)
+        err = np.abs(O.cpu().numpy() - r.out)
+        assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("name", ["llama_like_ragged", "d64_bq128_g1"])
+def test_bk128_dense_equals_bk64_and_counts_blocks(name):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, V = _mid_inputs(name, 23)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    c64 = torch.zeros((B, Hq, -(-N // Bq)), dtype=torch.int32, device="cuda")
+    c128 = torch.zeros_like(c64)
+    O64 = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, gate_mode="dense", kept_counts=c64)
+    O128 = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, block_k=128, gate_mode="dense",
+                             kept_counts=c128)
+    torch.cuda.synchronize()
+    assert torch.equal(O64, O128)
+    for i in range(c64.shape[2]):
+        assert (c128[:, :, i] == oracle.key_block_range(i, N, Bq, 128)[0]).all()
+        assert (c64[:, :, i] == oracle.key_block_range(i, N, Bq, 64)[0]).all()
+
+
+@pytest.mark.parametrize("name", ["llama_like_ragged", "g8"])
+def test_bk128_calibration_kernel_matches_oracle(name):
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, _ = _mid_inputs(name, 24)
+    (Qd, Kd), (Qh, Kh) = bf16_pair(Q, K)
+    budgets = [1, 2, 3]
+    kth = _lib.bsfa_calibrate_blockmax(Qd, Kd, budgets, block_q=Bq, block_k=128)
+    torch.cuda.synchronize()
+    kth = kth.cpu().numpy()
+    sm = oracle.off_diagonal_block_maxima(Qh, Kh, block_q=Bq, block_k=128)
+    for kk, k in enumerate(budgets):
+        for i in range(sm.shape[2]):
+            n_off = oracle.key_block_range(i, N, Bq, 128)[0]
+            for h in range(Hq):
+                ref = oracle.kth_highest(sm[0, h, i], n_off, k)
+                got = kth[kk, 0, h, i]
+                assert got == ref if math.isinf(ref) else abs(got - ref) <= 1e-3, (k, h, i)
 
 
 # ---------------------------------------------------------------------------------------------

@@ -35,7 +35,7 @@ def _const_table(value, Hq, t_len, n_budgets=1):
 # Block structure
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("N,Bq,Bk", [(384, 64, 64), (1000, 128, 64), (200, 64, 32), (300, 32, 64),
-                                     (129, 128, 64)])
+                                     (129, 128, 64), (1000, 128, 128)])
 def test_block_ranges_match_brute_force(N, Bq, Bk):
     noff = first_offdiag_blocks(N, Bq, Bk)
     nqb = -(-N // Bq)
@@ -111,6 +111,7 @@ CASES = [  # B, N, Hq, Hkv, d, Bq, Bk
     (2, 200, 4, 2, 16, 64, 32),     # batch, GQA, ragged tail
     (1, 300, 2, 2, 8, 128, 64),     # Bq = 2 Bk, ragged
     (1, 130, 2, 1, 16, 32, 64),     # Bq < Bk
+    (1, 400, 2, 1, 16, 128, 128),   # the wide key tile, ragged
 ]
 
 
