@@ -164,17 +164,19 @@ def block_ranges(N, Bq, Bk=64):
 
 
 def executed_flops(kept_counts, N, Bq, d, Bk=64, query_blocks=None):
-    """2*Bq*Bk*d per tile product: QK on every visible tile, PV on kept + diagonal tiles."""
+    """2*Bq*64*d per product of a query block with a 64-key tile: QK on every visible tile, PV
+    on every diagonal-region tile and on the tiles of kept blocks (kept_counts counts blocks of
+    Bk keys, Bk / 64 tiles each)."""
     import numpy as np
     kc = np.asarray(kept_counts, dtype=np.int64)        # [B, Hq, nqb]
-    rng = block_ranges(N, Bq, Bk)
+    rng = block_ranges(N, Bq, 64)
     qbs = range(len(rng)) if query_blocks is None else query_blocks
     B, Hq = kc.shape[0], kc.shape[1]
     tiles = 0
     for i in qbs:
         n_off, n_end = rng[i]
-        tiles += B * Hq * (n_end + (n_end - n_off)) + int(kc[:, :, i].sum())
-    return 2.0 * Bq * Bk * d * tiles
+        tiles += B * Hq * (n_end + (n_end - n_off)) + (Bk // 64) * int(kc[:, :, i].sum())
+    return 2.0 * Bq * 64 * d * tiles
 
 
 def dense_flops(B, Hq, N, Bq, d, Bk=64):
@@ -201,14 +203,15 @@ class Workload:
         self.Qd, self.Kd, self.Vd = (x.to(device) for x in self.host)
         self.O = torch.empty_like(self.Qd)
         self.N, self.Hq, self.d, self.Bq = c["n"], c["heads_q"], c["d"], c["block_q"]
+        self.Bk = c["block_k"]
         nqb = -(-self.N // self.Bq)
         self.counts = torch.zeros((1, self.Hq, nqb), dtype=torch.int32, device=device)
         self.table = None
         if c["budgets"]:
             self.table = ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{name}.bin"))
             self.dtable = self.table.to_device(device)
-        rng = block_ranges(self.N, self.Bq)
-        self.n_off_total = sum(n_off for n_off, _ in rng)
+        rng = block_ranges(self.N, self.Bq, self.Bk)
+        self.n_off_total = sum(n_off for n_off, _ in rng)     # off-diagonal gate blocks
 
     def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None, workspace=None):
         import torch
@@ -218,8 +221,8 @@ class Workload:
                 n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq)
                 self.workspace = torch.empty(n, dtype=torch.uint8, device=self.Qd.device)
             workspace = self.workspace
-        _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, gate_mode=mode,
-                          table=table if table is not None else
+        _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, block_k=self.Bk,
+                          gate_mode=mode, table=table if table is not None else
                           (self.dtable if mode == "absolute" else None),
                           budget_slice=budget_slice, log_lambda=log_lambda,
                           kept_counts=self.counts, workspace=workspace)
@@ -245,7 +248,7 @@ def timed(fn, steps, warmup):
 
 def sweep_flops(w):
     """QK on every off-diagonal tile of every (b, h, i): the gate sweep's work."""
-    return 2.0 * w.Bq * 64 * w.d * w.Hq * w.n_off_total
+    return 2.0 * w.Bq * w.Bk * w.d * w.Hq * w.n_off_total
 
 
 def run_sweep(w, steps, warmup):
@@ -301,7 +304,7 @@ def run_gate(w, mode, steps, warmup, **kw):
     ev_ms, wall_ms = timed(lambda: w.call(mode, **kw), steps, warmup)
     torch.cuda.synchronize()
     counts = w.counts.cpu().numpy()
-    flops = executed_flops(counts, w.N, w.Bq, w.d)
+    flops = executed_flops(counts, w.N, w.Bq, w.d, w.Bk)
     kept = int(counts.sum())
     return dict(ms=ev_ms, wall_ms=wall_ms, flops=flops, tflops=flops / ev_ms / 1e9, kept=kept,
                 kept_fraction=kept / (w.Hq * w.n_off_total) if w.n_off_total else 1.0,
@@ -319,12 +322,13 @@ def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
         blocks = sorted({nqb // 4 - 1, nqb // 2 - 1, nqb // 2, 3 * nqb // 4, nqb - 1})
     with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=64, mode=mode,
+        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=w.Bk, mode=mode,
                                   table=None if w.table is None else w.table.T,
                                   budget_slice=budget_slice, log_lambda=log_lambda,
                                   query_blocks=blocks)
         sec = time.perf_counter() - t0
-    flops = executed_flops(np.maximum(r.kept_counts, 0), w.N, w.Bq, w.d, query_blocks=blocks)
+    flops = executed_flops(np.maximum(r.kept_counts, 0), w.N, w.Bq, w.d, w.Bk,
+                           query_blocks=blocks)
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
             "kind": "oracle", "seconds": round(sec, 2),
             "sample": f"{w.name}: query blocks {blocks} x all {w.Hq} heads, same inputs and "
@@ -426,6 +430,19 @@ def main():
                                "predicted_density": round(predicted_density(32768, 128, kk), 4)}
         sweeps["llama_32k_sweep"] = rows
         del w32
+        torch.cuda.empty_cache()
+        wb = Workload("llama_32k_bk128", dev)
+        rows = {}
+        for sl, kk in enumerate(wb.table.budgets):
+            r = run_gate(wb, "absolute", args.steps, args.warmup, budget_slice=sl)
+            rows[f"k={kk}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
+                               "pct_mfma_peak": round(r["pct_peak"], 2),
+                               "speedup_vs_dense": round(d32["ms"] / r["ms"], 4),
+                               "kept_fraction": round(r["kept_fraction"], 4),
+                               "predicted_density": round(predicted_density(32768, 128, kk, 128),
+                                                          4)}
+        sweeps["llama_32k_bk128"] = rows
+        del wb
         torch.cuda.empty_cache()
         w64 = Workload("llama_64k_relative", dev)
         d64 = run_gate(w64, "dense", args.steps, args.warmup)
