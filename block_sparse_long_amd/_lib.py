@@ -31,7 +31,8 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
 
-EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_workspace_bytes",
+EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
+            "bsfa_prefill_workspace_bytes",
             "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error",
             "bsfa_version")
 
@@ -83,6 +84,11 @@ def load_library(path: str = LIB_PATH):
     lib.bsfa_prefill_varlen.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, vp, vp,
                                         ctypes.POINTER(BsfaTable), ctypes.c_int32, ctypes.c_int32,
                                         ctypes.c_float, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.bsfa_prefill_paged.restype = ctypes.c_int32
+    lib.bsfa_prefill_paged.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, vp, vp, vp,
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.POINTER(BsfaTable),
+                                       ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp, vp,
+                                       vp, vp, ctypes.c_uint64, vp]
     lib.bsfa_prefill_workspace_bytes.restype = ctypes.c_uint64
     lib.bsfa_prefill_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem), ctypes.c_int32]
     lib.bsfa_gate_masks.restype = ctypes.c_int32
@@ -252,6 +258,62 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                                  _ptr(kept_counts), _ptr(kept_total), _ptr(debug_block_stat),
                                  _ptr(workspace), ctypes.c_uint64(ws_bytes),
                                  _stream_handle(stream, Q.device))
+    _check(st)
+    return O
+
+
+def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
+                       max_seqlen_q: int, max_seqlen_k: int, O=None, *, block_q: int,
+                       block_k: int = 64, gate_mode="dense", table=None, budget_slice: int = 0,
+                       log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
+                       debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
+                       out_dtype=None, workspace=None):
+    """bsfa_prefill_varlen with K / V in a paged cache. Q: [total_q, Hq, d] bf16;
+    K_pages, V_pages: [num_pages, page_size, Hkv, d] bf16; cu_seqlens_q: int32 [B + 1];
+    kv_lens: int32 [B]; block_table: int32 [B, pages per sequence]. Returns O."""
+    import torch
+    lib = load_library()
+    if Q.dim() != 3 or K_pages.dim() != 4 or V_pages.dim() != 4:
+        raise ValueError("Q must be [tokens, heads, dim], K_pages / V_pages [pages, page, heads, dim]")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("kv_lens", kv_lens),
+                    ("block_table", block_table)):
+        if t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous int32 tensor")
+    if block_table.dim() != 2 or kv_lens.numel() != cu_seqlens_q.numel() - 1 or \
+            block_table.shape[0] != kv_lens.numel():
+        raise ValueError("block_table must be [B, pages]; kv_lens [B]; cu_seqlens_q [B + 1]")
+    if O is None:
+        O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
+    mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    p = make_problem(Q[None], K_pages[:, 0][None], V_pages[:, 0][None], O[None],
+                     block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    p.batch = kv_lens.numel()
+    p.seqlen = int(max_seqlen_q)
+    p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
+    p.q_stride[0] = p.o_stride[0] = 0
+    p.k_stride[:] = (K_pages.stride(0), K_pages.stride(1), K_pages.stride(2))
+    p.v_stride[:] = (V_pages.stride(0), V_pages.stride(1), V_pages.stride(2))
+    tbl = table.c_struct() if table is not None else None
+    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
+                        ("kept_total", kept_total, torch.int64),
+                        ("debug_block_stat", debug_block_stat, torch.float32)):
+        if t is not None and (t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    if workspace is None:
+        nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
+        if nbytes:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
+    if workspace is not None and workspace.numel() == 0:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.bsfa_prefill_paged(ctypes.byref(p), _ptr(Q), _ptr(K_pages), _ptr(V_pages),
+                                _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(block_table),
+                                int(block_table.shape[1]), int(K_pages.shape[1]),
+                                ctypes.byref(tbl) if tbl is not None else None,
+                                int(budget_slice), mode, float(log_lambda), _ptr(O),
+                                _ptr(kept_counts), _ptr(kept_total), _ptr(debug_block_stat),
+                                _ptr(workspace), ctypes.c_uint64(ws_bytes),
+                                _stream_handle(stream, Q.device))
     _check(st)
     return O
 

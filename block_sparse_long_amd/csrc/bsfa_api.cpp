@@ -191,12 +191,22 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
 
 namespace {
 
-// bsfa_prefill and bsfa_prefill_varlen: cu_q / cu_k are NULL for a fixed-length batch.
+// Key layout of a variable-length batch: packed (cu_k) or paged (pages, kv_lens).
+struct KeyLayout {
+  const int32_t* cu_k = nullptr;
+  const int32_t* pages = nullptr;
+  const int32_t* kv_lens = nullptr;
+  int32_t pages_stride = 0, page_size = 0;
+};
+
+// bsfa_prefill, bsfa_prefill_varlen and bsfa_prefill_paged: cu_q is NULL for a fixed-length
+// batch.
 bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, const void* V,
-                         const int32_t* cu_q, const int32_t* cu_k, const bsfa_table* table,
+                         const int32_t* cu_q, const KeyLayout& kl, const bsfa_table* table,
                          int32_t budget_slice, int32_t gate_mode, float log_lambda, void* O,
                          int32_t* kept_counts, uint64_t* kept_total, float* debug_block_stat,
                          void* workspace, uint64_t workspace_bytes, void* stream) {
+  const int32_t* cu_k = kl.cu_k;
   bsfa_status s = check_problem(p, true);
   if (s != BSFA_OK) return s;
   if (gate_mode != BSFA_GATE_DENSE && gate_mode != BSFA_GATE_ABSOLUTE &&
@@ -222,8 +232,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   }
   const bool empty = p->batch == 0 || p->seqlen == 0;
   if (!empty) {
-    if (cu_q && ((reinterpret_cast<uintptr_t>(cu_q) | reinterpret_cast<uintptr_t>(cu_k)) & 3u))
-      return fail(BSFA_ERR_ALIGN, "cu_seqlens_q and cu_seqlens_k must be 4-byte aligned");
+    if (cu_q && ((reinterpret_cast<uintptr_t>(cu_q) | reinterpret_cast<uintptr_t>(cu_k) |
+                  reinterpret_cast<uintptr_t>(kl.pages) | reinterpret_cast<uintptr_t>(kl.kv_lens)) &
+                 3u))
+      return fail(BSFA_ERR_ALIGN, "cu_seqlens, block_table and kv_lens must be 4-byte aligned");
     if (!Q || !K || !V || !O) return fail(BSFA_ERR_ARG, "Q, K, V and O must be non-NULL");
     if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O))
       return fail(BSFA_ERR_ALIGN, "Q, K, V and O must be 16-byte aligned");
@@ -264,6 +276,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   a.o = O;
   a.cu_q = cu_q;
   a.cu_k = cu_k;
+  a.pages = kl.pages;
+  a.kv_lens = kl.kv_lens;
+  a.pages_stride = kl.pages_stride;
+  a.page_tiles = kl.page_size / bsfa::kBlockK;
   a.kept_counts = kept_counts;
   a.kept_total = reinterpret_cast<unsigned long long*>(kept_total);
   a.dbg = debug_block_stat;
@@ -300,9 +316,9 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
                          float log_lambda, void* O, int32_t* kept_counts, uint64_t* kept_total,
                          float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
                          void* stream) {
-  return prefill_impl(p, Q, K, V, nullptr, nullptr, table, budget_slice, gate_mode, log_lambda,
-                      O, kept_counts, kept_total, debug_block_stat, workspace, workspace_bytes,
-                      stream);
+  return prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode,
+                      log_lambda, O, kept_counts, kept_total, debug_block_stat, workspace,
+                      workspace_bytes, stream);
 }
 
 bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void* K,
@@ -315,7 +331,37 @@ bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void
   if (!p) return fail(BSFA_ERR_ARG, "problem is NULL");
   if (p->batch > 0 && p->seqlen > 0 && (!cu_seqlens_q || !cu_seqlens_k))
     return fail(BSFA_ERR_ARG, "cu_seqlens_q and cu_seqlens_k must be non-NULL");
-  return prefill_impl(p, Q, K, V, cu_seqlens_q, cu_seqlens_k, table, budget_slice, gate_mode,
+  KeyLayout kl;
+  kl.cu_k = cu_seqlens_k;
+  return prefill_impl(p, Q, K, V, cu_seqlens_q, kl, table, budget_slice, gate_mode, log_lambda,
+                      O, kept_counts, kept_total, debug_block_stat, workspace, workspace_bytes,
+                      stream);
+}
+
+bsfa_status bsfa_prefill_paged(const bsfa_problem* p, const void* Q, const void* K_pages,
+                               const void* V_pages, const int32_t* cu_seqlens_q,
+                               const int32_t* kv_lens, const int32_t* block_table,
+                               int32_t block_table_stride, int32_t page_size,
+                               const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
+                               float log_lambda, void* O, int32_t* kept_counts,
+                               uint64_t* kept_total, float* debug_block_stat, void* workspace,
+                               uint64_t workspace_bytes, void* stream) {
+  if (!p) return fail(BSFA_ERR_ARG, "problem is NULL");
+  if (page_size < bsfa::kBlockK || page_size % bsfa::kBlockK != 0)
+    return fail(BSFA_ERR_SHAPE, "page_size %d must be a positive multiple of %d", page_size,
+                bsfa::kBlockK);
+  const int max_k = p->kv_seqlen > 0 ? p->kv_seqlen : p->seqlen;
+  if (block_table_stride < ceil_div(max_k, page_size))
+    return fail(BSFA_ERR_ARG, "block_table_stride %d below the pages of %d keys",
+                block_table_stride, max_k);
+  if (p->batch > 0 && p->seqlen > 0 && (!cu_seqlens_q || !kv_lens || !block_table))
+    return fail(BSFA_ERR_ARG, "cu_seqlens_q, kv_lens and block_table must be non-NULL");
+  KeyLayout kl;
+  kl.pages = block_table;
+  kl.kv_lens = kv_lens;
+  kl.pages_stride = block_table_stride;
+  kl.page_size = page_size;
+  return prefill_impl(p, Q, K_pages, V_pages, cu_seqlens_q, kl, table, budget_slice, gate_mode,
                       log_lambda, O, kept_counts, kept_total, debug_block_stat, workspace,
                       workspace_bytes, stream);
 }

@@ -29,6 +29,12 @@ struct PrefillArgs {
   // sequences packed along the token axis; N, Nk are then the longest), or nullptr
   const int* cu_q;
   const int* cu_k;
+  // paged K / V (with cu_q): K and V live in pages of page_tiles * 64 tokens; sequence b's key
+  // tokens are kv_lens[b], its page j is pages[b * pages_stride + j]; ks[0] / vs[0] are the
+  // page strides. nullptr: contiguous sequences.
+  const int* pages;
+  const int* kv_lens;
+  int pages_stride, page_tiles;
   int units;                       // B * Hkv * (G / heads per workgroup)
   int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads);
                                    // -1: KV-head-major order over all XCDs

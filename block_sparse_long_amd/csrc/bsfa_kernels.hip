@@ -519,13 +519,19 @@ struct Seq {
 __device__ __forceinline__ Seq seq_of(const PrefillArgs& a, int b) {
   Seq s;
   if (a.cu_q) {
-    const int q0 = a.cu_q[b], k0 = a.cu_k[b];
+    const int q0 = a.cu_q[b];
     s.N = a.cu_q[b + 1] - q0;
-    s.Nk = a.cu_k[b + 1] - k0;
     s.q = (long long)q0 * a.qs[1];
     s.o = (long long)q0 * a.os[1];
-    s.k = (long long)k0 * a.ks[1];
-    s.v = (long long)k0 * a.vs[1];
+    if (a.pages) {   // paged keys: tile addresses come from the page table (tile_offset)
+      s.Nk = a.kv_lens[b];
+      s.k = s.v = 0;
+    } else {
+      const int k0 = a.cu_k[b];
+      s.Nk = a.cu_k[b + 1] - k0;
+      s.k = (long long)k0 * a.ks[1];
+      s.v = (long long)k0 * a.vs[1];
+    }
   } else {
     s.N = a.N;
     s.Nk = a.Nk;
@@ -579,6 +585,19 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
   return r;
 }
 
+// Element offset (from the sequence's base) of 64-key tile j in K or V (token stride tst, page
+// stride pst). Contiguous sequences stride by tiles; a paged cache looks the tile's page up in
+// the block table: pages hold a whole number of tiles, so a tile never straddles two.
+template <bool PAGED>
+__device__ __forceinline__ long long tile_offset(const PrefillArgs& a, int b, int j,
+                                                 long long tst, long long pst) {
+  if constexpr (PAGED) {
+    const int page = a.pages[(long long)b * a.pages_stride + j / a.page_tiles];
+    return (long long)page * pst + (long long)(j % a.page_tiles) * kBlockK * tst;
+  }
+  return (long long)j * kBlockK * tst;
+}
+
 // ---------------------------------------------------------------------------------------------
 // Prefill kernel
 // ---------------------------------------------------------------------------------------------
@@ -586,7 +605,9 @@ constexpr int kRows = kRowsPerWave;
 
 constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
-template <int D, int BQ, int NW, int GATE>
+// PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
+// kernels carry no page lookups).
+template <int D, int BQ, int NW, int GATE, bool PAGED>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     PrefillArgs a) {
   constexpr int WPH = BQ / kRows;          // waves per head
@@ -663,7 +684,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   auto key_valid = [&](int j) { return min(BK, Nk - j * BK); };
   const unsigned krow = (unsigned)kst * 2u, vrow = (unsigned)vst * 2u;
   auto load_k = [&](int j, __bf16* dst) {
-    copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, key_valid(j), dst, w, lane);
+    copy_tile<D, STR, NW>(koff, Kb + tile_offset<PAGED>(a, b, j, kst, a.ks[0]), krow, key_valid(j),
+                          dst, w, lane);
   };
 
   bf16x8 qf[KS];
@@ -779,8 +801,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       }
     }
     const bool kload = t2 < n_end;
-    const __bf16* const kg = Kb + (long long)t2 * BK * kst;
-    const __bf16* const vg = Vb + (long long)t * BK * vst;
+    const __bf16* const kg = Kb + tile_offset<PAGED>(a, b, min(t2, n_end - 1), kst, a.ks[0]);
+    const __bf16* const vg = Vb + tile_offset<PAGED>(a, b, t, vst, a.vs[0]);
     auto copy_k = [&](int r) {
       copy_round<D, STR, NW>(r, koff, kg, krow, key_valid(t2), P ? sK1 : sK0, w, lane);
     };
@@ -1013,7 +1035,7 @@ __device__ __forceinline__ float tile_max64(f32x16 (&s)[2][2], bool ragged, int 
   return block_max(mx, s[1][1]);
 }
 
-template <int D, int BQ, int HPW>
+template <int D, int BQ, int HPW, bool PAGED>
 __global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gate_sweep_kernel(PrefillArgs a) {
   constexpr int WPH = BQ / 64;             // waves per head
@@ -1061,7 +1083,8 @@ void gate_sweep_kernel(PrefillArgs a) {
   unsigned koff[MK];
   copy_offsets<D, STR, NW>(koff, kst, w, lane);
   auto load_k = [&](int j, __bf16* dst) {
-    copy_tile<D, STR, NW>(koff, Kb + (long long)j * BK * kst, krow, BK, dst, w, lane);
+    copy_tile<D, STR, NW>(koff, Kb + tile_offset<PAGED>(a, b, j, kst, a.ks[0]), krow, BK, dst, w,
+                          lane);
   };
   auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
   const int tcol = min(pre / BQ + i, a.t_len - 1);   // the absolute query block's threshold
@@ -1235,29 +1258,38 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
 
-template <int D, int BQ, int NW>
-hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t stream) {
+template <int D, int BQ, int NW, bool PAGED>
+hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
   const dim3 grid(a.units * a.nqb), block(NW * 64);
   switch (gate) {
     case kDense:
-      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kDense>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kDense, PAGED>), grid, block, 0, stream, a);
       break;
     case kAbsolute:
     case kAbsVote:
       if constexpr (NW == BQ / kRows) {   // one head per workgroup
         if (gate == kAbsolute)
-          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute>), grid, block, 0, stream, a);
+          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute, PAGED>), grid, block, 0,
+                             stream, a);
         else
-          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsVote>), grid, block, 0, stream, a);
+          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsVote, PAGED>), grid, block, 0,
+                             stream, a);
       } else {
         return hipErrorInvalidConfiguration;
       }
       break;
     default:
-      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kRelative>), grid, block, 0, stream, a);
+      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kRelative, PAGED>), grid, block, 0, stream,
+                         a);
       break;
   }
   return hipGetLastError();
+}
+
+template <int D, int BQ, int NW>
+hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t stream) {
+  return a.pages ? launch_prefill_paged<D, BQ, NW, true>(a, gate, stream)
+                 : launch_prefill_paged<D, BQ, NW, false>(a, gate, stream);
 }
 
 // Waves per workgroup: BQ / 32 waves per head times 1, 2 or 4 heads (BQ = 128: 4 or 8 waves;
@@ -1291,10 +1323,18 @@ template <int D, int BQ>
 hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
   constexpr int WPH = BQ / 64;
   const dim3 grid(a.units * a.nqb);
-  if (hpw == 2)
-    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2>), grid, dim3(WPH * 128), 0, stream, a);
-  else
-    hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1>), grid, dim3(WPH * 64), 0, stream, a);
+  const bool paged = a.pages != nullptr;
+  if (hpw == 2) {
+    if (paged)
+      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2, true>), grid, dim3(WPH * 128), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2, false>), grid, dim3(WPH * 128), 0, stream, a);
+  } else {
+    if (paged)
+      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1, true>), grid, dim3(WPH * 64), 0, stream, a);
+    else
+      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1, false>), grid, dim3(WPH * 64), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -180,6 +180,32 @@ bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void
                                 float* debug_block_stat, void* workspace,
                                 uint64_t workspace_bytes, void* stream);
 
+/* bsfa_prefill_varlen with K and V in a paged cache (the layout serving stacks keep their KV
+ * cache in; "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM Serving"
+ * names paged KV next to varlen scheduling). Sequence b's key positions 0 .. kv_lens[b] - 1
+ * live in pages block_table[b * block_table_stride + 0, 1, ...] of page_size tokens each; its
+ * queries are packed in Q / O as for bsfa_prefill_varlen (the last Nq_b of its key positions).
+ *   p             as for bsfa_prefill_varlen (kv_seqlen = max_b kv_lens[b]); k_stride[0] and
+ *                 v_stride[0] are the page strides, k_stride[1] / [2] the token / head strides
+ *   K_pages, V_pages  device [num_pages][page_size][Hkv][d] bf16 (any page order)
+ *   cu_seqlens_q  device int32 [batch + 1] query token offsets, 4-byte aligned
+ *   kv_lens       device int32 [batch] key tokens per sequence (>= its query tokens)
+ *   block_table   device int32 [batch][block_table_stride] page indices, 4-byte aligned;
+ *                 block_table_stride >= ceil(kv_seqlen / page_size)
+ *   page_size     a positive multiple of 64 tokens (a 64-key tile never straddles two pages;
+ *                 BSFA_ERR_SHAPE otherwise)
+ *   the rest      as for bsfa_prefill_varlen. The caller guarantees the device-side arrays
+ *                 (lengths within the maxima, page indices within K_pages / V_pages).
+ * The results equal bsfa_prefill_varlen on the keys gathered from their pages. */
+bsfa_status bsfa_prefill_paged(const bsfa_problem* p, const void* Q, const void* K_pages,
+                               const void* V_pages, const int32_t* cu_seqlens_q,
+                               const int32_t* kv_lens, const int32_t* block_table,
+                               int32_t block_table_stride, int32_t page_size,
+                               const bsfa_table* table, int32_t budget_slice, int32_t gate_mode,
+                               float log_lambda, void* O, int32_t* kept_counts,
+                               uint64_t* kept_total, float* debug_block_stat, void* workspace,
+                               uint64_t workspace_bytes, void* stream);
+
 /* The absolute gate's keep decisions alone ("Block Sparse Flash Attention", Method: a block
  * is kept when its exact maximum scaled score reaches the threshold T[layer, head, query
  * block]). For every (b, h, i) the exact scores of all off-diagonal blocks j < n_off(i) are

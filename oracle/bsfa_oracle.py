@@ -243,6 +243,25 @@ def oracle_prefill_varlen(Q, K, V, cu_q, cu_k, *, block_q: int, block_k: int, mo
     return OracleResult(out, kept_counts, stat, keep, margin)
 
 
+def gather_pages(pages, block_table, kv_lens):
+    """Keys (or values) of a paged cache laid out as packed sequences.
+
+    pages: [num_pages, page_size, H, d]; block_table: [B, pages per sequence]; kv_lens: [B].
+    Returns ([sum(kv_lens), H, d], cu [B + 1]): sequence b's token t lives at row
+    t % page_size of page block_table[b, t // page_size].
+    """
+    pages = np.asarray(pages)
+    page_size = pages.shape[1]
+    rows, cu = [], [0]
+    for b, n in enumerate(int(x) for x in kv_lens):
+        t = np.arange(n)
+        rows.append(pages[np.asarray(block_table)[b, t // page_size], t % page_size])
+        cu.append(cu[-1] + n)
+    if not rows:
+        return np.zeros((0,) + pages.shape[2:], pages.dtype), np.asarray(cu)
+    return np.concatenate(rows, axis=0), np.asarray(cu)
+
+
 def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float | None = None,
                               dtype=np.float32) -> np.ndarray:
     """s_max[b, h, i, j] for every off-diagonal block j < n_off(i); NaN elsewhere.

@@ -231,6 +231,22 @@ def test_varlen_validation():
                                    FAKE, None, None, None, None, 0, None) == _lib.BSFA_ERR_ARG
 
 
+def test_paged_validation():
+    lib = _lib.load_library()
+    p = problem()
+
+    def call(page=64, stride=4, cu=FAKE, lens=FAKE, bt=FAKE):
+        return lib.bsfa_prefill_paged(ctypes.byref(p), FAKE, FAKE, FAKE, cu, lens, bt, stride,
+                                      page, None, 0, _lib.BSFA_GATE_DENSE, -math.inf, FAKE, None,
+                                      None, None, None, 0, None)
+    assert call(page=96) == _lib.BSFA_ERR_SHAPE         # pages hold whole 64-key tiles
+    assert call(page=0) == _lib.BSFA_ERR_SHAPE
+    assert call(stride=3) == _lib.BSFA_ERR_ARG          # 256 keys need 4 pages of 64
+    assert call(lens=None) == _lib.BSFA_ERR_ARG
+    assert call(bt=None) == _lib.BSFA_ERR_ARG
+    assert call(bt=FAKE + 2) == _lib.BSFA_ERR_ALIGN
+
+
 def test_wide_key_blocks():
     # 128 x 128 tiles: dense and the absolute gate's two launches; the votes inside the loop
     # and the per-tile statistic dump are not built for them

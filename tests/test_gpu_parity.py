@@ -507,6 +507,77 @@ def test_calibration_kernel_matches_oracle(name):
 
 
 # ---------------------------------------------------------------------------------------------
+# Paged K / V
+# ---------------------------------------------------------------------------------------------
+def _to_pages(X, cu, page, seed):
+    """Scatter packed sequences [tokens, H, d] into a shuffled page pool with spare pages."""
+    rng = np.random.default_rng(seed)
+    lens = np.diff(cu)
+    n_pages = [-(-int(n) // page) for n in lens]
+    free = list(rng.permutation(sum(n_pages) + 5))
+    pool = torch.full((len(free), page) + tuple(X.shape[1:]), float("nan"), dtype=X.dtype,
+                      device=X.device)
+    table = torch.zeros((len(lens), max(max(n_pages), 1)), dtype=torch.int32)
+    for b, n in enumerate(lens):
+        for j in range(n_pages[b]):
+            pg = free.pop()
+            table[b, j] = int(pg)
+            m = min(page, int(n) - j * page)
+            pool[pg, :m] = X[cu[b] + j * page: cu[b] + j * page + m]
+    return pool, table.cuda()
+
+
+@pytest.mark.parametrize("page", [64, 128, 192])
+@pytest.mark.parametrize("mode", ["dense", "absolute", "relative"])
+def test_paged_equals_packed_bitwise(page, mode):
+    Hq, Hkv, d, Bq, nq, nk = VARLEN[0]
+    Q, K, V, cu_q, cu_k = _varlen_batch(25, Hq, Hkv, d, nq, nk)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    Kp, table = _to_pages(Kd, cu_k, page, 7)
+    Vp, table_v = _to_pages(Vd, cu_k, page, 7)
+    assert torch.equal(table, table_v)
+    kw = {}
+    if mode == "absolute":
+        T = np.random.default_rng(3).uniform(-1.0, 3.0, (2, Hq, 16)).astype(np.float32)
+        kw = dict(table=make_table(T, Bq, d).to_device("cuda"), budget_slice=1)
+    elif mode == "relative":
+        kw = dict(log_lambda=math.log(1e-2))
+    B, nqb = len(nq), -(-max(nq) // Bq)
+    cq = torch.tensor(cu_q, device="cuda")
+    c1 = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
+    c2 = torch.full_like(c1, -7)
+    O1 = _lib.bsfa_prefill_varlen(Qd, Kd, Vd, cq, torch.tensor(cu_k, device="cuda"), max(nq),
+                                  max(nk), block_q=Bq, gate_mode=mode, kept_counts=c1,
+                                  out_dtype=torch.float32, **kw)
+    O2 = _lib.bsfa_prefill_paged(Qd, Kp, Vp, cq, torch.tensor(np.diff(cu_k), dtype=torch.int32,
+                                                                 device="cuda"),
+                                 table, max(nq), max(nk), block_q=Bq, gate_mode=mode,
+                                 kept_counts=c2, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2)
+    assert torch.equal(c1, c2)
+
+
+def test_paged_parity_with_oracle():
+    Hq, Hkv, d, Bq, nq, nk = VARLEN[1]
+    Q, K, V, cu_q, cu_k = _varlen_batch(26, Hq, Hkv, d, nq, nk)
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    Kp, table = _to_pages(Kd, cu_k, 128, 8)
+    Vp, _ = _to_pages(Vd, cu_k, 128, 8)
+    lens = np.diff(cu_k).astype(np.int32)
+    O = _lib.bsfa_prefill_paged(Qd, Kp, Vp, torch.tensor(cu_q, device="cuda"),
+                                torch.tensor(lens, device="cuda"), table, max(nq), max(nk),
+                                block_q=Bq, gate_mode="dense", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    Kg, cu = oracle.gather_pages(Kp.float().cpu().numpy(), table.cpu().numpy(), lens)
+    Vg, _ = oracle.gather_pages(Vp.float().cpu().numpy(), table.cpu().numpy(), lens)
+    r = oracle.oracle_prefill_varlen(Qh, Kg, Vg, cu_q, cu, block_q=Bq, block_k=64, mode="dense")
+    err = np.abs(O.cpu().numpy() - r.out)
+    assert np.isfinite(O.cpu().numpy()).all()
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+# ---------------------------------------------------------------------------------------------
 # 128-key gate blocks (128 x 128 tiles): decided by the gate sweep
 # ---------------------------------------------------------------------------------------------
 BK128 = ["llama_like_ragged", "g8", "d64_bq128_g1"]

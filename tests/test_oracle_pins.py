@@ -526,3 +526,26 @@ def test_varlen_mixed_lengths_and_prefixes():
     ref = sdpa_masked(Q[None, cu_q[b]:cu_q[b + 1]], K[None, cu_k[b]:cu_k[b + 1]],
                       V[None, cu_k[b]:cu_k[b + 1]], np.broadcast_to(mask, (1, Hq) + mask.shape).copy())
     np.testing.assert_allclose(r.out[None, cu_q[b]:cu_q[b + 1]], ref, rtol=0, atol=3e-6)
+
+
+def test_gather_pages_inverts_a_paged_layout():
+    # scatter packed sequences into shuffled pages by hand, then gather them back
+    rng = np.random.default_rng(36)
+    page, H, d = 64, 2, 4
+    lens = [130, 0, 64, 257]
+    K = rng.standard_normal((sum(lens), H, d)).astype(np.float32)
+    n_pages = [-(-n // page) for n in lens]
+    free = list(rng.permutation(sum(n_pages) + 3))        # pool with unused pages
+    pool = np.full((len(free), page, H, d), np.nan, np.float32)
+    table = np.zeros((len(lens), max(n_pages)), np.int32)
+    off = 0
+    for b, n in enumerate(lens):
+        for j in range(n_pages[b]):
+            pg = free.pop()
+            table[b, j] = pg
+            m = min(page, n - j * page)
+            pool[pg, :m] = K[off + j * page: off + j * page + m]
+        off += n
+    G, cu = oracle.gather_pages(pool, table, lens)
+    np.testing.assert_array_equal(cu, np.cumsum([0] + lens))
+    np.testing.assert_array_equal(G, K)
