@@ -51,13 +51,18 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "block_sparse_long_amd", "csrc", "bsfa_kernels.hip")
+KERNEL_DIR = os.path.join(ROOT, "block_sparse_long_amd", "csrc")
 COPY_BYTES = 1 << 30
 
 
 def kernel_source_sha256():
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    """Digest of the device code: the kernel header, the argument structs and every HIP unit."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(KERNEL_DIR)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(KERNEL_DIR, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
 
 
 def measured_traffic(workload, kernel):

@@ -1,4 +1,7 @@
-// Exact-score-gated block-sparse causal prefill attention for gfx950 (MI355X).
+// Device code of the exact-score-gated block-sparse causal prefill attention for gfx950 (MI355X).
+// Included by the translation units that instantiate the kernels (one per head dimension,
+// query tile and K/V layout, so that they compile in parallel).
+//
 //
 // The method ("Block Sparse Flash Attention", paper notes, Method > Key Designs 2 and 3): every
 // causally visible QK^T tile is computed exactly; the tile's maximum scaled score s_max decides
@@ -27,6 +30,8 @@
 //     the workgroup keeps tile t.
 //   * Workgroups are ordered heaviest query block first, and (when the unit count allows)
 //     all query blocks of one KV head go to the same XCD so their K/V stream shares its L2.
+#pragma once
+
 #include "bsfa_internal.h"
 
 #include <math.h>
@@ -1256,8 +1261,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
-__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
-
 template <int D, int BQ, int NW, bool PAGED>
 hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
   const dim3 grid(a.units * a.nqb), block(NW * 64);
@@ -1284,23 +1287,6 @@ hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stre
       break;
   }
   return hipGetLastError();
-}
-
-template <int D, int BQ, int NW>
-hipError_t launch_prefill_gate(const PrefillArgs& a, int gate, hipStream_t stream) {
-  return a.pages ? launch_prefill_paged<D, BQ, NW, true>(a, gate, stream)
-                 : launch_prefill_paged<D, BQ, NW, false>(a, gate, stream);
-}
-
-// Waves per workgroup: BQ / 32 waves per head times 1, 2 or 4 heads (BQ = 128: 4 or 8 waves;
-// BQ = 64: 2, 4 or 8 waves).
-template <int D, int BQ>
-hipError_t launch_prefill_nw(const PrefillArgs& a, int nw, int gate, hipStream_t stream) {
-  switch (nw) {
-    case 8: return launch_prefill_gate<D, BQ, 8>(a, gate, stream);
-    case 4: return launch_prefill_gate<D, BQ, 4>(a, gate, stream);
-    default: return launch_prefill_gate<D, BQ, BQ / kRows>(a, gate, stream);
-  }
 }
 
 template <int D, int BQ, int NW>
@@ -1340,56 +1326,28 @@ hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
 
 }  // namespace
 
-int gate_sweep_heads(int block_q, int group) {
-  (void)block_q;
-  return group % 2 == 0 ? 2 : 1;
-}
-
-hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream) {
-  const int hpw = gate_sweep_heads(block_q, a.G);
-  if (head_dim == 128)
-    return block_q == 128 ? launch_sweep_hpw<128, 128>(a, hpw, stream)
-                          : launch_sweep_hpw<128, 64>(a, hpw, stream);
-  return block_q == 128 ? launch_sweep_hpw<64, 128>(a, hpw, stream)
-                        : launch_sweep_hpw<64, 64>(a, hpw, stream);
-}
-
-int waves_per_workgroup(int block_q, int group) {
-  const int wph = block_q / kRows;
-  int hpw = 4 / wph;
-  while (hpw > 1 && group % hpw != 0) hpw >>= 1;
-  return hpw * wph;
-}
-
-int prefill_waves_per_workgroup(int block_q, int group, int gate) {
-  return gate == kAbsolute || gate == kAbsVote ? block_q / kRows
-                                               : waves_per_workgroup(block_q, group);
-}
-
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
-                          hipStream_t stream) {
-  const int nw = prefill_waves_per_workgroup(block_q, a.G, gate);
-  if (head_dim == 128) {
-    return block_q == 128 ? launch_prefill_nw<128, 128>(a, nw, gate, stream)
-                          : launch_prefill_nw<128, 64>(a, nw, gate, stream);
+// Per (head dimension, query tile, K/V layout): the prefill kernel for any workgroup width and
+// gate, the calibration kernel and the gate sweep. Each is instantiated explicitly by one
+// translation unit.
+// Waves per workgroup of the prefill kernel: BQ / 32 waves per head times 1, 2 or 4 heads
+// (BQ = 128: 4 or 8 waves; BQ = 64: 2, 4 or 8 waves).
+template <int D, int BQ, bool PAGED>
+hipError_t launch_prefill_tile(const PrefillArgs& a, int nw, int gate, hipStream_t stream) {
+  switch (nw) {
+    case 8: return launch_prefill_paged<D, BQ, 8, PAGED>(a, gate, stream);
+    case 4: return launch_prefill_paged<D, BQ, 4, PAGED>(a, gate, stream);
+    default: return launch_prefill_paged<D, BQ, BQ / kRows, PAGED>(a, gate, stream);
   }
-  return block_q == 128 ? launch_prefill_nw<64, 128>(a, nw, gate, stream)
-                        : launch_prefill_nw<64, 64>(a, nw, gate, stream);
 }
 
-hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipStream_t stream) {
-  const int nw = waves_per_workgroup(block_q, a.G);
-  if (head_dim == 128) {
-    return block_q == 128 ? launch_calib_nw<128, 128>(a, nw, stream)
-                          : launch_calib_nw<128, 64>(a, nw, stream);
-  }
-  return block_q == 128 ? launch_calib_nw<64, 128>(a, nw, stream)
-                        : launch_calib_nw<64, 64>(a, nw, stream);
+template <int D, int BQ>
+hipError_t launch_calibrate_tile(const CalibArgs& a, int nw, hipStream_t stream) {
+  return launch_calib_nw<D, BQ>(a, nw, stream);
 }
 
-hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {
-  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, p);
-  return hipGetLastError();
+template <int D, int BQ>
+hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream) {
+  return launch_sweep_hpw<D, BQ>(a, hpw, stream);
 }
 
 }  // namespace bsfa

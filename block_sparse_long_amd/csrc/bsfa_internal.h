@@ -1,4 +1,5 @@
-// Internal interface between the C ABI (bsfa_api.cpp) and the HIP kernels (bsfa_kernels.hip).
+// Internal interface between the C ABI (bsfa_api.cpp) and the HIP kernels (device code in
+// bsfa_device.h, instantiated by the bsfa_*.hip units).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -99,5 +100,14 @@ hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hi
 // Heads per workgroup of the gate sweep.
 int gate_sweep_heads(int block_q, int group);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
+
+// Launchers of one (head dimension D, query tile BQ[, paged K/V]) instantiation; each is defined
+// in its own translation unit. nw = waves per workgroup, hpw = heads per sweep workgroup.
+template <int D, int BQ, bool PAGED>
+hipError_t launch_prefill_tile(const PrefillArgs& a, int nw, int gate, hipStream_t stream);
+template <int D, int BQ>
+hipError_t launch_calibrate_tile(const CalibArgs& a, int nw, hipStream_t stream);
+template <int D, int BQ>
+hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream);
 
 }  // namespace bsfa

@@ -1,0 +1,70 @@
+// Host-side dispatch of the prefill, gate-sweep and calibration kernels: picks the instantiation
+// for the head dimension, query tile, workgroup width, gate and K/V layout.
+#include "bsfa_internal.h"
+
+namespace bsfa {
+namespace {
+
+__global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+
+}  // namespace
+
+int gate_sweep_heads(int block_q, int group) {
+  (void)block_q;
+  return group % 2 == 0 ? 2 : 1;
+}
+
+hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream) {
+  const int hpw = gate_sweep_heads(block_q, a.G);
+  if (head_dim == 128)
+    return block_q == 128 ? launch_sweep_tile<128, 128>(a, hpw, stream)
+                          : launch_sweep_tile<128, 64>(a, hpw, stream);
+  return block_q == 128 ? launch_sweep_tile<64, 128>(a, hpw, stream)
+                        : launch_sweep_tile<64, 64>(a, hpw, stream);
+}
+
+int waves_per_workgroup(int block_q, int group) {
+  const int wph = block_q / kRowsPerWave;
+  int hpw = 4 / wph;
+  while (hpw > 1 && group % hpw != 0) hpw >>= 1;
+  return hpw * wph;
+}
+
+int prefill_waves_per_workgroup(int block_q, int group, int gate) {
+  return gate == kAbsolute || gate == kAbsVote ? block_q / kRowsPerWave
+                                               : waves_per_workgroup(block_q, group);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
+                          hipStream_t stream) {
+  const int nw = prefill_waves_per_workgroup(block_q, a.G, gate);
+  if (a.pages) {
+    if (head_dim == 128)
+      return block_q == 128 ? launch_prefill_tile<128, 128, true>(a, nw, gate, stream)
+                            : launch_prefill_tile<128, 64, true>(a, nw, gate, stream);
+    return block_q == 128 ? launch_prefill_tile<64, 128, true>(a, nw, gate, stream)
+                          : launch_prefill_tile<64, 64, true>(a, nw, gate, stream);
+  }
+  if (head_dim == 128)
+    return block_q == 128 ? launch_prefill_tile<128, 128, false>(a, nw, gate, stream)
+                          : launch_prefill_tile<128, 64, false>(a, nw, gate, stream);
+  return block_q == 128 ? launch_prefill_tile<64, 128, false>(a, nw, gate, stream)
+                        : launch_prefill_tile<64, 64, false>(a, nw, gate, stream);
+}
+
+hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipStream_t stream) {
+  const int nw = waves_per_workgroup(block_q, a.G);
+  if (head_dim == 128) {
+    return block_q == 128 ? launch_calibrate_tile<128, 128>(a, nw, stream)
+                          : launch_calibrate_tile<128, 64>(a, nw, stream);
+  }
+  return block_q == 128 ? launch_calibrate_tile<64, 128>(a, nw, stream)
+                        : launch_calibrate_tile<64, 64>(a, nw, stream);
+}
+
+hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {
+  hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace bsfa

@@ -1,0 +1,8 @@
+// Prefill kernels for head dimension 128, 128-row query tiles, contiguous or packed K/V: every
+// workgroup width and gate.
+#include "bsfa_device.h"
+
+namespace bsfa {
+template hipError_t launch_prefill_tile<128, 128, false>(const PrefillArgs&, int, int,
+                                        hipStream_t);
+}  // namespace bsfa

@@ -1,0 +1,8 @@
+// Prefill kernels for head dimension 64, 128-row query tiles, paged K/V (block table): every
+// workgroup width and gate.
+#include "bsfa_device.h"
+
+namespace bsfa {
+template hipError_t launch_prefill_tile<64, 128, true>(const PrefillArgs&, int, int,
+                                        hipStream_t);
+}  // namespace bsfa
