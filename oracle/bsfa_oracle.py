@@ -22,6 +22,10 @@ Sources (page title, then the part of the page followed):
       - Key Designs 3 (Selective Streaming Aggregation): online softmax on kept blocks; a
         rejected block touches neither V, nor the exponentials, nor m, l, O.
       - A Worked Example.
+  * "FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM Serving", mean
+    correction (a pruned block J stands in as |B_J| copies of its mean key and mean value:
+    |B_J| e^{s_J} vbar_J joins the numerator and |B_J| e^{s_J} the denominator, i.e. one more
+    online-softmax step on a single logit shifted by log|B_J|).
   * "Skipping attention blocks was the easy part" (BLASST blog), sections "FlashAttention"
     (running max m, running sum l, accumulator O, rescale by exp(m_old - m_new)) and
     "Vote, then skip" (skip iff block max minus running max < ln(lambda); any row that wants
@@ -41,6 +45,12 @@ Readings taken where the pages are silent or ambiguous (each is listed in the de
     P + i*Bq, the causal mask and n_off / n_end use absolute positions, and the absolute gate
     reads the threshold column of the absolute query block P/Bq + i, which needs P to be a
     multiple of Bq (thresholds are bound to the calibration's tile grid).
+  * Mean correction: the stand-in logit of a pruned block is the scaled score of the row's query
+    against the block's mean key, s_J = scale * q . kbar_J (the means are plain arithmetic
+    means over the block's keys and values); only pruned off-diagonal blocks are corrected (the
+    diagonal region always runs exactly); the stand-in step takes the pruned block's place in
+    the ascending block order. It is defined for the absolute gate (whose decisions do not
+    depend on the softmax state), not for the relative gate.
 
 Pins (tests that tie each function to something other than itself) are in
 tests/test_oracle_pins.py; every public function here is pinned.
@@ -103,7 +113,8 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                    scale: float | None = None, table: np.ndarray | None = None,
                    budget_slice: int = 0, log_lambda: float = -math.inf,
                    forced_keep: np.ndarray | None = None, band: float = 1e-2,
-                   query_blocks=None, dtype=np.float32) -> OracleResult:
+                   query_blocks=None, mean_correction: bool = False,
+                   dtype=np.float32) -> OracleResult:
     """Gated causal prefill attention, one (b, h, i) work unit at a time.
 
     Q: [B, Nq, Hq, d]; K, V: [B, Nk, Hkv, d] with Nk >= Nq and Hq % Hkv == 0. The query rows
@@ -115,6 +126,8 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     forced_keep: optional [B, Hq, nqb, nkb] decisions adopted where |margin| <= band (the
     near-tie rule used when comparing against a device that rounds differently).
     query_blocks: optional iterable of query-block indices to compute (default: all).
+    mean_correction: a pruned block adds its zero-order stand-in (FlashPrefill V2's mean
+    correction) instead of nothing.
     """
     if mode not in _MODES:
         raise ValueError(f"unknown gate mode {mode!r}")
@@ -130,6 +143,9 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
         raise ValueError("absolute gate needs a threshold table")
     if mode == GATE_ABSOLUTE and P % block_q != 0:
         raise ValueError("the absolute gate needs the prefix to be a multiple of block_q")
+    if mean_correction and mode == GATE_RELATIVE:
+        # the relative gate decides from the running max, which a stand-in step would move
+        raise ValueError("mean correction is defined for the dense and absolute gates only")
     G = Hq // Hkv
     sc = dtype(1.0 / math.sqrt(d) if scale is None else scale)
     nqb, nkb = num_blocks(N, block_q), num_blocks(Nk, block_k)
@@ -158,6 +174,17 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                     te = (effective_threshold(table, budget_slice, h, P // block_q + i)
                           if mode == GATE_ABSOLUTE else None)
                     kept = 0
+
+                    def absorb(s, vals):
+                        # one online-softmax step over the logits s [R, n] and values [n, d]
+                        nonlocal m, l, o
+                        m_new = np.maximum(m, s.max(axis=1))
+                        alpha = np.exp(m - m_new)          # exp(-inf) = 0 on the first step
+                        p = np.exp(s - m_new[:, None])
+                        l = alpha * l + p.sum(axis=1)
+                        o = alpha[:, None] * o + p @ vals
+                        m = m_new
+
                     for j in range(n_end):                    # ascending; diagonal region last
                         c0, c1 = j * block_k, min((j + 1) * block_k, Nk)
                         # exact scaled pre-softmax scores of the whole tile (keep-rule equation)
@@ -187,15 +214,16 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                                 keep = bool(forced_keep[b, h, i, j])
                             kept += int(keep)
                         keep_mask[b, h, i, j] = keep
-                        if not keep:
-                            continue        # skipped: no V, no exp, m, l and O untouched
-                        rmax = s.max(axis=1)
-                        m_new = np.maximum(m, rmax)
-                        alpha = np.exp(m - m_new)              # exp(-inf) = 0 on the first block
-                        p = np.exp(s - m_new[:, None])
-                        l = alpha * l + p.sum(axis=1)
-                        o = alpha[:, None] * o + p @ V[b, c0:c1, g, :]
-                        m = m_new
+                        if keep:
+                            absorb(s, V[b, c0:c1, g, :])
+                        elif mean_correction:
+                            # the block's stand-in: |B| copies of (mean key, mean value), i.e. one
+                            # logit scale * q . kbar shifted by log|B|
+                            kbar = K[b, c0:c1, g, :].mean(axis=0)
+                            vbar = V[b, c0:c1, g, :].mean(axis=0)
+                            sbar = (q @ kbar) * sc + dtype(math.log(c1 - c0))
+                            absorb(sbar[:, None], vbar[None, :])
+                        # else skipped: no V, no exp, m, l and O untouched
                     out[b, r0:r1, h, :] = o / l[:, None]     # renormalise over kept + diagonal
                     kept_counts[b, h, i] = kept
     return OracleResult(out, kept_counts, stat, keep_mask, margin)

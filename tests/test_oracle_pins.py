@@ -549,3 +549,149 @@ def test_gather_pages_inverts_a_paged_layout():
     G, cu = oracle.gather_pages(pool, table, lens)
     np.testing.assert_array_equal(cu, np.cumsum([0] + lens))
     np.testing.assert_array_equal(G, K)
+
+
+# ---------------------------------------------------------------------------------------------
+# Mean correction ("FlashPrefill V2: Block-Sparse Prefill Attention for Long-Context LLM
+# Serving", mean correction): a pruned block contributes |B| e^{s(q, kbar)} vbar to the
+# numerator and |B| e^{s(q, kbar)} to the denominator.
+# ---------------------------------------------------------------------------------------------
+def _block_constant_keys(K, Bk, rng, noise=0.0):
+    """K with every key of a block of Bk keys equal to one random key (plus noise * N(0, 1))."""
+    K = K.copy()
+    Nk = K.shape[1]
+    for j0 in range(0, Nk, Bk):
+        K[:, j0:j0 + Bk] = K[:, j0:j0 + 1]
+    if noise:
+        K = (K + noise * rng.standard_normal(K.shape)).astype(K.dtype)
+    return K
+
+
+MEAN_CASES = [   # B, Nq, P, Hq, Hkv, d, Bq, Bk
+    (1, 256, 0, 2, 1, 32, 64, 64),
+    (2, 300, 0, 4, 2, 16, 128, 64),     # batch, GQA, ragged tail
+    (1, 200, 128, 2, 1, 16, 64, 32),    # a prefix before the chunk
+    (1, 400, 0, 2, 1, 16, 128, 128),    # the wide key block
+]
+
+
+@pytest.mark.parametrize("case", MEAN_CASES)
+@pytest.mark.parametrize("table", ["plus_inf", "midpoint"])
+def test_mean_correction_is_exact_for_block_constant_keys(case, table):
+    # Keys equal within each block: sum_j e^{s_j} v_j = |B| e^{s(q, k)} vbar exactly, so the
+    # corrected output equals full causal attention whatever is pruned.
+    B, Nq, P, Hq, Hkv, d, Bq, Bk = case
+    rng = np.random.default_rng(11)
+    Q = rng.standard_normal((B, Nq, Hq, d)).astype(np.float32)
+    K = _block_constant_keys(rng.standard_normal((B, P + Nq, Hkv, d)).astype(np.float32), Bk, rng)
+    V = rng.standard_normal((B, P + Nq, Hkv, d)).astype(np.float32)
+    nqb = -(-Nq // Bq)
+    t_len = P // Bq + nqb
+    ref = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_DENSE, dtype=np.float64)
+    n_off = np.array([key_block_range(i, Nq, Bq, Bk, P)[0] for i in range(nqb)])
+    if table == "plus_inf":
+        T = _const_table(math.inf, Hq, t_len)
+    else:   # the median off-diagonal block maximum: about half the blocks pruned
+        off = np.arange(ref.stat.shape[3])[None, :] < n_off[:, None]
+        T = _const_table(np.median(ref.stat[:, :, off]), Hq, t_len)
+    kw = dict(block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T, dtype=np.float64)
+    r = oracle_prefill(Q, K, V, mean_correction=True, **kw)
+    plain = oracle_prefill(Q, K, V, **kw)
+    assert (plain.kept_counts < n_off).any()    # something was pruned
+    np.testing.assert_allclose(ref.out, sdpa_masked_prefix(Q, K, V, P), rtol=0, atol=1e-10)
+    np.testing.assert_allclose(r.out, ref.out, rtol=0, atol=1e-10)
+    assert np.abs(plain.out - ref.out).max() > 1e-3    # the correction is what closes the gap
+    np.testing.assert_array_equal(r.keep, plain.keep)   # it never changes a decision
+
+
+def sdpa_masked_prefix(Q, K, V, P):
+    """Causal attention of Nq query rows at absolute positions P .. P + Nq - 1 (float64)."""
+    B, Nq, Hq, d = Q.shape
+    Nk = K.shape[1]
+    rows = P + np.arange(Nq)[:, None]
+    mask = np.broadcast_to(np.arange(Nk)[None, :] <= rows, (B, Hq, Nq, Nk))
+    return sdpa_masked(Q, K, V, mask)
+
+
+@pytest.mark.parametrize("case", MEAN_CASES)
+def test_mean_correction_closed_form(case):
+    # Written as one sum per row over the kept keys and the pruned blocks' stand-ins (no online
+    # softmax): numerator sum e^{s} v + sum_J |B_J| e^{sbar_J} vbar_J, denominator likewise.
+    B, Nq, P, Hq, Hkv, d, Bq, Bk = case
+    rng = np.random.default_rng(12)
+    Q = rng.standard_normal((B, Nq, Hq, d))
+    K = rng.standard_normal((B, P + Nq, Hkv, d))
+    V = rng.standard_normal((B, P + Nq, Hkv, d))
+    Nk = P + Nq
+    sc = 1.0 / math.sqrt(d)
+    nqb = -(-Nq // Bq)
+    t_len = P // Bq + nqb
+    n_off = np.array([key_block_range(i, Nq, Bq, Bk, P)[0] for i in range(nqb)])
+    dense = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_DENSE, dtype=np.float64)
+    med = np.median(dense.stat[:, :, np.arange(dense.stat.shape[3])[None, :] < n_off[:, None]])
+    T = (med + 0.3 * rng.standard_normal((1, Hq, t_len))).astype(np.float32)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T,
+                       mean_correction=True, dtype=np.float64)
+    assert (r.kept_counts < n_off).any() and (r.kept_counts > 0).any()
+    G = Hq // Hkv
+    out = np.empty_like(Q)
+    for b in range(B):
+        for h in range(Hq):
+            k, v = K[b, :, h // G], V[b, :, h // G]
+            for row in range(Nq):
+                i, arow = row // Bq, P + row
+                n_off = (P + i * Bq) // Bk
+                logits, vals = [], []
+                for j in range(-(-Nk // Bk)):
+                    c0, c1 = j * Bk, min((j + 1) * Bk, Nk)
+                    if j >= n_off or r.keep[b, h, i, j]:
+                        cols = np.arange(c0, min(c1, arow + 1))
+                        logits += list(sc * (k[cols] @ Q[b, row, h]))
+                        vals += list(v[cols])
+                    else:
+                        logits.append(math.log(c1 - c0) + sc * (k[c0:c1].mean(0) @ Q[b, row, h]))
+                        vals.append(v[c0:c1].mean(0))
+                w = np.exp(np.array(logits) - max(logits))
+                out[b, row, h] = (w[:, None] * np.array(vals)).sum(0) / w.sum()
+    np.testing.assert_allclose(r.out, out, rtol=0, atol=1e-12)
+
+
+def test_mean_correction_error_vanishes_with_within_block_spread():
+    # Keys = block constant + eps * noise: the stand-in's error is first order in eps (the
+    # within-block covariance of e^{s} and v), the uncorrected output's is not small at all.
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 512, 2, 1, 32, 64, 64
+    rng = np.random.default_rng(13)
+    Q = rng.standard_normal((B, N, Hq, d))
+    K0 = rng.standard_normal((B, N, Hkv, d))
+    V = rng.standard_normal((B, N, Hkv, d))
+    T = _const_table(math.inf, Hq, N // Bq)
+    errs = []
+    for eps in (1e-2, 1e-3):
+        K = _block_constant_keys(K0, Bk, np.random.default_rng(14), noise=eps)
+        dense = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_DENSE, dtype=np.float64)
+        kw = dict(block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T, dtype=np.float64)
+        corr = oracle_prefill(Q, K, V, mean_correction=True, **kw)
+        plain = oracle_prefill(Q, K, V, **kw)
+        errs.append((np.abs(corr.out - dense.out).max(), np.abs(plain.out - dense.out).max()))
+    (c1, p1), (c2, p2) = errs
+    assert c1 < 0.05 * p1 and c2 < 0.2 * c1 and p2 > 0.5 * p1
+
+
+@pytest.mark.parametrize("mode", ["dense", "abs_minus_inf"])
+def test_mean_correction_changes_nothing_when_nothing_is_pruned(mode):
+    Q, K, V = _rand(15, 1, 300, 2, 1, 16)
+    kw = dict(block_q=64, block_k=64)
+    if mode == "dense":
+        kw["mode"] = GATE_DENSE
+    else:
+        kw.update(mode=GATE_ABSOLUTE, table=_const_table(-math.inf, 2, 5))
+    a = oracle_prefill(Q, K, V, mean_correction=True, **kw)
+    b = oracle_prefill(Q, K, V, **kw)
+    np.testing.assert_array_equal(a.out, b.out)
+
+
+def test_mean_correction_refuses_the_relative_gate():
+    Q, K, V = _rand(16, 1, 128, 1, 1, 16)
+    with pytest.raises(ValueError):
+        oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_RELATIVE, log_lambda=-1.0,
+                       mean_correction=True)
