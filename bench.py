@@ -218,19 +218,24 @@ class Workload:
         rng = block_ranges(self.N, self.Bq, self.Bk)
         self.n_off_total = sum(n_off for n_off, _ in rng)     # off-diagonal gate blocks
 
-    def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None, workspace=None):
+    def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None, workspace=None,
+             mean_correction=False):
         import torch
         from block_sparse_long_amd import _lib
         if workspace is None and mode == "absolute":
-            if getattr(self, "workspace", None) is None:
-                n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq)
-                self.workspace = torch.empty(n, dtype=torch.uint8, device=self.Qd.device)
-            workspace = self.workspace
+            attr = "workspace_mean" if mean_correction else "workspace"
+            if getattr(self, attr, None) is None:
+                n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq,
+                                                      block_k=self.Bk,
+                                                      mean_correction=mean_correction)
+                setattr(self, attr, torch.empty(n, dtype=torch.uint8, device=self.Qd.device))
+            workspace = getattr(self, attr)
         _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, block_k=self.Bk,
                           gate_mode=mode, table=table if table is not None else
                           (self.dtable if mode == "absolute" else None),
                           budget_slice=budget_slice, log_lambda=log_lambda,
-                          kept_counts=self.counts, workspace=workspace)
+                          kept_counts=self.counts, workspace=workspace,
+                          mean_correction=mean_correction)
 
 
 def timed(fn, steps, warmup):
@@ -314,6 +319,35 @@ def run_gate(w, mode, steps, warmup, **kw):
     return dict(ms=ev_ms, wall_ms=wall_ms, flops=flops, tflops=flops / ev_ms / 1e9, kept=kept,
                 kept_fraction=kept / (w.Hq * w.n_off_total) if w.n_off_total else 1.0,
                 pct_peak=100.0 * flops / ev_ms / 1e9 / PEAK_BF16_TFLOPS)
+
+
+def run_mean_correction(w, steps, warmup, gated_ms, dense_ms):
+    """The gated call with mean correction (block-means pass, sweep, walk with the pruned
+    blocks' stand-ins): its time, and the deviation of the outputs with and without the
+    correction from the dense output."""
+    import torch
+    r = run_gate(w, "absolute", steps, warmup, budget_slice=0, mean_correction=True)
+    outs = {}
+    for key, mode, mc in (("dense", "dense", False), ("plain", "absolute", False),
+                          ("mean", "absolute", True)):
+        w.call(mode, mean_correction=mc)
+        outs[key] = w.O.clone()
+    torch.cuda.synchronize()
+    dev = {}
+    for key in ("plain", "mean"):
+        mx, tot = 0.0, 0.0
+        for r0 in range(0, w.N, 8192):          # in row chunks: fp32 copies stay small
+            e = (outs[key][:, r0:r0 + 8192].float() - outs["dense"][:, r0:r0 + 8192].float()).abs()
+            mx, tot = max(mx, e.max().item()), tot + e.sum().item()
+        dev[key] = (mx, tot / outs[key].numel())
+    del outs
+    torch.cuda.empty_cache()
+    return {"ms": round(r["ms"], 3), "vs_gated": round(r["ms"] / gated_ms, 4),
+            "speedup_vs_dense": round(dense_ms / r["ms"], 4),
+            "max_abs_vs_dense": {"uncorrected": round(dev["plain"][0], 5),
+                                 "corrected": round(dev["mean"][0], 5)},
+            "mean_abs_vs_dense": {"uncorrected": round(dev["plain"][1], 7),
+                                  "corrected": round(dev["mean"][1], 7)}}
 
 
 def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
@@ -403,14 +437,20 @@ def main():
                            "flops": sweep["flops"]},
             "softmax_walk": {"ms": round(walk_ms, 3), "flops": walk_flops,
                              "tflops": round(walk_flops / walk_ms / 1e9, 2)}}
+        # kernel names as the profiler reports them (template arguments: head dim, query tile,
+        # heads or waves per workgroup, gate, paged K/V, mean correction)
         if sweep["ms"] >= walk_ms:
-            dom = dict(kernel="gate_sweep_kernel<128, 128, 2>", ms=sweep["ms"],
+            dom = dict(kernel=f"gate_sweep_kernel<{w.d}, {w.Bq}, 2, false>", ms=sweep["ms"],
                        flops=sweep["flops"])
         else:
-            dom = dict(kernel="prefill_kernel<128, 128, 4, 1>", ms=walk_ms, flops=walk_flops)
+            dom = dict(kernel=f"prefill_kernel<{w.d}, {w.Bq}, 4, 1, false, false>", ms=walk_ms,
+                       flops=walk_flops)
     else:
-        dom = dict(kernel=f"prefill_kernel<128, 128, 4, {2 if mode == 'relative' else 0}>",
-                   ms=gated["ms"], flops=gated["flops"])
+        dom = dict(kernel=f"prefill_kernel<{w.d}, {w.Bq}, 4, {2 if mode == 'relative' else 0}, "
+                          "false, false>", ms=gated["ms"], flops=gated["flops"])
+    if w.table is not None:
+        extras["mean_correction"] = run_mean_correction(w, args.steps, args.warmup, gated["ms"],
+                                                        dense["ms"])
 
     if not args.quick and w.table is not None:
         # chunked prefill of the same sequence (chunks of 16K after their KV prefix)

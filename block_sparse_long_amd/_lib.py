@@ -45,7 +45,7 @@ class BsfaProblem(ctypes.Structure):
         ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
-        ("kv_seqlen", ctypes.c_int32),
+        ("kv_seqlen", ctypes.c_int32), ("mean_correction", ctypes.c_int32),
     ]
 
 
@@ -144,7 +144,7 @@ def _stream_handle(stream, device) -> int:
 
 
 def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
-                 softmax_scale: float = 0.0) -> BsfaProblem:
+                 softmax_scale: float = 0.0, mean_correction: bool = False) -> BsfaProblem:
     import torch
     p = BsfaProblem()
     p.batch, p.seqlen, p.heads_q, p.head_dim = (int(x) for x in Q.shape)
@@ -153,6 +153,7 @@ def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
     p.kv_seqlen = int(K.shape[1]) if K.shape[1] != Q.shape[1] else 0
     p.block_q, p.block_k = int(block_q), int(block_k)
     p.softmax_scale = float(softmax_scale)
+    p.mean_correction = int(bool(mean_correction))
     dt = {torch.bfloat16: BSFA_BF16, torch.float32: BSFA_FP32}
     p.in_dtype = dt.get(Q.dtype, -1)
     p.out_dtype = dt.get(O.dtype, -1) if O is not None else BSFA_BF16
@@ -168,7 +169,8 @@ def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
 def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode="dense",
                  table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
                  kept_counts=None, kept_total=None, debug_block_stat=None,
-                 softmax_scale: float = 0.0, stream=None, out_dtype=None, workspace=None):
+                 softmax_scale: float = 0.0, stream=None, out_dtype=None, workspace=None,
+                 mean_correction: bool = False):
     """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, Nk, Hkv, d] bf16 (device),
     Nk >= N (Nk > N: a chunk of N query rows after Nk - N cached keys).
 
@@ -177,14 +179,17 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
     written by the kernel on ``stream`` (default: torch's current stream). ``table`` is a
     block_sparse_long_amd.table.DeviceTable (needed for gate_mode "absolute"). ``workspace`` is a
     device uint8 tensor of at least bsfa_prefill_workspace_bytes bytes for the absolute gate's
-    keep masks; None allocates one, and an empty tensor asks for the path without it. Returns O.
+    keep masks (and, with ``mean_correction``, the block means); None allocates one, and an
+    empty tensor asks for the path without it. ``mean_correction``: pruned blocks add their
+    mean-key / mean-value stand-ins (absolute gate with a workspace). Returns O.
     """
     import torch
     lib = load_library()
     if O is None:
         O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
-    p = make_problem(Q, K, V, O, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    p = make_problem(Q, K, V, O, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
+                     mean_correction=mean_correction)
     tbl = None
     if table is not None:
         tbl = table.c_struct()
@@ -214,7 +219,7 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                         gate_mode="dense", table=None, budget_slice: int = 0,
                         log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
                         debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
-                        out_dtype=None, workspace=None):
+                        out_dtype=None, workspace=None, mean_correction: bool = False):
     """bsfa_prefill over sequences packed along the token axis. Q: [total_q, Hq, d] bf16;
     K, V: [total_k, Hkv, d] bf16; cu_seqlens_q / cu_seqlens_k: device int32 [B + 1] token
     offsets. Per-sequence outputs are padded to the longest sequence. Returns O."""
@@ -232,7 +237,7 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
     # the per-token views as [1, tokens, heads, dim] give the token and head strides
     p = make_problem(Q[None], K[None], V[None], O[None], block_q=block_q, block_k=block_k,
-                     softmax_scale=softmax_scale)
+                     softmax_scale=softmax_scale, mean_correction=mean_correction)
     p.batch = cu_seqlens_q.numel() - 1
     p.seqlen = int(max_seqlen_q)
     p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
@@ -267,7 +272,7 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
                        block_k: int = 64, gate_mode="dense", table=None, budget_slice: int = 0,
                        log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
                        debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
-                       out_dtype=None, workspace=None):
+                       out_dtype=None, workspace=None, mean_correction: bool = False):
     """bsfa_prefill_varlen with K / V in a paged cache. Q: [total_q, Hq, d] bf16;
     K_pages, V_pages: [num_pages, page_size, Hkv, d] bf16; cu_seqlens_q: int32 [B + 1];
     kv_lens: int32 [B]; block_table: int32 [B, pages per sequence]. Returns O."""
@@ -286,7 +291,8 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
         O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
     p = make_problem(Q[None], K_pages[:, 0][None], V_pages[:, 0][None], O[None],
-                     block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+                     block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
+                     mean_correction=mean_correction)
     p.batch = kv_lens.numel()
     p.seqlen = int(max_seqlen_q)
     p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
@@ -364,8 +370,8 @@ def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_
 
 
 def bsfa_prefill_workspace_bytes(Q, K, *, block_q: int, block_k: int = 64,
-                                 gate_mode="absolute") -> int:
+                                 gate_mode="absolute", mean_correction: bool = False) -> int:
     """Bytes of workspace bsfa_prefill can use for this problem and gate mode (0: none)."""
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
-    p = make_problem(Q, K, block_q=block_q, block_k=block_k)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, mean_correction=mean_correction)
     return int(load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))

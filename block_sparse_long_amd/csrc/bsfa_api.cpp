@@ -146,6 +146,31 @@ bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K,
   return a;
 }
 
+// The absolute gate's workspace: the keep bitmasks (one bit per 64-key tile; a gate block of
+// 128 keys sets two), then, for mean correction, the block means of K (bf16 high and low
+// parts) and of V, [B][Hkv][mean_blocks][d] each, every part on a 256-byte boundary.
+struct WorkspaceLayout {
+  uint64_t mask_bytes;
+  int mean_blocks;
+  uint64_t kbar_hi, kbar_lo, vbar, means_end;   // byte offsets
+};
+
+uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
+
+WorkspaceLayout workspace_layout(const bsfa_problem* p) {
+  WorkspaceLayout l;
+  const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
+  const uint64_t words = ceil_div(ceil_div(key_len(p), bsfa::kBlockK), 64);
+  l.mask_bytes = (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
+  l.mean_blocks = key_len(p) / p->block_k;
+  const uint64_t part = (uint64_t)p->batch * p->heads_kv * l.mean_blocks * p->head_dim * 2u;
+  l.kbar_hi = align256(l.mask_bytes);
+  l.kbar_lo = l.kbar_hi + align256(part);
+  l.vbar = l.kbar_lo + align256(part);
+  l.means_end = l.vbar + align256(part);
+  return l;
+}
+
 // The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i).
 hipError_t launch_sweep(bsfa::PrefillArgs sw, const bsfa_problem* p, hipStream_t st) {
   const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G);
@@ -181,10 +206,8 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
   if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
     return 0;
-  // one bit per 64-key tile (a gate block of 128 keys sets two)
-  const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
-  const uint64_t words = ceil_div(ceil_div(key_len(p), bsfa::kBlockK), 64);
-  return (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
+  const WorkspaceLayout l = workspace_layout(p);
+  return p->mean_correction ? l.means_end : l.mask_bytes;
 }
 
 }  // extern "C"
@@ -218,6 +241,17 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     s = check_table(p, table, budget_slice);
     if (s != BSFA_OK) return s;
   }
+  if (p->mean_correction != 0 && p->mean_correction != 1)
+    return fail(BSFA_ERR_ARG, "mean_correction must be 0 or 1");
+  // mean correction adds stand-ins for pruned blocks: after the absolute gate's sweep (the
+  // relative gate decides from the running max, which a stand-in would move)
+  const bool mean = p->mean_correction && gate_mode == BSFA_GATE_ABSOLUTE;
+  if (p->mean_correction && gate_mode == BSFA_GATE_RELATIVE)
+    return fail(BSFA_ERR_UNSUPPORTED, "mean correction is defined for the absolute gate");
+  if (mean && !workspace)
+    return fail(BSFA_ERR_UNSUPPORTED, "mean correction needs a workspace (the block means)");
+  if (mean && (reinterpret_cast<uintptr_t>(workspace) & 15u))
+    return fail(BSFA_ERR_ALIGN, "mean correction needs a 16-byte-aligned workspace");
   if (p->block_k != bsfa::kBlockK) {
     // 128-key gate blocks are decided by the gate sweep; a vote inside the softmax loop, which
     // walks 64-key tiles, is not built for them
@@ -296,6 +330,20 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   // that all workgroups stream K in step), then the prefill kernel runs over the kept ones
   if (use_masks) {
     a.keep_mask = static_cast<unsigned long long*>(workspace);
+    if (mean) {
+      const WorkspaceLayout l = workspace_layout(p);
+      char* const ws = static_cast<char*>(workspace);
+      a.kbar_hi = ws + l.kbar_hi;
+      a.kbar_lo = ws + l.kbar_lo;
+      a.vbar = ws + l.vbar;
+      a.mean_blocks = l.mean_blocks;
+      a.mean_bias = logf((float)p->block_k) / a.scale;
+      if (l.mean_blocks > 0) {
+        hipError_t e = bsfa::launch_block_means(a, p->head_dim, st);
+        if (e != hipSuccess)
+          return fail(BSFA_ERR_HIP, "block means launch: %s", hipGetErrorString(e));
+      }
+    }
     hipError_t e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
     // the walk over kept tiles: one KV head at a time on all XCDs (its K/V stays in the
@@ -392,7 +440,7 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
                 key_len(p) - p->seqlen, p->block_q);
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
-  const uint64_t need = bsfa_prefill_workspace_bytes(p, BSFA_GATE_ABSOLUTE);
+  const uint64_t need = workspace_layout(p).mask_bytes;
   if (mask_bytes < need)
     return fail(BSFA_ERR_ARG, "mask_bytes %llu below the required %llu",
                 (unsigned long long)mask_bytes, (unsigned long long)need);

@@ -611,8 +611,9 @@ constexpr int kRows = kRowsPerWave;
 constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
 // PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
-// kernels carry no page lookups).
-template <int D, int BQ, int NW, int GATE, bool PAGED>
+// kernels carry no page lookups). MEAN (absolute walk only): the pruned gate blocks' stand-ins
+// join the softmax after the walk (mean correction).
+template <int D, int BQ, int NW, int GATE, bool PAGED, bool MEAN = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2))) void prefill_kernel(
     PrefillArgs a) {
   constexpr int WPH = BQ / kRows;          // waves per head
@@ -626,6 +627,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   constexpr bool kAbs = GATE == kAbsolute;          // walks the gate sweep's keep masks
   constexpr bool kThr = kAbs || GATE == kAbsVote;    // thresholds from the table
   static_assert(!kThr || HPW == 1, "the absolute gate runs one head per workgroup");
+  static_assert(!MEAN || kAbs, "mean correction walks the gate sweep's masks");
 
   // Separate objects per buffer: the compiler then sees that a direct copy into one buffer
   // cannot alias reads of the other and does not wait for the copy before those reads.
@@ -942,6 +944,80 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     else
       pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sv, pb[0], o, vb, sb[0], 0.f, c,
                                       dummy, dsum, lane, [](int) {});
+  }
+
+  if constexpr (MEAN) {
+    // ---- mean correction ("FlashPrefill V2", mean correction) ----
+    // A pruned gate block J enters the softmax as one more key: its mean key, with the logit
+    // shifted by ln(block keys), and its mean value, i.e. |B| e^{s(q, kbar)} joins l and
+    // |B| e^{s(q, kbar)} vbar joins O. 64 such pseudo-keys (blocks m0 .. m0 + 63) make a tile:
+    // scored against Q by MFMAs over the mean key's bf16 high and low parts in turn, masked
+    // where the block was kept or does not exist, then the online-softmax update and the PV
+    // product of a key tile. Blocks are whole here: off-diagonal blocks never reach the end.
+    if (two_pass && kept_all < n_off) {
+      const int n_gb = min(n_off / a.kpb, a.mean_blocks);
+      const long long mbase = ((long long)b * a.Hkv + g) * a.mean_blocks * D;
+      const __bf16* const khi = static_cast<const __bf16*>(a.kbar_hi) + mbase;
+      const __bf16* const klo = static_cast<const __bf16*>(a.kbar_lo) + mbase;
+      const __bf16* const vme = static_cast<const __bf16*>(a.vbar) + mbase;
+      unsigned mko[MK], mvo[MV];
+      copy_offsets<D, STR, NW>(mko, D, w, lane);
+      copy_offsets<D, STRV, NW>(mvo, D, w, lane);
+      const int hs = lane >> 5;
+      for (int m0 = 0; m0 < n_gb; m0 += 64) {
+        const int valid = min(64, n_gb - m0);
+        __syncthreads();   // every wave is done with the tile buffers
+        copy_tile<D, STR, NW>(mko, khi + (long long)m0 * D, 2u * D, valid, sK0, w, lane);
+        copy_tile<D, STR, NW>(mko, klo + (long long)m0 * D, 2u * D, valid, sK1, w, lane);
+        copy_tile<D, STRV, NW>(mvo, vme + (long long)m0 * D, 2u * D, valid, sV0, w, lane);
+        wait_vmem();
+        __syncthreads();
+        // S^T of the pseudo-keys: the high and low parts into one accumulator
+        f32x16 sm[2];
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) sm[mb][v] = 0.f;
+        const int kro = (lane & 31) * STR + 8 * (lane >> 5);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb) {
+            const int ko = kro + mb * 32 * STR + 16 * ks;
+            sm[mb] = mfma32(*reinterpret_cast<const bf16x8*>(sK0 + ko), qf[ks], sm[mb]);
+            sm[mb] = mfma32(*reinterpret_cast<const bf16x8*>(sK1 + ko), qf[ks], sm[mb]);
+          }
+        float mx = kNegInf;
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int J = m0 + mb * 32 + 8 * (v >> 2) + 4 * hs + (v & 3);
+            const int t0 = J * a.kpb;   // a kept block sets the bits of all its tiles
+            const bool pruned =
+                rvalid && J < n_gb && !((sMask[t0 >> 6] >> (t0 & 63)) & 1ull);
+            const float x = pruned ? sm[mb][v] + a.mean_bias : kNegInf;
+            sm[mb][v] = x;
+            mx = fmaxf(mx, x);
+          }
+        float alpha = 1.f;
+        if (update_reference(st, half_max(mx), c, alpha)) {
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) o[md][v] *= alpha;
+          st.l *= alpha;
+        }
+        bf16x8 pm[4], vb[3], dummy[4];
+        float sum = 0.f, dsum = 0.f;
+#pragma unroll
+        for (int pi = 0; pi < kPairs; ++pi) exp_pair(pi, sm, -st.mref * c, c, pm, sum);
+        st.l += sum;
+        pv_prefetch<D>(sV0, vb, lane);
+        pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sV0, pm, o, vb, sm, 0.f, c, dummy,
+                                        dsum, lane, [](int) {});
+      }
+    }
   }
 
   // ---- epilogue: O / l (renormalised over kept + diagonal), kept counts ----
@@ -1261,6 +1337,72 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block means for mean correction ("FlashPrefill V2", mean correction): the mean key and mean
+// value of every whole gate block of every (batch, KV head). The mean key goes out as two bf16
+// parts, hi = bf16(mean) and lo = bf16(mean - hi), so that the stand-in's logit keeps about 16
+// mantissa bits through the bf16 MFMA; the mean value as one bf16 row. One wave per block:
+// lane l sums dims 8 (l % LPR) .. + 7 over rows l / LPR, l / LPR + RPI, .. in fp32 (16-byte
+// loads, RPI rows per load), then the lanes of equal l % LPR add up their sums. A streaming
+// read of K and V once: HBM-bound.
+// ---------------------------------------------------------------------------------------------
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void block_mean_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 8;          // lanes per row
+  constexpr int RPI = 64 / LPR;       // rows per load
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int per = (a.mean_blocks + 3) / 4;    // workgroups per (batch, KV head)
+  const int bg = blockIdx.x / per;
+  const int J = (blockIdx.x % per) * 4 + w;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const Seq sq = seq_of(a, b);
+  const int bkeys = a.kpb * kBlockK;
+  if (J >= min(sq.Nk / bkeys, a.mean_blocks)) return;   // past this sequence's whole blocks
+  const long long kst = a.ks[1], vst = a.vs[1];
+  const __bf16* const Kb = static_cast<const __bf16*>(a.k) + sq.k + g * a.ks[2];
+  const __bf16* const Vb = static_cast<const __bf16*>(a.v) + sq.v + g * a.vs[2];
+  const int col = (lane % LPR) * 8;
+  float ksum[8], vsum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) ksum[e] = vsum[e] = 0.f;
+#pragma unroll 4
+  for (int r = lane / LPR; r < bkeys; r += RPI) {
+    const int key = J * bkeys + r;
+    const int t = key / kBlockK, rt = key % kBlockK;
+    const bf16x8 kx = *reinterpret_cast<const bf16x8*>(
+        Kb + tile_offset<PAGED>(a, b, t, kst, a.ks[0]) + rt * kst + col);
+    const bf16x8 vx = *reinterpret_cast<const bf16x8*>(
+        Vb + tile_offset<PAGED>(a, b, t, vst, a.vs[0]) + rt * vst + col);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ksum[e] += (float)kx[e];
+      vsum[e] += (float)vx[e];
+    }
+  }
+#pragma unroll
+  for (int x = LPR; x < 64; x <<= 1)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      ksum[e] += __shfl_xor(ksum[e], x);
+      vsum[e] += __shfl_xor(vsum[e], x);
+    }
+  if (lane < LPR) {
+    const float inv = 1.f / (float)bkeys;    // a power of two: exact
+    bf16x8 hi, lo, vm;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float mk = ksum[e] * inv;
+      hi[e] = (__bf16)mk;
+      lo[e] = (__bf16)(mk - (float)hi[e]);
+      vm[e] = (__bf16)(vsum[e] * inv);
+    }
+    const long long o = (((long long)b * a.Hkv + g) * a.mean_blocks + J) * D + col;
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.kbar_hi) + o) = hi;
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.kbar_lo) + o) = lo;
+    *reinterpret_cast<bf16x8*>(static_cast<__bf16*>(a.vbar) + o) = vm;
+  }
+}
+
 template <int D, int BQ, int NW, bool PAGED>
 hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
   const dim3 grid(a.units * a.nqb), block(NW * 64);
@@ -1271,7 +1413,10 @@ hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stre
     case kAbsolute:
     case kAbsVote:
       if constexpr (NW == BQ / kRows) {   // one head per workgroup
-        if (gate == kAbsolute)
+        if (gate == kAbsolute && a.kbar_hi)
+          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute, PAGED, true>), grid, block, 0,
+                             stream, a);
+        else if (gate == kAbsolute)
           hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute, PAGED>), grid, block, 0,
                              stream, a);
         else
@@ -1348,6 +1493,14 @@ hipError_t launch_calibrate_tile(const CalibArgs& a, int nw, hipStream_t stream)
 template <int D, int BQ>
 hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream) {
   return launch_sweep_hpw<D, BQ>(a, hpw, stream);
+}
+
+template <int D, bool PAGED>
+hipError_t launch_means_tile(const PrefillArgs& a, hipStream_t stream) {
+  const int per = (a.mean_blocks + 3) / 4;
+  hipLaunchKernelGGL((block_mean_kernel<D, PAGED>), dim3(a.B * a.Hkv * per), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace bsfa

@@ -54,6 +54,15 @@ struct PrefillArgs {
   // iterations stay at 64 keys; decisions, kept counts and the statistic dump are per block,
   // and a kept block sets the mask bits of all its tiles. nkb counts gate blocks.
   int kpb;
+  // Mean correction (ABSOLUTE walk): the mean key of every whole gate block as two bf16 parts
+  // (kbar_hi = bf16(mean), kbar_lo = bf16(mean - kbar_hi)) and its mean value, each
+  // [B][Hkv][mean_blocks][D]; kbar_hi == nullptr: no correction. mean_bias = ln(block keys) /
+  // scale, the stand-in logit's shift in raw score units.
+  void* kbar_hi;
+  void* kbar_lo;
+  void* vbar;
+  int mean_blocks;
+  float mean_bias;
 };
 
 struct CalibArgs {
@@ -101,6 +110,10 @@ hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hi
 int gate_sweep_heads(int block_q, int group);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 
+// Block means for mean correction: fills a.kbar_hi, a.kbar_lo and a.vbar for every whole gate
+// block of every (batch, KV head) (a.mean_blocks per sequence at most).
+hipError_t launch_block_means(const PrefillArgs& a, int head_dim, hipStream_t stream);
+
 // Launchers of one (head dimension D, query tile BQ[, paged K/V]) instantiation; each is defined
 // in its own translation unit. nw = waves per workgroup, hpw = heads per sweep workgroup.
 template <int D, int BQ, bool PAGED>
@@ -109,5 +122,7 @@ template <int D, int BQ>
 hipError_t launch_calibrate_tile(const CalibArgs& a, int nw, hipStream_t stream);
 template <int D, int BQ>
 hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream);
+template <int D, bool PAGED>
+hipError_t launch_means_tile(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace bsfa

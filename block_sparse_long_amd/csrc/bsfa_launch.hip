@@ -62,6 +62,14 @@ hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipSt
                         : launch_calibrate_tile<64, 64>(a, nw, stream);
 }
 
+hipError_t launch_block_means(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+  if (a.pages)
+    return head_dim == 128 ? launch_means_tile<128, true>(a, stream)
+                           : launch_means_tile<64, true>(a, stream);
+  return head_dim == 128 ? launch_means_tile<128, false>(a, stream)
+                         : launch_means_tile<64, false>(a, stream);
+}
+
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, p);
   return hipGetLastError();

@@ -97,6 +97,17 @@ typedef struct {
                               * range and the threshold column (P/Bq + i) use absolute positions,
                               * and the absolute gate needs P % Bq == 0 (thresholds live on the
                               * calibration's tile grid). K and V hold Nk rows. */
+  int32_t mean_correction;   /* 0 or 1. 1: every pruned off-diagonal gate block J adds a
+                              * zero-order stand-in, |B_J| e^{s_J} vbar_J to the numerator and
+                              * |B_J| e^{s_J} to the denominator, with kbar_J, vbar_J the block's
+                              * mean key and value, s_J = softmax_scale * q . kbar_J and |B_J| its
+                              * keys ("FlashPrefill V2: Block-Sparse Prefill Attention for
+                              * Long-Context LLM Serving", mean correction). Needs ABSOLUTE with
+                              * a 16-byte-aligned workspace, which then also holds the block means
+                              * (bsfa_prefill_workspace_bytes counts them); RELATIVE (whose
+                              * decisions read the running max a stand-in would move) and
+                              * ABSOLUTE without a workspace return BSFA_ERR_UNSUPPORTED. DENSE
+                              * prunes nothing: no effect. */
 } bsfa_problem;
 
 /* One layer's threshold table (the offline calibration artifact), fp32 in device memory.
@@ -117,7 +128,9 @@ typedef struct {
 
 /* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
  * ABSOLUTE, one keep bitmask per (b, h, i) with one bit per 64-key tile,
- * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words. */
+ * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words; with mean_correction, then (each
+ * part starting on a 256-byte boundary) three bf16 arrays [B][Hkv][floor(Nk/Bk)][d]: the
+ * block means of K in two parts (high and low bf16) and of V. */
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
 
 /* Gated causal prefill attention (the method's hot path).
@@ -143,7 +156,8 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 decisions of all blocks are made in a separate launch first (scores only),
  *                 and the softmax launch then walks the kept blocks; without one, both happen
  *                 in one launch. The results are the same. A non-NULL workspace that is too
- *                 small is an error (BSFA_ERR_ARG).
+ *                 small is an error (BSFA_ERR_ARG). With mean_correction it is required and
+ *                 must be 16-byte aligned; a third launch computes the block means.
  *   stream        hipStream_t
  * The absolute gate supports Nk up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
  * Returns BSFA_OK or an error status (see the conventions above). */
@@ -215,7 +229,8 @@ bsfa_status bsfa_prefill_paged(const bsfa_problem* p, const void* Q, const void*
  *   keep_mask     device uint64 [B][Hq][ceil(N/Bq)][W], W = ceil(ceil(Nk/64)/64), 8-byte
  *                 aligned, one bit per 64-key tile (a kept 128-key block sets both of its
  *                 tiles); every word is written (bits past the off-diagonal tiles are zero)
- *   mask_bytes    size of keep_mask; at least bsfa_prefill_workspace_bytes(p, ABSOLUTE)
+ *   mask_bytes    size of keep_mask; at least B * Hq * ceil(N/Bq) * W * 8 (mean_correction
+ *                 is ignored here)
  *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
  *   stream        hipStream_t
  * This is the first of the two launches bsfa_prefill makes when given a workspace; on its own

@@ -311,3 +311,33 @@ def test_stored_tables_load(golden_dir):
                 for i in range(t.t_len):
                     n_off = (i * t.block_q) // t.block_k
                     assert np.isneginf(t.T[kk, :, i]).all() == (n_off < k)
+
+
+def test_mean_correction_workspace_and_validation():
+    lib = _lib.load_library()
+    p = problem(N=1000)
+    masks = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    p.mean_correction = 1
+    need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    # masks, then three [B][Hkv][floor(Nk / Bk)][d] bf16 arrays, each on a 256-byte boundary
+    part = p.batch * p.heads_kv * (1000 // 64) * p.head_dim * 2
+    r256 = lambda x: -(-x // 256) * 256
+    assert need == r256(masks) + 3 * r256(part)
+    for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+    abs_call = dict(tbl=table(t_len=8), mode=_lib.BSFA_GATE_ABSOLUTE)
+    # the block means live in the workspace: none, or an 8-byte-aligned one, is refused
+    assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_UNSUPPORTED
+    assert "workspace" in _lib.bsfa_last_error()
+    assert call_prefill(p, ws=FAKE + 8, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, ws=FAKE, ws_bytes=need - 1, **abs_call) == _lib.BSFA_ERR_ARG
+    # the relative gate's decisions depend on the running max: no stand-ins there
+    assert call_prefill(p, mode=_lib.BSFA_GATE_RELATIVE, log_lambda=-1.0) == \
+        _lib.BSFA_ERR_UNSUPPORTED
+    assert "absolute" in _lib.bsfa_last_error()
+    p.mean_correction = 2
+    assert call_prefill(p) == _lib.BSFA_ERR_ARG
+    # the gate masks need only the masks
+    p.mean_correction = 1
+    assert call_masks(p, table(t_len=8), mask_bytes=masks - 8) == _lib.BSFA_ERR_ARG
+    assert f"required {masks}" in _lib.bsfa_last_error()
