@@ -26,6 +26,9 @@ Sources (page title, then the part of the page followed):
     correction (a pruned block J stands in as |B_J| copies of its mean key and mean value:
     |B_J| e^{s_J} vbar_J joins the numerator and |B_J| e^{s_J} the denominator, i.e. one more
     online-softmax step on a single logit shifted by log|B_J|).
+  * FP8 (e4m3) scores for the gate (FlashPrefill V2's FP8 path quantises on the fly; the
+    format is OCP FP8 E4M3: 4 exponent bits with bias 7, 3 mantissa bits, largest finite value
+    448, subnormal spacing 2^-9, no infinities).
   * "Skipping attention blocks was the easy part" (BLASST blog), sections "FlashAttention"
     (running max m, running sum l, accumulator O, rescale by exp(m_old - m_new)) and
     "Vote, then skip" (skip iff block max minus running max < ln(lambda); any row that wants
@@ -51,6 +54,12 @@ Readings taken where the pages are silent or ambiguous (each is listed in the de
     diagonal region always runs exactly); the stand-in step takes the pruned block's place in
     the ascending block order. It is defined for the absolute gate (whose decisions do not
     depend on the softmax state), not for the relative gate.
+
+  * FP8 gate: only the gate statistic of off-diagonal blocks uses FP8 scores; the softmax
+    and the output use the exact scores of the kept blocks. Q is quantised per (token, head)
+    row and K per (64-key tile, KV head), each with scale amax / 448 (codes = x * (448 / amax)
+    rounded to nearest even, all in float32; an all-zero row or tile has codes 0 and scale 0),
+    and a score is (q8 . k8) * scale_q(row) * scale_k(tile) * softmax_scale.
 
 Pins (tests that tie each function to something other than itself) are in
 tests/test_oracle_pins.py; every public function here is pinned.
@@ -109,12 +118,70 @@ class OracleResult:
     margin: np.ndarray       # [B, Hq, nqb, nkb] stat - threshold (off-diagonal only); NaN elsewhere
 
 
+E4M3_MAX = 448.0
+
+
+def quantize_e4m3(x) -> np.ndarray:
+    """Round float32 values to the nearest E4M3 value (ties to even), saturating at +-448.
+
+    E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; normal values 2^e (1 + m/8) for
+    e = -6 .. 8 (the largest finite one 448 = 2^8 * 1.75), subnormals m * 2^-9. The grid step
+    near |x| is 2^(max(e, -6) - 3) with e = floor(log2 |x|); rounding to that step is exact in
+    float64 and numpy rounds halves to even. Returns float32.
+    """
+    x = np.asarray(x, dtype=np.float32).astype(np.float64)
+    a = np.abs(x)
+    with np.errstate(divide="ignore"):
+        e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    step = np.exp2(np.maximum(e, -6.0) - 3.0)
+    q = np.round(a / step) * step
+    q = np.minimum(q, E4M3_MAX)
+    return (np.sign(x) * q).astype(np.float32)
+
+
+def _e4m3_codes(x, amax):
+    """Codes of x (float32) against a float32 amax (broadcast): x * (448 / amax), rounded; and
+    the scale amax / 448. amax == 0 gives codes 0 and scale 0."""
+    x = np.asarray(x, dtype=np.float32)
+    amax = np.asarray(amax, dtype=np.float32)
+    safe = np.where(amax > 0, amax, np.float32(1))
+    inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
+    y = np.clip((x * inv).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+    scale = np.where(amax > 0, safe / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
+    return quantize_e4m3(y), scale
+
+
+def quantize_q_rows(Q):
+    """FP8 copy of Q [B, N, Hq, d]: codes [B, N, Hq, d] (float32 values of E4M3) and one scale
+    per (b, token, head) row, [B, N, Hq]."""
+    Q = np.asarray(Q, dtype=np.float32)
+    amax = np.abs(Q).max(axis=-1)
+    codes, scale = _e4m3_codes(Q, amax[..., None])
+    return codes, scale[..., 0]
+
+
+def quantize_k_tiles(K, tile: int = 64):
+    """FP8 copy of K [B, Nk, Hkv, d]: codes [B, Nk, Hkv, d] and one scale per (b, 64-key tile,
+    KV head), [B, ceil(Nk / 64), Hkv] (a last short tile uses its own keys)."""
+    K = np.asarray(K, dtype=np.float32)
+    B, Nk, Hkv, d = K.shape
+    nt = num_blocks(Nk, tile)
+    codes = np.zeros_like(K)
+    scales = np.zeros((B, nt, Hkv), dtype=np.float32)
+    for t in range(nt):
+        c0, c1 = t * tile, min((t + 1) * tile, Nk)
+        amax = np.abs(K[:, c0:c1]).max(axis=(1, 3))                    # [B, Hkv]
+        codes[:, c0:c1], sc = _e4m3_codes(K[:, c0:c1], amax[:, None, :, None])
+        scales[:, t] = sc[:, 0, :, 0]
+    return codes, scales
+
+
 def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                    scale: float | None = None, table: np.ndarray | None = None,
                    budget_slice: int = 0, log_lambda: float = -math.inf,
                    forced_keep: np.ndarray | None = None, band: float = 1e-2,
                    query_blocks=None, mean_correction: bool = False,
-                   dtype=np.float32) -> OracleResult:
+                   gate_dtype: str = "bf16", dtype=np.float32) -> OracleResult:
     """Gated causal prefill attention, one (b, h, i) work unit at a time.
 
     Q: [B, Nq, Hq, d]; K, V: [B, Nk, Hkv, d] with Nk >= Nq and Hq % Hkv == 0. The query rows
@@ -128,6 +195,8 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     query_blocks: optional iterable of query-block indices to compute (default: all).
     mean_correction: a pruned block adds its zero-order stand-in (FlashPrefill V2's mean
     correction) instead of nothing.
+    gate_dtype: "bf16" (the exact scores) or "fp8" (the absolute gate's off-diagonal block
+    maxima from E4M3 copies of Q and K; see quantize_q_rows / quantize_k_tiles).
     """
     if mode not in _MODES:
         raise ValueError(f"unknown gate mode {mode!r}")
@@ -143,6 +212,10 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
         raise ValueError("absolute gate needs a threshold table")
     if mode == GATE_ABSOLUTE and P % block_q != 0:
         raise ValueError("the absolute gate needs the prefix to be a multiple of block_q")
+    if gate_dtype not in ("bf16", "fp8"):
+        raise ValueError(f"unknown gate dtype {gate_dtype!r}")
+    if gate_dtype == "fp8" and mode == GATE_RELATIVE:
+        raise ValueError("FP8 gate scores are defined for the absolute gate")
     if mean_correction and mode == GATE_RELATIVE:
         # the relative gate decides from the running max, which a stand-in step would move
         raise ValueError("mean correction is defined for the dense and absolute gates only")
@@ -151,6 +224,10 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     nqb, nkb = num_blocks(N, block_q), num_blocks(Nk, block_k)
     blocks = range(nqb) if query_blocks is None else sorted(set(int(x) for x in query_blocks))
 
+    if gate_dtype == "fp8":
+        q8, q8s = quantize_q_rows(Q)
+        k8, k8s = quantize_k_tiles(K)
+        k8s_key = np.repeat(k8s, 64, axis=1)[:, :Nk]               # [B, Nk, Hkv]: its tile's
     out = np.full((B, N, Hq, d), np.nan, dtype=dtype)
     kept_counts = np.full((B, Hq, nqb), -1, dtype=np.int64)
     stat = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
@@ -203,6 +280,14 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                                 # wants the block vetoes the skip
                                 st = float((rmax - m).max())
                                 thr = float(log_lambda)
+                            elif gate_dtype == "fp8" and mode == GATE_ABSOLUTE:
+                                # the same tile maximum over FP8 scores
+                                s8 = (q8[b, r0:r1, h, :].astype(np.float64)
+                                      @ k8[b, c0:c1, g, :].T.astype(np.float64))
+                                s8 *= q8s[b, r0:r1, h, None].astype(np.float64)
+                                s8 *= k8s_key[b, None, c0:c1, g].astype(np.float64)
+                                st = float(s8.max()) * float(sc)
+                                thr = te
                             else:
                                 st = float(rmax.max())            # s_max over the whole tile
                                 thr = te if mode == GATE_ABSOLUTE else -math.inf
@@ -291,14 +376,20 @@ def gather_pages(pages, block_table, kv_lens):
 
 
 def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float | None = None,
-                              dtype=np.float32) -> np.ndarray:
+                              dtype=np.float32, gate_dtype: str = "bf16") -> np.ndarray:
     """s_max[b, h, i, j] for every off-diagonal block j < n_off(i); NaN elsewhere.
 
     The maximum of the scaled pre-softmax scores over the whole Bq x Bk tile
     ("Block Sparse Flash Attention", Method > Key Designs 2, keep-rule equation). The scores of
     one (b, h, i) against all its off-diagonal keys come from one matrix product, then each
-    Bk-wide column group is reduced.
+    Bk-wide column group is reduced. gate_dtype "fp8": the scores of the FP8 gate (E4M3 copies
+    of Q and K and their scales, as in oracle_prefill).
     """
+    fp8 = gate_dtype == "fp8"
+    if fp8:
+        q8, q8s = quantize_q_rows(Q)
+        k8, k8s = quantize_k_tiles(K)
+        k8s_key = np.repeat(k8s, 64, axis=1)[:, :np.asarray(K).shape[1]]
     Q = np.asarray(Q, dtype=dtype)
     K = np.asarray(K, dtype=dtype)
     B, N, Hq, d = Q.shape
@@ -315,7 +406,15 @@ def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float 
                 if n_off == 0:
                     continue
                 r0, r1 = i * block_q, min((i + 1) * block_q, N)
-                s = (Q[b, r0:r1, h, :] @ K[b, :n_off * block_k, g, :].T) * sc
+                c1 = n_off * block_k
+                if fp8:
+                    s = (q8[b, r0:r1, h, :].astype(np.float64)
+                         @ k8[b, :c1, g, :].T.astype(np.float64))
+                    s *= q8s[b, r0:r1, h, None].astype(np.float64)
+                    s *= k8s_key[b, None, :c1, g].astype(np.float64)
+                    s *= float(sc)
+                else:
+                    s = (Q[b, r0:r1, h, :] @ K[b, :c1, g, :].T) * sc
                 sm[b, h, i, :n_off] = s.reshape(r1 - r0, n_off, block_k).max(axis=(0, 2))
     return sm
 
@@ -332,14 +431,15 @@ def kth_highest(maxima: np.ndarray, n_off: int, k: int) -> float:
 
 
 def calibrate(samples, *, block_q: int, block_k: int, budgets, scale: float | None = None,
-              dtype=np.float32) -> np.ndarray:
+              dtype=np.float32, gate_dtype: str = "bf16") -> np.ndarray:
     """Offline threshold calibration: T[n_budgets][Hq][T_len] (float32).
 
     samples: iterable of (Q, K) pairs of equal shape [B, N, Hq, d] / [B, N, Hkv, d]; every
     batch entry counts as one calibration sample. For each sample, head and query block the
     k-th highest off-diagonal block maximum is taken; thresholds are the arithmetic mean over
     samples ("Block Sparse Flash Attention", Method > Key Designs 1). T_len = number of query
-    blocks of the calibration length.
+    blocks of the calibration length. gate_dtype "fp8" calibrates against the FP8 gate's
+    block maxima (thresholds are bound to the scores they were measured on).
     """
     budgets = [int(k) for k in budgets]
     acc = None
@@ -352,7 +452,7 @@ def calibrate(samples, *, block_q: int, block_k: int, budgets, scale: float | No
         elif Q.shape[1:] != shape0[1:]:
             raise ValueError("calibration samples must share one shape")
         sm = off_diagonal_block_maxima(Q, K, block_q=block_q, block_k=block_k, scale=scale,
-                                       dtype=dtype)
+                                       dtype=dtype, gate_dtype=gate_dtype)
         B, Hq, nqb, _ = sm.shape
         N = Q.shape[1]
         if acc is None:

@@ -11,6 +11,7 @@ import os
 
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from oracle import (GATE_ABSOLUTE, GATE_DENSE, GATE_RELATIVE, calibrate, key_block_range,
@@ -695,3 +696,185 @@ def test_mean_correction_refuses_the_relative_gate():
     with pytest.raises(ValueError):
         oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_RELATIVE, log_lambda=-1.0,
                        mean_correction=True)
+
+
+# ---------------------------------------------------------------------------------------------
+# FP8 (E4M3) gate scores
+# ---------------------------------------------------------------------------------------------
+def _e4m3_positive_grid():
+    """Every finite positive E4M3 value from the format's definition: subnormals m 2^-9
+    (m = 1..7) and normals 2^e (1 + m/8), e = -6..8, without the top code (e = 8, m = 7)."""
+    vals = [m * 2.0 ** -9 for m in range(1, 8)]
+    vals += [2.0 ** e * (1 + m / 8) for e in range(-6, 9) for m in range(8)
+             if not (e == 8 and m == 7)]
+    return np.array(sorted(vals))
+
+
+def test_e4m3_grid_fixed_points_and_ties_to_even():
+    grid = _e4m3_positive_grid()
+    assert len(grid) == 126 and grid[-1] == 448.0
+    full = np.concatenate([-grid[::-1], [0.0], grid])
+    np.testing.assert_array_equal(oracle.quantize_e4m3(full), full.astype(np.float32))
+    # a midpoint goes to the neighbour whose last mantissa bit is 0
+    mids = 0.5 * (grid[:-1] + grid[1:])
+    got = oracle.quantize_e4m3(mids)
+    k = np.arange(len(mids))
+    even_lo = (k % 2 == 0)          # grid[k] has an even code when k is even (k = code - 1)
+    # code of grid[k] is k + 1: even code when k is odd
+    want = np.where((k + 1) % 2 == 0, grid[:-1], grid[1:])
+    np.testing.assert_array_equal(got, want.astype(np.float32))
+    assert even_lo.any()
+    # just off the midpoint: plain nearest
+    np.testing.assert_array_equal(oracle.quantize_e4m3(mids * (1 + 1e-6)), grid[1:].astype(np.float32))
+    np.testing.assert_array_equal(oracle.quantize_e4m3(mids * (1 - 1e-6)), grid[:-1].astype(np.float32))
+
+
+def test_e4m3_matches_torch_float8_conversion():
+    rng = np.random.default_rng(40)
+    x = np.concatenate([rng.uniform(-448, 448, 100000),
+                        rng.standard_normal(100000) * 0.01,
+                        np.linspace(-2.0 ** -5, 2.0 ** -5, 20001)]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).float().numpy()
+    np.testing.assert_array_equal(oracle.quantize_e4m3(x), ref)
+
+
+def test_q_rows_and_k_tiles_quantisation():
+    rng = np.random.default_rng(41)
+    Q = rng.standard_normal((2, 70, 3, 32)).astype(np.float32)
+    Q[1, 5, 2] = 0.0                                     # an all-zero row
+    K = rng.standard_normal((2, 150, 2, 32)).astype(np.float32)
+    K[0, 64:128, 1] = 0.0                                # an all-zero tile of one head
+    for X, (codes, scale), axes in ((Q, oracle.quantize_q_rows(Q), None),
+                                    (K, oracle.quantize_k_tiles(K), "tiles")):
+        assert np.abs(codes).max() <= 448
+        if axes is None:
+            amax = np.abs(X).max(-1)
+            deq = codes * scale[..., None]
+            # the largest element of each nonzero row becomes +-448 exactly
+            nz = amax > 0
+            np.testing.assert_array_equal(np.abs(codes).max(-1)[nz], 448.0)
+            np.testing.assert_array_equal(scale, np.where(nz, amax / np.float32(448), 0))
+            assert (codes[~nz] == 0).all()
+        else:
+            nt = -(-X.shape[1] // 64)
+            assert scale.shape == (2, nt, 2)
+            for t in range(nt):
+                blk = np.abs(X[:, t * 64:(t + 1) * 64]).max(axis=(1, 3))
+                np.testing.assert_array_equal(scale[:, t], blk / np.float32(448))
+            deq = codes * np.repeat(scale, 64, axis=1)[:, :X.shape[1], :, None]
+            assert (codes[0, 64:128, 1] == 0).all() and scale[0, 1, 1] == 0
+        # relative error 2^-4 for values in E4M3's normal range, absolute 2^-10 * scale below
+        s_b = scale[..., None] if axes is None else np.repeat(scale, 64, axis=1)[:, :X.shape[1], :, None]
+        bound = np.maximum(np.abs(X) * 2.0 ** -4, 2.0 ** -10 * s_b) * (1 + 1e-6)
+        assert (np.abs(deq - X) <= bound).all()
+
+
+def _representable_inputs(rng, B, N, Hq, Hkv, d):
+    """Q rows and K tiles whose FP8 copies are exact: E4M3 values times a power of two, with one
+    element of each row / tile at +-448 times that power (so amax / 448 is the power)."""
+    grid = _e4m3_positive_grid()
+    def draw(shape):
+        v = rng.choice(grid[40:], size=shape) * rng.choice([-1.0, 1.0], size=shape)
+        return v.astype(np.float32)
+    Q = draw((B, N, Hq, d))
+    Q[..., 0] = 448.0
+    Q *= (2.0 ** rng.integers(-9, -5, size=(B, N, Hq, 1))).astype(np.float32)
+    K = draw((B, N, Hkv, d))
+    for t in range(-(-N // 64)):
+        K[:, t * 64, :, 0] = -448.0
+        K[:, t * 64:(t + 1) * 64] *= (2.0 ** rng.integers(-9, -5, size=(B, 1, Hkv, 1))).astype(np.float32)
+    return Q, K
+
+
+def test_fp8_gate_equals_exact_gate_on_representable_inputs():
+    rng = np.random.default_rng(42)
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 520, 4, 2, 32, 128, 64
+    Q, K = _representable_inputs(rng, B, N, Hq, Hkv, d)
+    V = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    q8, qs = oracle.quantize_q_rows(Q)
+    np.testing.assert_array_equal(q8 * qs[..., None], Q)
+    k8, ks = oracle.quantize_k_tiles(K)
+    np.testing.assert_array_equal(k8 * np.repeat(ks, 64, axis=1)[:, :N, :, None], K)
+    bm = brute_block_max(Q, K, Bq, Bk)
+    T = _midpoint_table(bm, Hq, -(-N // Bq), np.random.default_rng(43))
+    kw = dict(block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T, dtype=np.float64)
+    a = oracle_prefill(Q, K, V, gate_dtype="fp8", **kw)
+    b = oracle_prefill(Q, K, V, **kw)
+    np.testing.assert_array_equal(a.keep, b.keep)
+    np.testing.assert_allclose(a.stat, b.stat, rtol=1e-12, atol=0)
+    np.testing.assert_array_equal(a.out, b.out)
+
+
+@pytest.mark.parametrize("Bk", [64, 128])
+def test_fp8_block_maxima_brute_force(Bk):
+    # one full score matrix of the dequantised copies, then block maxima
+    rng = np.random.default_rng(44)
+    B, N, Hq, Hkv, d, Bq = 1, 600, 4, 2, 32, 128
+    Q = rng.standard_normal((B, N, Hq, d)).astype(np.float32)
+    K = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    V = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    q8, qs = oracle.quantize_q_rows(Q)
+    k8, ks = oracle.quantize_k_tiles(K)
+    Qd = (q8 * qs[..., None]).astype(np.float64)
+    Kd = (k8 * np.repeat(ks, 64, axis=1)[:, :N, :, None]).astype(np.float64)
+    bm = brute_block_max(Qd, Kd, Bq, Bk)
+    sm = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, gate_dtype="fp8")
+    T = _const_table(math.inf, Hq, 8)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T,
+                       gate_dtype="fp8")
+    for i in range(-(-N // Bq)):
+        n_off = key_block_range(i, N, Bq, Bk)[0]
+        # (the oracle holds the softmax scale in float32, as the device does: 2^-24 relative)
+        np.testing.assert_allclose(sm[:, :, i, :n_off], bm[:, :, i, :n_off], rtol=2e-7, atol=0)
+        np.testing.assert_allclose(r.stat[:, :, i, :n_off], bm[:, :, i, :n_off], rtol=2e-7,
+                                   atol=0)
+
+
+def test_fp8_block_maxima_within_the_quantisation_bound():
+    rng = np.random.default_rng(45)
+    B, N, Hq, Hkv, d, Bq, Bk = 1, 512, 2, 1, 64, 64, 64
+    Q = rng.standard_normal((B, N, Hq, d)).astype(np.float32) * 1.5
+    K = rng.standard_normal((B, N, Hkv, d)).astype(np.float32)
+    sc = 1 / math.sqrt(d)
+    exact = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, dtype=np.float64)
+    fp8 = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, gate_dtype="fp8")
+    _, qs = oracle.quantize_q_rows(Q)
+    _, ks = oracle.quantize_k_tiles(K)
+    # per element error <= max(2^-4 |x|, 2^-10 scale): bound sum_d |dq||k| + |q||dk| + |dq||dk|
+    eq = np.maximum(np.abs(Q) * 2.0 ** -4, 2.0 ** -10 * qs[..., None])
+    ek = np.maximum(np.abs(K) * 2.0 ** -4, 2.0 ** -10 * np.repeat(ks, 64, axis=1)[:, :N, :, None])
+    for i in range(N // Bq):
+        for h in range(Hq):
+            q, dq = np.abs(Q[0, i * Bq:(i + 1) * Bq, h]), eq[0, i * Bq:(i + 1) * Bq, h]
+            k, dk = np.abs(K[0, :i * Bq, 0]), ek[0, :i * Bq, 0]
+            if i == 0:
+                continue
+            bound = (dq @ k.T + q @ dk.T + dq @ dk.T) * sc
+            bmax = bound.reshape(Bq, i, Bk).max(axis=(0, 2))
+            diff = np.abs(fp8[0, h, i, :i] - exact[0, h, i, :i])
+            assert (diff <= bmax * (1 + 1e-6) + 1e-9).all()
+            assert diff.max() > 0                                 # it is not the exact gate
+
+
+@pytest.mark.parametrize("k", [1, 3])
+def test_fp8_calibration_keeps_exactly_k_under_the_fp8_gate(k):
+    Q, K, V = _exact_sample(46)
+    Bq, Bk = 64, 64
+    T = calibrate([(Q, K)], block_q=Bq, block_k=Bk, budgets=[k], gate_dtype="fp8")
+    # FP8 maxima are not float32 numbers: the stored threshold may round above the k-th
+    # maximum itself, so take it one float32 step lower
+    T = np.nextafter(T, np.float32(-np.inf)).astype(np.float32)
+    r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T,
+                       gate_dtype="fp8")
+    N = Q.shape[1]
+    for i in range(-(-N // Bq)):
+        n_off = key_block_range(i, N, Bq, Bk)[0]
+        want = k if n_off >= k else n_off
+        assert (r.kept_counts[:, :, i] == want).all(), (i, r.kept_counts[:, :, i])
+
+
+def test_fp8_gate_refuses_the_relative_gate():
+    Q, K, V = _rand(47, 1, 128, 1, 1, 16)
+    with pytest.raises(ValueError):
+        oracle_prefill(Q, K, V, block_q=64, block_k=64, mode=GATE_RELATIVE, log_lambda=-1.0,
+                       gate_dtype="fp8")
