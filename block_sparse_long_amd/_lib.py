@@ -25,6 +25,8 @@ BSFA_GATE_RELATIVE = 2
 
 BSFA_BF16 = 0
 BSFA_FP32 = 1
+BSFA_FP8_E4M3 = 2
+GATE_DTYPES = {"bf16": BSFA_BF16, "fp8": BSFA_FP8_E4M3}
 
 GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
               "relative": BSFA_GATE_RELATIVE}
@@ -46,6 +48,7 @@ class BsfaProblem(ctypes.Structure):
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
         ("kv_seqlen", ctypes.c_int32), ("mean_correction", ctypes.c_int32),
+        ("gate_dtype", ctypes.c_int32),
     ]
 
 
@@ -144,7 +147,8 @@ def _stream_handle(stream, device) -> int:
 
 
 def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
-                 softmax_scale: float = 0.0, mean_correction: bool = False) -> BsfaProblem:
+                 softmax_scale: float = 0.0, mean_correction: bool = False,
+                 gate_dtype="bf16") -> BsfaProblem:
     import torch
     p = BsfaProblem()
     p.batch, p.seqlen, p.heads_q, p.head_dim = (int(x) for x in Q.shape)
@@ -154,6 +158,7 @@ def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
     p.block_q, p.block_k = int(block_q), int(block_k)
     p.softmax_scale = float(softmax_scale)
     p.mean_correction = int(bool(mean_correction))
+    p.gate_dtype = GATE_DTYPES[gate_dtype] if isinstance(gate_dtype, str) else int(gate_dtype)
     dt = {torch.bfloat16: BSFA_BF16, torch.float32: BSFA_FP32}
     p.in_dtype = dt.get(Q.dtype, -1)
     p.out_dtype = dt.get(O.dtype, -1) if O is not None else BSFA_BF16
@@ -170,7 +175,7 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                  table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
                  kept_counts=None, kept_total=None, debug_block_stat=None,
                  softmax_scale: float = 0.0, stream=None, out_dtype=None, workspace=None,
-                 mean_correction: bool = False):
+                 mean_correction: bool = False, gate_dtype="bf16"):
     """Run the gated prefill kernel. Q: [B, N, Hq, d] bf16; K, V: [B, Nk, Hkv, d] bf16 (device),
     Nk >= N (Nk > N: a chunk of N query rows after Nk - N cached keys).
 
@@ -181,7 +186,9 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
     device uint8 tensor of at least bsfa_prefill_workspace_bytes bytes for the absolute gate's
     keep masks (and, with ``mean_correction``, the block means); None allocates one, and an
     empty tensor asks for the path without it. ``mean_correction``: pruned blocks add their
-    mean-key / mean-value stand-ins (absolute gate with a workspace). Returns O.
+    mean-key / mean-value stand-ins (absolute gate with a workspace). ``gate_dtype`` "fp8":
+    the absolute gate scores E4M3 copies of Q and K (the table must be calibrated on the same
+    scores). Returns O.
     """
     import torch
     lib = load_library()
@@ -189,7 +196,8 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
         O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
     p = make_problem(Q, K, V, O, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
-                     mean_correction=mean_correction)
+                     mean_correction=mean_correction,
+                     gate_dtype=gate_dtype)
     tbl = None
     if table is not None:
         tbl = table.c_struct()
@@ -219,7 +227,8 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
                         gate_mode="dense", table=None, budget_slice: int = 0,
                         log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
                         debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
-                        out_dtype=None, workspace=None, mean_correction: bool = False):
+                        out_dtype=None, workspace=None, mean_correction: bool = False,
+                        gate_dtype="bf16"):
     """bsfa_prefill over sequences packed along the token axis. Q: [total_q, Hq, d] bf16;
     K, V: [total_k, Hkv, d] bf16; cu_seqlens_q / cu_seqlens_k: device int32 [B + 1] token
     offsets. Per-sequence outputs are padded to the longest sequence. Returns O."""
@@ -237,7 +246,8 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
     # the per-token views as [1, tokens, heads, dim] give the token and head strides
     p = make_problem(Q[None], K[None], V[None], O[None], block_q=block_q, block_k=block_k,
-                     softmax_scale=softmax_scale, mean_correction=mean_correction)
+                     softmax_scale=softmax_scale, mean_correction=mean_correction,
+                     gate_dtype=gate_dtype)
     p.batch = cu_seqlens_q.numel() - 1
     p.seqlen = int(max_seqlen_q)
     p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
@@ -272,7 +282,8 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
                        block_k: int = 64, gate_mode="dense", table=None, budget_slice: int = 0,
                        log_lambda: float = -math.inf, kept_counts=None, kept_total=None,
                        debug_block_stat=None, softmax_scale: float = 0.0, stream=None,
-                       out_dtype=None, workspace=None, mean_correction: bool = False):
+                       out_dtype=None, workspace=None, mean_correction: bool = False,
+                       gate_dtype="bf16"):
     """bsfa_prefill_varlen with K / V in a paged cache. Q: [total_q, Hq, d] bf16;
     K_pages, V_pages: [num_pages, page_size, Hkv, d] bf16; cu_seqlens_q: int32 [B + 1];
     kv_lens: int32 [B]; block_table: int32 [B, pages per sequence]. Returns O."""
@@ -292,7 +303,8 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
     p = make_problem(Q[None], K_pages[:, 0][None], V_pages[:, 0][None], O[None],
                      block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
-                     mean_correction=mean_correction)
+                     mean_correction=mean_correction,
+                     gate_dtype=gate_dtype)
     p.batch = kv_lens.numel()
     p.seqlen = int(max_seqlen_q)
     p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
@@ -326,28 +338,45 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
 
 def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block_q: int,
                     block_k: int = 64, debug_block_stat=None, softmax_scale: float = 0.0,
-                    stream=None):
+                    stream=None, gate_dtype="bf16"):
     """Keep bitmasks of the absolute gate: int64 [B, Hq, nqb, W] (bit j % 64 of word j // 64 set
     iff off-diagonal 64-key tile j is kept; a kept 128-key block sets both of its tiles);
-    allocated if None. Returns keep_mask."""
+    allocated if None. Returns keep_mask. With ``gate_dtype`` "fp8" the call also needs room
+    for the FP8 copies: keep_mask is then None or a contiguous 1-D buffer of at least
+    bsfa_prefill_workspace_bytes(..., gate_dtype="fp8") bytes, and the masks come back as a view
+    of its start."""
     import torch
     lib = load_library()
     B, N, Hq, _ = Q.shape
     nqb, ntile = -(-N // block_q), -(-int(K.shape[1]) // 64)   # one bit per 64-key tile
-    if keep_mask is None:
-        keep_mask = torch.empty((B, Hq, nqb, -(-ntile // 64)), dtype=torch.int64,
-                                device=Q.device)
+    shape = (B, Hq, nqb, -(-ntile // 64))
+    fp8 = (GATE_DTYPES[gate_dtype] if isinstance(gate_dtype, str) else int(gate_dtype)) \
+        == BSFA_FP8_E4M3
+    buf = None
+    if fp8:
+        nbytes = bsfa_prefill_workspace_bytes(Q, K, block_q=block_q, block_k=block_k,
+                                              gate_dtype="fp8")
+        buf = keep_mask if keep_mask is not None else torch.empty(nbytes, dtype=torch.uint8,
+                                                                  device=Q.device)
+        if not buf.is_contiguous() or buf.numel() * buf.element_size() < nbytes:
+            raise ValueError(f"an FP8 gate needs a contiguous buffer of {nbytes} bytes")
+        nbuf = buf.numel() * buf.element_size()
+        keep_mask = buf.view(torch.uint8)[:B * Hq * nqb * shape[3] * 8].view(torch.int64)
+        keep_mask = keep_mask.view(shape)
+    elif keep_mask is None:
+        keep_mask = torch.empty(shape, dtype=torch.int64, device=Q.device)
     if not keep_mask.is_contiguous() or keep_mask.element_size() != 8:
         raise ValueError("keep_mask must be a contiguous 8-byte-element tensor")
     if debug_block_stat is not None and (debug_block_stat.dtype != torch.float32
                                          or not debug_block_stat.is_contiguous()):
         raise ValueError("debug_block_stat must be a contiguous float32 tensor")
-    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
+                     gate_dtype=gate_dtype)
     tbl = table.c_struct()
     st = lib.bsfa_gate_masks(ctypes.byref(p), _ptr(Q), _ptr(K), ctypes.byref(tbl),
                              int(budget_slice), _ptr(keep_mask),
-                             ctypes.c_uint64(keep_mask.numel() * 8), _ptr(debug_block_stat),
-                             _stream_handle(stream, Q.device))
+                             ctypes.c_uint64(nbuf if fp8 else keep_mask.numel() * 8),
+                             _ptr(debug_block_stat), _stream_handle(stream, Q.device))
     _check(st)
     return keep_mask
 
@@ -370,8 +399,10 @@ def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_
 
 
 def bsfa_prefill_workspace_bytes(Q, K, *, block_q: int, block_k: int = 64,
-                                 gate_mode="absolute", mean_correction: bool = False) -> int:
+                                 gate_mode="absolute", mean_correction: bool = False,
+                                 gate_dtype="bf16") -> int:
     """Bytes of workspace bsfa_prefill can use for this problem and gate mode (0: none)."""
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
-    p = make_problem(Q, K, block_q=block_q, block_k=block_k, mean_correction=mean_correction)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, mean_correction=mean_correction,
+                     gate_dtype=gate_dtype)
     return int(load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))

@@ -147,12 +147,15 @@ bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K,
 }
 
 // The absolute gate's workspace: the keep bitmasks (one bit per 64-key tile; a gate block of
-// 128 keys sets two), then, for mean correction, the block means of K (bf16 high and low
-// parts) and of V, [B][Hkv][mean_blocks][d] each, every part on a 256-byte boundary.
+// 128 keys sets two); then, every part on a 256-byte boundary, for an FP8 gate the E4M3 copies
+// of Q and K and their scales, and for mean correction the block means of K (bf16 high and
+// low parts) and of V, [B][Hkv][mean_blocks][d] each.
 struct WorkspaceLayout {
   uint64_t mask_bytes;
+  int q8_rows, k8_rows, k8_tiles;
+  uint64_t q8, q8_scale, k8, k8_scale, fp8_end;   // byte offsets
   int mean_blocks;
-  uint64_t kbar_hi, kbar_lo, vbar, means_end;   // byte offsets
+  uint64_t kbar_hi, kbar_lo, vbar, means_end;     // byte offsets
 };
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
@@ -162,13 +165,37 @@ WorkspaceLayout workspace_layout(const bsfa_problem* p) {
   const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
   const uint64_t words = ceil_div(ceil_div(key_len(p), bsfa::kBlockK), 64);
   l.mask_bytes = (uint64_t)p->batch * p->heads_q * nqb * words * 8u;
+  const bool fp8 = p->gate_dtype == BSFA_FP8_E4M3;
+  l.q8_rows = p->seqlen;
+  l.k8_rows = key_len(p);
+  l.k8_tiles = ceil_div(key_len(p), bsfa::kBlockK);
+  const uint64_t B = p->batch, d = p->head_dim;
+  l.q8 = align256(l.mask_bytes);
+  l.q8_scale = l.q8 + (fp8 ? align256(B * l.q8_rows * p->heads_q * d) : 0);
+  l.k8 = l.q8_scale + (fp8 ? align256(B * p->heads_q * l.q8_rows * 4u) : 0);
+  l.k8_scale = l.k8 + (fp8 ? align256(B * l.k8_rows * p->heads_kv * d) : 0);
+  l.fp8_end = l.k8_scale + (fp8 ? align256(B * p->heads_kv * l.k8_tiles * 4u) : 0);
   l.mean_blocks = key_len(p) / p->block_k;
   const uint64_t part = (uint64_t)p->batch * p->heads_kv * l.mean_blocks * p->head_dim * 2u;
-  l.kbar_hi = align256(l.mask_bytes);
+  l.kbar_hi = l.fp8_end;
   l.kbar_lo = l.kbar_hi + align256(part);
   l.vbar = l.kbar_lo + align256(part);
   l.means_end = l.vbar + align256(part);
   return l;
+}
+
+// FP8 gate: point `a` at the copies in the workspace and quantise Q and K into them.
+hipError_t set_fp8(bsfa::PrefillArgs& a, const bsfa_problem* p, void* workspace, hipStream_t st) {
+  const WorkspaceLayout l = workspace_layout(p);
+  char* const ws = static_cast<char*>(workspace);
+  a.q8 = ws + l.q8;
+  a.q8_scale = reinterpret_cast<float*>(ws + l.q8_scale);
+  a.k8 = ws + l.k8;
+  a.k8_scale = reinterpret_cast<float*>(ws + l.k8_scale);
+  a.q8_rows = l.q8_rows;
+  a.k8_rows = l.k8_rows;
+  a.k8_tiles = l.k8_tiles;
+  return bsfa::launch_quantize_qk(a, p->head_dim, st);
 }
 
 // The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i).
@@ -207,7 +234,8 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) 
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
     return 0;
   const WorkspaceLayout l = workspace_layout(p);
-  return p->mean_correction ? l.means_end : l.mask_bytes;
+  return p->mean_correction ? l.means_end
+         : p->gate_dtype == BSFA_FP8_E4M3 ? l.fp8_end : l.mask_bytes;
 }
 
 }  // extern "C"
@@ -252,6 +280,17 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     return fail(BSFA_ERR_UNSUPPORTED, "mean correction needs a workspace (the block means)");
   if (mean && (reinterpret_cast<uintptr_t>(workspace) & 15u))
     return fail(BSFA_ERR_ALIGN, "mean correction needs a 16-byte-aligned workspace");
+  if (p->gate_dtype != BSFA_BF16 && p->gate_dtype != BSFA_FP8_E4M3)
+    return fail(BSFA_ERR_DTYPE, "gate_dtype %d not supported (BF16 or FP8_E4M3)", p->gate_dtype);
+  // FP8 gate scores: the absolute gate's sweep (the relative gate votes on the softmax's own
+  // scores)
+  const bool fp8 = p->gate_dtype == BSFA_FP8_E4M3 && gate_mode == BSFA_GATE_ABSOLUTE;
+  if (p->gate_dtype == BSFA_FP8_E4M3 && gate_mode == BSFA_GATE_RELATIVE)
+    return fail(BSFA_ERR_UNSUPPORTED, "FP8 gate scores are defined for the absolute gate");
+  if (fp8 && !workspace)
+    return fail(BSFA_ERR_UNSUPPORTED, "an FP8 gate needs a workspace (the FP8 copies)");
+  if (fp8 && (reinterpret_cast<uintptr_t>(workspace) & 15u))
+    return fail(BSFA_ERR_ALIGN, "an FP8 gate needs a 16-byte-aligned workspace");
   if (p->block_k != bsfa::kBlockK) {
     // 128-key gate blocks are decided by the gate sweep; a vote inside the softmax loop, which
     // walks 64-key tiles, is not built for them
@@ -330,6 +369,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   // that all workgroups stream K in step), then the prefill kernel runs over the kept ones
   if (use_masks) {
     a.keep_mask = static_cast<unsigned long long*>(workspace);
+    if (fp8) {
+      hipError_t e = set_fp8(a, p, workspace, st);
+      if (e != hipSuccess) return fail(BSFA_ERR_HIP, "FP8 copies launch: %s", hipGetErrorString(e));
+    }
     if (mean) {
       const WorkspaceLayout l = workspace_layout(p);
       char* const ws = static_cast<char*>(workspace);
@@ -440,14 +483,24 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
                 key_len(p) - p->seqlen, p->block_q);
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
-  const uint64_t need = workspace_layout(p).mask_bytes;
+  if (p->gate_dtype != BSFA_BF16 && p->gate_dtype != BSFA_FP8_E4M3)
+    return fail(BSFA_ERR_DTYPE, "gate_dtype %d not supported (BF16 or FP8_E4M3)", p->gate_dtype);
+  const bool fp8 = p->gate_dtype == BSFA_FP8_E4M3;
+  // with an FP8 gate the buffer continues with the FP8 copies
+  const uint64_t need = fp8 ? workspace_layout(p).fp8_end : workspace_layout(p).mask_bytes;
   if (mask_bytes < need)
     return fail(BSFA_ERR_ARG, "mask_bytes %llu below the required %llu",
                 (unsigned long long)mask_bytes, (unsigned long long)need);
+  if (fp8 && (reinterpret_cast<uintptr_t>(keep_mask) & 15u))
+    return fail(BSFA_ERR_ALIGN, "an FP8 gate needs a 16-byte-aligned keep_mask buffer");
   bsfa::PrefillArgs a = base_args(p, Q, K, nullptr, table, budget_slice, BSFA_GATE_ABSOLUTE);
   a.keep_mask = reinterpret_cast<unsigned long long*>(keep_mask);
   a.dbg = debug_block_stat;
   a.full_masks = 1;
+  if (fp8) {
+    hipError_t e = set_fp8(a, p, keep_mask, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "FP8 copies launch: %s", hipGetErrorString(e));
+  }
   hipError_t e = launch_sweep(a, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
   return ok();
@@ -465,6 +518,9 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
     if (budgets_host[t] < 1) return fail(BSFA_ERR_ARG, "budget %d is < 1", budgets_host[t]);
   if (key_len(p) != p->seqlen)
     return fail(BSFA_ERR_UNSUPPORTED, "calibration takes whole sequences (kv_seqlen 0 or seqlen)");
+  if (p->gate_dtype != BSFA_BF16)
+    return fail(BSFA_ERR_UNSUPPORTED, "the calibration kernel scores in bf16 (gate_dtype %d)",
+                p->gate_dtype);
   const int nkb = ceil_div(p->seqlen, bsfa::kBlockK);   // 64-key tiles
   if (nkb > bsfa::kCalibMaxKeyBlocks)
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the calibration limit %d", p->seqlen,

@@ -1239,6 +1239,281 @@ void gate_sweep_kernel(PrefillArgs a) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// FP8 (E4M3) gate scores. Q is quantised per (token, head) row and K per (64-key tile, KV head):
+// scale = amax / 448, codes = x * (448 / amax) rounded to nearest even on the E4M3 grid (the
+// hardware conversion; the product is clamped to +-448 first, so nothing saturates), in fp32;
+// an all-zero row or tile gets codes 0 and scale 0. The copies are dense:
+// q8 [B][q8_rows][Hq][D] with scales [B][Hq][q8_rows], k8 [B][k8_rows][Hkv][D] with scales
+// [B][Hkv][k8_tiles], whatever the layout of Q and K (strided, packed or paged).
+// ---------------------------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+
+// Four fp32 values as four E4M3 codes in one 32-bit word (value k in byte k).
+__device__ __forceinline__ unsigned pack_e4m3(float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(x0, x1, 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(x2, x3, w, true);
+  return (unsigned)w;
+}
+
+__device__ __forceinline__ float e4m3_inv(float amax) {
+  return amax > 0.f ? __fdiv_rn(448.f, amax) : 0.f;
+}
+__device__ __forceinline__ float e4m3_scale(float amax) {
+  return amax > 0.f ? __fdiv_rn(amax, 448.f) : 0.f;
+}
+
+// Eight bf16 values times inv, clamped to +-448, as eight codes.
+__device__ __forceinline__ uint2 quant8(const bf16x8& x, float inv) {
+  float y[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) y[e] = fminf(fmaxf((float)x[e] * inv, -448.f), 448.f);
+  return make_uint2(pack_e4m3(y[0], y[1], y[2], y[3]), pack_e4m3(y[4], y[5], y[6], y[7]));
+}
+
+__device__ __forceinline__ float amax8(const bf16x8& x) {
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)x[e]));
+  return m;
+}
+
+// One (token, head) row of Q per D/8 lanes; 256 threads hold 4 * 64 / (D/8) rows.
+template <int D>
+__global__ __launch_bounds__(256) void quant_q_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 8, RPW = 64 / LPR, RPB = 4 * RPW;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int per = (a.q8_rows * a.Hq + RPB - 1) / RPB;    // workgroups per sequence
+  const int b = blockIdx.x / per;
+  const int u = (blockIdx.x % per) * RPB + w * RPW + lane / LPR;
+  const Seq sq = seq_of(a, b);
+  const int r = u / a.Hq, h = u % a.Hq;
+  if (r >= sq.N) return;                       // whole row groups leave together
+  const int col = (lane % LPR) * 8;
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(static_cast<const __bf16*>(a.q) + sq.q +
+                                                     (long long)r * a.qs[1] + h * a.qs[2] + col);
+  float m = amax8(x);
+#pragma unroll
+  for (int s = 1; s < LPR; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+  const long long row = (long long)b * a.q8_rows + r;
+  *reinterpret_cast<uint2*>(static_cast<unsigned char*>(a.q8) + (row * a.Hq + h) * D + col) =
+      quant8(x, e4m3_inv(m));
+  if (lane % LPR == 0)
+    a.q8_scale[((long long)b * a.Hq + h) * a.q8_rows + r] = e4m3_scale(m);
+}
+
+// One (64-key tile, KV head) of K per workgroup of 256 threads.
+template <int D, bool PAGED>
+__global__ __launch_bounds__(256) void quant_k_kernel(PrefillArgs a) {
+  constexpr int LPR = D / 8, CH = 64 * LPR / 256;    // 8-element chunks per thread
+  __shared__ float sAmax[4];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int t = blockIdx.x % a.k8_tiles;
+  const int bg = blockIdx.x / a.k8_tiles;
+  const int b = bg / a.Hkv, g = bg % a.Hkv;
+  const Seq sq = seq_of(a, b);
+  if (t * kBlockK >= sq.Nk) return;                  // uniform: past this sequence's keys
+  const int valid = min(kBlockK, sq.Nk - t * kBlockK);
+  const long long kst = a.ks[1];
+  const __bf16* const Kt = static_cast<const __bf16*>(a.k) + sq.k + g * a.ks[2] +
+                           tile_offset<PAGED>(a, b, t, kst, a.ks[0]);
+  bf16x8 x[CH];
+  float m = 0.f;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int q = tid + 256 * c, r = q / LPR;
+    if (r < valid) {
+      x[c] = *reinterpret_cast<const bf16x8*>(Kt + (long long)r * kst + (q % LPR) * 8);
+      m = fmaxf(m, amax8(x[c]));
+    }
+  }
+  m = wave_max(m);
+  if (lane == 0) sAmax[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(sAmax[0], sAmax[1]), fmaxf(sAmax[2], sAmax[3]));
+  const float inv = e4m3_inv(m);
+  unsigned char* const out = static_cast<unsigned char*>(a.k8) +
+                             (((long long)b * a.k8_rows + t * kBlockK) * a.Hkv + g) * D;
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int q = tid + 256 * c, r = q / LPR;
+    if (r < valid)
+      *reinterpret_cast<uint2*>(out + (long long)r * a.Hkv * D + (q % LPR) * 8) = quant8(x[c], inv);
+  }
+  if (tid == 0) a.k8_scale[((long long)b * a.Hkv + g) * a.k8_tiles + t] = e4m3_scale(m);
+}
+
+// The gate sweep on FP8 scores: the structure of gate_sweep_kernel (three K tiles in LDS, one
+// per barrier, 64-row waves, the heads of a KV group sharing each tile), with E4M3 Q and K and
+// v_mfma_scale_f32_32x32x64_f8f6f4 at unit block scales: a 64-row wave takes D/64 k-steps of
+// four MFMAs per tile (32 bf16 ones at d = 128). A lane holds 32 consecutive bytes of its row
+// per operand (lanes 32..63 the second 32 of each 64); both operands use the same order, which
+// is all a dot product needs. The row maximum of the raw dot products is scaled by the row's
+// Q scale, the tile maximum by the tile's K scale and the softmax scale.
+// LDS K rows: D bytes + 16 of padding, so that 16 rows start 36 banks apart and a 16-byte read
+// of 16 rows covers the 64 banks once.
+template <int D, int BQ, int HPW>
+__global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void gate_sweep_fp8_kernel(PrefillArgs a) {
+  constexpr int WPH = BQ / 64;
+  constexpr int NW = HPW * WPH;
+  constexpr int D2 = D / 2, STR8 = D2 + 8;     // a row in 2-byte units: D bytes + 16 of padding
+  constexpr int KS8 = D / 64;                  // k-steps of 64 bytes
+  constexpr int MK = copy_iters<STR8, NW>(), CPS = STR8 / 8;
+
+  __shared__ __attribute__((aligned(16))) __bf16 sKa[64 * STR8];
+  __shared__ __attribute__((aligned(16))) __bf16 sKb[64 * STR8];
+  __shared__ __attribute__((aligned(16))) __bf16 sKc[64 * STR8];
+  __shared__ float sStage[2][NW];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hw = w / WPH, rw = w % WPH;
+  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
+  const int b = un.b, g = un.g, i = un.i;
+  const int h0 = g * a.G + un.hg * HPW;
+  const int h = h0 + hw;
+  const Seq sq = seq_of(a, b);
+  if (i * BQ >= sq.N) return;
+  const int N = sq.N, pre = sq.pre;
+  const int row0 = i * BQ + rw * 64;
+  const int n_off = (pre + i * BQ) / BK;
+  const bool leader = rw == 0 && lane == 0;
+  unsigned long long* const mask = a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) *
+                                                     a.mask_words;
+  const int nw64 = (n_off + 63) >> 6;
+  auto zero_tail = [&]() {
+    if (a.full_masks && leader)
+      for (int x = nw64; x < a.mask_words; ++x) mask[x] = 0ull;
+  };
+  if (n_off == 0) {
+    zero_tail();
+    return;
+  }
+
+  // K tiles of this (b, g) in the dense FP8 copy, addressed in 2-byte units for the copies
+  const long long kst2 = (long long)a.Hkv * D2;
+  const __bf16* const K8 = reinterpret_cast<const __bf16*>(
+      static_cast<const unsigned char*>(a.k8) + ((long long)b * a.k8_rows * a.Hkv + g) * D);
+  const unsigned krow = (unsigned)(a.Hkv * D);
+  unsigned koff[MK];
+  copy_offsets<D2, STR8, NW>(koff, kst2, w, lane);
+  auto load_k = [&](int j, __bf16* dst) {
+    copy_tile<D2, STR8, NW>(koff, K8 + (long long)j * kBlockK * kst2, krow, BK, dst, w, lane);
+  };
+  auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
+  const int tcol = min(pre / BQ + i, a.t_len - 1);
+  const float thr = a.thr[h * a.t_len + tcol];
+  bool all_keep = a.dbg == nullptr && !a.full_masks;
+#pragma unroll
+  for (int hh = 0; hh < HPW; ++hh)
+    all_keep = all_keep && a.thr[(h0 + hh) * a.t_len + tcol] == kNegInf;
+  if (all_keep) return;
+
+  const bool last_round = w + NW * (MK - 1) < CPS;
+  auto wait_all_but_newest_tile = [&]() {
+    if (last_round)
+      wait_vmem_n<MK>();
+    else
+      wait_vmem_n<MK - 1>();
+  };
+  const float* const ksc = a.k8_scale + ((long long)b * a.Hkv + g) * a.k8_tiles;
+  unsigned long long word = 0ull;
+  float xblk = kNegInf;
+  auto combine = [&](int j) {
+    if (leader) {
+      float x = sStage[j & 1][hw * WPH];
+#pragma unroll
+      for (int r = 1; r < WPH; ++r) x = fmaxf(x, sStage[j & 1][hw * WPH + r]);
+      x *= ksc[j];
+      xblk = (j % a.kpb == 0) ? x : fmaxf(xblk, x);
+      if (j % a.kpb == a.kpb - 1) {
+        const int jb = j / a.kpb;
+        const float sm = xblk * a.scale;
+        if (a.dbg) a.dbg[(((long long)b * a.Hq + h) * a.nqb + i) * a.nkb + jb] = sm;
+        if (sm >= thr) word |= (a.kpb == 2 ? 3ull : 1ull) << ((j + 1 - a.kpb) & 63);
+      }
+      if ((j & 63) == 63 || j == n_off - 1) {
+        mask[j >> 6] = word;
+        word = 0ull;
+      }
+    }
+  };
+
+  load_k(0, sKa);
+  if (n_off > 1) load_k(1, sKb);
+  // Q rows row0 + 32 rb + lane % 32 (zero past N) and their scales
+  i32x8 qf[2][KS8];
+  float qs[2];
+  bool rv[2];
+  const unsigned char* const Q8 = static_cast<const unsigned char*>(a.q8) +
+                                  ((long long)b * a.q8_rows * a.Hq + h) * D;
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int row = row0 + 32 * rb + (lane & 31);
+    rv[rb] = row < N;
+    const unsigned char* p = Q8 + (long long)min(row, N - 1) * a.Hq * D + 32 * (lane >> 5);
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      uint4 lo = *reinterpret_cast<const uint4*>(p + 64 * ks);
+      uint4 hi = *reinterpret_cast<const uint4*>(p + 64 * ks + 16);
+      if (!rv[rb]) lo = hi = make_uint4(0, 0, 0, 0);
+      qf[rb][ks] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                         (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+    }
+    qs[rb] = a.q8_scale[((long long)b * a.Hq + h) * a.q8_rows + min(row, N - 1)];
+  }
+  wait_vmem();
+  __syncthreads();
+  const int kfo = (lane & 31) * (2 * STR8) + 32 * (lane >> 5);   // byte offset in a tile
+  for (int j = 0; j < n_off; ++j) {
+    if (j + 2 < n_off) load_k(j + 2, kbuf((j + 2) % 3));
+    const unsigned char* const kt = reinterpret_cast<const unsigned char*>(kbuf(j % 3)) + kfo;
+    f32x16 s[2][2];
+#pragma unroll
+    for (int ks = 0; ks < KS8; ++ks) {
+      i32x8 kf[2];
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const uint4 lo = *reinterpret_cast<const uint4*>(kt + mb * 32 * (2 * STR8) + 64 * ks);
+        const uint4 hi = *reinterpret_cast<const uint4*>(kt + mb * 32 * (2 * STR8) + 64 * ks + 16);
+        kf[mb] = i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+                       (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          f32x16 acc;
+          if (ks == 0) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+          } else {
+            acc = s[rb][mb];
+          }
+          s[rb][mb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(kf[mb], qf[rb][ks], acc,
+                                                                       0, 0, 0, 127, 0, 127);
+        }
+    }
+    float m = kNegInf;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mr = block_max(block_max(kNegInf, s[rb][0]), s[rb][1]);
+      m = fmaxf(m, rv[rb] ? mr * qs[rb] : kNegInf);
+    }
+    m = wave_max(m);
+    if (lane == 0) sStage[j & 1][w] = m;
+    if (j > 0) combine(j - 1);
+    if (j + 2 < n_off)
+      wait_all_but_newest_tile();
+    else
+      wait_vmem();
+    __syncthreads();
+  }
+  combine(n_off - 1);
+  zero_tail();
+}
+
+// ---------------------------------------------------------------------------------------------
 // Calibration: per (b, h, i) the off-diagonal block maxima, then the k-th highest per budget.
 // Waves of 32 rows as in the prefill kernel, QK only; the per-wave tile maxima collect in LDS.
 // ---------------------------------------------------------------------------------------------
@@ -1493,6 +1768,29 @@ hipError_t launch_calibrate_tile(const CalibArgs& a, int nw, hipStream_t stream)
 template <int D, int BQ>
 hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream) {
   return launch_sweep_hpw<D, BQ>(a, hpw, stream);
+}
+
+template <int D, int BQ>
+hipError_t launch_sweep_fp8_tile(const PrefillArgs& a, int hpw, hipStream_t stream) {
+  constexpr int WPH = BQ / 64;
+  const dim3 grid(a.units * a.nqb);
+  if (hpw == 2)
+    hipLaunchKernelGGL((gate_sweep_fp8_kernel<D, BQ, 2>), grid, dim3(WPH * 128), 0, stream, a);
+  else
+    hipLaunchKernelGGL((gate_sweep_fp8_kernel<D, BQ, 1>), grid, dim3(WPH * 64), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D, bool PAGED>
+hipError_t launch_quant_tile(const PrefillArgs& a, hipStream_t stream) {
+  constexpr int RPB = 4 * 64 / (D / 8);
+  const int per = (a.q8_rows * a.Hq + RPB - 1) / RPB;
+  hipLaunchKernelGGL((quant_q_kernel<D>), dim3(a.B * per), dim3(256), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((quant_k_kernel<D, PAGED>), dim3(a.B * a.Hkv * a.k8_tiles), dim3(256), 0,
+                     stream, a);
+  return hipGetLastError();
 }
 
 template <int D, bool PAGED>

@@ -63,6 +63,14 @@ struct PrefillArgs {
   void* vbar;
   int mean_blocks;
   float mean_bias;
+  // FP8 gate scores (ABSOLUTE sweep): E4M3 copies of Q [B][q8_rows][Hq][D] and K
+  // [B][k8_rows][Hkv][D] with fp32 scales per (b, h, row) [B][Hq][q8_rows] and per (b, g,
+  // 64-key tile) [B][Hkv][k8_tiles]; q8 == nullptr: bf16 scores.
+  void* q8;
+  float* q8_scale;
+  void* k8;
+  float* k8_scale;
+  int q8_rows, k8_rows, k8_tiles;
 };
 
 struct CalibArgs {
@@ -113,6 +121,8 @@ hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 // Block means for mean correction: fills a.kbar_hi, a.kbar_lo and a.vbar for every whole gate
 // block of every (batch, KV head) (a.mean_blocks per sequence at most).
 hipError_t launch_block_means(const PrefillArgs& a, int head_dim, hipStream_t stream);
+// FP8 gate: fills a.q8 / a.q8_scale and a.k8 / a.k8_scale from Q and K.
+hipError_t launch_quantize_qk(const PrefillArgs& a, int head_dim, hipStream_t stream);
 
 // Launchers of one (head dimension D, query tile BQ[, paged K/V]) instantiation; each is defined
 // in its own translation unit. nw = waves per workgroup, hpw = heads per sweep workgroup.
@@ -124,5 +134,9 @@ template <int D, int BQ>
 hipError_t launch_sweep_tile(const PrefillArgs& a, int hpw, hipStream_t stream);
 template <int D, bool PAGED>
 hipError_t launch_means_tile(const PrefillArgs& a, hipStream_t stream);
+template <int D, bool PAGED>
+hipError_t launch_quant_tile(const PrefillArgs& a, hipStream_t stream);
+template <int D, int BQ>
+hipError_t launch_sweep_fp8_tile(const PrefillArgs& a, int hpw, hipStream_t stream);
 
 }  // namespace bsfa

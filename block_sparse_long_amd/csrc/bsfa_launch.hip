@@ -16,6 +16,13 @@ int gate_sweep_heads(int block_q, int group) {
 
 hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream) {
   const int hpw = gate_sweep_heads(block_q, a.G);
+  if (a.q8) {
+    if (head_dim == 128)
+      return block_q == 128 ? launch_sweep_fp8_tile<128, 128>(a, hpw, stream)
+                            : launch_sweep_fp8_tile<128, 64>(a, hpw, stream);
+    return block_q == 128 ? launch_sweep_fp8_tile<64, 128>(a, hpw, stream)
+                          : launch_sweep_fp8_tile<64, 64>(a, hpw, stream);
+  }
   if (head_dim == 128)
     return block_q == 128 ? launch_sweep_tile<128, 128>(a, hpw, stream)
                           : launch_sweep_tile<128, 64>(a, hpw, stream);
@@ -68,6 +75,14 @@ hipError_t launch_block_means(const PrefillArgs& a, int head_dim, hipStream_t st
                            : launch_means_tile<64, true>(a, stream);
   return head_dim == 128 ? launch_means_tile<128, false>(a, stream)
                          : launch_means_tile<64, false>(a, stream);
+}
+
+hipError_t launch_quantize_qk(const PrefillArgs& a, int head_dim, hipStream_t stream) {
+  if (a.pages)
+    return head_dim == 128 ? launch_quant_tile<128, true>(a, stream)
+                           : launch_quant_tile<64, true>(a, stream);
+  return head_dim == 128 ? launch_quant_tile<128, false>(a, stream)
+                         : launch_quant_tile<64, false>(a, stream);
 }
 
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {

@@ -150,6 +150,10 @@ CONFIGS = {
                             calib_seeds=list(range(1, 9))),
     "llama_128k": dict(kind="structured", n=131072, heads_q=32, heads_kv=8, d=128, block_q=128,
                        block_k=64, budgets=[64], calib_n=65536, calib_seeds=list(range(1, 9))),
+    # the 128K workload under the FP8 gate: its thresholds calibrated on FP8 scores
+    "llama_128k_fp8": dict(kind="structured", n=131072, heads_q=32, heads_kv=8, d=128,
+                           block_q=128, block_k=64, budgets=[64], calib_n=65536,
+                           calib_seeds=list(range(1, 9)), gate_dtype="fp8"),
     "llama_64k_relative": dict(kind="structured", n=65536, heads_q=32, heads_kv=8, d=128,
                                block_q=128, block_k=64, budgets=[], calib_n=0, calib_seeds=[],
                                log_lambdas=[-math.inf, math.log(1e-4), math.log(1e-3),

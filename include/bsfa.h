@@ -66,7 +66,7 @@ typedef enum {
   BSFA_GATE_RELATIVE = 2     /* keep iff max_r(rowmax_j[r] - m[r]) >= log_lambda */
 } bsfa_gate_mode;
 
-typedef enum { BSFA_BF16 = 0, BSFA_FP32 = 1 } bsfa_dtype;
+typedef enum { BSFA_BF16 = 0, BSFA_FP32 = 1, BSFA_FP8_E4M3 = 2 } bsfa_dtype;
 
 /* One causal prefill self-attention call (one layer). */
 typedef struct {
@@ -108,6 +108,17 @@ typedef struct {
                               * decisions read the running max a stand-in would move) and
                               * ABSOLUTE without a workspace return BSFA_ERR_UNSUPPORTED. DENSE
                               * prunes nothing: no effect. */
+  int32_t gate_dtype;        /* precision of the absolute gate's scores: BSFA_BF16 (0, the exact
+                              * scores) or BSFA_FP8_E4M3: the gate sweep scores E4M3 copies of Q
+                              * and K on the FP8 matrix cores (FlashPrefill V2's FP8 path; the
+                              * softmax and O still use the exact bf16 scores of the kept
+                              * blocks). Q is quantised per (token, head) row and K per (64-key
+                              * tile, KV head): scale = amax / 448, code = x * (448 / amax)
+                              * rounded to nearest even on the E4M3 grid (fp32); a score is
+                              * (q8 . k8) * scale_q * scale_k * softmax_scale. Thresholds must be
+                              * calibrated on the same FP8 scores. Needs ABSOLUTE with a
+                              * 16-byte-aligned workspace, which then also holds the copies;
+                              * RELATIVE returns BSFA_ERR_UNSUPPORTED; DENSE ignores it. */
 } bsfa_problem;
 
 /* One layer's threshold table (the offline calibration artifact), fp32 in device memory.
@@ -128,8 +139,10 @@ typedef struct {
 
 /* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
  * ABSOLUTE, one keep bitmask per (b, h, i) with one bit per 64-key tile,
- * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words; with mean_correction, then (each
- * part starting on a 256-byte boundary) three bf16 arrays [B][Hkv][floor(Nk/Bk)][d]: the
+ * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words; then, each part starting on a
+ * 256-byte boundary: with gate_dtype FP8_E4M3 the E4M3 copies of Q [B][N][Hq][d] and K
+ * [B][Nk][Hkv][d] (one byte per element) and their fp32 scales [B][Hq][N] and
+ * [B][Hkv][ceil(Nk/64)]; with mean_correction three bf16 arrays [B][Hkv][floor(Nk/Bk)][d]: the
  * block means of K in two parts (high and low bf16) and of V. */
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
 
@@ -156,8 +169,9 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 decisions of all blocks are made in a separate launch first (scores only),
  *                 and the softmax launch then walks the kept blocks; without one, both happen
  *                 in one launch. The results are the same. A non-NULL workspace that is too
- *                 small is an error (BSFA_ERR_ARG). With mean_correction it is required and
- *                 must be 16-byte aligned; a third launch computes the block means.
+ *                 small is an error (BSFA_ERR_ARG). With mean_correction or an FP8 gate it
+ *                 is required and must be 16-byte aligned; a launch before the sweep computes
+ *                 the block means, and one the FP8 copies.
  *   stream        hipStream_t
  * The absolute gate supports Nk up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
  * Returns BSFA_OK or an error status (see the conventions above). */
@@ -230,7 +244,9 @@ bsfa_status bsfa_prefill_paged(const bsfa_problem* p, const void* Q, const void*
  *                 aligned, one bit per 64-key tile (a kept 128-key block sets both of its
  *                 tiles); every word is written (bits past the off-diagonal tiles are zero)
  *   mask_bytes    size of keep_mask; at least B * Hq * ceil(N/Bq) * W * 8 (mean_correction
- *                 is ignored here)
+ *                 is ignored here). With gate_dtype FP8_E4M3, keep_mask is a 16-byte-aligned
+ *                 buffer of at least bsfa_prefill_workspace_bytes(p, ABSOLUTE) bytes (with
+ *                 mean_correction 0): the masks, then the FP8 copies this call writes
  *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
  *   stream        hipStream_t
  * This is the first of the two launches bsfa_prefill makes when given a workspace; on its own

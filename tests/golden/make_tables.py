@@ -5,7 +5,8 @@
 Each table is calibrated by the CPU oracle (oracle.calibrate: k-th highest off-diagonal block
 maximum per sample, head and query block, averaged over samples; "Block Sparse Flash
 Attention", Method > Key Designs 1) on the calibration seeds of a named synthetic workload,
-on the bf16-rounded inputs the device consumes. Nothing here calls the HIP library.
+on the bf16-rounded inputs the device consumes (a workload with gate_dtype "fp8" against the
+FP8 gate's block maxima). Nothing here calls the HIP library.
 
 File format: one JSON header line, then little-endian float32 [n_budgets][heads_q][t_len].
 """
@@ -46,14 +47,16 @@ def make(config: str) -> None:
         return
     t0 = time.time()
     scale = float(np.float32(1.0 / math.sqrt(c["d"])))
+    gate_dtype = c.get("gate_dtype", "bf16")
     T = oracle.calibrate(samples(config, c["calib_seeds"], c["calib_n"]), block_q=c["block_q"],
-                         block_k=c["block_k"], budgets=c["budgets"], scale=scale)
+                         block_k=c["block_k"], budgets=c["budgets"], scale=scale,
+                         gate_dtype=gate_dtype)
     hdr = {"magic": MAGIC, "n_budgets": len(c["budgets"]), "heads_q": int(T.shape[1]),
            "t_len": int(T.shape[2]), "budgets": c["budgets"], "block_q": c["block_q"],
            "block_k": c["block_k"], "head_dim": c["d"], "softmax_scale": scale,
            "calib_seqlen": c["calib_n"], "seeds": c["calib_seeds"],
            "generator": f"block_sparse_long_amd.synth.make_inputs('{config}')",
-           "calibrated_by": "oracle.calibrate (CPU, float32)"}
+           "calibrated_by": "oracle.calibrate (CPU, float32)", "gate_dtype": gate_dtype}
     with open(table_path(config), "wb") as f:
         f.write((json.dumps(hdr) + "\n").encode())
         f.write(T.astype("<f4").tobytes())

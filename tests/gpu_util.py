@@ -114,3 +114,104 @@ def check_parity(dev, Qh, Kh, Vh, *, block_q, mode, table=None, budget_slice=0,
     assert err.max() <= MAX_ABS, f"max-abs {err.max():.3e}"
     assert err.mean() <= MEAN_ABS, f"mean-abs {err.mean():.3e}"
     return r
+
+
+def quantile_table(Qh, Kh, Bq, Bk, q=0.75, n_budgets=2):
+    """Per-head thresholds at the q-quantile of the off-diagonal block maxima of a few query
+    blocks (host numpy on the rounded inputs), so that about 1 - q of the blocks are kept."""
+    B, N, Hq, d = Qh.shape
+    Nk, G = Kh.shape[1], Hq // Kh.shape[2]
+    P = Nk - N
+    sc = np.float32(1 / math.sqrt(d))
+    nqb = -(-N // Bq)
+    T = np.zeros((n_budgets, Hq, P // Bq + nqb), np.float32)
+    for h in range(Hq):
+        maxima = []
+        for i in sorted({nqb // 2, nqb - 1}):
+            n_off = oracle.key_block_range(i, N, Bq, Bk, P)[0]
+            if n_off == 0:
+                continue
+            s = (Qh[0, i * Bq:(i + 1) * Bq, h] @ Kh[0, :n_off * Bk, h // G].T) * sc
+            maxima += list(s.reshape(s.shape[0], n_off, Bk).max(axis=(0, 2)))
+        for sl in range(n_budgets):
+            T[sl, h] = np.quantile(maxima, q - 0.2 * sl)
+    return make_table(T, Bq, d, list(range(1, n_budgets + 1)), block_k=Bk)
+
+
+def varlen_batch(seed, Hq, Hkv, d, nq, nk):
+    """Packed sequences [tokens, H, d] of the given query / key lengths, and cu_q, cu_k."""
+    g = torch.Generator().manual_seed(seed)
+    cu_q = np.cumsum([0] + nq).astype(np.int32)
+    cu_k = np.cumsum([0] + nk).astype(np.int32)
+    Q = torch.randn(int(cu_q[-1]), Hq, d, generator=g) * 1.5
+    K = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
+    V = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
+    return Q, K, V, cu_q, cu_k
+
+
+def pages_of(X, cu, page, seed):
+    """Scatter packed sequences [tokens, H, d] into a shuffled page pool (spare pages NaN);
+    returns (pool, block table on the device)."""
+    rng = np.random.default_rng(seed)
+    lens = np.diff(cu)
+    n_pages = [-(-int(n) // page) for n in lens]
+    free = list(rng.permutation(sum(n_pages) + 3))
+    pool = torch.full((len(free), page) + tuple(X.shape[1:]), float("nan"), dtype=X.dtype,
+                      device=X.device)
+    table = torch.zeros((len(lens), max(max(n_pages), 1)), dtype=torch.int32)
+    for b, n in enumerate(lens):
+        for j in range(n_pages[b]):
+            pg = free.pop()
+            table[b, j] = int(pg)
+            m = min(page, int(n) - j * page)
+            pool[pg, :m] = X[cu[b] + j * page: cu[b] + j * page + m]
+    return pool, table.cuda()
+
+
+def absolute_parity(Qd, Kd, Vd, Qh, Kh, Vh, *, Bq, Bk, tab, sl=0, query_blocks=None,
+                    mean_correction=False, gate_dtype="bf16"):
+    """One absolute-gate device call (masks and statistics from bsfa_gate_masks, the sweep the
+    call itself runs) against the oracle under the near-tie rule; returns (O, oracle result,
+    device keep decisions)."""
+    B, N, Hq, d = Qh.shape
+    Nk = Kh.shape[1]
+    P = Nk - N
+    kpb = Bk // 64
+    dtab = tab.to_device("cuda")
+    nqb, nkb = -(-N // Bq), -(-Nk // Bk)
+    stat = torch.full((B, Hq, nqb, nkb), float("nan"), device="cuda")
+    mask = _lib.bsfa_gate_masks(Qd, Kd, dtab, sl, block_q=Bq, block_k=Bk, debug_block_stat=stat,
+                                gate_dtype=gate_dtype)
+    counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
+    O = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, block_k=Bk, gate_mode="absolute", table=dtab,
+                          budget_slice=sl, kept_counts=counts, out_dtype=torch.float32,
+                          mean_correction=mean_correction, gate_dtype=gate_dtype)
+    torch.cuda.synchronize()
+    m = np.ascontiguousarray(mask.cpu().numpy()).view(np.uint8)
+    bits = np.unpackbits(m, axis=-1, bitorder="little").astype(bool)
+    st = stat.cpu().numpy()
+    keep = np.zeros((B, Hq, nqb, nkb), bool)
+    n_off = np.array([oracle.key_block_range(i, N, Bq, Bk, P)[0] for i in range(nqb)])
+    for i in range(nqb):
+        keep[:, :, i, :n_off[i]] = bits[:, :, i, 0:kpb * n_off[i]:kpb]
+    np.testing.assert_array_equal(counts.cpu().numpy(), keep.sum(-1))
+    assert (counts.cpu().numpy() < n_off).any(), "nothing pruned"
+    r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=Bq, block_k=Bk, mode="absolute", table=tab.T,
+                              budget_slice=sl, forced_keep=keep, band=BAND,
+                              mean_correction=mean_correction, gate_dtype=gate_dtype,
+                              query_blocks=query_blocks)
+    blocks = range(nqb) if query_blocks is None else query_blocks
+    rows = np.zeros(N, bool)
+    for i in blocks:
+        mg = r.margin[:, :, i, :n_off[i]]
+        out = np.abs(mg) > BAND
+        np.testing.assert_array_equal(r.keep[:, :, i, :n_off[i]][out], keep[:, :, i, :n_off[i]][out])
+        fin = np.isfinite(r.stat[:, :, i, :n_off[i]])
+        np.testing.assert_allclose(st[:, :, i, :n_off[i]][fin], r.stat[:, :, i, :n_off[i]][fin],
+                                   rtol=1e-5, atol=2e-3)
+        rows[i * Bq:min((i + 1) * Bq, N)] = True
+    Oh = O.cpu().numpy()
+    assert np.isfinite(Oh[:, rows]).all()
+    err = np.abs(Oh[:, rows] - r.out[:, rows])
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+    return O, r, keep

@@ -341,3 +341,38 @@ def test_mean_correction_workspace_and_validation():
     p.mean_correction = 1
     assert call_masks(p, table(t_len=8), mask_bytes=masks - 8) == _lib.BSFA_ERR_ARG
     assert f"required {masks}" in _lib.bsfa_last_error()
+
+
+def test_fp8_gate_workspace_and_validation():
+    lib = _lib.load_library()
+    p = problem(N=1000)
+    masks = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    p.gate_dtype = _lib.BSFA_FP8_E4M3
+    need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    r256 = lambda x: -(-x // 256) * 256
+    B, N, Hq, Hkv, d = p.batch, 1000, p.heads_q, p.heads_kv, p.head_dim
+    parts = [B * N * Hq * d, B * Hq * N * 4, B * N * Hkv * d, B * Hkv * (-(-N // 64)) * 4]
+    assert need == r256(masks) + sum(r256(x) for x in parts)
+    # with mean correction the block means follow the FP8 copies
+    p.mean_correction = 1
+    both = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    assert both == need + 3 * r256(B * Hkv * (N // 64) * d * 2)
+    p.mean_correction = 0
+    for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+    abs_call = dict(tbl=table(t_len=8), mode=_lib.BSFA_GATE_ABSOLUTE)
+    assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_UNSUPPORTED
+    assert "workspace" in _lib.bsfa_last_error()
+    assert call_prefill(p, ws=FAKE + 8, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_ALIGN
+    assert call_prefill(p, ws=FAKE, ws_bytes=need - 1, **abs_call) == _lib.BSFA_ERR_ARG
+    assert call_prefill(p, mode=_lib.BSFA_GATE_RELATIVE, log_lambda=-1.0) == \
+        _lib.BSFA_ERR_UNSUPPORTED
+    p.gate_dtype = _lib.BSFA_FP32
+    assert call_prefill(p, ws=FAKE, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_DTYPE
+    # the gate masks need the masks and the FP8 copies, 16-byte aligned
+    p.gate_dtype = _lib.BSFA_FP8_E4M3
+    assert call_masks(p, table(t_len=8), mask_bytes=need - 8) == _lib.BSFA_ERR_ARG
+    assert f"required {need}" in _lib.bsfa_last_error()
+    assert call_masks(p, table(t_len=8), mask=FAKE + 8, mask_bytes=need) == _lib.BSFA_ERR_ALIGN
+    # the calibration kernel scores in bf16
+    assert call_calib(p, [1]) == _lib.BSFA_ERR_UNSUPPORTED

@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from block_sparse_long_amd import _lib, synth
-from gpu_util import BAND, MAX_ABS, MEAN_ABS, bf16_pair, make_table
+from gpu_util import (BAND, MAX_ABS, MEAN_ABS, absolute_parity, bf16_pair, make_table,
+                      pages_of, quantile_table, varlen_batch)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,68 +36,6 @@ def _inputs(seed, N, Hq, Hkv, d, B=1):
         Q, K, V = synth.uniform_mix(seed, B, N, Hq, Hkv, d)
         Q = Q * 1.5
     return Q, K, V
-
-
-def _quantile_table(Qh, Kh, Bq, Bk, q=0.75, n_budgets=2):
-    """Per-head thresholds at the q-quantile of the off-diagonal block maxima of a few query
-    blocks (host numpy on the rounded inputs), so that about 1 - q of the blocks are kept."""
-    B, N, Hq, d = Qh.shape
-    Nk, G = Kh.shape[1], Hq // Kh.shape[2]
-    P = Nk - N
-    sc = np.float32(1 / math.sqrt(d))
-    nqb = -(-N // Bq)
-    T = np.zeros((n_budgets, Hq, P // Bq + nqb), np.float32)
-    for h in range(Hq):
-        maxima = []
-        for i in sorted({nqb // 2, nqb - 1}):
-            n_off = oracle.key_block_range(i, N, Bq, Bk, P)[0]
-            if n_off == 0:
-                continue
-            s = (Qh[0, i * Bq:(i + 1) * Bq, h] @ Kh[0, :n_off * Bk, h // G].T) * sc
-            maxima += list(s.reshape(s.shape[0], n_off, Bk).max(axis=(0, 2)))
-        for sl in range(n_budgets):
-            T[sl, h] = np.quantile(maxima, q - 0.2 * sl)
-    return make_table(T, Bq, d, list(range(1, n_budgets + 1)), block_k=Bk)
-
-
-def _mean_parity(Qd, Kd, Vd, Qh, Kh, Vh, *, Bq, Bk, tab, sl=0, query_blocks=None):
-    """One corrected device call against the oracle; returns (O, oracle result, keep)."""
-    B, N, Hq, d = Qh.shape
-    Nk = Kh.shape[1]
-    P = Nk - N
-    kpb = Bk // 64
-    dtab = tab.to_device("cuda")
-    nqb, ntile, nkb = -(-N // Bq), -(-Nk // 64), -(-Nk // Bk)
-    mask = torch.full((B, Hq, nqb, -(-ntile // 64)), -1, dtype=torch.int64, device="cuda")
-    _lib.bsfa_gate_masks(Qd, Kd, dtab, sl, mask, block_q=Bq, block_k=Bk)
-    counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
-    O = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, block_k=Bk, gate_mode="absolute", table=dtab,
-                          budget_slice=sl, kept_counts=counts, out_dtype=torch.float32,
-                          mean_correction=True)
-    torch.cuda.synchronize()
-    m = np.ascontiguousarray(mask.cpu().numpy()).view(np.uint8)
-    bits = np.unpackbits(m, axis=-1, bitorder="little").astype(bool)
-    keep = np.zeros((B, Hq, nqb, nkb), bool)
-    n_off = np.array([oracle.key_block_range(i, N, Bq, Bk, P)[0] for i in range(nqb)])
-    for i in range(nqb):
-        keep[:, :, i, :n_off[i]] = bits[:, :, i, 0:kpb * n_off[i]:kpb]
-    np.testing.assert_array_equal(counts.cpu().numpy(), keep.sum(-1))
-    assert (counts.cpu().numpy() < n_off).any(), "nothing pruned: the correction is untested"
-    r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=Bq, block_k=Bk, mode="absolute", table=tab.T,
-                              budget_slice=sl, forced_keep=keep, band=BAND,
-                              mean_correction=True, query_blocks=query_blocks)
-    blocks = range(nqb) if query_blocks is None else query_blocks
-    rows = np.zeros(N, bool)
-    for i in blocks:
-        mg = r.margin[:, :, i, :n_off[i]]
-        out = np.abs(mg) > BAND
-        np.testing.assert_array_equal(r.keep[:, :, i, :n_off[i]][out], keep[:, :, i, :n_off[i]][out])
-        rows[i * Bq:min((i + 1) * Bq, N)] = True
-    Oh = O.cpu().numpy()
-    assert np.isfinite(Oh[:, rows]).all()
-    err = np.abs(Oh[:, rows] - r.out[:, rows])
-    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
-    return O, r, keep
 
 
 CASES = {   # name: (B, N, P, Hq, Hkv, d, Bq, Bk, query blocks checked or None for all)
@@ -120,9 +59,10 @@ def test_mean_correction_parity(name):
     Q, K, V = _inputs(31, N + P, Hq, Hkv, d, B)
     Q = Q[:, P:]
     (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
-    tab = _quantile_table(Qh, Kh, Bq, Bk)
+    tab = quantile_table(Qh, Kh, Bq, Bk)
     for sl in (0, 1):
-        _mean_parity(Qd, Kd, Vd, Qh, Kh, Vh, Bq=Bq, Bk=Bk, tab=tab, sl=sl, query_blocks=qb)
+        absolute_parity(Qd, Kd, Vd, Qh, Kh, Vh, Bq=Bq, Bk=Bk, tab=tab, sl=sl, query_blocks=qb,
+                        mean_correction=True)
 
 
 @pytest.mark.parametrize("Bq,Bk,d", [(128, 64, 128), (64, 64, 64), (128, 128, 128)])
@@ -163,38 +103,11 @@ def test_nothing_pruned_is_bitwise_the_uncorrected_call(T):
     assert torch.equal(a, b)
 
 
-def _varlen(seed, Hq, Hkv, d, nq, nk):
-    g = torch.Generator().manual_seed(seed)
-    cu_q = np.cumsum([0] + nq).astype(np.int32)
-    cu_k = np.cumsum([0] + nk).astype(np.int32)
-    Q = torch.randn(int(cu_q[-1]), Hq, d, generator=g) * 1.5
-    K = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
-    V = torch.randn(int(cu_k[-1]), Hkv, d, generator=g)
-    return Q, K, V, cu_q, cu_k
-
-
-def _pages(X, cu, page, seed):
-    rng = np.random.default_rng(seed)
-    lens = np.diff(cu)
-    n_pages = [-(-int(n) // page) for n in lens]
-    free = list(rng.permutation(sum(n_pages) + 3))
-    pool = torch.full((len(free), page) + tuple(X.shape[1:]), float("nan"), dtype=X.dtype,
-                      device=X.device)
-    table = torch.zeros((len(lens), max(max(n_pages), 1)), dtype=torch.int32)
-    for b, n in enumerate(lens):
-        for j in range(n_pages[b]):
-            pg = free.pop()
-            table[b, j] = int(pg)
-            m = min(page, int(n) - j * page)
-            pool[pg, :m] = X[cu[b] + j * page: cu[b] + j * page + m]
-    return pool, table.cuda()
-
-
 @pytest.mark.parametrize("Bk", [64, 128])
 def test_varlen_and_paged_equal_one_call_per_sequence_bitwise(Bk):
     Hq, Hkv, d, Bq = 8, 2, 128, 128
     nq, nk = [1000, 0, 300, 128, 517], [1000, 0, 556, 256, 773]
-    Q, K, V, cu_q, cu_k = _varlen(34, Hq, Hkv, d, nq, nk)
+    Q, K, V, cu_q, cu_k = varlen_batch(34, Hq, Hkv, d, nq, nk)
     (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
     # thresholds around the median block maximum of these inputs: about half the blocks pruned
     T = np.random.default_rng(5).uniform(5.0, 6.5, (1, Hq, 16)).astype(np.float32)
@@ -203,8 +116,8 @@ def test_varlen_and_paged_equal_one_call_per_sequence_bitwise(Bk):
               mean_correction=True)
     cq, ck = torch.tensor(cu_q, device="cuda"), torch.tensor(cu_k, device="cuda")
     Ov = _lib.bsfa_prefill_varlen(Qd, Kd, Vd, cq, ck, max(nq), max(nk), **kw)
-    Kp, tbl = _pages(Kd, cu_k, 128, 9)
-    Vp, _ = _pages(Vd, cu_k, 128, 9)
+    Kp, tbl = pages_of(Kd, cu_k, 128, 9)
+    Vp, _ = pages_of(Vd, cu_k, 128, 9)
     lens = torch.tensor(np.diff(cu_k), dtype=torch.int32, device="cuda")
     Op = _lib.bsfa_prefill_paged(Qd, Kp, Vp, cq, lens, tbl, max(nq), max(nk), **kw)
     plain = dict(kw, mean_correction=False)
@@ -226,7 +139,7 @@ def test_varlen_and_paged_equal_one_call_per_sequence_bitwise(Bk):
 def test_varlen_mean_correction_matches_oracle():
     Hq, Hkv, d, Bq = 4, 2, 64, 64
     nq, nk = [200, 333, 64], [328, 333, 192]
-    Q, K, V, cu_q, cu_k = _varlen(35, Hq, Hkv, d, nq, nk)
+    Q, K, V, cu_q, cu_k = varlen_batch(35, Hq, Hkv, d, nq, nk)
     (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
     T = np.full((1, Hq, 8), 5.3, np.float32)      # about the median block maximum here
     tab = make_table(T, Bq, d, [1])
