@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "gated prefill attn ms + executed TFLOP/s (% MFMA peak) at 32K/128K vs dense"
 PEAK_BF16_TFLOPS = 2500.0          # MI355X dense bf16 MFMA, published
+PEAK_FP8_TFLOPS = 5000.0           # MI355X dense fp8 MFMA, published
 PEAK_HBM_GBS = 8000.0
 GOLDEN = os.path.join(ROOT, "tests", "golden")
 
@@ -219,15 +220,16 @@ class Workload:
         self.n_off_total = sum(n_off for n_off, _ in rng)     # off-diagonal gate blocks
 
     def call(self, mode, budget_slice=0, log_lambda=-math.inf, table=None, workspace=None,
-             mean_correction=False):
+             mean_correction=False, gate_dtype="bf16"):
         import torch
         from block_sparse_long_amd import _lib
         if workspace is None and mode == "absolute":
-            attr = "workspace_mean" if mean_correction else "workspace"
+            attr = f"workspace_{int(mean_correction)}_{gate_dtype}"
             if getattr(self, attr, None) is None:
                 n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq,
                                                       block_k=self.Bk,
-                                                      mean_correction=mean_correction)
+                                                      mean_correction=mean_correction,
+                                                      gate_dtype=gate_dtype)
                 setattr(self, attr, torch.empty(n, dtype=torch.uint8, device=self.Qd.device))
             workspace = getattr(self, attr)
         _lib.bsfa_prefill(self.Qd, self.Kd, self.Vd, self.O, block_q=self.Bq, block_k=self.Bk,
@@ -235,7 +237,7 @@ class Workload:
                           (self.dtable if mode == "absolute" else None),
                           budget_slice=budget_slice, log_lambda=log_lambda,
                           kept_counts=self.counts, workspace=workspace,
-                          mean_correction=mean_correction)
+                          mean_correction=mean_correction, gate_dtype=gate_dtype)
 
 
 def timed(fn, steps, warmup):
@@ -350,6 +352,49 @@ def run_mean_correction(w, steps, warmup, gated_ms, dense_ms):
                                   "corrected": round(dev["mean"][1], 7)}}
 
 
+def run_fp8_gate(w, steps, warmup, gated, dense_ms):
+    """The gated call with FP8 gate scores (its own table, calibrated on FP8 scores): the call,
+    its FP8 sweep on its own (bsfa_gate_masks), kept density, and the deviation of its output
+    from the bf16-gated and the dense outputs. None if the table is not there."""
+    import torch
+    from block_sparse_long_amd import _lib
+    from block_sparse_long_amd.table import ThresholdTable
+    path = os.path.join(GOLDEN, f"thresholds_{w.name}_fp8.bin")
+    if not os.path.exists(path):
+        return None
+    tab = ThresholdTable.load(path).to_device(w.Qd.device)
+    r = run_gate(w, "absolute", steps, warmup, table=tab, gate_dtype="fp8")
+    buf = torch.empty(_lib.bsfa_prefill_workspace_bytes(w.Qd, w.Kd, block_q=w.Bq,
+                                                        gate_dtype="fp8"),
+                      dtype=torch.uint8, device=w.Qd.device)
+    sw_ms, _ = timed(lambda: _lib.bsfa_gate_masks(w.Qd, w.Kd, tab, 0, buf, block_q=w.Bq,
+                                                  gate_dtype="fp8"), steps, warmup)
+    fl = sweep_flops(w)
+    outs = {}
+    for key, kw in (("dense", dict(mode="dense")), ("bf16", dict(mode="absolute")),
+                    ("fp8", dict(mode="absolute", table=tab, gate_dtype="fp8"))):
+        w.call(**kw)
+        outs[key] = w.O.clone()
+    torch.cuda.synchronize()
+    dev = {}
+    for a_, b_ in (("fp8", "bf16"), ("fp8", "dense"), ("bf16", "dense")):
+        tot = 0.0
+        for r0 in range(0, w.N, 8192):
+            tot += (outs[a_][:, r0:r0 + 8192].float()
+                    - outs[b_][:, r0:r0 + 8192].float()).abs().sum().item()
+        dev[f"{a_}_vs_{b_}"] = round(tot / outs[a_].numel(), 7)
+    del outs
+    torch.cuda.empty_cache()
+    return {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
+            "speedup_vs_dense": round(dense_ms / r["ms"], 4),
+            "vs_bf16_gate": round(r["ms"] / gated["ms"], 4),
+            "kept_fraction": round(r["kept_fraction"], 4),
+            "kept_fraction_bf16_gate": round(gated["kept_fraction"], 4),
+            "sweep": {"ms": round(sw_ms, 3), "tflops": round(fl / sw_ms / 1e9, 2),
+                      "pct_fp8_peak": round(100.0 * fl / sw_ms / 1e9 / PEAK_FP8_TFLOPS, 2)},
+            "mean_abs_output_deviation": dev}
+
+
 def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
     """The oracle as it stands, single-threaded BLAS, on a bounded sample of the workload."""
     import numpy as np
@@ -451,6 +496,9 @@ def main():
     if w.table is not None:
         extras["mean_correction"] = run_mean_correction(w, args.steps, args.warmup, gated["ms"],
                                                         dense["ms"])
+        fp8 = run_fp8_gate(w, args.steps, args.warmup, gated, dense["ms"])
+        if fp8 is not None:
+            extras["fp8_gate"] = fp8
 
     if not args.quick and w.table is not None:
         # chunked prefill of the same sequence (chunks of 16K after their KV prefix)

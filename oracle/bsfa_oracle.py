@@ -127,16 +127,20 @@ def quantize_e4m3(x) -> np.ndarray:
     E4M3: sign, 4 exponent bits (bias 7), 3 mantissa bits; normal values 2^e (1 + m/8) for
     e = -6 .. 8 (the largest finite one 448 = 2^8 * 1.75), subnormals m * 2^-9. The grid step
     near |x| is 2^(max(e, -6) - 3) with e = floor(log2 |x|); rounding to that step is exact in
-    float64 and numpy rounds halves to even. Returns float32.
+    float64 and numpy rounds halves to even. Returns float32. (Elementwise; done in slices of
+    2^20 values so that the float64 temporaries stay small.)
     """
-    x = np.asarray(x, dtype=np.float32).astype(np.float64)
-    a = np.abs(x)
-    with np.errstate(divide="ignore"):
+    x = np.asarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.float32)
+    src, dst = x.reshape(-1), out.reshape(-1)
+    for s0 in range(0, src.size, 1 << 20):
+        v = src[s0:s0 + (1 << 20)].astype(np.float64)
+        a = np.abs(v)
         e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
-    step = np.exp2(np.maximum(e, -6.0) - 3.0)
-    q = np.round(a / step) * step
-    q = np.minimum(q, E4M3_MAX)
-    return (np.sign(x) * q).astype(np.float32)
+        step = np.exp2(np.maximum(e, -6.0) - 3.0)
+        q = np.minimum(np.round(a / step) * step, E4M3_MAX)
+        dst[s0:s0 + (1 << 20)] = np.sign(v) * q
+    return out
 
 
 def _e4m3_codes(x, amax):
@@ -146,7 +150,8 @@ def _e4m3_codes(x, amax):
     amax = np.asarray(amax, dtype=np.float32)
     safe = np.where(amax > 0, amax, np.float32(1))
     inv = np.where(amax > 0, np.float32(E4M3_MAX) / safe, np.float32(0)).astype(np.float32)
-    y = np.clip((x * inv).astype(np.float32), -E4M3_MAX, E4M3_MAX)
+    lim = np.float32(E4M3_MAX)
+    y = np.minimum(np.maximum((x * inv).astype(np.float32), -lim), lim)
     scale = np.where(amax > 0, safe / np.float32(E4M3_MAX), np.float32(0)).astype(np.float32)
     return quantize_e4m3(y), scale
 
@@ -225,9 +230,12 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
     blocks = range(nqb) if query_blocks is None else sorted(set(int(x) for x in query_blocks))
 
     if gate_dtype == "fp8":
+        # the dequantised copies, (q8 sq) . (k8 sk) = sq sk (q8 . k8), in the oracle's
+        # precision (exact in float64)
         q8, q8s = quantize_q_rows(Q)
         k8, k8s = quantize_k_tiles(K)
-        k8s_key = np.repeat(k8s, 64, axis=1)[:, :Nk]               # [B, Nk, Hkv]: its tile's
+        Q8f = (q8.astype(np.float64) * q8s[..., None]).astype(dtype)
+        K8f = (k8.astype(np.float64) * np.repeat(k8s, 64, axis=1)[:, :Nk, :, None]).astype(dtype)
     out = np.full((B, N, Hq, d), np.nan, dtype=dtype)
     kept_counts = np.full((B, Hq, nqb), -1, dtype=np.int64)
     stat = np.full((B, Hq, nqb, nkb), np.nan, dtype=np.float64)
@@ -282,10 +290,7 @@ def oracle_prefill(Q, K, V, *, block_q: int, block_k: int, mode: str,
                                 thr = float(log_lambda)
                             elif gate_dtype == "fp8" and mode == GATE_ABSOLUTE:
                                 # the same tile maximum over FP8 scores
-                                s8 = (q8[b, r0:r1, h, :].astype(np.float64)
-                                      @ k8[b, c0:c1, g, :].T.astype(np.float64))
-                                s8 *= q8s[b, r0:r1, h, None].astype(np.float64)
-                                s8 *= k8s_key[b, None, c0:c1, g].astype(np.float64)
+                                s8 = Q8f[b, r0:r1, h, :] @ K8f[b, c0:c1, g, :].T
                                 st = float(s8.max()) * float(sc)
                                 thr = te
                             else:
@@ -387,9 +392,13 @@ def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float 
     """
     fp8 = gate_dtype == "fp8"
     if fp8:
+        # the dequantised copies, (q8 sq) . (k8 sk) = sq sk (q8 . k8), in the oracle's
+        # precision (exact in float64)
         q8, q8s = quantize_q_rows(Q)
         k8, k8s = quantize_k_tiles(K)
-        k8s_key = np.repeat(k8s, 64, axis=1)[:, :np.asarray(K).shape[1]]
+        Qf = (q8.astype(np.float64) * q8s[..., None]).astype(dtype)
+        Kf = (k8.astype(np.float64) * np.repeat(k8s, 64, axis=1)[:, :k8.shape[1], :, None]
+              ).astype(dtype)
     Q = np.asarray(Q, dtype=dtype)
     K = np.asarray(K, dtype=dtype)
     B, N, Hq, d = Q.shape
@@ -408,11 +417,7 @@ def off_diagonal_block_maxima(Q, K, *, block_q: int, block_k: int, scale: float 
                 r0, r1 = i * block_q, min((i + 1) * block_q, N)
                 c1 = n_off * block_k
                 if fp8:
-                    s = (q8[b, r0:r1, h, :].astype(np.float64)
-                         @ k8[b, :c1, g, :].T.astype(np.float64))
-                    s *= q8s[b, r0:r1, h, None].astype(np.float64)
-                    s *= k8s_key[b, None, :c1, g].astype(np.float64)
-                    s *= float(sc)
+                    s = (Qf[b, r0:r1, h, :] @ Kf[b, :c1, g, :].T) * sc
                 else:
                     s = (Q[b, r0:r1, h, :] @ K[b, :c1, g, :].T) * sc
                 sm[b, h, i, :n_off] = s.reshape(r1 - r0, n_off, block_k).max(axis=(0, 2))

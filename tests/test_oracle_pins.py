@@ -818,14 +818,18 @@ def test_fp8_block_maxima_brute_force(Bk):
     Qd = (q8 * qs[..., None]).astype(np.float64)
     Kd = (k8 * np.repeat(ks, 64, axis=1)[:, :N, :, None]).astype(np.float64)
     bm = brute_block_max(Qd, Kd, Bq, Bk)
-    sm = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, gate_dtype="fp8")
+    sm = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, gate_dtype="fp8",
+                                          dtype=np.float64)
+    sm32 = oracle.off_diagonal_block_maxima(Q, K, block_q=Bq, block_k=Bk, gate_dtype="fp8")
     T = _const_table(math.inf, Hq, 8)
     r = oracle_prefill(Q, K, V, block_q=Bq, block_k=Bk, mode=GATE_ABSOLUTE, table=T,
-                       gate_dtype="fp8")
+                       gate_dtype="fp8", dtype=np.float64)
     for i in range(-(-N // Bq)):
         n_off = key_block_range(i, N, Bq, Bk)[0]
         # (the oracle holds the softmax scale in float32, as the device does: 2^-24 relative)
         np.testing.assert_allclose(sm[:, :, i, :n_off], bm[:, :, i, :n_off], rtol=2e-7, atol=0)
+        # the default float32 run: float32 operands and sums
+        np.testing.assert_allclose(sm32[:, :, i, :n_off], bm[:, :, i, :n_off], rtol=1e-5, atol=1e-6)
         np.testing.assert_allclose(r.stat[:, :, i, :n_off], bm[:, :, i, :n_off], rtol=2e-7,
                                    atol=0)
 
