@@ -35,8 +35,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so"
 
 EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
             "bsfa_prefill_workspace_bytes",
-            "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_status_string", "bsfa_last_error",
-            "bsfa_version")
+            "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_calibrate_workspace_bytes",
+            "bsfa_status_string", "bsfa_last_error", "bsfa_version")
 
 
 class BsfaProblem(ctypes.Structure):
@@ -99,7 +99,10 @@ def load_library(path: str = LIB_PATH):
                                     ctypes.c_int32, vp, ctypes.c_uint64, vp, vp]
     lib.bsfa_calibrate_blockmax.restype = ctypes.c_int32
     lib.bsfa_calibrate_blockmax.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp,
-                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp, vp]
+                                            ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp,
+                                            vp, ctypes.c_uint64, vp]
+    lib.bsfa_calibrate_workspace_bytes.restype = ctypes.c_uint64
+    lib.bsfa_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem)]
     lib.bsfa_status_string.restype = ctypes.c_char_p
     lib.bsfa_status_string.argtypes = [ctypes.c_int32]
     lib.bsfa_last_error.restype = ctypes.c_char_p
@@ -382,18 +385,27 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
 
 
 def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_k: int = 64,
-                            softmax_scale: float = 0.0, stream=None):
-    """k-th highest off-diagonal block max per (budget, b, h, i): fp32 [n_budgets, B, Hq, nqb]."""
+                            softmax_scale: float = 0.0, stream=None, gate_dtype="bf16",
+                            workspace=None):
+    """k-th highest off-diagonal block max per (budget, b, h, i): fp32 [n_budgets, B, Hq, nqb].
+    ``gate_dtype`` "fp8": on the FP8 gate's scores (a workspace is allocated if None)."""
     import torch
     lib = load_library()
     B, N, Hq, _ = Q.shape
     nqb = -(-N // block_q)
     if kth_out is None:
         kth_out = torch.empty((len(budgets), B, Hq, nqb), dtype=torch.float32, device=Q.device)
-    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale)
+    p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
+                     gate_dtype=gate_dtype)
+    if workspace is None:
+        n = int(lib.bsfa_calibrate_workspace_bytes(ctypes.byref(p)))
+        if n:
+            workspace = torch.empty(n, dtype=torch.uint8, device=Q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     arr = (ctypes.c_int32 * max(1, len(budgets)))(*[int(k) for k in budgets])
     st = lib.bsfa_calibrate_blockmax(ctypes.byref(p), _ptr(Q), _ptr(K), arr, len(budgets),
-                                     _ptr(kth_out), _stream_handle(stream, Q.device))
+                                     _ptr(kth_out), _ptr(workspace), ctypes.c_uint64(ws_bytes),
+                                     _stream_handle(stream, Q.device))
     _check(st)
     return kth_out
 

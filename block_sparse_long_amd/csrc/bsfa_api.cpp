@@ -506,9 +506,19 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
   return ok();
 }
 
+uint64_t bsfa_calibrate_workspace_bytes(const bsfa_problem* p) {
+  if (!p || p->gate_dtype != BSFA_FP8_E4M3 || p->batch <= 0 || p->seqlen <= 0 ||
+      p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
+    return 0;
+  const WorkspaceLayout l = workspace_layout(p);
+  return align256(l.fp8_end) + (uint64_t)p->batch * p->heads_q * ceil_div(p->seqlen, p->block_q) *
+                                   ceil_div(p->seqlen, p->block_k) * 4u;
+}
+
 bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
                                     const int32_t* budgets_host, int32_t n_budgets,
-                                    float* kth_out, void* stream) {
+                                    float* kth_out, void* workspace, uint64_t workspace_bytes,
+                                    void* stream) {
   bsfa_status s = check_problem(p, false);
   if (s != BSFA_OK) return s;
   if (n_budgets < 1 || n_budgets > 16)
@@ -518,9 +528,9 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
     if (budgets_host[t] < 1) return fail(BSFA_ERR_ARG, "budget %d is < 1", budgets_host[t]);
   if (key_len(p) != p->seqlen)
     return fail(BSFA_ERR_UNSUPPORTED, "calibration takes whole sequences (kv_seqlen 0 or seqlen)");
-  if (p->gate_dtype != BSFA_BF16)
-    return fail(BSFA_ERR_UNSUPPORTED, "the calibration kernel scores in bf16 (gate_dtype %d)",
-                p->gate_dtype);
+  if (p->gate_dtype != BSFA_BF16 && p->gate_dtype != BSFA_FP8_E4M3)
+    return fail(BSFA_ERR_DTYPE, "gate_dtype %d not supported (BF16 or FP8_E4M3)", p->gate_dtype);
+  const bool fp8 = p->gate_dtype == BSFA_FP8_E4M3;
   const int nkb = ceil_div(p->seqlen, bsfa::kBlockK);   // 64-key tiles
   if (nkb > bsfa::kCalibMaxKeyBlocks)
     return fail(BSFA_ERR_UNSUPPORTED, "seqlen %d above the calibration limit %d", p->seqlen,
@@ -530,6 +540,15 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
   if (!Q || !K || !kth_out) return fail(BSFA_ERR_ARG, "Q, K and kth_out must be non-NULL");
   if (!aligned16(Q) || !aligned16(K)) return fail(BSFA_ERR_ALIGN, "Q and K must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(kth_out) & 3u) return fail(BSFA_ERR_ALIGN, "kth_out misaligned");
+  const uint64_t ws_need = bsfa_calibrate_workspace_bytes(p);
+  if (fp8 && !workspace)
+    return fail(BSFA_ERR_ARG, "FP8 calibration needs a workspace of %llu bytes",
+                (unsigned long long)ws_need);
+  if (fp8 && (reinterpret_cast<uintptr_t>(workspace) & 15u))
+    return fail(BSFA_ERR_ALIGN, "the workspace is not 16-byte aligned");
+  if (fp8 && workspace_bytes < ws_need)
+    return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
+                (unsigned long long)workspace_bytes, (unsigned long long)ws_need);
 
   bsfa::CalibArgs a;
   memset(&a, 0, sizeof(a));
@@ -555,7 +574,25 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
   a.n_budgets = n_budgets;
   for (int t = 0; t < n_budgets; ++t) a.budgets[t] = budgets_host[t];
   a.kth = kth_out;
-  hipError_t e = bsfa::launch_calibrate(a, p->head_dim, p->block_q, static_cast<hipStream_t>(stream));
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (fp8) {
+    // the FP8 gate sweep without a table dumps every off-diagonal block maximum; then the
+    // k-th highest of each (b, h, i)
+    char* const ws = static_cast<char*>(workspace);
+    float* const maxima = reinterpret_cast<float*>(ws + align256(workspace_layout(p).fp8_end));
+    bsfa::PrefillArgs sw = base_args(p, Q, K, nullptr, nullptr, 0, BSFA_GATE_DENSE);
+    sw.keep_mask = reinterpret_cast<unsigned long long*>(ws);
+    sw.dbg = maxima;
+    hipError_t e = set_fp8(sw, p, workspace, st);
+    if (e == hipSuccess) e = launch_sweep(sw, p, st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "FP8 maxima launch: %s", hipGetErrorString(e));
+    bsfa::CalibArgs ca = a;
+    ca.nkb = sw.nkb;   // the dump's row length: gate blocks
+    e = bsfa::launch_kth_select(ca, maxima, p->block_q, st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "k-th select launch: %s", hipGetErrorString(e));
+    return ok();
+  }
+  hipError_t e = bsfa::launch_calibrate(a, p->head_dim, p->block_q, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "calibration launch: %s", hipGetErrorString(e));
   return ok();
 }

@@ -111,6 +111,10 @@ constexpr int kMaxGateTiles = 32768;
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
                           hipStream_t stream);
 hipError_t launch_calibrate(const CalibArgs& a, int head_dim, int block_q, hipStream_t stream);
+// k-th highest per (budget, b, h, i) from a dump of the off-diagonal gate-block maxima
+// (fp32 [B][Hq][nqb][nkb]); uses a.B, Hq, nqb, nkb, kpb, budgets, n_budgets, kth.
+hipError_t launch_kth_select(const CalibArgs& a, const float* maxima, int block_q,
+                             hipStream_t stream);
 // The gate sweep for the absolute gate: fills a.keep_mask (and the off-diagonal entries of
 // a.dbg). a.units must describe launch_gate_sweep's own workgroups (gate_sweep_heads()).
 hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream);

@@ -266,12 +266,24 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
  *   budgets_host  host int32 [n_budgets], each >= 1
  *   n_budgets     1 .. 16
  *   kth_out       device fp32 [n_budgets][B][Hq][ceil(N/Bq)]
+ *   workspace     device, 16-byte aligned, caller-owned scratch of workspace_bytes, or NULL;
+ *                 needed only with gate_dtype FP8_E4M3 (at least
+ *                 bsfa_calibrate_workspace_bytes(p) bytes): thresholds for an FP8 gate are
+ *                 calibrated on its own scores (FP8 copies of Q and K, the FP8 gate sweep's
+ *                 block maxima, then the k-th highest); the bf16 scores need none
  *   stream        hipStream_t
  * This build supports seqlen up to 262144 here, whole sequences only (kv_seqlen 0 or equal to
  * seqlen; BSFA_ERR_UNSUPPORTED otherwise). */
 bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
                                     const int32_t* budgets_host, int32_t n_budgets,
-                                    float* kth_out, void* stream);
+                                    float* kth_out, void* workspace, uint64_t workspace_bytes,
+                                    void* stream);
+
+/* Bytes of workspace bsfa_calibrate_blockmax needs for `p` (0 for bf16 scores): with
+ * gate_dtype FP8_E4M3, the layout of bsfa_prefill_workspace_bytes(p, ABSOLUTE) without the
+ * block means, then (on a 256-byte boundary) fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] block
+ * maxima. */
+uint64_t bsfa_calibrate_workspace_bytes(const bsfa_problem* p);
 
 /* Static description of a status code. Never NULL. */
 const char* bsfa_status_string(int32_t status);

@@ -207,7 +207,8 @@ def test_kv_seqlen_validation():
     assert call_masks(p, table(t_len=4)) == _lib.BSFA_ERR_SHAPE
     # calibration takes whole sequences
     arr = (ctypes.c_int32 * 1)(4)
-    assert lib.bsfa_calibrate_blockmax(ctypes.byref(p), FAKE, FAKE, arr, 1, FAKE, None) == \
+    assert lib.bsfa_calibrate_blockmax(ctypes.byref(p), FAKE, FAKE, arr, 1, FAKE, None, 0,
+                                       None) == \
         _lib.BSFA_ERR_UNSUPPORTED
     # the masks cover the keys: 65 key tiles after a prefix need two words per query block
     p.kv_seqlen = 65 * 64
@@ -270,11 +271,11 @@ def test_absolute_gate_length_limit():
     assert st == _lib.BSFA_ERR_UNSUPPORTED
 
 
-def call_calib(p, budgets, q=FAKE, k=FAKE, out=FAKE):
+def call_calib(p, budgets, q=FAKE, k=FAKE, out=FAKE, ws=None, ws_bytes=0):
     lib = _lib.load_library()
     arr = (ctypes.c_int32 * max(1, len(budgets)))(*budgets)
     return lib.bsfa_calibrate_blockmax(ctypes.byref(p), q, k, arr if budgets is not None else None,
-                                       len(budgets), out, None)
+                                       len(budgets), out, ws, ws_bytes, None)
 
 
 def test_calibrate_validation():
@@ -374,5 +375,12 @@ def test_fp8_gate_workspace_and_validation():
     assert call_masks(p, table(t_len=8), mask_bytes=need - 8) == _lib.BSFA_ERR_ARG
     assert f"required {need}" in _lib.bsfa_last_error()
     assert call_masks(p, table(t_len=8), mask=FAKE + 8, mask_bytes=need) == _lib.BSFA_ERR_ALIGN
-    # the calibration kernel scores in bf16
-    assert call_calib(p, [1]) == _lib.BSFA_ERR_UNSUPPORTED
+    # FP8 calibration: the FP8 copies and the block maxima live in a workspace
+    cw = lib.bsfa_calibrate_workspace_bytes(ctypes.byref(p))
+    nqb, nkb = -(-N // p.block_q), -(-N // p.block_k)
+    assert cw == r256(need) + B * Hq * nqb * nkb * 4
+    assert call_calib(p, [1]) == _lib.BSFA_ERR_ARG
+    assert call_calib(p, [1], ws=FAKE, ws_bytes=cw - 4) == _lib.BSFA_ERR_ARG
+    assert call_calib(p, [1], ws=FAKE + 8, ws_bytes=cw) == _lib.BSFA_ERR_ALIGN
+    p.gate_dtype = _lib.BSFA_BF16
+    assert lib.bsfa_calibrate_workspace_bytes(ctypes.byref(p)) == 0

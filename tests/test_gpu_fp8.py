@@ -211,3 +211,27 @@ def test_fp8_varlen_matches_oracle():
                                      forced_keep=keep, band=1e-2)
     err = np.abs(O.cpu().numpy() - r.out)
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("Bk", [64, 128])
+def test_fp8_calibration_matches_oracle(Bk):
+    # thresholds for an FP8 gate are calibrated on its own scores: the k-th highest FP8 block
+    # maximum per (b, h, i)
+    B, N, Hq, Hkv, d, Bq = 1, 1000, 8, 2, 128, 128
+    Q, K, _ = _inputs(56, N, Hq, Hkv, d)
+    (Qd, Kd), (Qh, Kh) = bf16_pair(Q, K)
+    budgets = [1, 2, 3, 5]
+    kth = _lib.bsfa_calibrate_blockmax(Qd, Kd, budgets, block_q=Bq, block_k=Bk, gate_dtype="fp8")
+    torch.cuda.synchronize()
+    kth = kth.cpu().numpy()
+    sm = oracle.off_diagonal_block_maxima(Qh, Kh, block_q=Bq, block_k=Bk, gate_dtype="fp8")
+    for kk, k in enumerate(budgets):
+        for h in range(Hq):
+            for i in range(-(-N // Bq)):
+                n_off = oracle.key_block_range(i, N, Bq, Bk)[0]
+                ref = oracle.kth_highest(sm[0, h, i], n_off, k)
+                got = kth[kk, 0, h, i]
+                if math.isinf(ref):
+                    assert got == ref
+                else:
+                    assert abs(got - ref) <= 1e-3, (k, h, i, got, ref)
