@@ -954,6 +954,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     // scored against Q by MFMAs over the mean key's bf16 high and low parts in turn, masked
     // where the block was kept or does not exist, then the online-softmax update and the PV
     // product of a key tile. Blocks are whole here: off-diagonal blocks never reach the end.
+    // (The walk has drained: its last barrier waited for every copy.)
     if (two_pass && kept_all < n_off) {
       const int n_gb = min(n_off / a.kpb, a.mean_blocks);
       const long long mbase = ((long long)b * a.Hkv + g) * a.mean_blocks * D;
@@ -964,14 +965,29 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       copy_offsets<D, STR, NW>(mko, D, w, lane);
       copy_offsets<D, STRV, NW>(mvo, D, w, lane);
       const int hs = lane >> 5;
-      for (int m0 = 0; m0 < n_gb; m0 += 64) {
-        const int valid = min(64, n_gb - m0);
-        __syncthreads();   // every wave is done with the tile buffers
-        copy_tile<D, STR, NW>(mko, khi + (long long)m0 * D, 2u * D, valid, sK0, w, lane);
-        copy_tile<D, STR, NW>(mko, klo + (long long)m0 * D, 2u * D, valid, sK1, w, lane);
-        copy_tile<D, STRV, NW>(mvo, vme + (long long)m0 * D, 2u * D, valid, sV0, w, lane);
+      // mean tile m0 (pseudo-keys m0 .. m0 + 63): k-bar parts in sK0 / sK1, v-bar in sV0 or
+      // sV1 by parity. The next tile's v-bar is copied into the other V buffer during this
+      // tile's scores, and its k-bar parts once every wave has read this tile's (a second
+      // barrier), during the exponentials and the PV product.
+      auto stage_k = [&](int m) {
+        const int valid = min(64, n_gb - m);
+        copy_tile<D, STR, NW>(mko, khi + (long long)m * D, 2u * D, valid, sK0, w, lane);
+        copy_tile<D, STR, NW>(mko, klo + (long long)m * D, 2u * D, valid, sK1, w, lane);
+      };
+      auto stage_v = [&](int m, __bf16* dst) {
+        copy_tile<D, STRV, NW>(mvo, vme + (long long)m * D, 2u * D, min(64, n_gb - m), dst, w,
+                               lane);
+      };
+      __syncthreads();   // every wave is done with the walk's tile buffers
+      stage_k(0);
+      stage_v(0, sV0);
+      bool par = false;
+      for (int m0 = 0; m0 < n_gb; m0 += 64, par = !par) {
+        __bf16* const sv = par ? sV1 : sV0;
+        const bool more = m0 + 64 < n_gb;
         wait_vmem();
-        __syncthreads();
+        __syncthreads();   // tile m0 visible; every wave is done with the other V buffer
+        if (more) stage_v(m0 + 64, par ? sV0 : sV1);
         // S^T of the pseudo-keys: the high and low parts into one accumulator
         f32x16 sm[2];
 #pragma unroll
@@ -987,6 +1003,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
             sm[mb] = mfma32(*reinterpret_cast<const bf16x8*>(sK0 + ko), qf[ks], sm[mb]);
             sm[mb] = mfma32(*reinterpret_cast<const bf16x8*>(sK1 + ko), qf[ks], sm[mb]);
           }
+        __syncthreads();   // every wave has read this tile's k-bar parts
+        if (more) stage_k(m0 + 64);
         float mx = kNegInf;
 #pragma unroll
         for (int mb = 0; mb < 2; ++mb)
@@ -1013,8 +1031,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 #pragma unroll
         for (int pi = 0; pi < kPairs; ++pi) exp_pair(pi, sm, -st.mref * c, c, pm, sum);
         st.l += sum;
-        pv_prefetch<D>(sV0, vb, lane);
-        pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sV0, pm, o, vb, sm, 0.f, c, dummy,
+        pv_prefetch<D>(sv, vb, lane);
+        pv_steps<D, 0, NSTEP, NSTEP, 1>(true, false, false, sv, pm, o, vb, sm, 0.f, c, dummy,
                                         dsum, lane, [](int) {});
       }
     }
