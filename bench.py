@@ -46,9 +46,10 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 1 GiB device copy and one gated call, then exit (counter runs)")
-    ap.add_argument("--counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="summarise two rocprofv3 --pmc runs of --profile-once (FETCH_SIZE, "
-                         "WRITE_SIZE) into profiles/traffic_<workload>.json")
+    ap.add_argument("--counters", nargs="+", metavar="DIR",
+                    help="summarise rocprofv3 --pmc runs of --profile-once: FETCH_SIZE, "
+                         "WRITE_SIZE and optionally MfmaUtil MfmaFlopsBF16 "
+                         "SQ_INSTS_VALU_MFMA_MOPS_F8, into profiles/traffic_<workload>.json")
     return ap.parse_args()
 
 
@@ -66,20 +67,22 @@ def kernel_source_sha256():
     return h.hexdigest()
 
 
-def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` (a name prefix) from the committed counter summary, if
-    it was taken on the current kernel source; else None."""
+def measured_counters(workload, kernel):
+    """The committed counter summary of `kernel` (its profiler name), if it was taken on the
+    current kernel source; else {}."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
     if not os.path.exists(path):
-        return None
+        return {}
     with open(path) as f:
         rec = json.load(f)
     if rec.get("kernel_source_sha256") != kernel_source_sha256():
-        return None
-    for k, v in rec.get("kernels", {}).items():
-        if k.startswith(kernel):
-            return v["hbm_bytes_per_launch"]
-    return None
+        return {}
+    return rec.get("kernels", {}).get(kernel, {})
+
+
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None."""
+    return measured_counters(workload, kernel).get("hbm_bytes_per_launch")
 
 
 def summarise_counters(args):
@@ -103,6 +106,8 @@ def summarise_counters(args):
                 rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
         return rows
 
+    if len(args.counters) not in (2, 3):
+        sys.exit("--counters takes FETCH_DIR WRITE_DIR [MFMA_DIR]")
     fetch, write = per_dispatch(args.counters[0], "FETCH_SIZE"), per_dispatch(args.counters[1],
                                                                               "WRITE_SIZE")
     def copy_kib(rows):
@@ -123,6 +128,16 @@ def summarise_counters(args):
             k[f"{tag}_bytes"] = kib * 1024.0 * sc
     for k in kernels.values():
         k["hbm_bytes_per_launch"] = k.get("fetch_bytes", 0.0) + k.get("write_bytes", 0.0)
+    # MFMA counters (third run): rocprofv3's derived MfmaUtil (MFMA-busy cycles per SIMD over
+    # GPU-active cycles, %) and MfmaFlopsBF16 (bf16 MFMA ops x 512), and the FP8 op count
+    if len(args.counters) == 3:
+        for counter, key, sc in (("MfmaUtil", "mfma_util_pct", 1.0),
+                                 ("MfmaFlopsBF16", "mfma_flops_bf16", 1.0),
+                                 ("SQ_INSTS_VALU_MFMA_MOPS_F8", "mfma_flops_f8", 512.0)):
+            for (_, name), v in per_dispatch(args.counters[2], counter).items():
+                m = re.search(r"bsfa::\(anonymous namespace\)::(\w+<[^>]*>)", name)
+                if m and m.group(1) in kernels:
+                    kernels[m.group(1)][key] = v * sc
     rec = {"workload": args.workload, "kernel_source_sha256": kernel_source_sha256(),
            "copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": fk, "copy_write_kib": wk, "kernels": kernels,
@@ -131,8 +146,11 @@ def summarise_counters(args):
                         "<repo>/bench.py --profile-once --workload " + args.workload,
                         "rocprofv3 --pmc WRITE_SIZE -d <write_dir> -- python3 "
                         "<repo>/bench.py --profile-once --workload " + args.workload,
-                        "python3 bench.py --counters <fetch_dir> <write_dir> --workload "
-                        + args.workload]}
+                        "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
+                        "-d <mfma_dir> -- python3 <repo>/bench.py --profile-once --workload "
+                        + args.workload,
+                        "python3 bench.py --counters <fetch_dir> <write_dir> <mfma_dir> "
+                        "--workload " + args.workload]}
     path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -572,7 +590,13 @@ def main():
                      "frac": round(dom["flops"] / dom["ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(args.workload, dom["kernel"]),
                      "kernel": dom["kernel"], "ms_per_launch": round(dom["ms"], 3),
-                     "flops_per_launch": dom["flops"]},
+                     "flops_per_launch": dom["flops"],
+                     # from the committed counter runs of the same kernel source (else null):
+                     # MFMA-busy share of SIMD cycles and the MFMA FLOPs the hardware counted
+                     "mfma_util_pct": measured_counters(args.workload, dom["kernel"]).get(
+                         "mfma_util_pct"),
+                     "mfma_flops_counted": measured_counters(args.workload, dom["kernel"]).get(
+                         "mfma_flops_bf16")},
         "cpu_baseline": cpu,
         "extras": extras,
     }
