@@ -235,3 +235,31 @@ def test_fp8_calibration_matches_oracle(Bk):
                     assert got == ref
                 else:
                     assert abs(got - ref) <= 1e-3, (k, h, i, got, ref)
+
+
+def test_fp8_zero_rows_and_tiles():
+    # an all-zero Q row or K tile has codes 0 and scale 0: its FP8 scores are exactly 0
+    B, N, Hq, Hkv, d, Bq = 1, 700, 4, 2, 128, 128
+    Q, K, V = _inputs(57, N, Hq, Hkv, d)
+    Q[0, 100:180, 1] = 0.0          # rows of head 1 (a whole query block and more)
+    K[0, 128:192, 0] = 0.0          # key tile 2 of KV head 0
+    K[0, 320:384, 1] = 0.0          # key tile 5 of KV head 1
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    q8, qs = oracle.quantize_q_rows(Qh)
+    assert (qs[0, 100:180, 1] == 0).all()
+    tab = quantile_table(Qh, Kh, Bq, 64)
+    absolute_parity(Qd, Kd, Vd, Qh, Kh, Vh, Bq=Bq, Bk=64, tab=tab, gate_dtype="fp8")
+
+
+def test_fp8_minus_inf_threshold_is_bitwise_the_bf16_call():
+    # nothing to decide: the FP8 copies are made but no block is dropped
+    N, Hq, Hkv, d, Bq = 1000, 8, 2, 128, 128
+    Q, K, V = _inputs(58, N, Hq, Hkv, d)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    dtab = make_table(np.full((1, Hq, 8), -np.inf, np.float32), Bq, d, [1]).to_device("cuda")
+    kw = dict(block_q=Bq, gate_mode="absolute", table=dtab, out_dtype=torch.float32)
+    a = _lib.bsfa_prefill(Qd, Kd, Vd, gate_dtype="fp8", **kw)
+    b = _lib.bsfa_prefill(Qd, Kd, Vd, **kw)
+    c = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, gate_mode="dense", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(a, c)

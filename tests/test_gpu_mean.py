@@ -171,3 +171,24 @@ def test_varlen_mean_correction_matches_oracle():
                                      forced_keep=keep, band=BAND)
     err = np.abs(O.cpu().numpy() - r.out)
     assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
+
+
+@pytest.mark.parametrize("N,Bq", [(64, 64), (100, 64), (130, 128), (1, 64)])
+def test_short_sequences(N, Bq):
+    # at most one off-diagonal block: corrected and plain calls agree where nothing is pruned,
+    # and the corrected one matches the oracle where the single block is pruned (T = +inf)
+    Hq, Hkv, d = 2, 1, 64
+    g = torch.Generator().manual_seed(36)
+    Q, K, V = (torch.randn(1, N, h, d, generator=g) for h in (Hq, Hkv, Hkv))
+    (Qd, Kd, Vd), (Qh, Kh, Vh) = bf16_pair(Q, K, V)
+    T = np.full((1, Hq, 4), np.inf, np.float32)
+    tab = make_table(T, Bq, d, [1])
+    O = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, gate_mode="absolute",
+                          table=tab.to_device("cuda"), out_dtype=torch.float32,
+                          mean_correction=True)
+    torch.cuda.synchronize()
+    r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=Bq, block_k=64, mode="absolute", table=T,
+                              mean_correction=True)
+    err = np.abs(O.cpu().numpy() - r.out)
+    assert np.isfinite(O.cpu().numpy()).all()
+    assert err.max() <= MAX_ABS and err.mean() <= MEAN_ABS, (err.max(), err.mean())
