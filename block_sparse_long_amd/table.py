@@ -99,3 +99,34 @@ class DeviceTable:
         t.head_dim = self.host.head_dim
         t.softmax_scale = float(self.host.softmax_scale)
         return t
+
+
+def calibrate_table(samples, *, budgets, block_q: int, block_k: int = 64,
+                    softmax_scale: float = 0.0, gate_dtype="bf16") -> ThresholdTable:
+    """Offline calibration on the GPU ("Block Sparse Flash Attention", Method > Key Designs 1):
+    for each sample (Q [B, N, Hq, d], K [B, N, Hkv, d], bf16 device tensors; every batch entry
+    counts as one sample) the k-th highest off-diagonal block maximum per head and query block
+    (bsfa_calibrate_blockmax, on the FP8 gate's scores for gate_dtype "fp8"), then the
+    arithmetic mean over samples in float64 (-inf where a query block has fewer than k
+    candidates). All samples share one shape; T_len = their number of query blocks."""
+    import math
+    import torch
+    acc, count, shape = None, 0, None
+    for Q, K in samples:
+        if shape is None:
+            shape = tuple(Q.shape[1:])
+        elif tuple(Q.shape[1:]) != shape:
+            raise ValueError("calibration samples must share one shape")
+        kth = _lib.bsfa_calibrate_blockmax(Q, K, list(budgets), block_q=block_q, block_k=block_k,
+                                           softmax_scale=softmax_scale, gate_dtype=gate_dtype)
+        torch.cuda.synchronize(Q.device)
+        kth = kth.cpu().numpy().astype(np.float64)          # [n_budgets, B, Hq, nqb]
+        acc = kth.sum(axis=1) if acc is None else acc + kth.sum(axis=1)
+        count += kth.shape[1]
+    if not count:
+        raise ValueError("no calibration samples")
+    N, d = shape[0], shape[2]
+    scale = softmax_scale if softmax_scale > 0 else float(np.float32(1 / math.sqrt(d)))
+    return ThresholdTable(T=(acc / count).astype(np.float32), budgets=[int(k) for k in budgets],
+                          block_q=block_q, block_k=block_k, head_dim=d, softmax_scale=scale,
+                          calib_seqlen=N)

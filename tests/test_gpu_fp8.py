@@ -263,3 +263,25 @@ def test_fp8_minus_inf_threshold_is_bitwise_the_bf16_call():
     c = _lib.bsfa_prefill(Qd, Kd, Vd, block_q=Bq, gate_mode="dense", out_dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(a, c)
+
+
+@pytest.mark.parametrize("gate_dtype", ["bf16", "fp8"])
+def test_calibrate_table_matches_the_oracle_calibration(gate_dtype):
+    # the GPU tool (k-th highest per sample on the device, mean over samples on the host) against
+    # oracle.calibrate on the same two samples
+    from block_sparse_long_amd.table import calibrate_table
+    N, Hq, Hkv, d, Bq = 700, 4, 2, 128, 128
+    host, dev = [], []
+    for seed in (60, 61):
+        Q, K, _ = _inputs(seed, N, Hq, Hkv, d)
+        (Qd, Kd), (Qh, Kh) = bf16_pair(Q, K)
+        host.append((Qh, Kh))
+        dev.append((Qd, Kd))
+    budgets = [1, 3]
+    tab = calibrate_table(dev, budgets=budgets, block_q=Bq, gate_dtype=gate_dtype)
+    ref = oracle.calibrate(host, block_q=Bq, block_k=64, budgets=budgets,
+                           scale=float(np.float32(1 / math.sqrt(d))), gate_dtype=gate_dtype)
+    assert tab.T.shape == ref.shape
+    inf = np.isinf(ref)
+    np.testing.assert_array_equal(tab.T[inf], ref[inf])
+    np.testing.assert_allclose(tab.T[~inf], ref[~inf], rtol=0, atol=1e-3)
