@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--profile-once", action="store_true",
                     help="run a 1 GiB device copy and one gated call, then exit (counter runs)")
+    ap.add_argument("--gate-dtype", choices=("bf16", "fp8"), default="bf16",
+                    help="--profile-once / --counters: the gated call with bf16 or FP8 gate "
+                         "scores (FP8: its own FP8-calibrated table)")
     ap.add_argument("--counters", nargs="+", metavar="DIR",
                     help="summarise rocprofv3 --pmc runs of --profile-once: FETCH_SIZE, "
                          "WRITE_SIZE and optionally MfmaUtil MfmaFlopsBF16 "
@@ -138,20 +141,23 @@ def summarise_counters(args):
                 m = re.search(r"bsfa::\(anonymous namespace\)::(\w+<[^>]*>)", name)
                 if m and m.group(1) in kernels:
                     kernels[m.group(1)][key] = v * sc
-    rec = {"workload": args.workload, "kernel_source_sha256": kernel_source_sha256(),
+    tag = "" if args.gate_dtype == "bf16" else f" --gate-dtype {args.gate_dtype}"
+    rec = {"workload": args.workload, "gate_dtype": args.gate_dtype,
+           "kernel_source_sha256": kernel_source_sha256(),
            "copy_bytes": COPY_BYTES, "fetch_scale": f_scale, "write_scale": w_scale,
            "copy_fetch_kib": fk, "copy_write_kib": wk, "kernels": kernels,
            "commands": ["cd /tmp && export TMPDIR=/tmp",
                         "rocprofv3 --pmc FETCH_SIZE -d <fetch_dir> -- python3 "
-                        "<repo>/bench.py --profile-once --workload " + args.workload,
+                        "<repo>/bench.py --profile-once --workload " + args.workload + tag,
                         "rocprofv3 --pmc WRITE_SIZE -d <write_dir> -- python3 "
-                        "<repo>/bench.py --profile-once --workload " + args.workload,
+                        "<repo>/bench.py --profile-once --workload " + args.workload + tag,
                         "rocprofv3 --pmc MfmaUtil MfmaFlopsBF16 SQ_INSTS_VALU_MFMA_MOPS_F8 "
                         "-d <mfma_dir> -- python3 <repo>/bench.py --profile-once --workload "
-                        + args.workload,
+                        + args.workload + tag,
                         "python3 bench.py --counters <fetch_dir> <write_dir> <mfma_dir> "
-                        "--workload " + args.workload]}
-    path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}.json")
+                        "--workload " + args.workload + tag]}
+    suffix = "" if args.gate_dtype == "bf16" else f"_{args.gate_dtype}"
+    path = os.path.join(ROOT, "profiles", f"traffic_{args.workload}{suffix}.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec, indent=1))
@@ -171,9 +177,14 @@ def profile_once(args):
     w = Workload(args.workload, dev)
     mode = "absolute" if w.table is not None else "relative"
     kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
+    if args.gate_dtype == "fp8":
+        from block_sparse_long_amd.table import ThresholdTable
+        path = os.path.join(GOLDEN, f"thresholds_{args.workload}_fp8.bin")
+        kw.update(gate_dtype="fp8", table=ThresholdTable.load(path).to_device(dev))
     w.call(mode, **kw)
     torch.cuda.synchronize()
-    print(json.dumps({"profile_once": args.workload, "copy_bytes": COPY_BYTES,
+    print(json.dumps({"profile_once": args.workload, "gate_dtype": args.gate_dtype,
+                      "copy_bytes": COPY_BYTES,
                       "kernel_source_sha256": kernel_source_sha256()}), flush=True)
 
 
