@@ -200,7 +200,7 @@ hipError_t set_fp8(bsfa::PrefillArgs& a, const bsfa_problem* p, void* workspace,
 
 // The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i).
 hipError_t launch_sweep(bsfa::PrefillArgs sw, const bsfa_problem* p, hipStream_t st) {
-  const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G);
+  const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G, sw.q8 != nullptr);
   sw.units = p->batch * p->heads_kv * (sw.G / shpw);
   sw.xcd_map = (sw.units % 8) == 0;
   sw.xcd_rot = 0;

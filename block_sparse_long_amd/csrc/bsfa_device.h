@@ -1842,7 +1842,9 @@ template <int D, int BQ>
 hipError_t launch_sweep_fp8_tile(const PrefillArgs& a, int hpw, hipStream_t stream) {
   constexpr int WPH = BQ / 64;
   const dim3 grid(a.units * a.nqb);
-  if (hpw == 2)
+  if (hpw == 4)
+    hipLaunchKernelGGL((gate_sweep_fp8_kernel<D, BQ, 4>), grid, dim3(WPH * 256), 0, stream, a);
+  else if (hpw == 2)
     hipLaunchKernelGGL((gate_sweep_fp8_kernel<D, BQ, 2>), grid, dim3(WPH * 128), 0, stream, a);
   else
     hipLaunchKernelGGL((gate_sweep_fp8_kernel<D, BQ, 1>), grid, dim3(WPH * 64), 0, stream, a);

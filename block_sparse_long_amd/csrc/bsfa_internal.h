@@ -118,8 +118,8 @@ hipError_t launch_kth_select(const CalibArgs& a, const float* maxima, int block_
 // The gate sweep for the absolute gate: fills a.keep_mask (and the off-diagonal entries of
 // a.dbg). a.units must describe launch_gate_sweep's own workgroups (gate_sweep_heads()).
 hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hipStream_t stream);
-// Heads per workgroup of the gate sweep.
-int gate_sweep_heads(int block_q, int group);
+// Heads per workgroup of the gate sweep (bf16 or FP8 scores).
+int gate_sweep_heads(int block_q, int group, bool fp8);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
 
 // Block means for mean correction: fills a.kbar_hi, a.kbar_lo and a.vbar for every whole gate
