@@ -352,6 +352,36 @@ def run_gate(w, mode, steps, warmup, **kw):
                 pct_peak=100.0 * flops / ev_ms / 1e9 / PEAK_BF16_TFLOPS)
 
 
+def measured_mfma_rate(steps=5, warmup=2):
+    """The device's sustained bf16 MFMA rate (bsfa_mfma_rate_probe), TFLOP/s."""
+    from block_sparse_long_amd import _lib
+    sink, fl = _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=64)
+    ms, _ = timed(lambda: _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=64, sink=sink),
+                  steps, warmup)
+    return fl / ms / 1e9
+
+
+def flushed_median_ms(w, mode, n=20, warmup=3, **kw):
+    """Median over n calls of one call's time (HIP events), a 512 MiB buffer written before
+    each call so that no input is left in L2 or the last-level cache."""
+    import statistics
+    import torch
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=w.Qd.device)
+    stream = torch.cuda.current_stream()
+    out = []
+    for t in range(warmup + n):
+        scratch.fill_(t & 255)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        w.call(mode, **kw)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        if t >= warmup:
+            out.append(e0.elapsed_time(e1))
+    del scratch
+    return statistics.median(out)
+
+
 def run_mean_correction(w, steps, warmup, gated_ms, dense_ms):
     """The gated call with mean correction (block-means pass, sweep, walk with the pruned
     blocks' stand-ins): its time, and the deviation of the outputs with and without the
@@ -424,16 +454,22 @@ def run_fp8_gate(w, steps, warmup, gated, dense_ms):
             "mean_abs_output_deviation": dev}
 
 
-def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
-    """The oracle as it stands, single-threaded BLAS, on a bounded sample of the workload."""
+def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None, k=None):
+    """The oracle as it stands, on the host's cores (BLAS threads; at most 16, the share of one
+    GPU), on a bounded sample of the workload: every head of the query blocks {0, 1, k/2 - 1,
+    k/2, nqb/4, nqb/2 - 1, nqb/2, 3 nqb/4, nqb - 1} (the first ones, the -inf boundary of the
+    table, the last calibrated and first reused columns at 128K, the last)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_limits
     Qh, Kh, Vh = (x.float().numpy() for x in w.host)
     nqb = -(-w.N // w.Bq)
     if blocks is None:
-        blocks = sorted({nqb // 4 - 1, nqb // 2 - 1, nqb // 2, 3 * nqb // 4, nqb - 1})
-    with threadpool_limits(limits=1):
+        kk = k or 2
+        blocks = sorted(x for x in {0, 1, kk // 2 - 1, kk // 2, nqb // 4, nqb // 2 - 1, nqb // 2,
+                                    3 * nqb // 4, nqb - 1} if 0 <= x < nqb)
+    cores = min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=w.Bk, mode=mode,
                                   table=None if w.table is None else w.table.T,
@@ -442,10 +478,11 @@ def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None):
         sec = time.perf_counter() - t0
     flops = executed_flops(np.maximum(r.kept_counts, 0), w.N, w.Bq, w.d, w.Bk,
                            query_blocks=blocks)
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(sec, 2),
             "sample": f"{w.name}: query blocks {blocks} x all {w.Hq} heads, same inputs and "
-                      f"table, float32 numpy, 1 BLAS thread; executed TFLOP/s of the sample"}
+                      f"table, float32 numpy, {cores} BLAS threads; executed TFLOP/s of the "
+                      f"sample"}
 
 
 def main():
@@ -499,6 +536,12 @@ def main():
     }
     if w.table is not None:
         extras["zero_skip_tax_absolute"] = round(abs_ninf["ms"] / dense["ms"] - 1, 4)
+    # the same gated call with L2 and the last-level cache flushed before each call (median)
+    extras["gated_ms_flushed_median"] = round(flushed_median_ms(w, mode, **gate_kw), 3)
+    # executed TFLOP/s against the matrix cores' measured sustained rate as well as the spec
+    rate = measured_mfma_rate()
+    extras["measured_mfma_tflops"] = round(rate, 1)
+    extras["pct_measured_mfma_peak"] = round(100.0 * gated["tflops"] / rate, 2)
     # the call's launches: under the absolute gate the sweep, then the walk over kept tiles
     # (QK again and PV on every kept and diagonal tile)
     walk_tiles = gated["kept"] + w.Hq * sum(
@@ -584,7 +627,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, mode, **gate_kw)
+        cpu = cpu_baseline(w, mode, k=k, **gate_kw)
 
     c = w.c
     line = {

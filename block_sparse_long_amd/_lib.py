@@ -36,7 +36,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so"
 EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
             "bsfa_prefill_workspace_bytes",
             "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_calibrate_workspace_bytes",
-            "bsfa_status_string", "bsfa_last_error", "bsfa_version")
+            "bsfa_mfma_rate_probe", "bsfa_status_string", "bsfa_last_error", "bsfa_version")
 
 
 class BsfaProblem(ctypes.Structure):
@@ -101,6 +101,8 @@ def load_library(path: str = LIB_PATH):
     lib.bsfa_calibrate_blockmax.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp,
                                             ctypes.POINTER(ctypes.c_int32), ctypes.c_int32, vp,
                                             vp, ctypes.c_uint64, vp]
+    lib.bsfa_mfma_rate_probe.restype = ctypes.c_int32
+    lib.bsfa_mfma_rate_probe.argtypes = [ctypes.c_int32, ctypes.c_int32, vp, vp]
     lib.bsfa_calibrate_workspace_bytes.restype = ctypes.c_uint64
     lib.bsfa_calibrate_workspace_bytes.argtypes = [ctypes.POINTER(BsfaProblem)]
     lib.bsfa_status_string.restype = ctypes.c_char_p
@@ -418,3 +420,15 @@ def bsfa_prefill_workspace_bytes(Q, K, *, block_q: int, block_k: int = 64,
     p = make_problem(Q, K, block_q=block_q, block_k=block_k, mean_correction=mean_correction,
                      gate_dtype=gate_dtype)
     return int(load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
+
+
+def bsfa_mfma_rate_probe(workgroups: int = 1024, iters: int = 256, sink=None, stream=None,
+                         device="cuda"):
+    """Enqueue the MFMA rate probe; returns (sink, executed FLOPs). Time it on `stream`."""
+    import torch
+    lib = load_library()
+    if sink is None:
+        sink = torch.empty(workgroups * 256, dtype=torch.float32, device=device)
+    _check(lib.bsfa_mfma_rate_probe(int(workgroups), int(iters), _ptr(sink),
+                                    _stream_handle(stream, sink.device)))
+    return sink, float(workgroups) * 4 * 4 * iters * 32768

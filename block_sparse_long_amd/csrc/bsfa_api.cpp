@@ -506,6 +506,16 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
   return ok();
 }
 
+bsfa_status bsfa_mfma_rate_probe(int32_t workgroups, int32_t iters, float* sink, void* stream) {
+  if (workgroups < 1 || iters < 1 || !sink)
+    return fail(BSFA_ERR_ARG, "workgroups (%d) and iters (%d) must be >= 1, sink non-NULL",
+                workgroups, iters);
+  if (reinterpret_cast<uintptr_t>(sink) & 3u) return fail(BSFA_ERR_ALIGN, "sink misaligned");
+  hipError_t e = bsfa::launch_mfma_rate(workgroups, iters, sink, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(BSFA_ERR_HIP, "probe launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
 uint64_t bsfa_calibrate_workspace_bytes(const bsfa_problem* p) {
   if (!p || p->gate_dtype != BSFA_FP8_E4M3 || p->batch <= 0 || p->seqlen <= 0 ||
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)

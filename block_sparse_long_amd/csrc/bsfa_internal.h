@@ -121,6 +121,9 @@ hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hi
 // Heads per workgroup of the gate sweep (bf16 or FP8 scores).
 int gate_sweep_heads(int block_q, int group, bool fp8);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
+// The MFMA rate probe: workgroups x 4 waves, each 4 * iters bf16 32x32x16 MFMAs; sink holds
+// workgroups * 256 floats.
+hipError_t launch_mfma_rate(int workgroups, int iters, float* sink, hipStream_t stream);
 
 // Block means for mean correction: fills a.kbar_hi, a.kbar_lo and a.vbar for every whole gate
 // block of every (batch, KV head) (a.mean_blocks per sequence at most).

@@ -279,6 +279,15 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
                                     float* kth_out, void* workspace, uint64_t workspace_bytes,
                                     void* stream);
 
+/* Diagnostic: the sustained bf16 matrix-core rate of this device, against which the kernels'
+ * executed FLOP rates can be read (the pages quote kernel speed as a share of the matrix peak:
+ * "Skipping attention blocks was the easy part", Trusting the numbers). Enqueues one launch of
+ * `workgroups` x 4 waves, each issuing 4 * iters v_mfma_f32_32x32x16_bf16 (32768 FLOP each) on
+ * register operands, and writes workgroups * 256 floats to `sink` (device, 4-byte aligned).
+ * Executed FLOPs = workgroups * 4 * 4 * iters * 32768; the caller times the launch on `stream`.
+ * BSFA_ERR_ARG for workgroups < 1, iters < 1 or a NULL sink. */
+bsfa_status bsfa_mfma_rate_probe(int32_t workgroups, int32_t iters, float* sink, void* stream);
+
 /* Bytes of workspace bsfa_calibrate_blockmax needs for `p` (0 for bf16 scores): with
  * gate_dtype FP8_E4M3, the layout of bsfa_prefill_workspace_bytes(p, ABSOLUTE) without the
  * block means, then (on a 256-byte boundary) fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] block

@@ -384,3 +384,11 @@ def test_fp8_gate_workspace_and_validation():
     assert call_calib(p, [1], ws=FAKE + 8, ws_bytes=cw) == _lib.BSFA_ERR_ALIGN
     p.gate_dtype = _lib.BSFA_BF16
     assert lib.bsfa_calibrate_workspace_bytes(ctypes.byref(p)) == 0
+
+
+def test_mfma_rate_probe_validation():
+    lib = _lib.load_library()
+    assert lib.bsfa_mfma_rate_probe(0, 4, FAKE, None) == _lib.BSFA_ERR_ARG
+    assert lib.bsfa_mfma_rate_probe(4, 0, FAKE, None) == _lib.BSFA_ERR_ARG
+    assert lib.bsfa_mfma_rate_probe(4, 4, None, None) == _lib.BSFA_ERR_ARG
+    assert lib.bsfa_mfma_rate_probe(4, 4, FAKE + 2, None) == _lib.BSFA_ERR_ALIGN

@@ -285,3 +285,20 @@ def test_calibrate_table_matches_the_oracle_calibration(gate_dtype):
     inf = np.isinf(ref)
     np.testing.assert_array_equal(tab.T[inf], ref[inf])
     np.testing.assert_allclose(tab.T[~inf], ref[~inf], rtol=0, atol=1e-3)
+
+
+def test_calibration_cli_reproduces_the_oracle_table(tmp_path):
+    # the GPU calibration command on the tiny workload's calibration seeds against the stored
+    # oracle-calibrated table of the same workload
+    import os
+    from block_sparse_long_amd import calibrate
+    from block_sparse_long_amd.table import ThresholdTable
+    out = str(tmp_path / "t.bin")
+    calibrate.main(["--config", "tiny_1k", "--seeds", "1-4", "--budgets", "4", "--out", out])
+    got = ThresholdTable.load(out)
+    ref = ThresholdTable.load(os.path.join(os.path.dirname(__file__), "golden",
+                                           "thresholds_tiny_1k.bin"))
+    assert got.T.shape == ref.T.shape and got.budgets == ref.budgets
+    inf = np.isinf(ref.T)
+    np.testing.assert_array_equal(got.T[inf], ref.T[inf])
+    np.testing.assert_allclose(got.T[~inf], ref.T[~inf], rtol=0, atol=1e-3)
