@@ -355,8 +355,8 @@ def run_gate(w, mode, steps, warmup, **kw):
 def measured_mfma_rate(steps=5, warmup=2):
     """The device's sustained bf16 MFMA rate (bsfa_mfma_rate_probe), TFLOP/s."""
     from block_sparse_long_amd import _lib
-    sink, fl = _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=64)
-    ms, _ = timed(lambda: _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=64, sink=sink),
+    sink, fl = _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=8192)
+    ms, _ = timed(lambda: _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=8192, sink=sink),
                   steps, warmup)
     return fl / ms / 1e9
 
@@ -455,10 +455,11 @@ def run_fp8_gate(w, steps, warmup, gated, dense_ms):
 
 
 def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None, k=None):
-    """The oracle as it stands, on the host's cores (BLAS threads; at most 16, the share of one
-    GPU), on a bounded sample of the workload: every head of the query blocks {0, 1, k/2 - 1,
-    k/2, nqb/4, nqb/2 - 1, nqb/2, 3 nqb/4, nqb - 1} (the first ones, the -inf boundary of the
-    table, the last calibrated and first reused columns at 128K, the last)."""
+    """The oracle as it stands, on one host core, on a bounded sample of the workload: every
+    head of the query blocks {0, 1, k/2 - 1, k/2, nqb/4, nqb/2 - 1, nqb/2, 3 nqb/4, nqb - 1}
+    (the first ones, the -inf boundary of the table, the last calibrated and first reused
+    columns at 128K, the last). One BLAS thread: the oracle multiplies one 128 x 64 tile at a
+    time, too small for threads to help (16 threads measured 0.068 against 0.082 TFLOP/s)."""
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_limits
@@ -468,7 +469,7 @@ def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None, k=N
         kk = k or 2
         blocks = sorted(x for x in {0, 1, kk // 2 - 1, kk // 2, nqb // 4, nqb // 2 - 1, nqb // 2,
                                     3 * nqb // 4, nqb - 1} if 0 <= x < nqb)
-    cores = min(16, len(os.sched_getaffinity(0)))
+    cores = 1
     with threadpool_limits(limits=cores):
         t0 = time.perf_counter()
         r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=w.Bk, mode=mode,
@@ -481,7 +482,7 @@ def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None, k=N
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle", "seconds": round(sec, 2),
             "sample": f"{w.name}: query blocks {blocks} x all {w.Hq} heads, same inputs and "
-                      f"table, float32 numpy, {cores} BLAS threads; executed TFLOP/s of the "
+                      f"table, float32 numpy, {cores} BLAS thread; executed TFLOP/s of the "
                       f"sample"}
 
 

@@ -14,13 +14,13 @@ def test_mfma_rate_probe():
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     _lib.load_library()
-    sink, fl = _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=16)
+    sink, fl = _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=4096)
     torch.cuda.synchronize()
     assert torch.isfinite(sink).all()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(3):
-        _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=16, sink=sink)
+        _lib.bsfa_mfma_rate_probe(workgroups=1024, iters=4096, sink=sink)
     e1.record()
     torch.cuda.synchronize()
     tflops = 3 * fl / e0.elapsed_time(e1) / 1e9
