@@ -651,7 +651,11 @@ def main():
                      "mfma_util_pct": measured_counters(args.workload, dom["kernel"]).get(
                          "mfma_util_pct"),
                      "mfma_flops_counted": measured_counters(args.workload, dom["kernel"]).get(
-                         "mfma_flops_bf16")},
+                         "mfma_flops_bf16"),
+                     # the measured HBM traffic over this run's launch time (GB/s), or null
+                     "hbm_gbs": (None if measured_traffic(args.workload, dom["kernel"]) is None
+                                 else round(measured_traffic(args.workload, dom["kernel"])
+                                            / dom["ms"] / 1e6, 1))},
         "cpu_baseline": cpu,
         "extras": extras,
     }
