@@ -819,6 +819,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const __bf16* const sv = P ? sV0 : sV1;     // V of the previous tile
     bf16x8 vb[3];
     float sum = 0.f;
+    // The reference update of tile t, made before the vote into a copy: the exponentials
+    // need its offset and would otherwise wait for the statistics' LDS round trip and the
+    // vote. A skipped tile leaves the state as it was (its exponentials are computed and not
+    // used); a kept one takes the copy, so the arithmetic is the same either way.
+    RowState sp = st;
+    float alpha = 1.f;
+    bool moved = update_reference(sp, rc, c, alpha);
+    const float off = -sp.mref * c;
     if (keep_prev) {
       pv_prefetch<D>(sv, vb, lane);
       pv_steps<D, 0, DEC, DEC, MVR>(true, false, false, sv, pb[P ^ 1], o, vb, sb[P], 0.f, c,
@@ -854,12 +862,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     }
     if (loop_gate && head_leader && !diag) kept += mykeep ? 1 : 0;
 
-    float alpha = 1.f, off = 0.f;
-    bool moved = false;
-    if (mykeep) {
-      moved = update_reference(st, rc, c, alpha);
-      off = -st.mref * c;
-    }
+    if (mykeep)
+      st = sp;
+    else
+      moved = false;
     // rest of PV of the previous tile with the first half of tile t's exponentials and the V_t
     // copy (skipped as a whole when there is none of the three)
     // Step sequences without per-step tests wherever possible. Dense and the mask walk keep
