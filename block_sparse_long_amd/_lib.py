@@ -32,6 +32,7 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
               "relative": BSFA_GATE_RELATIVE}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
+ABI_MAJOR = 2    # the layout of bsfa_problem and the entry points' signatures below
 
 EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
             "bsfa_prefill_workspace_bytes",
@@ -78,6 +79,10 @@ def load_library(path: str = LIB_PATH):
         raise RuntimeError(f"{path} is missing: build it with python -m "
                            "block_sparse_long_amd.build_lib (there is no CPU fallback)")
     lib = ctypes.CDLL(path)
+    lib.bsfa_version.restype = ctypes.c_int32
+    if lib.bsfa_version() >> 16 != ABI_MAJOR:
+        raise RuntimeError(f"{path} has ABI {lib.bsfa_version() >> 16}, this binding "
+                           f"expects {ABI_MAJOR}: rebuild it")
     vp = ctypes.c_void_p
     lib.bsfa_prefill.restype = ctypes.c_int32
     lib.bsfa_prefill.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, ctypes.POINTER(BsfaTable),

@@ -300,7 +300,8 @@ const char* bsfa_status_string(int32_t status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* ABI version: (major << 16) | minor. */
+/* ABI version: (major << 16) | minor. Major 2: bsfa_problem ends with mean_correction and
+ * gate_dtype, and bsfa_calibrate_blockmax takes a workspace. */
 int32_t bsfa_version(void);
 
 #ifdef __cplusplus
