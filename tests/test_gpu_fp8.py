@@ -83,6 +83,10 @@ CASES = {   # name: (B, N, P, Hq, Hkv, d, Bq, Bk, query blocks checked or None f
     "prefix_256": (1, 744, 256, 8, 2, 128, 128, 64, None),
     "bk128_ragged": (1, 1000, 0, 8, 2, 128, 128, 128, None),
     "long_4k": (1, 4600, 0, 2, 1, 128, 128, 64, [0, 20, 34, 35]),
+    # two tiles per barrier (four heads per KV group, Bq = 128) after a prefix, up to 200
+    # tiles: past the third 64-tile slot of K scales
+    "g4_prefix128_12k": (1, 12800, 128, 4, 1, 128, 128, 64, [0, 1, 50, 99]),
+    "d64_g4_prefix256": (1, 900, 256, 8, 2, 64, 128, 64, None),
 }
 
 
