@@ -231,6 +231,49 @@ def test_absolute_gate_sweep_and_single_launch_agree_bitwise(name, dbg, mid_tabl
             np.testing.assert_array_equal(a["stat"], b["stat"])
 
 
+def test_full_size_two_launch_call_equals_single_launch_bitwise():
+    # at 32K (256 query blocks): the absolute gate with a workspace (gate sweep, then the walk)
+    # gives the single launch's output, counts and statistics, and the masks it leaves in the
+    # workspace (bf16 and FP8 scores) are those of a separate gate-mask launch
+    name = "llama_32k_sweep"
+    c = synth.CONFIGS[name]
+    Bq, N, Hq = c["block_q"], c["n"], c["heads_q"]
+    nqb = -(-N // Bq)
+    print(f"case {name} two launches vs one", flush=True)
+    Q, K, V = synth.make_inputs(name, 3)
+    Qd, Kd, Vd = (x.to("cuda") for x in synth.to_bf16(Q, K, V))
+    tab = ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{name}.bin"))
+    dtab = tab.to_device("cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    a = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=1,
+                   dbg=True)
+    b = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=1,
+                   dbg=True, workspace=none)
+    assert torch.equal(a["O"], b["O"])
+    np.testing.assert_array_equal(a["counts"], b["counts"])
+    assert a["total"] == b["total"]
+    np.testing.assert_array_equal(a["stat"], b["stat"])
+    # query blocks whose thresholds are finite for every head (the others keep all without a
+    # mask)
+    T = tab.T[1]
+    qbs = [i for i in range(nqb) if np.isfinite(T[:, min(i, T.shape[1] - 1)]).all()]
+    assert len(qbs) > nqb // 2
+    for gd in ("bf16", "fp8"):
+        need = _lib.bsfa_prefill_workspace_bytes(Qd, Kd, block_q=Bq, gate_dtype=gd)
+        ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+        O = torch.empty_like(Qd)
+        _lib.bsfa_prefill(Qd, Kd, Vd, O, block_q=Bq, gate_mode="absolute", table=dtab,
+                          budget_slice=1, workspace=ws, gate_dtype=gd)
+        ref = _lib.bsfa_gate_masks(Qd, Kd, dtab, 1, block_q=Bq, gate_dtype=gd)
+        torch.cuda.synchronize()
+        ref = ref.cpu().numpy()
+        got = ws[:ref.size * 8].view(torch.int64).view(ref.shape).cpu().numpy()
+        for i in qbs:
+            words = -(-(i * Bq // 64) // 64)
+            np.testing.assert_array_equal(got[:, :, i, :words], ref[:, :, i, :words],
+                                          err_msg=f"{gd} query block {i}")
+
+
 def _unpack_masks(mask, nkb):
     m = np.ascontiguousarray(mask.cpu().numpy()).view(np.uint8)
     bits = np.unpackbits(m, axis=-1, bitorder="little").astype(bool)
