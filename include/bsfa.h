@@ -33,9 +33,11 @@
  *     results are valid once the caller has synchronised the stream. The library never
  *     synchronises.
  *   - Arguments are validated on the host before anything is enqueued. On any status other
- *     than BSFA_OK nothing was enqueued and every output is untouched; bsfa_last_error() then
- *     describes the problem. BSFA_ERR_HIP means the launch itself failed. No C++ exception
- *     crosses the ABI.
+ *     than BSFA_OK and BSFA_ERR_HIP nothing was enqueued and every output is untouched;
+ *     bsfa_last_error() then describes the problem. BSFA_ERR_HIP means a launch failed; earlier
+ *     launches of the same call (zeroing kept_total, FP8 copies, block means, the gate sweep)
+ *     may already be enqueued, and the outputs are then undefined. No C++ exception crosses
+ *     the ABI.
  *   - Tensors are indexed [batch][token][head][dim] with element strides given per tensor for
  *     batch, token and head; the dim axis is contiguous. Base pointers and every row
  *     (batch/token/head offset) must be 16-byte aligned.
