@@ -767,6 +767,24 @@ def test_full_llama_128k_k64_reuses_last_threshold():
     _full_check("llama_128k", "absolute", blocks=[0, 31, 32, 511, 512, 1023])
 
 
+def test_full_llama_256k_largest_tensors():
+    # the 128K workload's shape at 256K tokens: Q holds 2^30 elements (2 GiB), so every global
+    # offset must be formed in 64 bits, and the last query block walks 4094 key tiles (64 mask
+    # words). The 128K table (calibrated at 64K) serves unchanged: rows past its last column
+    # reuse it, as at 128K.
+    c = synth.CONFIGS["llama_128k"]
+    n = 2 * c["n"]
+    print(f"case llama_128k shape at n={n}", flush=True)
+    Qd, Kd, Vd, Qh, Kh, Vh = _full("llama_128k", n=n)
+    assert Qd.numel() == 1 << 30
+    tab = golden_table("llama_128k")
+    nqb = n // c["block_q"]
+    dev = run_device(Qd, Kd, Vd, block_q=c["block_q"], mode="absolute", table=tab,
+                     budget_slice=0)
+    check_parity(dev, Qh, Kh, Vh, block_q=c["block_q"], mode="absolute", table=tab,
+                 budget_slice=0, query_blocks=[0, nqb // 2, nqb - 1])
+
+
 def test_full_llama_64k_relative():
     _full_check("llama_64k_relative", "relative",
                 log_lambdas=(math.log(1e-4), math.log(1e-2)), blocks=[0, 1, 128, 255, 511])
