@@ -32,7 +32,7 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
               "relative": BSFA_GATE_RELATIVE}
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
-ABI_MAJOR = 2    # the layout of bsfa_problem and the entry points' signatures below
+ABI_MAJOR = 3    # the layout of bsfa_problem and the entry points' signatures below
 
 EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
             "bsfa_prefill_workspace_bytes",
@@ -58,6 +58,7 @@ class BsfaTable(ctypes.Structure):
         ("T", ctypes.c_void_p), ("n_budgets", ctypes.c_int32), ("t_len", ctypes.c_int32),
         ("heads_q", ctypes.c_int32), ("block_q", ctypes.c_int32), ("block_k", ctypes.c_int32),
         ("head_dim", ctypes.c_int32), ("softmax_scale", ctypes.c_float),
+        ("budgets", ctypes.POINTER(ctypes.c_int32)),
     ]
 
 
@@ -156,10 +157,52 @@ def _stream_handle(stream, device) -> int:
     return int(stream.cuda_stream)
 
 
+def _check_shapes(Q, K, V, O, positions: bool = True) -> None:
+    """The kernels size every access from Q's shape and the problem: refuse tensors that
+    disagree with it (a mismatch would make them read or write past a buffer)."""
+    if K.device != Q.device or (V is not None and V.device != Q.device) or \
+            (O is not None and O.device != Q.device):
+        raise ValueError("Q, K, V and O must be on one device")
+    if K.dim() != Q.dim():
+        raise ValueError("Q and K must have the same number of dimensions")
+    if K.shape[0] != Q.shape[0]:
+        raise ValueError(f"K batch {K.shape[0]} differs from Q batch {Q.shape[0]}")
+    if K.shape[-1] != Q.shape[-1]:
+        raise ValueError(f"K head_dim {K.shape[-1]} differs from Q head_dim {Q.shape[-1]}")
+    if positions and K.shape[1] < Q.shape[1]:
+        raise ValueError(f"K holds {K.shape[1]} positions, fewer than Q's {Q.shape[1]}")
+    if V is not None and tuple(V.shape) != tuple(K.shape):
+        raise ValueError(f"V shape {tuple(V.shape)} differs from K shape {tuple(K.shape)}")
+    if O is not None and tuple(O.shape) != tuple(Q.shape):
+        raise ValueError(f"O shape {tuple(O.shape)} differs from Q shape {tuple(Q.shape)}")
+
+
+def _check_outputs(batch: int, heads_q: int, seqlen: int, kv_seqlen: int, block_q: int,
+                   block_k: int, kept_counts=None, kept_total=None, debug_block_stat=None,
+                   device=None) -> None:
+    """dtype, layout, device and size of the optional per-block outputs."""
+    import torch
+    nqb = -(-seqlen // block_q)
+    nkb = -(-kv_seqlen // block_k)
+    for name, t, dt, n in (("kept_counts", kept_counts, torch.int32, batch * heads_q * nqb),
+                           ("kept_total", kept_total, torch.int64, 1),
+                           ("debug_block_stat", debug_block_stat, torch.float32,
+                            batch * heads_q * nqb * nkb)):
+        if t is None:
+            continue
+        if t.dtype != dt or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+        if device is not None and t.device != device:
+            raise ValueError(f"{name} must be on {device}")
+        if t.numel() != n:
+            raise ValueError(f"{name} holds {t.numel()} elements, the problem needs {n}")
+
+
 def make_problem(Q, K, V=None, O=None, *, block_q: int, block_k: int = 64,
                  softmax_scale: float = 0.0, mean_correction: bool = False,
-                 gate_dtype="bf16") -> BsfaProblem:
+                 gate_dtype="bf16", paged: bool = False) -> BsfaProblem:
     import torch
+    _check_shapes(Q, K, V, O, positions=not paged)
     p = BsfaProblem()
     p.batch, p.seqlen, p.heads_q, p.head_dim = (int(x) for x in Q.shape)
     p.heads_kv = int(K.shape[2])
@@ -211,17 +254,16 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
     tbl = None
     if table is not None:
         tbl = table.c_struct()
-    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
-                        ("kept_total", kept_total, torch.int64),
-                        ("debug_block_stat", debug_block_stat, torch.float32)):
-        if t is not None and (t.dtype != dt or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    _check_outputs(p.batch, p.heads_q, p.seqlen, int(K.shape[1]), block_q, block_k, kept_counts,
+                   kept_total, debug_block_stat, Q.device)
     if workspace is None:
         nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
     if workspace is not None and workspace.numel() == 0:
         workspace = None
+    if workspace is not None and (not workspace.is_contiguous() or workspace.device != Q.device):
+        raise ValueError("workspace must be a contiguous tensor on Q's device")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.bsfa_prefill(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
                           ctypes.byref(tbl) if tbl is not None else None, int(budget_slice),
@@ -264,17 +306,16 @@ def bsfa_prefill_varlen(Q, K, V, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int,
     for st in (p.q_stride, p.k_stride, p.v_stride, p.o_stride):
         st[0] = 0
     tbl = table.c_struct() if table is not None else None
-    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
-                        ("kept_total", kept_total, torch.int64),
-                        ("debug_block_stat", debug_block_stat, torch.float32)):
-        if t is not None and (t.dtype != dt or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    _check_outputs(p.batch, p.heads_q, p.seqlen, p.kv_seqlen or p.seqlen, block_q, block_k,
+                   kept_counts, kept_total, debug_block_stat, Q.device)
     if workspace is None:
         nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
     if workspace is not None and workspace.numel() == 0:
         workspace = None
+    if workspace is not None and (not workspace.is_contiguous() or workspace.device != Q.device):
+        raise ValueError("workspace must be a contiguous tensor on Q's device")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.bsfa_prefill_varlen(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V), _ptr(cu_seqlens_q),
                                  _ptr(cu_seqlens_k),
@@ -311,10 +352,12 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
     if O is None:
         O = torch.empty(Q.shape, dtype=out_dtype or torch.bfloat16, device=Q.device)
     mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    if tuple(V_pages.shape) != tuple(K_pages.shape):
+        raise ValueError("K_pages and V_pages must have the same shape")
     p = make_problem(Q[None], K_pages[:, 0][None], V_pages[:, 0][None], O[None],
                      block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
                      mean_correction=mean_correction,
-                     gate_dtype=gate_dtype)
+                     gate_dtype=gate_dtype, paged=True)
     p.batch = kv_lens.numel()
     p.seqlen = int(max_seqlen_q)
     p.kv_seqlen = int(max_seqlen_k) if int(max_seqlen_k) != int(max_seqlen_q) else 0
@@ -322,17 +365,16 @@ def bsfa_prefill_paged(Q, K_pages, V_pages, cu_seqlens_q, kv_lens, block_table,
     p.k_stride[:] = (K_pages.stride(0), K_pages.stride(1), K_pages.stride(2))
     p.v_stride[:] = (V_pages.stride(0), V_pages.stride(1), V_pages.stride(2))
     tbl = table.c_struct() if table is not None else None
-    for name, t, dt in (("kept_counts", kept_counts, torch.int32),
-                        ("kept_total", kept_total, torch.int64),
-                        ("debug_block_stat", debug_block_stat, torch.float32)):
-        if t is not None and (t.dtype != dt or not t.is_contiguous()):
-            raise ValueError(f"{name} must be a contiguous {dt} tensor")
+    _check_outputs(p.batch, p.heads_q, p.seqlen, p.kv_seqlen or p.seqlen, block_q, block_k,
+                   kept_counts, kept_total, debug_block_stat, Q.device)
     if workspace is None:
         nbytes = int(lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode))
         if nbytes:
             workspace = torch.empty(nbytes, dtype=torch.uint8, device=Q.device)
     if workspace is not None and workspace.numel() == 0:
         workspace = None
+    if workspace is not None and (not workspace.is_contiguous() or workspace.device != Q.device):
+        raise ValueError("workspace must be a contiguous tensor on Q's device")
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.bsfa_prefill_paged(ctypes.byref(p), _ptr(Q), _ptr(K_pages), _ptr(V_pages),
                                 _ptr(cu_seqlens_q), _ptr(kv_lens), _ptr(block_table),
@@ -377,9 +419,10 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
         keep_mask = torch.empty(shape, dtype=torch.int64, device=Q.device)
     if not keep_mask.is_contiguous() or keep_mask.element_size() != 8:
         raise ValueError("keep_mask must be a contiguous 8-byte-element tensor")
-    if debug_block_stat is not None and (debug_block_stat.dtype != torch.float32
-                                         or not debug_block_stat.is_contiguous()):
-        raise ValueError("debug_block_stat must be a contiguous float32 tensor")
+    if keep_mask.device != Q.device:
+        raise ValueError("keep_mask must be on Q's device")
+    _check_outputs(B, Hq, N, int(K.shape[1]), block_q, block_k,
+                   debug_block_stat=debug_block_stat, device=Q.device)
     p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
                      gate_dtype=gate_dtype)
     tbl = table.c_struct()
@@ -402,6 +445,10 @@ def bsfa_calibrate_blockmax(Q, K, budgets, kth_out=None, *, block_q: int, block_
     nqb = -(-N // block_q)
     if kth_out is None:
         kth_out = torch.empty((len(budgets), B, Hq, nqb), dtype=torch.float32, device=Q.device)
+    if kth_out.dtype != torch.float32 or not kth_out.is_contiguous() or \
+            kth_out.device != Q.device or kth_out.numel() != len(budgets) * B * Hq * nqb:
+        raise ValueError(f"kth_out must be a contiguous float32 tensor of {len(budgets)} x {B} x "
+                         f"{Hq} x {nqb} elements on Q's device")
     p = make_problem(Q, K, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
                      gate_dtype=gate_dtype)
     if workspace is None:

@@ -111,6 +111,26 @@ bsfa_status check_table(const bsfa_problem* p, const bsfa_table* table, int32_t 
   return BSFA_OK;
 }
 
+// The share of off-diagonal gate blocks a budget of k blocks per (b, h, i) keeps if it held
+// exactly, sum_i min(n_off(i), k) / sum_i n_off(i), above 1/2 (the budget is a target count of
+// kept blocks per query block, "Block Sparse Flash Attention", Method > Key Designs 1). With
+// most blocks kept, a second pass over them costs more than deciding inside the softmax loop.
+// Unknown budgets (no array, k <= 0) count as not keeping most. For a variable-length batch
+// the longest sequence stands for all.
+bool budget_keeps_most(const bsfa_problem* p, const bsfa_table* table, int32_t budget_slice) {
+  if (!table || !table->budgets) return false;
+  const long long k = table->budgets[budget_slice];
+  if (k <= 0) return false;
+  const long long pre = key_len(p) - p->seqlen;
+  long long kept = 0, all = 0;
+  for (int i = 0; i < ceil_div(p->seqlen, p->block_q); ++i) {
+    const long long n_off = (pre + (long long)i * p->block_q) / p->block_k;
+    kept += n_off < k ? n_off : k;
+    all += n_off;
+  }
+  return all > 0 && 2 * kept > all;
+}
+
 // Kernel arguments common to the prefill kernel and the gate sweep.
 bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K, const void* V,
                             const bsfa_table* table, int32_t budget_slice, int32_t gate_mode) {
@@ -227,7 +247,7 @@ const char* bsfa_status_string(int32_t s) {
 
 const char* bsfa_last_error(void) { return g_last_error; }
 
-int32_t bsfa_version(void) { return (2 << 16) | 0; }
+int32_t bsfa_version(void) { return (3 << 16) | 0; }
 
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) {
   if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
@@ -333,7 +353,11 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   const uint64_t ws_need = bsfa_prefill_workspace_bytes(p, gate_mode);
-  const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty;
+  // the absolute gate with a workspace takes two launches unless the slice's budget keeps
+  // most blocks (then one launch; mean correction, FP8 scores and 128-key blocks need two)
+  const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty &&
+                         (mean || fp8 || p->block_k != bsfa::kBlockK ||
+                          !budget_keeps_most(p, table, budget_slice));
   if (use_masks && workspace_bytes < ws_need)
     return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
                 (unsigned long long)workspace_bytes, (unsigned long long)ws_need);

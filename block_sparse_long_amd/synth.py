@@ -123,6 +123,47 @@ def structured(seed: int, n: int, heads_q: int = 32, heads_kv: int = 8, d: int =
     return Q, K, V
 
 
+def dialled(seed: int, n: int, skip: float, heads_q: int = 32, heads_kv: int = 8, d: int = 128,
+            shift: float = 6.0, depth: float = 4.0, noise: float = 0.25, block: int = 64):
+    """The structured generator (without sinks) with a dialled share of negligible key blocks,
+    for the relative gate: the skip rate is an input of the workload ("Skipping attention
+    blocks was the easy part", BLASST blog, The scoreboard: sparsity dialled synthetically).
+
+      * every query of KV group g gets a shared component ``shift`` * u_g along a unit
+        direction u_g of its group (queries of a group share a dominant direction), and a
+        query whose component along u_g is still below shift / 2 is moved along u_g up to
+        shift / 2 (so that the claim below holds for every row, not just typical ones);
+      * each key block j >= 1 of group g (``block`` keys) is cold with probability ``skip``
+        (a seeded draw per (g, j)); a cold block's keys are -depth * sqrt(d) * u_g +
+        ``noise`` * N(0, 1): every query scores at most about -depth * shift / 2 = -12
+        against them (typically -24),
+        far below the running max the first (never cold) block already sets, so every row's
+        block max sits more than |ln lambda| below its running max for lambda >= 1e-4 and the
+        relative gate skips the block; the other blocks keep their maxima near the running max
+        and are kept;
+      * values are unchanged.
+
+    Returns (Q, K, V, cold) with cold a bool tensor [heads_kv, ceil(n / block)].
+    """
+    Q, K, V = structured(seed, n, heads_q=heads_q, heads_kv=heads_kv, d=d, sinks=0)
+    G = heads_q // heads_kv
+    U = normal((heads_kv, d), seed, 8)
+    U = U / U.norm(dim=1, keepdim=True)
+    nb = -(-n // block)
+    gen = torch.Generator().manual_seed(_mix(seed, 9))
+    cold = torch.rand((heads_kv, nb), generator=gen) < skip
+    cold[:, 0] = False
+    Z = normal((1, n, heads_kv, d), seed, 10)
+    for g in range(heads_kv):
+        Qg = Q[0, :, g * G:(g + 1) * G, :]
+        Qg += shift * U[g]
+        Qg += torch.clamp(0.5 * shift - Qg @ U[g], min=0.0)[..., None] * U[g]
+        for j in torch.nonzero(cold[g]).flatten().tolist():
+            r = slice(j * block, min(n, (j + 1) * block))
+            K[0, r, g, :] = -depth * math.sqrt(d) * U[g] + noise * Z[0, r, g, :]
+    return Q, K, V, cold
+
+
 def uniform_mix(seed: int, b: int, n: int, heads_q: int, heads_kv: int, d: int):
     """Plain N(0, 1) Q, K, V with batch ``b`` (parity cases with no structure)."""
     return (normal((b, n, heads_q, d), seed, 1), normal((b, n, heads_kv, d), seed, 2),
@@ -158,13 +199,23 @@ CONFIGS = {
                                block_q=128, block_k=64, budgets=[], calib_n=0, calib_seeds=[],
                                log_lambdas=[-math.inf, math.log(1e-4), math.log(1e-3),
                                             math.log(1e-2)]),
+    # the relative-gate workload with its skip rate dialled by the generator (cold key blocks)
+    "llama_64k_dial": dict(kind="dialled", n=65536, heads_q=32, heads_kv=8, d=128, block_q=128,
+                           block_k=64, budgets=[], calib_n=0, calib_seeds=[],
+                           skips=[0.25, 0.5, 0.75, 0.95], skip=0.5,
+                           log_lambdas=[-math.inf, math.log(1e-4), math.log(1e-3),
+                                        math.log(1e-2)]),
 }
 
 
-def make_inputs(config: str, seed: int, n: int | None = None):
-    """float32 CPU (Q, K, V) for a named workload at its length (or ``n``)."""
+def make_inputs(config: str, seed: int, n: int | None = None, skip: float | None = None):
+    """float32 CPU (Q, K, V) for a named workload at its length (or ``n``; a dialled workload
+    at its default skip rate or ``skip``)."""
     c = CONFIGS[config]
     n = c["n"] if n is None else n
     if c["kind"] == "tiny":
         return tiny_single_head(seed, n=n, d=c["d"])
+    if c["kind"] == "dialled":
+        return dialled(seed, n, c["skip"] if skip is None else skip, heads_q=c["heads_q"],
+                       heads_kv=c["heads_kv"], d=c["d"])[:3]
     return structured(seed, n, heads_q=c["heads_q"], heads_kv=c["heads_kv"], d=c["d"])

@@ -11,6 +11,7 @@ little-endian order, C-contiguous [n_budgets][heads_q][t_len].
 """
 from __future__ import annotations
 
+import ctypes
 import json
 from dataclasses import dataclass, field
 
@@ -76,17 +77,21 @@ class ThresholdTable:
                    softmax_scale=hdr["softmax_scale"], calib_seqlen=hdr.get("calib_seqlen", 0),
                    seeds=hdr.get("seeds", []), generator=hdr.get("generator", ""))
 
-    def to_device(self, device) -> "DeviceTable":
+    def to_device(self, device, record_budgets: bool = True) -> "DeviceTable":
+        """The table in device memory. record_budgets=False hands the library no budgets (it
+        then cannot predict a call's density and runs the absolute gate in two launches
+        whenever it has a workspace)."""
         import torch
-        return DeviceTable(torch.from_numpy(self.T.copy()).to(device), self)
+        return DeviceTable(torch.from_numpy(self.T.copy()).to(device), self, record_budgets)
 
 
 class DeviceTable:
     """A table resident in device memory, passed to bsfa_prefill."""
 
-    def __init__(self, T_dev, host: ThresholdTable):
+    def __init__(self, T_dev, host: ThresholdTable, record_budgets: bool = True):
         self.T = T_dev
         self.host = host
+        self.record_budgets = record_budgets
 
     def c_struct(self) -> _lib.BsfaTable:
         t = _lib.BsfaTable()
@@ -98,6 +103,11 @@ class DeviceTable:
         t.block_k = self.host.block_k
         t.head_dim = self.host.head_dim
         t.softmax_scale = float(self.host.softmax_scale)
+        # the k of each slice (host memory, read during the call): kept alive with the table
+        if self.record_budgets:
+            self._budgets = (ctypes.c_int32 * len(self.host.budgets))(
+                *[int(k) for k in self.host.budgets])
+            t.budgets = self._budgets
         return t
 
 

@@ -137,6 +137,13 @@ typedef struct {
   int32_t block_k;           /* must equal problem block_k */
   int32_t head_dim;          /* must equal problem head_dim */
   float softmax_scale;       /* must equal the effective scale within 1e-6 relative */
+  const int32_t* budgets;    /* host, n_budgets entries: the budget k (off-diagonal blocks) each
+                              * slice was calibrated for, or NULL if unknown; an entry <= 0 also
+                              * means unknown. Read during the call only. The library uses it
+                              * to predict how many blocks a call keeps (the budget is a target
+                              * on the count of kept blocks, "Block Sparse Flash Attention",
+                              * Method > Key Designs 1) and so to choose how to run the absolute
+                              * gate (see bsfa_prefill's workspace). */
 } bsfa_table;
 
 /* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
@@ -166,14 +173,21 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
  *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
  *   workspace     device, 8-byte aligned, or NULL; caller-owned scratch of workspace_bytes
- *                 (its contents on return are unspecified). For ABSOLUTE with a workspace of
- *                 at least bsfa_prefill_workspace_bytes(p, gate_mode) bytes, the keep
- *                 decisions of all blocks are made in a separate launch first (scores only),
- *                 and the softmax launch then walks the kept blocks; without one, both happen
- *                 in one launch. The results are the same. A non-NULL workspace that is too
- *                 small is an error (BSFA_ERR_ARG). With mean_correction or an FP8 gate it
- *                 is required and must be 16-byte aligned; a launch before the sweep computes
- *                 the block means, and one the FP8 copies.
+ *                 (its contents on return are unspecified). The absolute gate runs in one of
+ *                 two ways with the same results (O, kept counts and statistics bit for bit):
+ *                 two launches, a gate sweep that decides every block from its scores alone
+ *                 and writes keep masks into the workspace, then a softmax launch that walks
+ *                 the kept blocks only; or one launch that decides each block inside the
+ *                 softmax loop. Without a workspace the call takes one launch. With a
+ *                 workspace of at least bsfa_prefill_workspace_bytes(p, gate_mode) bytes it
+ *                 takes two, unless the table records the slice's budget k and
+ *                 sum_i min(n_off(i), k) / sum_i n_off(i) (the share of off-diagonal blocks
+ *                 the budget keeps) exceeds 1/2 for this problem: when most blocks are kept
+ *                 the second pass over them costs more than deciding inside the loop. A
+ *                 non-NULL workspace that is too small is an error (BSFA_ERR_ARG). With
+ *                 mean_correction, an FP8 gate or block_k = 128 it is required (two launches
+ *                 always) and must be 16-byte aligned; a launch before the sweep computes the
+ *                 block means, and one the FP8 copies.
  *   stream        hipStream_t
  * The absolute gate supports Nk up to 2097152 (BSFA_ERR_UNSUPPORTED beyond).
  * Returns BSFA_OK or an error status (see the conventions above). */
@@ -302,8 +316,9 @@ const char* bsfa_status_string(int32_t status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* ABI version: (major << 16) | minor. Major 2: bsfa_problem ends with mean_correction and
- * gate_dtype, and bsfa_calibrate_blockmax takes a workspace. */
+/* ABI version: (major << 16) | minor. Major 3: bsfa_table ends with the budgets array
+ * (major 2: bsfa_problem ends with mean_correction and gate_dtype, and
+ * bsfa_calibrate_blockmax takes a workspace). */
 int32_t bsfa_version(void);
 
 #ifdef __cplusplus

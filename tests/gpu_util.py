@@ -31,13 +31,13 @@ def bf16_pair(*xs):
 
 def run_device(Qd, Kd, Vd, *, block_q, mode, table=None, budget_slice=0,
                log_lambda=-math.inf, out_dtype=torch.float32, dbg=True, O=None,
-               workspace=None):
+               workspace=None, record_budgets=True):
     B, N, Hq, _ = Qd.shape
     nqb, nkb = -(-N // block_q), -(-int(Kd.shape[1]) // 64)
     counts = torch.full((B, Hq, nqb), -7, dtype=torch.int32, device="cuda")
     total = torch.zeros(1, dtype=torch.int64, device="cuda")
     stat = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32, device="cuda") if dbg else None
-    dtab = table.to_device("cuda") if table is not None else None
+    dtab = table.to_device("cuda", record_budgets) if table is not None else None
     O = _lib.bsfa_prefill(Qd, Kd, Vd, O, block_q=block_q, gate_mode=mode, table=dtab,
                           budget_slice=budget_slice, log_lambda=log_lambda, kept_counts=counts,
                           kept_total=total, debug_block_stat=stat, out_dtype=out_dtype,

@@ -43,7 +43,7 @@ def test_status_strings_and_version():
     for s in range(8):
         assert _lib.bsfa_status_string(s)
     assert _lib.bsfa_status_string(99) == "unknown status"
-    assert _lib.bsfa_version() >> 16 == _lib.ABI_MAJOR == 2
+    assert _lib.bsfa_version() >> 16 == _lib.ABI_MAJOR == 3
 
 
 def problem(B=1, N=256, Hq=4, Hkv=2, d=128, bq=128, bk=64, out=_lib.BSFA_BF16):
@@ -392,3 +392,46 @@ def test_mfma_rate_probe_validation():
     assert lib.bsfa_mfma_rate_probe(4, 0, FAKE, None) == _lib.BSFA_ERR_ARG
     assert lib.bsfa_mfma_rate_probe(4, 4, None, None) == _lib.BSFA_ERR_ARG
     assert lib.bsfa_mfma_rate_probe(4, 4, FAKE + 2, None) == _lib.BSFA_ERR_ALIGN
+
+
+def test_binding_refuses_inconsistent_tensors():
+    # the kernels size every access from Q's shape: tensors that disagree with it are refused
+    # by the binding before the library is called (CPU tensors: nothing reaches a device)
+    import torch
+    bf = torch.bfloat16
+    Q = torch.zeros(1, 256, 4, 128, dtype=bf)
+    K = torch.zeros(1, 256, 2, 128, dtype=bf)
+    V = torch.zeros(1, 256, 2, 128, dtype=bf)
+    bad = [
+        dict(K=torch.zeros(2, 256, 2, 128, dtype=bf)),            # batch
+        dict(K=torch.zeros(1, 256, 2, 64, dtype=bf)),             # head_dim
+        dict(K=torch.zeros(1, 128, 2, 128, dtype=bf), V=torch.zeros(1, 128, 2, 128, dtype=bf)),
+        dict(V=torch.zeros(1, 64, 2, 128, dtype=bf)),             # V differs from K
+        dict(O=torch.zeros(1, 16, 4, 128, dtype=bf)),             # O differs from Q
+    ]
+    for kw in bad:
+        args = dict(Q=Q, K=K, V=V, O=None)
+        args.update(kw)
+        with pytest.raises(ValueError):
+            _lib.bsfa_prefill(args["Q"], args["K"], args["V"], args["O"], block_q=128)
+    # per-block outputs must have the problem's size: [B][Hq][nqb], [B][Hq][nqb][nkb]
+    with pytest.raises(ValueError, match="kept_counts"):
+        _lib.bsfa_prefill(Q, K, V, block_q=128, kept_counts=torch.zeros(3, dtype=torch.int32))
+    with pytest.raises(ValueError, match="debug_block_stat"):
+        _lib.bsfa_prefill(Q, K, V, block_q=128, debug_block_stat=torch.zeros(4 * 2 * 3))
+    with pytest.raises(ValueError, match="kept_total"):
+        _lib.bsfa_prefill(Q, K, V, block_q=128, kept_total=torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(ValueError, match="kth_out"):
+        _lib.bsfa_calibrate_blockmax(Q, K, [4], torch.zeros(4 * 2 - 1), block_q=128)
+    with pytest.raises(ValueError, match="debug_block_stat"):
+        _lib.bsfa_gate_masks(Q, K, None, 0, torch.zeros(1, 4, 2, 1, dtype=torch.int64),
+                             block_q=128, debug_block_stat=torch.zeros(5))
+    # varlen: packed [tokens, heads, dim]; paged: K / V pages of one shape
+    cu = torch.tensor([0, 256], dtype=torch.int32)
+    with pytest.raises(ValueError):
+        _lib.bsfa_prefill_varlen(Q[0], K[0], V[0, :100], cu, cu, 256, 256, block_q=128)
+    pages = torch.zeros(4, 64, 2, 128, dtype=bf)
+    with pytest.raises(ValueError):
+        _lib.bsfa_prefill_paged(Q[0], pages, pages[:3], cu, torch.tensor([256], dtype=torch.int32),
+                                torch.zeros(1, 4, dtype=torch.int32), 256, 256, block_q=128)
+

@@ -306,3 +306,25 @@ def test_calibration_cli_reproduces_the_oracle_table(tmp_path):
     inf = np.isinf(ref.T)
     np.testing.assert_array_equal(got.T[inf], ref.T[inf])
     np.testing.assert_allclose(got.T[~inf], ref.T[~inf], rtol=0, atol=1e-3)
+
+
+def test_calibrate_table_at_workload_size_reproduces_the_stored_16k_table():
+    # the GPU calibration tool on the 16K workload's 8 calibration seeds (32 query heads, 128
+    # query blocks, k = 32) against the table the oracle calibrated from the same seeds
+    import os
+    from block_sparse_long_amd.table import ThresholdTable, calibrate_table
+    c = synth.CONFIGS["llama_16k"]
+    ref = ThresholdTable.load(os.path.join(os.path.dirname(__file__), "golden",
+                                           "thresholds_llama_16k.bin"))
+    samples = []
+    for seed in c["calib_seeds"]:
+        print(f"case llama_16k calibration seed {seed}", flush=True)
+        Q, K, _ = synth.make_inputs("llama_16k", seed)
+        samples.append(tuple(x.to(torch.bfloat16).cuda() for x in (Q, K)))
+        del Q, K
+    got = calibrate_table(samples, budgets=c["budgets"], block_q=c["block_q"],
+                          block_k=c["block_k"])
+    assert got.T.shape == ref.T.shape == (1, 32, 128) and got.budgets == ref.budgets
+    inf = np.isinf(ref.T)
+    np.testing.assert_array_equal(got.T[inf], ref.T[inf])
+    np.testing.assert_allclose(got.T[~inf], ref.T[~inf], rtol=0, atol=1e-3)
