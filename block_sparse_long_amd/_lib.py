@@ -34,7 +34,7 @@ GATE_MODES = {"dense": BSFA_GATE_DENSE, "absolute": BSFA_GATE_ABSOLUTE,
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libbsfa.so")
 ABI_MAJOR = 3    # the layout of bsfa_problem and the entry points' signatures below
 
-EXPORTED = ("bsfa_prefill", "bsfa_prefill_varlen", "bsfa_prefill_paged",
+EXPORTED = ("bsfa_prefill", "bsfa_prefill_noalloc", "bsfa_prefill_varlen", "bsfa_prefill_paged",
             "bsfa_prefill_workspace_bytes",
             "bsfa_gate_masks", "bsfa_calibrate_blockmax", "bsfa_calibrate_workspace_bytes",
             "bsfa_mfma_rate_probe", "bsfa_status_string", "bsfa_last_error", "bsfa_version")
@@ -89,6 +89,10 @@ def load_library(path: str = LIB_PATH):
     lib.bsfa_prefill.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, ctypes.POINTER(BsfaTable),
                                  ctypes.c_int32, ctypes.c_int32, ctypes.c_float, vp, vp, vp, vp,
                                  vp, ctypes.c_uint64, vp]
+    lib.bsfa_prefill_noalloc.restype = ctypes.c_int32
+    lib.bsfa_prefill_noalloc.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp,
+                                         ctypes.POINTER(BsfaTable), ctypes.c_int32, ctypes.c_int32,
+                                         ctypes.c_float, vp, vp, vp, vp, vp]
     lib.bsfa_prefill_varlen.restype = ctypes.c_int32
     lib.bsfa_prefill_varlen.argtypes = [ctypes.POINTER(BsfaProblem), vp, vp, vp, vp, vp,
                                         ctypes.POINTER(BsfaTable), ctypes.c_int32, ctypes.c_int32,
@@ -270,6 +274,32 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
                           mode, float(log_lambda), _ptr(O), _ptr(kept_counts), _ptr(kept_total),
                           _ptr(debug_block_stat), _ptr(workspace), ctypes.c_uint64(ws_bytes),
                           _stream_handle(stream, Q.device))
+    _check(st)
+    return O
+
+
+def bsfa_prefill_noalloc(Q, K, V, O, *, block_q: int, block_k: int = 64, gate_mode="dense",
+                         table=None, budget_slice: int = 0, log_lambda: float = -math.inf,
+                         kept_counts=None, kept_total=None, debug_block_stat=None,
+                         softmax_scale: float = 0.0, stream=None, mean_correction: bool = False,
+                         gate_dtype="bf16"):
+    """bsfa_prefill with the absolute gate's workspace in the library's static device scratch:
+    neither this function nor the library allocates (O and every output are the caller's).
+    Same arguments and results as bsfa_prefill with a workspace. Returns O."""
+    lib = load_library()
+    if O is None:
+        raise ValueError("bsfa_prefill_noalloc writes into a caller-provided O")
+    mode = GATE_MODES[gate_mode] if isinstance(gate_mode, str) else int(gate_mode)
+    p = make_problem(Q, K, V, O, block_q=block_q, block_k=block_k, softmax_scale=softmax_scale,
+                     mean_correction=mean_correction, gate_dtype=gate_dtype)
+    tbl = table.c_struct() if table is not None else None
+    _check_outputs(p.batch, p.heads_q, p.seqlen, int(K.shape[1]), block_q, block_k, kept_counts,
+                   kept_total, debug_block_stat, Q.device)
+    st = lib.bsfa_prefill_noalloc(ctypes.byref(p), _ptr(Q), _ptr(K), _ptr(V),
+                                  ctypes.byref(tbl) if tbl is not None else None,
+                                  int(budget_slice), mode, float(log_lambda), _ptr(O),
+                                  _ptr(kept_counts), _ptr(kept_total), _ptr(debug_block_stat),
+                                  _stream_handle(stream, Q.device))
     _check(st)
     return O
 

@@ -9,6 +9,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "bsfa_internal.h"
 
 namespace {
@@ -247,7 +249,7 @@ const char* bsfa_status_string(int32_t s) {
 
 const char* bsfa_last_error(void) { return g_last_error; }
 
-int32_t bsfa_version(void) { return (3 << 16) | 0; }
+int32_t bsfa_version(void) { return (3 << 16) | 1; }
 
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) {
   if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
@@ -276,7 +278,8 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
                          const int32_t* cu_q, const KeyLayout& kl, const bsfa_table* table,
                          int32_t budget_slice, int32_t gate_mode, float log_lambda, void* O,
                          int32_t* kept_counts, uint64_t* kept_total, float* debug_block_stat,
-                         void* workspace, uint64_t workspace_bytes, void* stream) {
+                         void* workspace, uint64_t workspace_bytes, void* stream,
+                         bool validate_only = false) {
   const int32_t* cu_k = kl.cu_k;
   bsfa_status s = check_problem(p, true);
   if (s != BSFA_OK) return s;
@@ -362,6 +365,7 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
                 (unsigned long long)workspace_bytes, (unsigned long long)ws_need);
 
+  if (validate_only) return ok();
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (kept_total) {
     hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(kept_total), st);
@@ -422,6 +426,34 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   return ok();
 }
 
+// ---- Static scratch for bsfa_prefill_noalloc ----
+// The absolute gate's workspace (keep masks, block means) for callers that cannot allocate:
+// one array per device, part of the library's code object, held until the process ends. In
+// host code `scratch` names a host-side stand-in, not device memory: its device address is
+// looked up once per device (with that device current) and only that address is used.
+constexpr uint64_t kScratchBytes = uint64_t(64) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's copy of the scratch array.
+hipError_t scratch_of_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  *ptr = g_scratch_ptr[dev];
+  return g_scratch_err[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -434,6 +466,39 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
   return prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode,
                       log_lambda, O, kept_counts, kept_total, debug_block_stat, workspace,
                       workspace_bytes, stream);
+}
+
+bsfa_status bsfa_prefill_noalloc(const bsfa_problem* p, const void* Q, const void* K,
+                                 const void* V, const bsfa_table* table, int32_t budget_slice,
+                                 int32_t gate_mode, float log_lambda, void* O,
+                                 int32_t* kept_counts, uint64_t* kept_total,
+                                 float* debug_block_stat, void* stream) {
+  bsfa_status s = check_problem(p, true);
+  if (s != BSFA_OK) return s;
+  // DENSE and RELATIVE use no workspace; ABSOLUTE takes the static scratch as its workspace
+  if (gate_mode != BSFA_GATE_ABSOLUTE)
+    return prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode,
+                        log_lambda, O, kept_counts, kept_total, debug_block_stat, nullptr, 0,
+                        stream);
+  const uint64_t need = bsfa_prefill_workspace_bytes(p, gate_mode);
+  if (need > kScratchBytes)
+    return fail(BSFA_ERR_UNSUPPORTED,
+                "this call needs %llu bytes of workspace, above the %llu-byte static scratch of "
+                "bsfa_prefill_noalloc (bsfa_prefill takes a caller workspace)",
+                (unsigned long long)need, (unsigned long long)kScratchBytes);
+  // every check first, against a stand-in with the scratch's size and alignment (never
+  // dereferenced), so that an invalid call touches no device
+  s = prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode, log_lambda,
+                   O, kept_counts, kept_total, debug_block_stat,
+                   reinterpret_cast<void*>(uintptr_t(256)), kScratchBytes, stream, true);
+  if (s != BSFA_OK) return s;
+  void* ptr = nullptr;
+  const hipError_t e = scratch_of_current_device(&ptr);
+  if (e != hipSuccess || !ptr)
+    return fail(BSFA_ERR_HIP, "device address of the static scratch: %s", hipGetErrorString(e));
+  return prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode,
+                      log_lambda, O, kept_counts, kept_total, debug_block_stat, ptr,
+                      kScratchBytes, stream);
 }
 
 bsfa_status bsfa_prefill_varlen(const bsfa_problem* p, const void* Q, const void* K,

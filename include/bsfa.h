@@ -197,6 +197,30 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
                          float* debug_block_stat, void* workspace, uint64_t workspace_bytes,
                          void* stream);
 
+/* bsfa_prefill for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): the same computation and results as
+ * bsfa_prefill with a caller workspace of bsfa_prefill_workspace_bytes(p, gate_mode) bytes, with
+ * the absolute gate's workspace (keep masks; with mean_correction also the block means; with
+ * an FP8 gate also the FP8 copies) taken from a static 64 MiB device array that the library
+ * holds on each device it runs on until the process ends. The call itself allocates and frees
+ * nothing; the caller passes inputs and outputs as for bsfa_prefill (arguments of the same
+ * names mean the same). The array's device address is looked up on the first call on each
+ * device (that call must find the device current, as every call must).
+ *   Limit: a call whose workspace would exceed 64 MiB returns BSFA_ERR_UNSUPPORTED before
+ *   anything is enqueued (the keep masks take B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) * 8
+ *   bytes: 8 MiB for one 128K-token sequence with 32 query heads at Bq = 128; FP8 copies do
+ *   not fit beyond short sequences). DENSE and RELATIVE use no workspace.
+ *   Sharing: every call on one device uses that device's one array, which keeps the last
+ *   call's contents (each call writes before it reads; nothing needs clearing). Calls that
+ *   overlap on one device (another stream, another thread) race on it: the caller orders them.
+ * Returns BSFA_OK or an error status as bsfa_prefill does; BSFA_ERR_HIP also when the array's
+ * device address cannot be obtained. */
+bsfa_status bsfa_prefill_noalloc(const bsfa_problem* p, const void* Q, const void* K,
+                                 const void* V, const bsfa_table* table, int32_t budget_slice,
+                                 int32_t gate_mode, float log_lambda, void* O,
+                                 int32_t* kept_counts, uint64_t* kept_total,
+                                 float* debug_block_stat, void* stream);
+
 /* bsfa_prefill over a batch of sequences of different lengths, packed along the token axis
  * (the interface of variable-length attention kernels; "FlashPrefill V2: Block-Sparse Prefill
  * Attention for Long-Context LLM Serving" names varlen scheduling, chunked prefill and
@@ -316,7 +340,8 @@ const char* bsfa_status_string(int32_t status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* ABI version: (major << 16) | minor. Major 3: bsfa_table ends with the budgets array
+/* ABI version: (major << 16) | minor. Minor 1 adds bsfa_prefill_noalloc. Major 3: bsfa_table
+ * ends with the budgets array
  * (major 2: bsfa_problem ends with mean_correction and gate_dtype, and
  * bsfa_calibrate_blockmax takes a workspace). */
 int32_t bsfa_version(void);

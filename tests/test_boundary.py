@@ -435,3 +435,31 @@ def test_binding_refuses_inconsistent_tensors():
         _lib.bsfa_prefill_paged(Q[0], pages, pages[:3], cu, torch.tensor([256], dtype=torch.int32),
                                 torch.zeros(1, 4, dtype=torch.int32), 256, 256, block_q=128)
 
+
+def test_noalloc_validates_and_refuses_calls_beyond_its_scratch():
+    # the static-scratch entry point checks the problem like bsfa_prefill, and refuses a call
+    # whose workspace exceeds its 64 MiB array before anything is enqueued
+    lib = _lib.load_library()
+
+    def call(p, tbl=None, mode=_lib.BSFA_GATE_DENSE, q=FAKE):
+        return lib.bsfa_prefill_noalloc(ctypes.byref(p), q, FAKE, FAKE,
+                                        ctypes.byref(tbl) if tbl else None, 0, mode, -math.inf,
+                                        FAKE, None, None, None, None)
+    p = problem()
+    p.head_dim = 96
+    assert call(p) == _lib.BSFA_ERR_SHAPE
+    assert call(problem(), q=None) == _lib.BSFA_ERR_ARG
+    assert call(problem(), mode=_lib.BSFA_GATE_ABSOLUTE, q=None) == _lib.BSFA_ERR_TABLE
+    # 512K tokens x 32 heads: 4096 query blocks x 128 mask words x 8 B = 128 MiB of masks
+    big = problem(N=1 << 19, Hq=32, Hkv=8)
+    need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(big), _lib.BSFA_GATE_ABSOLUTE)
+    assert need == 32 * 4096 * 128 * 8
+    assert call(big, tbl=table(Hq=32, t_len=4096), mode=_lib.BSFA_GATE_ABSOLUTE) == \
+        _lib.BSFA_ERR_UNSUPPORTED
+    assert "static scratch" in _lib.bsfa_last_error()
+    # the binding needs a caller-provided O (it allocates nothing)
+    import torch
+    Q = torch.zeros(1, 256, 4, 128, dtype=torch.bfloat16)
+    K = torch.zeros(1, 256, 2, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        _lib.bsfa_prefill_noalloc(Q, K, K, None, block_q=128)
