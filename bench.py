@@ -226,13 +226,14 @@ def predicted_density(N, Bq, k, Bk=64):
 
 
 class Workload:
-    def __init__(self, name, device):
+    def __init__(self, name, device, skip=None):
         import torch
         from block_sparse_long_amd import synth
         from block_sparse_long_amd.table import ThresholdTable
         self.name = name
         self.c = c = synth.CONFIGS[name]
-        Q, K, V = synth.make_inputs(name, 0)
+        self.skip = skip
+        Q, K, V = synth.make_inputs(name, 0, skip=skip)
         self.host = synth.to_bf16(Q, K, V)
         del Q, K, V
         self.Qd, self.Kd, self.Vd = (x.to(device) for x in self.host)

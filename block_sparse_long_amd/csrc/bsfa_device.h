@@ -385,11 +385,13 @@ __device__ __forceinline__ void exp_pair(int p, const f32x16 (&s)[2], float off,
 }
 
 constexpr int kPairs = 16;        // P pairs per lane per tile (32 rows x 64 keys / 64 lanes / 2)
-constexpr int kPairsQK = 8;       // of which issued under the QK MFMAs; the rest under PV
+// Of these, the dense and mask-walk loops issue the first kPairsPV next to the PV MFMAs and the
+// rest next to the QK MFMAs; the voting kernels issue all of them next to the QK MFMAs.
+constexpr int kPairsPV = 8;
 
 // Steps [FIRST, LAST) of the PV product of the previous kept tile (O^T += V^T P^T, one MFMA per
 // (k-step, M-block); fragments read two steps ahead into vb, the first two by pv_prefetch)
-// with, next to the MFMAs, exponential pairs 0 .. kPairsQK-1 of the current tile (do_exp) and
+// with, next to the MFMAs, exponential pairs 0 .. NPV-1 of the current tile (do_exp) and
 // the MV rounds of the V_t copy (vload, copy_v(r)), both spread over steps DEC .. NSTEP-1.
 template <int D>
 __device__ __forceinline__ void pv_prefetch(const __bf16* sv, bf16x8 (&vb)[3], int lane) {
@@ -407,7 +409,7 @@ __device__ __forceinline__ bool part_on(int mode, bool flag) {
 }
 
 template <int D, int FIRST, int LAST, int DEC, int MV, int PVM = kFlag, int EXM = kFlag,
-          int VLM = kFlag, typename CopyV>
+          int VLM = kFlag, int NPV = kPairsPV, typename CopyV>
 __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, const __bf16* sv,
                                          const bf16x8 (&pbp)[4], f32x16 (&o)[D / 32],
                                          bf16x8 (&vb)[3], const f32x16 (&sc)[2], float off,
@@ -434,7 +436,7 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
     }
     if (do_exp && st >= DEC) {
 #pragma unroll
-      for (int pi = (st - DEC) * kPairsQK / NE; pi < (st - DEC + 1) * kPairsQK / NE; ++pi)
+      for (int pi = (st - DEC) * NPV / NE; pi < (st - DEC + 1) * NPV / NE; ++pi)
         exp_pair(pi, sc, off, c, pbn, sum);
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -443,19 +445,21 @@ __device__ __forceinline__ void pv_steps(bool do_pv, bool do_exp, bool vload, co
 
 // S^T = K Q^T for the next tile, M-block outer (step st: block st / KS, k-step st % KS), each
 // step reading the next step's K fragment. Next to the MFMAs: the MK rounds of the K_{t+2}
-// copy (kload, copy_k(r)) on the first steps, the remaining exponential pairs of the current
-// tile (do_exp) and, during the second M-block, the in-lane max over the first block's 16
-// scores (into mx).
-template <int D, int MK, int EXM = kFlag, int KLM = kFlag, typename CopyK>
+// copy (kload, copy_k(r)) on the first steps and the MV rounds of a V copy (vload, copy_v(r))
+// on the last ones, the remaining exponential pairs of the current tile (do_exp) and, during
+// the second M-block, the in-lane max over the first block's 16 scores (into mx).
+template <int D, int MK, int EXM = kFlag, int KLM = kFlag, int NPV = kPairsPV, int MV = 1,
+          int VLM = kNever, typename CopyK, typename CopyV>
 __device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* kbase,
                                          const bf16x8 (&qf)[D / 16],
                                          f32x16 (&sn)[2], const f32x16 (&sc)[2], float off,
                                          float c, bf16x8 (&pbn)[4], float& sum, float& mx,
-                                         CopyK&& copy_k) {
+                                         CopyK&& copy_k, bool vload, CopyV&& copy_v) {
   do_exp = part_on(EXM, do_exp);
   kload = part_on(KLM, kload);
+  vload = part_on(VLM, vload);
   constexpr int KS = Tile<D>::KS, STR = Tile<D>::STR, NST = 2 * KS;
-  constexpr int NP = kPairs - kPairsQK;
+  constexpr int NP = kPairs - NPV;
   bf16x8 ka[2];
   ka[0] = *reinterpret_cast<const bf16x8*>(kbase);
 #pragma unroll
@@ -480,9 +484,14 @@ __device__ __forceinline__ void qk_phase(bool do_exp, bool kload, const __bf16* 
       for (int r = 0; r < MK; ++r)
         if (r * (NST / 2) / MK == st) copy_k(r);
     }
+    if (vload) {
+#pragma unroll
+      for (int r = 0; r < MV; ++r)
+        if (NST / 2 + r * (NST / 2) / MV == st) copy_v(r);
+    }
     if (do_exp) {
 #pragma unroll
-      for (int pi = kPairsQK + st * NP / NST; pi < kPairsQK + (st + 1) * NP / NST; ++pi)
+      for (int pi = NPV + st * NP / NST; pi < NPV + (st + 1) * NP / NST; ++pi)
         exp_pair(pi, sc, off, c, pbn, sum);
     }
     if (mb == 1) {
@@ -774,7 +783,9 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of the previous tile reads pb[P ^ 1]
   const int kfo = (lane & 31) * STR + 8 * (lane >> 5);
   constexpr int NSTEP = 4 * MD;               // PV MFMA steps
-  constexpr int DEC = 2;                      // PV steps issued before the tile-t decision
+  // PV steps issued before the decision on tile t: all of them in the voting kernels; dense
+  // and the mask walk decide nothing and start tile t's exponentials after two
+  constexpr int DEC = (GATE == kRelative || GATE == kAbsVote) ? NSTEP : 2;
   constexpr int GV = WPH * kRows / 64;        // statistics per lane per head
   constexpr int MKR = copy_iters<STR, NW>(), MVR = copy_iters<STRV, NW>();
 
@@ -819,6 +830,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const __bf16* const sv = P ? sV0 : sV1;     // V of the previous tile
     bf16x8 vb[3];
     float sum = 0.f;
+    // this tile's P buffer was last read by the previous iteration's PV: its old contents are
+    // dead (a skipped tile leaves it unwritten, and then the next PV does not read it)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) asm("" : "=v"(pb[P][k]));
     // The reference update of tile t, made before the vote into a copy: the exponentials
     // need its offset and would otherwise wait for the statistics' LDS round trip and the
     // vote. A skipped tile leaves the state as it was (its exponentials are computed and not
@@ -827,6 +842,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     float alpha = 1.f;
     bool moved = update_reference(sp, rc, c, alpha);
     const float off = -sp.mref * c;
+    constexpr bool kVote = GATE == kRelative || GATE == kAbsVote;
+    // The voting kernels run the whole PV phase of the previous tile first (the statistics'
+    // LDS read lands meanwhile), then vote; dense and the mask walk keep every tile they visit
+    // and start tile t's exponentials and V copy after the first PV steps.
     if (keep_prev) {
       pv_prefetch<D>(sv, vb, lane);
       pv_steps<D, 0, DEC, DEC, MVR>(true, false, false, sv, pb[P ^ 1], o, vb, sb[P], 0.f, c,
@@ -866,15 +885,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st = sp;
     else
       moved = false;
-    // rest of PV of the previous tile with the first half of tile t's exponentials and the V_t
-    // copy (skipped as a whole when there is none of the three)
-    // Step sequences without per-step tests wherever possible. Dense and the mask walk keep
-    // every tile they visit: one straight-line form (and a flagged one for the first tile).
-    // The voting kernels take the PV test out of the steps (a form with and one without the
-    // MFMAs) and compute the exponentials of every tile: those of a skipped tile are never
-    // used, which costs less than a test per step (and a second full copy of the phase costs
-    // more registers than the tests it saves).
-    constexpr bool kVote = GATE == kRelative || GATE == kAbsVote;
+    // Rest of the PV phase (dense and the mask walk) with the first kPairsPV exponential pairs
+    // of tile t and the V_t copy, in straight-line forms (and a flagged one for the first tile).
     if constexpr (!kVote) {
       if (keep_prev)
         pv_steps<D, DEC, NSTEP, DEC, MVR, kAlways, kAlways, kAlways>(
@@ -882,13 +894,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       else
         pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kAlways>(
             false, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
-    } else {
-      if (keep_prev)
-        pv_steps<D, DEC, NSTEP, DEC, MVR, kAlways, kAlways, kFlag>(
-            true, true, anyv, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
-      else
-        pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kFlag>(
-            false, true, anyv, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
     }
     // the previous P is dead from here on (the next write of its buffer precedes the next read)
 #pragma unroll
@@ -902,15 +907,34 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       st.l *= alpha;
     }
 
-    // scores of tile t1 with the second half of tile t's exponentials
+    // Scores of tile t1 with the K_{t2} copy, the remaining exponentials of tile t and the
+    // first half of t1's row max next to the MFMAs. In the voting kernels this phase also
+    // carries all of tile t's exponentials, left out when t is skipped (a skipped tile
+    // computes no exponentials, "Skipping attention blocks was the easy part", Vote, then
+    // skip), and the V_t copy, made when some head of the workgroup keeps t. One form per
+    // combination, chosen once per phase.
     const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K of t1
     float mx = kNegInf;
-    if (kload)
-      qk_phase<D, MKR, kAlways, kAlways>(true, true, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P],
-                                         sum, mx, copy_k);
-    else
-      qk_phase<D, MKR, kAlways, kNever>(true, false, kb, qf, sb[P ^ 1], sb[P], off, c, pb[P],
-                                        sum, mx, copy_k);
+    constexpr int NPV = kVote ? 0 : kPairsPV;
+    constexpr int VQ = kVote ? kFlag : kNever;
+    if (!kVote || mykeep) {
+      if (kload)
+        qk_phase<D, MKR, kAlways, kAlways, NPV, MVR, VQ>(true, true, kb, qf, sb[P ^ 1], sb[P], off,
+                                                         c, pb[P], sum, mx, copy_k, anyv, copy_v);
+      else
+        qk_phase<D, MKR, kAlways, kNever, NPV, MVR, VQ>(true, false, kb, qf, sb[P ^ 1], sb[P],
+                                                        off, c, pb[P], sum, mx, copy_k, anyv,
+                                                        copy_v);
+    } else {
+      if (kload)
+        qk_phase<D, MKR, kNever, kAlways, NPV, MVR, VQ>(false, true, kb, qf, sb[P ^ 1], sb[P],
+                                                        off, c, pb[P], sum, mx, copy_k, anyv,
+                                                        copy_v);
+      else
+        qk_phase<D, MKR, kNever, kNever, NPV, MVR, VQ>(false, false, kb, qf, sb[P ^ 1], sb[P],
+                                                       off, c, pb[P], sum, mx, copy_k, anyv,
+                                                       copy_v);
+    }
     if (mykeep) st.l += sum;
     if (tile_masked(t1)) {
       mask_tile(sb[P ^ 1], t1 * BK, arow, rvalid, lane);
