@@ -226,16 +226,18 @@ def predicted_density(N, Bq, k, Bk=64):
 
 
 class Workload:
-    def __init__(self, name, device, skip=None):
+    def __init__(self, name, device, skip=None, host=None):
         import torch
         from block_sparse_long_amd import synth
         from block_sparse_long_amd.table import ThresholdTable
         self.name = name
         self.c = c = synth.CONFIGS[name]
         self.skip = skip
-        Q, K, V = synth.make_inputs(name, 0, skip=skip)
-        self.host = synth.to_bf16(Q, K, V)
-        del Q, K, V
+        if host is None:
+            Q, K, V = synth.make_inputs(name, 0, skip=skip)
+            host = synth.to_bf16(Q, K, V)
+            del Q, K, V
+        self.host = host
         self.Qd, self.Kd, self.Vd = (x.to(device) for x in self.host)
         self.O = torch.empty_like(self.Qd)
         self.N, self.Hq, self.d, self.Bq = c["n"], c["heads_q"], c["d"], c["block_q"]
@@ -455,36 +457,188 @@ def run_fp8_gate(w, steps, warmup, gated, dense_ms):
             "mean_abs_output_deviation": dev}
 
 
-def cpu_baseline(w, mode, budget_slice=0, log_lambda=-math.inf, blocks=None, k=None):
-    """The oracle as it stands, on one host core, on a bounded sample of the workload: every
-    head of the query blocks {0, 1, k/2 - 1, k/2, nqb/4, nqb/2 - 1, nqb/2, 3 nqb/4, nqb - 1}
-    (the first ones, the -inf boundary of the table, the last calibrated and first reused
-    columns at 128K, the last). One BLAS thread: the oracle multiplies one 128 x 64 tile at a
-    time, too small for threads to help (16 threads measured 0.068 against 0.082 TFLOP/s)."""
+# ---- the CPU oracle, timed on the host's cores (before the GPU is touched) ----
+# Worker processes are forked from this process while it has not initialised the GPU, so no
+# child inherits device state; each runs the unchanged oracle on one query head (one BLAS
+# thread: the oracle multiplies one tile at a time, too small for threads to help) and returns
+# its kept counts and the output rows of the sampled query blocks.
+_POOL = {}
+
+
+def _oracle_head(h):
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_limits
-    Qh, Kh, Vh = (x.float().numpy() for x in w.host)
-    nqb = -(-w.N // w.Bq)
-    if blocks is None:
-        kk = k or 2
-        blocks = sorted(x for x in {0, 1, kk // 2 - 1, kk // 2, nqb // 4, nqb // 2 - 1, nqb // 2,
-                                    3 * nqb // 4, nqb - 1} if 0 <= x < nqb)
-    cores = 1
-    with threadpool_limits(limits=cores):
-        t0 = time.perf_counter()
-        r = oracle.oracle_prefill(Qh, Kh, Vh, block_q=w.Bq, block_k=w.Bk, mode=mode,
-                                  table=None if w.table is None else w.table.T,
-                                  budget_slice=budget_slice, log_lambda=log_lambda,
-                                  query_blocks=blocks)
-        sec = time.perf_counter() - t0
-    flops = executed_flops(np.maximum(r.kept_counts, 0), w.N, w.Bq, w.d, w.Bk,
-                           query_blocks=blocks)
-    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
-            "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"{w.name}: query blocks {blocks} x all {w.Hq} heads, same inputs and "
-                      f"table, float32 numpy, {cores} BLAS thread; executed TFLOP/s of the "
-                      f"sample"}
+    d = _POOL
+    Qh, Kh, Vh, T, kw, blocks, Bq = d["Q"], d["K"], d["V"], d["T"], d["kw"], d["blocks"], d["Bq"]
+    G = Qh.shape[2] // Kh.shape[2]
+    g = h // G
+    with threadpool_limits(limits=1):
+        r = oracle.oracle_prefill(Qh[:, :, h:h + 1], Kh[:, :, g:g + 1], Vh[:, :, g:g + 1],
+                                  table=None if T is None else T[:, h:h + 1, :],
+                                  query_blocks=blocks, **kw)
+    rows = np.concatenate([np.arange(i * Bq, min((i + 1) * Bq, Qh.shape[1])) for i in blocks])
+    return h, r.kept_counts[:, 0], r.out[:, rows, 0, :]
+
+
+def host_cores():
+    """Worker count: the host cores this process may run on, at most 16 (the CPU share of one
+    GPU on the benchmark machines)."""
+    return max(1, min(16, len(os.sched_getaffinity(0))))
+
+
+def cpu_info():
+    import numpy as np
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas = ""
+    try:
+        from threadpoolctl import threadpool_info
+        blas = ", ".join(f"{x.get('internal_api')} {x.get('version')}" for x in threadpool_info()
+                         if x.get("user_api") == "blas")
+    except Exception:
+        pass
+    return {"cpu": model, "blas": blas or "numpy", "numpy": np.__version__}
+
+
+def oracle_timed(host, table_T, Bq, Bk, mode, blocks, log_lambda=-math.inf, budget_slice=0):
+    """The oracle over every head of the given query blocks, one head per worker process, on
+    all host cores. Returns (seconds, kept counts [B, Hq, nqb] (-1 outside the blocks), output
+    rows [B, rows, Hq, d], cores)."""
+    import multiprocessing as mp
+    import numpy as np
+    Qh, Kh, Vh = (x.float().numpy() for x in host)
+    _POOL.update(Q=Qh, K=Kh, V=Vh, T=table_T, Bq=Bq, blocks=list(blocks),
+                 kw=dict(block_q=Bq, block_k=Bk, mode=mode, budget_slice=budget_slice,
+                         log_lambda=log_lambda))
+    Hq = Qh.shape[2]
+    cores = min(host_cores(), Hq)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(cores) as pool:
+        res = pool.map(_oracle_head, range(Hq), chunksize=1)
+    sec = time.perf_counter() - t0
+    nqb = -(-Qh.shape[1] // Bq)
+    counts = np.full((Qh.shape[0], Hq, nqb), -1, np.int64)
+    out = None
+    for h, kc, o in res:
+        counts[:, h] = kc
+        if out is None:
+            out = np.empty((o.shape[0], o.shape[1], Hq, o.shape[2]), np.float32)
+        out[:, :, h] = o
+    _POOL.clear()
+    return sec, counts, out, cores
+
+
+def sample_blocks(nqb, k):
+    """Bounded sample of query blocks for the headline oracle timing: every 32nd block, the
+    first two, the table's -inf boundary (k/2 - 1, k/2), the last calibrated and first reused
+    threshold columns at 128K (511, 512) and the last."""
+    kk = k or 2
+    s = set(range(0, nqb, 32)) | {0, 1, kk // 2 - 1, kk // 2, nqb // 2 - 1, nqb // 2, nqb - 1}
+    return sorted(x for x in s if 0 <= x < nqb)
+
+
+def deviation(dev_O, oracle_out, blocks, Bq):
+    """max-abs and mean-abs of the device output against the oracle on the given blocks."""
+    import numpy as np
+    N = dev_O.shape[1]
+    rows = np.concatenate([np.arange(i * Bq, min((i + 1) * Bq, N)) for i in blocks])
+    got = dev_O[:, rows].float().cpu().numpy()
+    e = np.abs(got - oracle_out)
+    return {"max_abs": float(e.max()), "mean_abs": float(e.mean())}
+
+
+def device_out_fp32(w, mode, **kw):
+    """One call of workload w with a float32 output (for the comparison with the oracle)."""
+    import torch
+    from block_sparse_long_amd import _lib
+    O = torch.empty(w.Qd.shape, dtype=torch.float32, device=w.Qd.device)
+    _lib.bsfa_prefill(w.Qd, w.Kd, w.Vd, O, block_q=w.Bq, block_k=w.Bk, gate_mode=mode,
+                      table=kw.pop("table", w.dtable if mode == "absolute" else None), **kw)
+    torch.cuda.synchronize()
+    return O
+
+
+def gate_row(r, dense_ms, N, Bq, k=None, Bk=64):
+    row = {"ms": round(r["ms"], 4), "tflops": round(r["tflops"], 2),
+           "pct_mfma_peak": round(r["pct_peak"], 2),
+           "speedup_vs_dense": round(dense_ms / r["ms"], 4),
+           "kept_fraction": round(r["kept_fraction"], 4)}
+    if k is not None:
+        row["predicted_density"] = round(predicted_density(N, Bq, k, Bk), 4)
+    return row
+
+
+def config_rows(name, dev, steps, warmup, oracle_run=None, slice_for_oracle=0):
+    """Configs 1-3 of the workload list: dense and every budget slice (both ways of running the
+    absolute gate where they differ), and the oracle's full-size time and output deviation."""
+    import numpy as np
+    import torch
+    from block_sparse_long_amd.table import ThresholdTable
+    w = Workload(name, dev, host=None if oracle_run is None else oracle_run["host"])
+    d = run_gate(w, "dense", steps, warmup)
+    rows = {"dense": {"ms": round(d["ms"], 4), "tflops": round(d["tflops"], 2),
+                      "pct_mfma_peak": round(d["pct_peak"], 2)}}
+    none = torch.empty(0, dtype=torch.uint8, device=dev)
+    for sl, kk in enumerate(w.table.budgets):
+        r = run_gate(w, "absolute", steps, warmup, budget_slice=sl)
+        row = gate_row(r, d["ms"], w.N, w.Bq, kk, w.Bk)
+        # the library's choice against both ways forced: two launches (table without its
+        # budgets) and one launch (no workspace)
+        two = run_gate(w, "absolute", steps, warmup, budget_slice=sl,
+                       table=w.table.to_device(dev, record_budgets=False))
+        one = run_gate(w, "absolute", steps, warmup, budget_slice=sl, workspace=none)
+        row["two_launches_ms"] = round(two["ms"], 4)
+        row["one_launch_ms"] = round(one["ms"], 4)
+        rows[f"k={kk}"] = row
+    if name == "tiny_1k":
+        for label, v in (("T=-inf", -np.inf), ("T=+inf", np.inf)):
+            T = np.full_like(w.table.T[:1], v)
+            tab = ThresholdTable(T=T, budgets=[0], block_q=w.Bq, block_k=w.Bk, head_dim=w.d,
+                                 softmax_scale=w.table.softmax_scale).to_device(dev)
+            r = run_gate(w, "absolute", steps, warmup, table=tab)
+            rows[label] = gate_row(r, d["ms"], w.N, w.Bq)
+    if oracle_run is not None:
+        sec, counts, out, cores = (oracle_run[x] for x in ("sec", "counts", "out", "cores"))
+        fl = executed_flops(np.maximum(counts, 0), w.N, w.Bq, w.d, w.Bk)
+        O = device_out_fp32(w, "absolute", budget_slice=slice_for_oracle)
+        rows["oracle"] = {"budget_k": w.table.budgets[slice_for_oracle], "seconds": round(sec, 2),
+                          "cores": cores, "tflops": round(fl / sec / 1e12, 6),
+                          "kind": "oracle, whole workload",
+                          "device_vs_oracle": deviation(O, out, range(-(-w.N // w.Bq)), w.Bq)}
+        del O
+    del w
+    torch.cuda.empty_cache()
+    return rows
+
+
+def dialled_rows(dev, steps, warmup):
+    """The relative gate on the 64K workload whose skip rate its generator dials (cold key
+    blocks): kept fraction, time and speed-up over dense per skip rate at lambda = 1e-3, and
+    the lambda grid at a 50 % skip rate."""
+    import torch
+    from block_sparse_long_amd import synth
+    c = synth.CONFIGS["llama_64k_dial"]
+    out = {}
+    for skip in [0.0] + list(c["skips"]):
+        w = Workload("llama_64k_dial", dev, skip=skip)
+        d = run_gate(w, "dense", steps, warmup)
+        row = {"dense_ms": round(d["ms"], 3)}
+        lams = (0.0, 1e-4, 1e-3, 1e-2) if skip == c["skip"] else (0.0, 1e-3)
+        for lam in lams:
+            r = run_gate(w, "relative", steps, warmup,
+                         log_lambda=math.log(lam) if lam else -math.inf)
+            row[f"lambda={lam:g}"] = gate_row(r, d["ms"], w.N, w.Bq)
+        out[f"skip={skip:g}"] = row
+        del w
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -501,24 +655,59 @@ def main():
         summarise_counters(args)
         return
     import numpy as np
+    from block_sparse_long_amd import synth
+    from block_sparse_long_amd.table import ThresholdTable
+
+    c = synth.CONFIGS[args.workload]
+    k = c["budgets"][0] if c["budgets"] else None
+    mode = "absolute" if c["budgets"] else "relative"
+    gate_kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
+    N, Bq, Bk = c["n"], c["block_q"], c["block_k"]
+
+    # ---- CPU phase: the oracle on the host cores, before anything touches the GPU ----
+    host_main = synth.to_bf16(*synth.make_inputs(args.workload, 0))
+    cpu, oracle_main, oracle_cfg = None, None, {}
+    if not args.no_cpu_baseline:
+        T = (ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{args.workload}.bin")).T
+             if mode == "absolute" else None)
+        blocks = sample_blocks(-(-N // Bq), k)
+        sec, counts, out, cores = oracle_timed(host_main, T, Bq, Bk, mode, blocks,
+                                               log_lambda=gate_kw.get("log_lambda", -math.inf))
+        fl = executed_flops(np.maximum(counts, 0), N, Bq, c["d"], Bk, query_blocks=blocks)
+        cpu = {"value": round(fl / sec / 1e12, 6), "unit": "TFLOP/s", "cores": cores,
+               "kind": "oracle", "seconds": round(sec, 2),
+               "sample": f"{args.workload}: query blocks {blocks} ({len(blocks)} of "
+                         f"{-(-N // Bq)}) x all {c['heads_q']} heads, same inputs and table, "
+                         f"float32 numpy, one process per head on {cores} host cores, one BLAS "
+                         f"thread each; executed TFLOP/s of the sample",
+               **cpu_info()}
+        oracle_main = dict(blocks=blocks, out=out)
+        if not args.quick:
+            # configs 1-3 in full (32K at k = 64)
+            for name, sl in (("tiny_1k", 0), ("llama_16k", 0), ("llama_32k_sweep", 1)):
+                cc = synth.CONFIGS[name]
+                host = synth.to_bf16(*synth.make_inputs(name, 0))
+                Tn = ThresholdTable.load(os.path.join(GOLDEN, f"thresholds_{name}.bin")).T
+                nb = -(-cc["n"] // cc["block_q"])
+                sec, counts, out, cores = oracle_timed(host, Tn, cc["block_q"], cc["block_k"],
+                                                       "absolute", range(nb), budget_slice=sl)
+                oracle_cfg[name] = dict(host=host, sec=sec, counts=counts, out=out, cores=cores,
+                                        slice=sl)
+
+    # ---- GPU phase ----
     import torch
     from block_sparse_long_amd import _lib
     _lib.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
-    w = Workload(args.workload, dev)
-    k = w.table.budgets[0] if w.table is not None else None
-    mode = "absolute" if w.table is not None else "relative"
-    gate_kw = dict(budget_slice=0) if mode == "absolute" else dict(log_lambda=math.log(1e-3))
-
+    w = Workload(args.workload, dev, host=host_main)
     gated = run_gate(w, mode, args.steps, args.warmup, **gate_kw)
     sweep = run_sweep(w, args.steps, args.warmup) if mode == "absolute" else None
     dense = run_gate(w, "dense", args.steps, args.warmup)
     # zero-skip taxes: the gated instantiations with a gate that never skips
     ninf = None
     if w.table is not None:
-        from block_sparse_long_amd.table import ThresholdTable
         T = np.full_like(w.table.T[:1], -np.inf)
         ninf = ThresholdTable(T=T, budgets=[0], block_q=w.table.block_q, block_k=64,
                               head_dim=w.d, softmax_scale=w.table.softmax_scale).to_device(dev)
@@ -538,6 +727,11 @@ def main():
     }
     if w.table is not None:
         extras["zero_skip_tax_absolute"] = round(abs_ninf["ms"] / dense["ms"] - 1, 4)
+    if oracle_main is not None:
+        O = device_out_fp32(w, mode, **dict(gate_kw))
+        extras["device_vs_oracle_sample"] = deviation(O, oracle_main["out"],
+                                                      oracle_main["blocks"], w.Bq)
+        del O
     # the same gated call with L2 and the last-level cache flushed before each call (median)
     extras["gated_ms_flushed_median"] = round(flushed_median_ms(w, mode, **gate_kw), 3)
     # executed TFLOP/s against the matrix cores' measured sustained rate as well as the spec
@@ -581,33 +775,29 @@ def main():
                                  "tflops": round(ch["tflops"], 2),
                                  "kept_blocks": ch["kept"], "kept_blocks_whole_call": gated["kept"],
                                  "vs_whole_call": round(ch["ms"] / gated["ms"], 4)}
+    line_cfg = {"workload": args.workload, "batch": 1, "seq_len": w.N,
+                "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": w.d,
+                "tile": f"{w.Bq}x64", "gate": mode,
+                "budget_k": k, "calibrated_len": c["calib_n"] if k else None}
+    del w
+    torch.cuda.empty_cache()
     if not args.quick:
+        # configs 1-3 (tiny 1K, 16K k = 32, the 32K budget sweep), with the oracle's full-size
+        # runs from the CPU phase
+        cfg = {}
+        for name in ("tiny_1k", "llama_16k", "llama_32k_sweep"):
+            orc = oracle_cfg.get(name)
+            cfg[name] = config_rows(name, dev, args.steps, args.warmup, orc,
+                                    orc["slice"] if orc else 0)
+        oracle_cfg.clear()
+        extras["configs"] = cfg
         sweeps = {}
-        del w
-        torch.cuda.empty_cache()
-        w32 = Workload("llama_32k_sweep", dev)
-        d32 = run_gate(w32, "dense", args.steps, args.warmup)
-        rows = {"dense": {"ms": round(d32["ms"], 3), "tflops": round(d32["tflops"], 2)}}
-        for sl, kk in enumerate(w32.table.budgets):
-            r = run_gate(w32, "absolute", args.steps, args.warmup, budget_slice=sl)
-            rows[f"k={kk}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
-                               "pct_mfma_peak": round(r["pct_peak"], 2),
-                               "speedup_vs_dense": round(d32["ms"] / r["ms"], 4),
-                               "kept_fraction": round(r["kept_fraction"], 4),
-                               "predicted_density": round(predicted_density(32768, 128, kk), 4)}
-        sweeps["llama_32k_sweep"] = rows
-        del w32
-        torch.cuda.empty_cache()
         wb = Workload("llama_32k_bk128", dev)
+        d32 = cfg["llama_32k_sweep"]["dense"]["ms"]
         rows = {}
         for sl, kk in enumerate(wb.table.budgets):
             r = run_gate(wb, "absolute", args.steps, args.warmup, budget_slice=sl)
-            rows[f"k={kk}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
-                               "pct_mfma_peak": round(r["pct_peak"], 2),
-                               "speedup_vs_dense": round(d32["ms"] / r["ms"], 4),
-                               "kept_fraction": round(r["kept_fraction"], 4),
-                               "predicted_density": round(predicted_density(32768, 128, kk, 128),
-                                                          4)}
+            rows[f"k={kk}"] = gate_row(r, d32, wb.N, wb.Bq, kk, 128)
         sweeps["llama_32k_bk128"] = rows
         del wb
         torch.cuda.empty_cache()
@@ -617,30 +807,19 @@ def main():
         for lam in (0.0, 1e-4, 1e-3, 1e-2):
             ll = math.log(lam) if lam > 0 else -math.inf
             r = run_gate(w64, "relative", args.steps, args.warmup, log_lambda=ll)
-            rows[f"lambda={lam:g}"] = {"ms": round(r["ms"], 3), "tflops": round(r["tflops"], 2),
-                                       "pct_mfma_peak": round(r["pct_peak"], 2),
-                                       "speedup_vs_dense": round(d64["ms"] / r["ms"], 4),
-                                       "kept_fraction": round(r["kept_fraction"], 4)}
+            rows[f"lambda={lam:g}"] = gate_row(r, d64["ms"], w64.N, w64.Bq)
         sweeps["llama_64k_relative"] = rows
-        extras["sweeps"] = sweeps
         del w64
         torch.cuda.empty_cache()
-        w = Workload(args.workload, dev)
+        sweeps["llama_64k_dial"] = dialled_rows(dev, args.steps, args.warmup)
+        extras["sweeps"] = sweeps
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, mode, k=k, **gate_kw)
-
-    c = w.c
     line = {
         "metric": METRIC, "value": round(gated["tflops"], 3), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(gated["wall_ms"], 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": args.workload, "batch": 1, "seq_len": w.N,
-                   "heads_q": c["heads_q"], "heads_kv": c["heads_kv"], "head_dim": w.d,
-                   "tile": f"{w.Bq}x64", "gate": mode,
-                   "budget_k": k, "calibrated_len": c["calib_n"] if k else None},
+        "config": line_cfg,
         "roofline": {"bound": "mfma", "achieved": round(dom["flops"] / dom["ms"] / 1e9, 2),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(dom["flops"] / dom["ms"] / 1e9 / PEAK_BF16_TFLOPS, 4),
