@@ -193,6 +193,32 @@ __device__ __forceinline__ void copy_offsets(unsigned* off, long long gst, int w
 // just been written by v_readfirstlane, and a memory instruction reading an SGPR written by a
 // vector instruction needs 5 wait states; the asm supplies them itself (the compiler cannot
 // see the read): two moves plus s_nop 2.
+// 32-bit LDS byte address of a __shared__ object (the cast checks for null, so it is done once
+// per buffer, outside the loops).
+__device__ __forceinline__ unsigned lds_addr(const void* lds) {
+  typedef __attribute__((address_space(3))) const char lds_char;
+  return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)lds);
+}
+
+// dma16 with the LDS destination as a 32-bit LDS byte address (wave-uniform).
+__device__ __forceinline__ void dma16_at(const void* gbase, unsigned voff, unsigned lds) {
+  const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
+  const unsigned glo = __builtin_amdgcn_readfirstlane((unsigned)g);
+  const unsigned ghi = __builtin_amdgcn_readfirstlane((unsigned)(g >> 32));
+  const unsigned long long gs = ((unsigned long long)ghi << 32) | glo;
+  const unsigned m0 = __builtin_amdgcn_readfirstlane(lds);
+  unsigned saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 2\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(gs), "s"(m0)
+      : "memory");
+}
+
 __device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
   typedef __attribute__((address_space(3))) const char lds_char;
   const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
@@ -229,6 +255,17 @@ __device__ __forceinline__ void copy_round(int m, const unsigned* off, const __b
     }
     dma16(gbase, o, tile + k * 512);
   }
+}
+
+// Round m of the copy of a whole 64-row tile (valid = 64) into the LDS buffer at byte address
+// lds: no ragged-row handling, the destination a precomputed LDS address (the steady state of
+// the softmax loop; a ragged tile goes through copy_round).
+template <int D, int STRIDE, int NW>
+__device__ __forceinline__ void copy_round_full(int m, const unsigned* off, const __bf16* gbase,
+                                                unsigned lds, int w) {
+  constexpr int CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
+  const int k = w + NW * m;
+  if (m + 1 < M || k < CPS) dma16_at(gbase, off[m], lds + k * 1024u);
 }
 
 // Copy one 64-row tile starting at gbase (all rounds).
@@ -781,6 +818,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   bool keep_prev = false;
   bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of the previous tile reads pb[P ^ 1]
+  const unsigned lK0 = lds_addr(sK0), lK1 = lds_addr(sK1);
+  const unsigned lV0 = lds_addr(sV0), lV1 = lds_addr(sV1);
   const int kfo = (lane & 31) * STR + 8 * (lane >> 5);
   constexpr int NSTEP = 4 * MD;               // PV MFMA steps
   // PV steps issued before the decision on tile t: all of them in the voting kernels; dense
@@ -821,11 +860,17 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     const bool kload = t2 < n_end;
     const __bf16* const kg = Kb + tile_offset<PAGED>(a, b, min(t2, n_end - 1), kst, a.ks[0]);
     const __bf16* const vg = Vb + tile_offset<PAGED>(a, b, t, vst, a.vs[0]);
-    auto copy_k = [&](int r) {
-      copy_round<D, STR, NW>(r, koff, kg, krow, key_valid(t2), P ? sK1 : sK0, w, lane);
-    };
+    // Whole tiles are copied by lean rounds interleaved with the MFMAs; a ragged tile (the
+    // last key tile of a sequence whose length is not a multiple of 64) in one piece after the
+    // phase that would have carried it, with its rows past the end redirected (copy_tile).
+    const bool kfast = kload && key_valid(t2) == BK;
+    const bool vfast = key_valid(t) == BK;
+    auto copy_k = [&](int r) { copy_round_full<D, STR, NW>(r, koff, kg, P ? lK1 : lK0, w); };
     auto copy_v = [&](int r) {
-      copy_round<D, STRV, NW>(r, voff, vg, vrow, key_valid(t), P ? sV1 : sV0, w, lane);
+      if (vfast) copy_round_full<D, STRV, NW>(r, voff, vg, P ? lV1 : lV0, w);
+    };
+    auto copy_v_ragged = [&]() {
+      if (!vfast) copy_tile<D, STRV, NW>(voff, vg, vrow, key_valid(t), P ? sV1 : sV0, w, lane);
     };
     const __bf16* const sv = P ? sV0 : sV1;     // V of the previous tile
     bf16x8 vb[3];
@@ -894,6 +939,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
       else
         pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kAlways>(
             false, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+      copy_v_ragged();
     }
     // the previous P is dead from here on (the next write of its buffer precedes the next read)
 #pragma unroll
@@ -918,7 +964,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     constexpr int NPV = kVote ? 0 : kPairsPV;
     constexpr int VQ = kVote ? kFlag : kNever;
     if (!kVote || mykeep) {
-      if (kload)
+      if (kfast)
         qk_phase<D, MKR, kAlways, kAlways, NPV, MVR, VQ>(true, true, kb, qf, sb[P ^ 1], sb[P], off,
                                                          c, pb[P], sum, mx, copy_k, anyv, copy_v);
       else
@@ -926,7 +972,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
                                                         off, c, pb[P], sum, mx, copy_k, anyv,
                                                         copy_v);
     } else {
-      if (kload)
+      if (kfast)
         qk_phase<D, MKR, kNever, kAlways, NPV, MVR, VQ>(false, true, kb, qf, sb[P ^ 1], sb[P],
                                                         off, c, pb[P], sum, mx, copy_k, anyv,
                                                         copy_v);
@@ -934,6 +980,10 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
         qk_phase<D, MKR, kNever, kNever, NPV, MVR, VQ>(false, false, kb, qf, sb[P ^ 1], sb[P],
                                                        off, c, pb[P], sum, mx, copy_k, anyv,
                                                        copy_v);
+    }
+    if (kload && !kfast) load_k(t2, P ? sK1 : sK0);
+    if constexpr (kVote) {
+      if (anyv) copy_v_ragged();
     }
     if (mykeep) st.l += sum;
     if (tile_masked(t1)) {
