@@ -21,10 +21,13 @@
 //   * O^T = V^T P^T: P^T is the MFMA B operand straight from the softmax registers; V^T is read
 //     from the natural [key][d] V tile with transposing LDS reads, in the key order in which
 //     the S^T accumulator (and so P^T) holds them.
-//   * A workgroup holds the 32-row waves of one or more query heads of one KV group for one
-//     query block (2 heads x 128 rows = 8 waves for the 128x64 tile under GQA): each K/V tile
-//     is staged in LDS once, by direct global->LDS loads, and read by every wave; K and V are
-//     double-buffered.
+//   * A workgroup holds the 32-row waves of the query rows of one query block that share a KV
+//     head: one head x 128 rows (4 waves) for the 128x64 tile, two heads x 64 rows for the
+//     64x64 tile. Each K/V tile is staged in LDS once per workgroup, by direct global->LDS
+//     loads, and read by every wave; K and V are double-buffered. (A whole KV group of four
+//     heads x 128 rows does not fit one CU at two waves per SIMD: 16 waves of ~230 VGPRs, or Q
+//     of 128 KB in LDS beside the K/V buffers. The gate sweep, which holds no softmax state,
+//     takes two heads per workgroup; its FP8 form four.)
 //   * QK of tile t+1 is issued after the softmax of tile t, so the gate statistics of tile t+1
 //     reach LDS before the one barrier of the iteration; V_t is fetched only when some head of
 //     the workgroup keeps tile t.
@@ -830,13 +833,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 
   // One iteration over sequence position u (P = u & 1 picks the LDS, P and score buffers) with
   // tile t and the next two tiles t1, t2 of the sequence:
-  //   PV phase: the PV product of the previous tile (if kept); for the relative gate, next to
-  //     its first MFMAs the per-row statistics of tile t are read and put to the vote (keep iff
-  //     some row's statistic reaches ln(lambda)); then the V_t copy (if some head of the
-  //     workgroup keeps t) and half of tile t's exponentials run next to the MFMAs;
-  //   QK phase: scores of tile t1 with the K_{t2} copy, the other half of the exponentials and
-  //     the first half of t1's row max next to the MFMAs; then t1's statistics are published
-  //     and the one barrier makes them and both copies visible.
+  //   PV phase: the PV product of the previous tile (if kept). Dense and the mask walk run the
+  //     V_t copy and half of tile t's exponentials next to its MFMAs. The voting kernels (the
+  //     relative gate, the absolute gate decided in the loop) read the per-row statistics of
+  //     tile t meanwhile and vote after the phase (keep iff some row's statistic reaches the
+  //     threshold);
+  //   QK phase: scores of tile t1 with the K_{t2} copy, the rest of tile t's exponentials (in
+  //     the voting kernels all of them, none if t is skipped, and the V_t copy if some head of
+  //     the workgroup keeps t) and the first half of t1's row max next to the MFMAs; then t1's
+  //     statistics are published and the one barrier makes them and both copies visible.
   // The last iteration computes scores of a tile past the end from stale LDS and discards them,
   // which keeps the loop body free of branches around the MFMAs.
   auto body = [&](auto par) {
