@@ -170,14 +170,15 @@ bsfa::PrefillArgs base_args(const bsfa_problem* p, const void* Q, const void* K,
 
 // The absolute gate's workspace: the keep bitmasks (one bit per 64-key tile; a gate block of
 // 128 keys sets two); then, every part on a 256-byte boundary, for an FP8 gate the E4M3 copies
-// of Q and K and their scales, and for mean correction the block means of K (bf16 high and
-// low parts) and of V, [B][Hkv][mean_blocks][d] each.
+// of Q and K and their scales, for mean correction the block means of K (bf16 high and low
+// parts) and of V, [B][Hkv][mean_blocks][d] each, and last the walk's ticket counter.
 struct WorkspaceLayout {
   uint64_t mask_bytes;
   int q8_rows, k8_rows, k8_tiles;
   uint64_t q8, q8_scale, k8, k8_scale, fp8_end;   // byte offsets
   int mean_blocks;
   uint64_t kbar_hi, kbar_lo, vbar, means_end;     // byte offsets
+  uint64_t ticket, total;                         // byte offset of the counter; the whole size
 };
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
@@ -203,6 +204,8 @@ WorkspaceLayout workspace_layout(const bsfa_problem* p) {
   l.kbar_lo = l.kbar_hi + align256(part);
   l.vbar = l.kbar_lo + align256(part);
   l.means_end = l.vbar + align256(part);
+  l.ticket = align256(p->mean_correction ? l.means_end : fp8 ? l.fp8_end : l.mask_bytes);
+  l.total = l.ticket + 256u;
   return l;
 }
 
@@ -249,15 +252,13 @@ const char* bsfa_status_string(int32_t s) {
 
 const char* bsfa_last_error(void) { return g_last_error; }
 
-int32_t bsfa_version(void) { return (3 << 16) | 1; }
+int32_t bsfa_version(void) { return (3 << 16) | 2; }
 
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) {
   if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
       p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
     return 0;
-  const WorkspaceLayout l = workspace_layout(p);
-  return p->mean_correction ? l.means_end
-         : p->gate_dtype == BSFA_FP8_E4M3 ? l.fp8_end : l.mask_bytes;
+  return workspace_layout(p).total;
 }
 
 }  // extern "C"
@@ -418,8 +419,13 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     hipError_t e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
     // the walk over kept tiles: one KV head at a time on all XCDs (its K/V stays in the
-    // last-level cache, and walks whose lengths differ between heads spread over every XCD)
+    // last-level cache), units in the order the workgroups start (walk lengths differ, so a
+    // fixed assignment would load some XCDs more than others)
     a.xcd_map = -1;
+    a.ticket = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                           workspace_layout(p).ticket);
+    e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(a.ticket), st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -659,6 +659,10 @@ constexpr int kRows = kRowsPerWave;
 
 constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
+// Prefill kernels that take their units from a ticket counter when given one (the mask walk).
+template <int GATE, bool MEAN>
+constexpr bool kResidentLoop = GATE == kAbsolute && !MEAN;
+
 // PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
 // kernels carry no page lookups). MEAN (absolute walk only): the pruned gate blocks' stand-ins
 // join the softmax after the walk (mean correction).
@@ -687,18 +691,40 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) float sGate[2][NW * kRows];   // per-row gate statistics
   __shared__ unsigned long long sMask[kAbs ? kMaskWords : 1];           // kept off-diagonal tiles
   __shared__ int sKept;
+  __shared__ int sUnit;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
+  // Workgroup L runs unit L, except in the mask walk: its launch holds as many workgroups as
+  // stay resident, and each takes units in turn from a ticket counter (zero at the launch)
+  // until none is left. Workgroups go to the XCDs in turn whatever their work, and a new one
+  // waits for a slot on its own XCD; as walk lengths vary, slots would sit idle on the other
+  // XCDs meanwhile. Resident workgroups that take the next unit as they finish one keep every
+  // slot busy until the work runs out. (In the other kernels the work per unit is even.)
+  constexpr bool kLoop = kResidentLoop<GATE, MEAN>;
+  int L = blockIdx.x;
+next_unit:
+  if constexpr (kLoop) {
+    if (tid == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
+    __syncthreads();
+    L = __builtin_amdgcn_readfirstlane(sUnit);
+    if (L >= a.units * a.nqb) return;   // uniform: every unit taken
+  }
+  const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
   // N query rows at absolute positions pre .. pre + N - 1 against Nk = pre + N keys (a chunk
   // after a prefix of cached keys; pre = 0 for a whole prefill)
   const Seq sq = seq_of(a, b);
-  if (i * BQ >= sq.N) return;   // uniform: past this sequence's query blocks (variable length)
+  if (i * BQ >= sq.N) {          // uniform: past this sequence's query blocks (variable length)
+    if constexpr (kLoop) {
+      __syncthreads();             // every wave has read sUnit
+      goto next_unit;
+    }
+    return;
+  }
   const int N = sq.N, Nk = sq.Nk, pre = sq.pre;
   const int row0 = i * BQ + rw * kRows;
   const int row = row0 + (lane & 31);
@@ -1153,7 +1179,12 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     if (a.kept_counts) a.kept_counts[((long long)b * a.Hq + h) * a.nqb + i] = kept;
     if (a.kept_total) atomicAdd(a.kept_total, (unsigned long long)kept);
   }
+  if constexpr (kLoop) {
+    __syncthreads();   // every wave is done with this unit's LDS (and has read sUnit)
+    goto next_unit;
+  }
 }
+
 
 // ---------------------------------------------------------------------------------------------
 // Gate sweep (absolute gate; launched before the prefill kernel): for every (b, h, i) the
@@ -1826,33 +1857,34 @@ __global__ __launch_bounds__(256) void block_mean_kernel(PrefillArgs a) {
 
 template <int D, int BQ, int NW, bool PAGED>
 hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
-  const dim3 grid(a.units * a.nqb), block(NW * 64);
+  const int units = a.units * a.nqb;
+  // one workgroup per unit; with a ticket counter, as many as stay resident at once (each
+  // takes units in turn)
+  auto go = [&](void (*kernel)(PrefillArgs), bool resident_loop) {
+    if (resident_loop && !a.ticket) return hipErrorInvalidValue;   // the mask walk needs one
+    const int n = resident_loop ? min(units, resident_workgroups(reinterpret_cast<const void*>(
+                                                                     kernel), NW * 64, units))
+                                : units;
+    hipLaunchKernelGGL(kernel, dim3(n), dim3(NW * 64), 0, stream, a);
+    return hipGetLastError();
+  };
   switch (gate) {
     case kDense:
-      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kDense, PAGED>), grid, block, 0, stream, a);
-      break;
+      return go(prefill_kernel<D, BQ, NW, kDense, PAGED>, kResidentLoop<kDense, false>);
     case kAbsolute:
     case kAbsVote:
       if constexpr (NW == BQ / kRows) {   // one head per workgroup
         if (gate == kAbsolute && a.kbar_hi)
-          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute, PAGED, true>), grid, block, 0,
-                             stream, a);
-        else if (gate == kAbsolute)
-          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsolute, PAGED>), grid, block, 0,
-                             stream, a);
-        else
-          hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kAbsVote, PAGED>), grid, block, 0,
-                             stream, a);
-      } else {
-        return hipErrorInvalidConfiguration;
+          return go(prefill_kernel<D, BQ, NW, kAbsolute, PAGED, true>,
+                    kResidentLoop<kAbsolute, true>);
+        if (gate == kAbsolute)
+          return go(prefill_kernel<D, BQ, NW, kAbsolute, PAGED>, kResidentLoop<kAbsolute, false>);
+        return go(prefill_kernel<D, BQ, NW, kAbsVote, PAGED>, kResidentLoop<kAbsVote, false>);
       }
-      break;
+      return hipErrorInvalidConfiguration;
     default:
-      hipLaunchKernelGGL((prefill_kernel<D, BQ, NW, kRelative, PAGED>), grid, block, 0, stream,
-                         a);
-      break;
+      return go(prefill_kernel<D, BQ, NW, kRelative, PAGED>, kResidentLoop<kRelative, false>);
   }
-  return hipGetLastError();
 }
 
 template <int D, int BQ, int NW>

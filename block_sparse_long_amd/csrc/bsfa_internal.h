@@ -41,6 +41,9 @@ struct PrefillArgs {
                                    // -1: KV-head-major order over all XCDs
   int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
                                    // blocks (0: never)
+  unsigned* ticket;                // prefill kernel: a counter, zero at the launch, from which
+                                   // the workgroups resident at once take units in turn until
+                                   // all are taken; nullptr: one workgroup per unit
   float scale;                     // softmax scale applied to fp32 scores
   float c_log2;                    // scale * log2(e)
   float log_lambda;                // RELATIVE threshold
@@ -101,8 +104,10 @@ int waves_per_workgroup(int block_q, int group);
 // workgroup (its keep decisions are made per head before the softmax pass).
 int prefill_waves_per_workgroup(int block_q, int group, int gate);
 
-// Workgroups of the prefill kernel resident on the whole chip at once (256 CUs, two each).
-constexpr int kResidentWorkgroups = 512;
+// Workgroups of `kernel` (block threads, static LDS only) that the current device holds at
+// once: its CUs times the workgroups per CU that the kernel's registers and LDS allow. Cached
+// per (device, kernel); `fallback` if the runtime cannot tell.
+int resident_workgroups(const void* kernel, int block, int fallback);
 
 // Largest number of off-diagonal key tiles per query block under the absolute gate (the
 // keep bitmask lives in LDS): 32768 tiles of 64 keys.

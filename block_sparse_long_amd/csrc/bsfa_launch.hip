@@ -2,6 +2,10 @@
 // for the head dimension, query tile, workgroup width, gate and K/V layout.
 #include "bsfa_internal.h"
 
+#include <mutex>
+#include <utility>
+#include <vector>
+
 namespace bsfa {
 namespace {
 
@@ -85,6 +89,29 @@ hipError_t launch_quantize_qk(const PrefillArgs& a, int head_dim, hipStream_t st
                            : launch_quant_tile<64, true>(a, stream);
   return head_dim == 128 ? launch_quant_tile<128, false>(a, stream)
                          : launch_quant_tile<64, false>(a, stream);
+}
+
+int resident_workgroups(const void* kernel, int block, int fallback) {
+  static std::mutex mu;
+  static std::vector<std::pair<std::pair<int, const void*>, int>> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fallback;
+  const std::pair<int, const void*> key(dev, kernel);
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const auto& e : cache)
+      if (e.first == key) return e.second;
+  }
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+      cus < 1 || per_cu < 1) {
+    (void)hipGetLastError();
+    return fallback;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  cache.emplace_back(key, cus * per_cu);
+  return cus * per_cu;
 }
 
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {

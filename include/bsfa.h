@@ -152,7 +152,8 @@ typedef struct {
  * 256-byte boundary: with gate_dtype FP8_E4M3 the E4M3 copies of Q [B][N][Hq][d] and K
  * [B][Nk][Hkv][d] (one byte per element) and their fp32 scales [B][Hq][N] and
  * [B][Hkv][ceil(Nk/64)]; with mean_correction three bf16 arrays [B][Hkv][floor(Nk/Bk)][d]: the
- * block means of K in two parts (high and low bf16) and of V. */
+ * block means of K in two parts (high and low bf16) and of V; last, 256 bytes for a counter
+ * from which the workgroups of the softmax launch take their (b, h, i) units in turn. */
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
 
 /* Gated causal prefill attention (the method's hot path).
@@ -329,8 +330,8 @@ bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const 
 bsfa_status bsfa_mfma_rate_probe(int32_t workgroups, int32_t iters, float* sink, void* stream);
 
 /* Bytes of workspace bsfa_calibrate_blockmax needs for `p` (0 for bf16 scores): with
- * gate_dtype FP8_E4M3, the layout of bsfa_prefill_workspace_bytes(p, ABSOLUTE) without the
- * block means, then (on a 256-byte boundary) fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] block
+ * gate_dtype FP8_E4M3, the masks and FP8 copies of bsfa_prefill_workspace_bytes(p, ABSOLUTE)
+ * (without block means and counter), then (on a 256-byte boundary) fp32 [B][Hq][ceil(N/Bq)][ceil(N/Bk)] block
  * maxima. */
 uint64_t bsfa_calibrate_workspace_bytes(const bsfa_problem* p);
 
@@ -340,8 +341,9 @@ const char* bsfa_status_string(int32_t status);
 /* Detail of the last non-OK status returned on the calling thread ("" if none). */
 const char* bsfa_last_error(void);
 
-/* ABI version: (major << 16) | minor. Minor 1 adds bsfa_prefill_noalloc. Major 3: bsfa_table
- * ends with the budgets array
+/* ABI version: (major << 16) | minor. Minor 1 adds bsfa_prefill_noalloc; minor 2 ends the
+ * absolute gate's workspace with a ticket counter (256 bytes more). Major 3: bsfa_table ends
+ * with the budgets array
  * (major 2: bsfa_problem ends with mean_correction and gate_dtype, and
  * bsfa_calibrate_blockmax takes a workspace). */
 int32_t bsfa_version(void);

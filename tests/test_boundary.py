@@ -153,7 +153,9 @@ def test_workspace_size_and_validation():
     p = problem()
     N, bq, bk = p.seqlen, p.block_q, p.block_k
     words = -(-(-(-N // bk)) // 64)
-    need = p.batch * p.heads_q * (-(-N // bq)) * words * 8
+    masks = p.batch * p.heads_q * (-(-N // bq)) * words * 8
+    # the masks, then (on a 256-byte boundary) the walk's 256-byte ticket counter
+    need = -(-masks // 256) * 256 + 256
     assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == need
     for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
         assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
@@ -161,7 +163,7 @@ def test_workspace_size_and_validation():
     # 65 key tiles need two mask words per query block
     p2 = problem(N=65 * 64)
     assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p2), _lib.BSFA_GATE_ABSOLUTE) == \
-        p2.batch * p2.heads_q * (-(-p2.seqlen // p2.block_q)) * 2 * 8
+        -(-(p2.batch * p2.heads_q * (-(-p2.seqlen // p2.block_q)) * 2 * 8) // 256) * 256 + 256
     abs_call = dict(tbl=table(t_len=-(-N // bq)), mode=_lib.BSFA_GATE_ABSOLUTE)
     assert call_prefill(p, ws=FAKE + 4, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_ALIGN
     assert call_prefill(p, ws=FAKE, ws_bytes=need - 8, **abs_call) == _lib.BSFA_ERR_ARG
@@ -176,8 +178,8 @@ def call_masks(p, tbl, slice_=0, q=FAKE, k=FAKE, mask=FAKE, mask_bytes=1 << 20, 
 
 def test_gate_masks_validation():
     p = problem()
-    need = _lib.load_library().bsfa_prefill_workspace_bytes(ctypes.byref(p),
-                                                            _lib.BSFA_GATE_ABSOLUTE)
+    # the masks alone: B * Hq * nqb * words * 8 bytes
+    need = p.batch * p.heads_q * (-(-p.seqlen // p.block_q)) * (-(-(-(-p.seqlen // 64)) // 64)) * 8
     assert call_masks(p, None) == _lib.BSFA_ERR_TABLE
     assert call_masks(p, table(bq=64)) == _lib.BSFA_ERR_TABLE
     assert call_masks(p, table(), slice_=2) == _lib.BSFA_ERR_TABLE
@@ -214,7 +216,7 @@ def test_kv_seqlen_validation():
     p.kv_seqlen = 65 * 64
     p.seqlen = 128
     assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == \
-        p.batch * p.heads_q * 1 * 2 * 8
+        -(-(p.batch * p.heads_q * 1 * 2 * 8) // 256) * 256 + 256
 
 
 def test_varlen_validation():
@@ -317,13 +319,16 @@ def test_stored_tables_load(golden_dir):
 def test_mean_correction_workspace_and_validation():
     lib = _lib.load_library()
     p = problem(N=1000)
-    masks = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
+    r256 = lambda x: -(-x // 256) * 256
+    masks = p.batch * p.heads_q * (-(-1000 // p.block_q)) * 1 * 8
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == \
+        r256(masks) + 256
     p.mean_correction = 1
     need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
-    # masks, then three [B][Hkv][floor(Nk / Bk)][d] bf16 arrays, each on a 256-byte boundary
+    # masks, then three [B][Hkv][floor(Nk / Bk)][d] bf16 arrays and the ticket counter, each
+    # on a 256-byte boundary
     part = p.batch * p.heads_kv * (1000 // 64) * p.head_dim * 2
-    r256 = lambda x: -(-x // 256) * 256
-    assert need == r256(masks) + 3 * r256(part)
+    assert need == r256(masks) + 3 * r256(part) + 256
     for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
         assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
     abs_call = dict(tbl=table(t_len=8), mode=_lib.BSFA_GATE_ABSOLUTE)
@@ -347,13 +352,14 @@ def test_mean_correction_workspace_and_validation():
 def test_fp8_gate_workspace_and_validation():
     lib = _lib.load_library()
     p = problem(N=1000)
-    masks = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
-    p.gate_dtype = _lib.BSFA_FP8_E4M3
-    need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
     r256 = lambda x: -(-x // 256) * 256
     B, N, Hq, Hkv, d = p.batch, 1000, p.heads_q, p.heads_kv, p.head_dim
+    masks = B * Hq * (-(-N // p.block_q)) * 1 * 8
+    p.gate_dtype = _lib.BSFA_FP8_E4M3
+    need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
     parts = [B * N * Hq * d, B * Hq * N * 4, B * N * Hkv * d, B * Hkv * (-(-N // 64)) * 4]
-    assert need == r256(masks) + sum(r256(x) for x in parts)
+    copies = r256(masks) + sum(r256(x) for x in parts)     # what bsfa_gate_masks writes
+    assert need == copies + 256                              # then the ticket counter
     # with mean correction the block means follow the FP8 copies
     p.mean_correction = 1
     both = lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE)
@@ -372,13 +378,13 @@ def test_fp8_gate_workspace_and_validation():
     assert call_prefill(p, ws=FAKE, ws_bytes=need, **abs_call) == _lib.BSFA_ERR_DTYPE
     # the gate masks need the masks and the FP8 copies, 16-byte aligned
     p.gate_dtype = _lib.BSFA_FP8_E4M3
-    assert call_masks(p, table(t_len=8), mask_bytes=need - 8) == _lib.BSFA_ERR_ARG
-    assert f"required {need}" in _lib.bsfa_last_error()
+    assert call_masks(p, table(t_len=8), mask_bytes=copies - 8) == _lib.BSFA_ERR_ARG
+    assert f"required {copies}" in _lib.bsfa_last_error()
     assert call_masks(p, table(t_len=8), mask=FAKE + 8, mask_bytes=need) == _lib.BSFA_ERR_ALIGN
     # FP8 calibration: the FP8 copies and the block maxima live in a workspace
     cw = lib.bsfa_calibrate_workspace_bytes(ctypes.byref(p))
     nqb, nkb = -(-N // p.block_q), -(-N // p.block_k)
-    assert cw == r256(need) + B * Hq * nqb * nkb * 4
+    assert cw == copies + B * Hq * nqb * nkb * 4
     assert call_calib(p, [1]) == _lib.BSFA_ERR_ARG
     assert call_calib(p, [1], ws=FAKE, ws_bytes=cw - 4) == _lib.BSFA_ERR_ARG
     assert call_calib(p, [1], ws=FAKE + 8, ws_bytes=cw) == _lib.BSFA_ERR_ALIGN
@@ -453,7 +459,7 @@ def test_noalloc_validates_and_refuses_calls_beyond_its_scratch():
     # 512K tokens x 32 heads: 4096 query blocks x 128 mask words x 8 B = 128 MiB of masks
     big = problem(N=1 << 19, Hq=32, Hkv=8)
     need = lib.bsfa_prefill_workspace_bytes(ctypes.byref(big), _lib.BSFA_GATE_ABSOLUTE)
-    assert need == 32 * 4096 * 128 * 8
+    assert need == 32 * 4096 * 128 * 8 + 256
     assert call(big, tbl=table(Hq=32, t_len=4096), mode=_lib.BSFA_GATE_ABSOLUTE) == \
         _lib.BSFA_ERR_UNSUPPORTED
     assert "static scratch" in _lib.bsfa_last_error()

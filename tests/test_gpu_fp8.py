@@ -45,7 +45,8 @@ def _r256(x):
 @pytest.mark.parametrize("B,N,Hq,Hkv,d", [(1, 1000, 8, 2, 128), (2, 333, 4, 2, 64)])
 def test_fp8_copies_match_the_oracle_bitwise(B, N, Hq, Hkv, d):
     # the workspace of an FP8 gate: masks, then q8 [B][N][Hq][d], its scales [B][Hq][N],
-    # k8 [B][N][Hkv][d], its scales [B][Hkv][ceil(N / 64)], each on a 256-byte boundary
+    # k8 [B][N][Hkv][d], its scales [B][Hkv][ceil(N / 64)] and a ticket counter, each on a
+    # 256-byte boundary
     Bq = 128 if d == 128 else 64
     Q, K, _ = _inputs(50, N, Hq, Hkv, d, B)
     (Qd, Kd), (Qh, Kh) = bf16_pair(Q, K)
@@ -62,7 +63,7 @@ def test_fp8_copies_match_the_oracle_bitwise(B, N, Hq, Hkv, d):
     for size in (B * N * Hq * d, B * Hq * N * 4, B * N * Hkv * d, B * Hkv * nt * 4):
         parts.append(w[off:off + size])
         off += _r256(size)
-    assert off == nbytes
+    assert off + 256 == nbytes     # then the walk's 256-byte ticket counter
     dec = lambda u8: torch.from_numpy(u8.copy()).view(torch.float8_e4m3fn).float().numpy()
     q8, qs = oracle.quantize_q_rows(Qh)
     k8, ks = oracle.quantize_k_tiles(Kh)
