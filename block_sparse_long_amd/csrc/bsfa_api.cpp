@@ -223,11 +223,15 @@ hipError_t set_fp8(bsfa::PrefillArgs& a, const bsfa_problem* p, void* workspace,
   return bsfa::launch_quantize_qk(a, p->head_dim, st);
 }
 
-// The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i).
+// The gate sweep launch over `a` (keep_mask set): one workgroup per (b, head pair, i), or with
+// a ticket counter (bf16 scores only) the resident workgroups taking those units in turn.
 hipError_t launch_sweep(bsfa::PrefillArgs sw, const bsfa_problem* p, hipStream_t st) {
   const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G, sw.q8 != nullptr);
   sw.units = p->batch * p->heads_kv * (sw.G / shpw);
-  sw.xcd_map = (sw.units % 8) == 0;
+  if (sw.q8) sw.ticket = nullptr;
+  // with a ticket: one KV head at a time on every XCD (its K stream shared through each L2);
+  // without: each XCD serves fixed KV heads
+  sw.xcd_map = sw.ticket ? -1 : (sw.units % 8) == 0;
   sw.xcd_rot = 0;
   return bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
 }
@@ -416,16 +420,19 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
           return fail(BSFA_ERR_HIP, "block means launch: %s", hipGetErrorString(e));
       }
     }
-    hipError_t e = launch_sweep(a, p, st);
+    // two ticket counters, one for the sweep and one for the walk, zeroed together
+    unsigned* const tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
+                                                          workspace_layout(p).ticket);
+    hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(tickets), st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the tickets: %s", hipGetErrorString(e));
+    a.ticket = tickets;
+    e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
     // the walk over kept tiles: one KV head at a time on all XCDs (its K/V stays in the
     // last-level cache), units in the order the workgroups start (walk lengths differ, so a
     // fixed assignment would load some XCDs more than others)
     a.xcd_map = -1;
-    a.ticket = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
-                                           workspace_layout(p).ticket);
-    e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(a.ticket), st);
-    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
+    a.ticket = tickets + 1;
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));

@@ -1264,10 +1264,14 @@ void gate_sweep_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 sKc[64 * STR];
   __shared__ float sStage[2][NW];
 
+  __shared__ int sUnit;
+
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(blockIdx.x, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
+  // one unit (b, KV head, head pair, query block) at place L of the unit order
+  auto run_unit = [&](const int L) {
+  const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
@@ -1370,6 +1374,23 @@ void gate_sweep_kernel(PrefillArgs a) {
   }
   combine(n_off - 1);
   zero_tail();
+  };
+
+  // Workgroup L runs unit L; with a ticket counter (zero at the launch) the launch holds the
+  // workgroups resident at once and each takes units in turn until none is left, so that the
+  // XCDs, whose speeds differ by a few per cent under this load, share the work as they go.
+  if (a.ticket) {
+    for (;;) {
+      if (tid == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
+      __syncthreads();
+      const int L = __builtin_amdgcn_readfirstlane(sUnit);
+      if (L >= a.units * a.nqb) break;   // uniform: every unit taken
+      run_unit(L);
+      __syncthreads();   // every wave is done with this unit's LDS (and has read sUnit)
+    }
+  } else {
+    run_unit(blockIdx.x);
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -1906,20 +1927,21 @@ hipError_t launch_calib_nw(const CalibArgs& a, int nw, hipStream_t stream) {
 template <int D, int BQ>
 hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
   constexpr int WPH = BQ / 64;
-  const dim3 grid(a.units * a.nqb);
+  const int units = a.units * a.nqb;
+  // one workgroup per unit; with a ticket counter, as many as stay resident at once
+  auto go = [&](void (*kernel)(PrefillArgs), int block) {
+    const int n = a.ticket ? min(units, resident_workgroups(reinterpret_cast<const void*>(kernel),
+                                                            block, units))
+                           : units;
+    hipLaunchKernelGGL(kernel, dim3(n), dim3(block), 0, stream, a);
+    return hipGetLastError();
+  };
   const bool paged = a.pages != nullptr;
-  if (hpw == 2) {
-    if (paged)
-      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2, true>), grid, dim3(WPH * 128), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 2, false>), grid, dim3(WPH * 128), 0, stream, a);
-  } else {
-    if (paged)
-      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1, true>), grid, dim3(WPH * 64), 0, stream, a);
-    else
-      hipLaunchKernelGGL((gate_sweep_kernel<D, BQ, 1, false>), grid, dim3(WPH * 64), 0, stream, a);
-  }
-  return hipGetLastError();
+  if (hpw == 2)
+    return paged ? go(gate_sweep_kernel<D, BQ, 2, true>, WPH * 128)
+                 : go(gate_sweep_kernel<D, BQ, 2, false>, WPH * 128);
+  return paged ? go(gate_sweep_kernel<D, BQ, 1, true>, WPH * 64)
+               : go(gate_sweep_kernel<D, BQ, 1, false>, WPH * 64);
 }
 
 }  // namespace
