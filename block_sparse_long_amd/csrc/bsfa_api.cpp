@@ -396,6 +396,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   const int hpw = nw / (p->block_q / bsfa::kRowsPerWave);
   a.units = p->batch * p->heads_kv * (a.G / hpw);
   a.xcd_map = (a.units % 8) == 0;
+  // the absolute gate decided in the loop: kept counts differ between heads (each has its own
+  // thresholds), so the KV-head-to-XCD assignment turns every 16 query blocks (about as many
+  // as are resident at once: 512 workgroups over 32 units at Bq = 128)
+  if (kgate == bsfa::kAbsVote) a.xcd_rot = 16;
   a.log_lambda = log_lambda;
   a.out_fp32 = p->out_dtype == BSFA_FP32;
   // ABSOLUTE with a workspace: the gate sweep decides every block first (its own launch, so
