@@ -296,13 +296,13 @@ def sweep_flops(w):
 
 
 def run_sweep(w, steps, warmup):
-    """The gate sweep on its own (bsfa_gate_masks), timed like a step."""
+    """The gate sweep on its own (bsfa_gate_masks), timed like a step. Its buffer is the size
+    of bsfa_prefill's workspace, so the sweep runs exactly as inside the gated call."""
     import torch
     from block_sparse_long_amd import _lib
     if getattr(w, "masks", None) is None:
-        nqb, nkb = -(-w.N // w.Bq), -(-w.N // 64)
-        w.masks = torch.empty((1, w.Hq, nqb, -(-nkb // 64)), dtype=torch.int64,
-                              device=w.Qd.device)
+        n = _lib.bsfa_prefill_workspace_bytes(w.Qd, w.Kd, block_q=w.Bq, block_k=w.Bk)
+        w.masks = torch.empty(n, dtype=torch.uint8, device=w.Qd.device)
     ev_ms, wall_ms = timed(lambda: _lib.bsfa_gate_masks(w.Qd, w.Kd, w.dtable, 0, w.masks,
                                                         block_q=w.Bq), steps, warmup)
     fl = sweep_flops(w)

@@ -426,7 +426,9 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
     allocated if None. Returns keep_mask. With ``gate_dtype`` "fp8" the call also needs room
     for the FP8 copies: keep_mask is then None or a contiguous 1-D buffer of at least
     bsfa_prefill_workspace_bytes(..., gate_dtype="fp8") bytes, and the masks come back as a view
-    of its start."""
+    of its start. A contiguous 1-D uint8 buffer with bf16 scores is taken the same way (masks
+    at its start); one of bsfa_prefill_workspace_bytes(...) bytes makes the sweep run as inside
+    bsfa_prefill (units from the workspace's counter)."""
     import torch
     lib = load_library()
     B, N, Hq, _ = Q.shape
@@ -435,13 +437,15 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
     fp8 = (GATE_DTYPES[gate_dtype] if isinstance(gate_dtype, str) else int(gate_dtype)) \
         == BSFA_FP8_E4M3
     buf = None
-    if fp8:
+    flat = keep_mask is not None and keep_mask.dim() == 1 and keep_mask.dtype == torch.uint8
+    if fp8 or flat:
         nbytes = bsfa_prefill_workspace_bytes(Q, K, block_q=block_q, block_k=block_k,
-                                              gate_dtype="fp8")
+                                              gate_dtype="fp8") if fp8 else \
+            B * Hq * nqb * shape[3] * 8
         buf = keep_mask if keep_mask is not None else torch.empty(nbytes, dtype=torch.uint8,
                                                                   device=Q.device)
         if not buf.is_contiguous() or buf.numel() * buf.element_size() < nbytes:
-            raise ValueError(f"an FP8 gate needs a contiguous buffer of {nbytes} bytes")
+            raise ValueError(f"keep_mask needs a contiguous buffer of {nbytes} bytes")
         nbuf = buf.numel() * buf.element_size()
         keep_mask = buf.view(torch.uint8)[:B * Hq * nqb * shape[3] * 8].view(torch.int64)
         keep_mask = keep_mask.view(shape)
@@ -458,7 +462,7 @@ def bsfa_gate_masks(Q, K, table, budget_slice: int = 0, keep_mask=None, *, block
     tbl = table.c_struct()
     st = lib.bsfa_gate_masks(ctypes.byref(p), _ptr(Q), _ptr(K), ctypes.byref(tbl),
                              int(budget_slice), _ptr(keep_mask),
-                             ctypes.c_uint64(nbuf if fp8 else keep_mask.numel() * 8),
+                             ctypes.c_uint64(nbuf if buf is not None else keep_mask.numel() * 8),
                              _ptr(debug_block_stat), _stream_handle(stream, Q.device))
     _check(st)
     return keep_mask

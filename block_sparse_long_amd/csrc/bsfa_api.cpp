@@ -607,6 +607,15 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
     hipError_t e = set_fp8(a, p, keep_mask, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "FP8 copies launch: %s", hipGetErrorString(e));
   }
+  // a buffer the size of bsfa_prefill's workspace: the bf16 sweep takes its units from the
+  // workspace's ticket counter, as it does inside bsfa_prefill
+  const WorkspaceLayout l = workspace_layout(p);
+  if (!fp8 && mask_bytes >= l.total) {
+    a.ticket = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(keep_mask) + l.ticket);
+    hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(a.ticket),
+                                         static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
+  }
   hipError_t e = launch_sweep(a, p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
   return ok();

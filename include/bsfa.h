@@ -287,7 +287,11 @@ bsfa_status bsfa_prefill_paged(const bsfa_problem* p, const void* Q, const void*
  *   mask_bytes    size of keep_mask; at least B * Hq * ceil(N/Bq) * W * 8 (mean_correction
  *                 is ignored here). With gate_dtype FP8_E4M3, keep_mask is a 16-byte-aligned
  *                 buffer of at least bsfa_prefill_workspace_bytes(p, ABSOLUTE) bytes (with
- *                 mean_correction 0): the masks, then the FP8 copies this call writes
+ *                 mean_correction 0): the masks, then the FP8 copies this call writes. With
+ *                 bf16 scores and mask_bytes >= bsfa_prefill_workspace_bytes(p, ABSOLUTE),
+ *                 keep_mask is taken as that workspace and the sweep runs as it does inside
+ *                 bsfa_prefill (its workgroups take units from the workspace's counter); the
+ *                 masks are the same bit for bit either way
  *   debug_block_stat  as for bsfa_prefill (off-diagonal entries only), or NULL
  *   stream        hipStream_t
  * This is the first of the two launches bsfa_prefill makes when given a workspace; on its own

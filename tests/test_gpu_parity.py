@@ -322,6 +322,30 @@ def test_gate_masks_match_oracle_decisions(name, mid_tables):
                                        rtol=1e-5, atol=2e-3)
 
 
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_gate_masks_through_a_workspace_match_the_mask_buffer(name, mid_tables):
+    # a buffer of bsfa_prefill's workspace size makes the sweep take its units from the
+    # workspace's counter (the order bsfa_prefill uses); masks and statistics are the same bits
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    dtab = mid_tables(name).to_device("cuda")
+    Q, K, V = _mid_inputs(name, 17)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    nqb, nkb = -(-N // Bq), -(-N // 64)
+    need = _lib.bsfa_prefill_workspace_bytes(Qd, Kd, block_q=Bq)
+    for sl in (0, 1):
+        out = []
+        for buf in (None, torch.full((need,), 0xA5, dtype=torch.uint8, device="cuda")):
+            stat = torch.full((B, Hq, nqb, nkb), float("nan"), dtype=torch.float32,
+                              device="cuda")
+            for _ in range(2):   # the second call finds the counter as the first left it
+                m = _lib.bsfa_gate_masks(Qd, Kd, dtab, sl, buf, block_q=Bq,
+                                         debug_block_stat=stat)
+            torch.cuda.synchronize()
+            out.append((m.cpu().numpy().copy(), stat.cpu().numpy()))
+        np.testing.assert_array_equal(out[0][0], out[1][0])
+        np.testing.assert_array_equal(out[0][1], out[1][1])
+
+
 def test_gate_masks_minus_inf_keeps_all_and_writes_every_word():
     B, N, Hq, Hkv, d, Bq = SHAPES["llama_like_ragged"]
     Q, K, V = _mid_inputs("llama_like_ragged", 16)
