@@ -229,9 +229,10 @@ hipError_t launch_sweep(bsfa::PrefillArgs sw, const bsfa_problem* p, hipStream_t
   const int shpw = bsfa::gate_sweep_heads(p->block_q, sw.G, sw.q8 != nullptr);
   sw.units = p->batch * p->heads_kv * (sw.G / shpw);
   if (sw.q8) sw.ticket = nullptr;
-  // with a ticket: one KV head at a time on every XCD (its K stream shared through each L2);
-  // without: each XCD serves fixed KV heads
-  sw.xcd_map = sw.ticket ? -1 : (sw.units % 8) == 0;
+  // each XCD serves fixed KV heads (their K streams shared through its L2); with tickets it
+  // takes its own units first and then helps the others. Unit counts that the XCDs cannot
+  // share that way: with tickets one KV head at a time on every XCD
+  sw.xcd_map = (sw.units % 8) == 0 ? 1 : sw.ticket ? -1 : 0;
   sw.xcd_rot = 0;
   return bsfa::launch_gate_sweep(sw, p->head_dim, p->block_q, st);
 }
@@ -424,10 +425,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
           return fail(BSFA_ERR_HIP, "block means launch: %s", hipGetErrorString(e));
       }
     }
-    // two ticket counters, one for the sweep and one for the walk, zeroed together
+    // the ticket counters of the sweep (one per XCD queue) and of the walk, zeroed together
     unsigned* const tickets = reinterpret_cast<unsigned*>(static_cast<char*>(workspace) +
                                                           workspace_layout(p).ticket);
-    hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(tickets), st);
+    hipError_t e = bsfa::launch_zero_words(tickets, bsfa::kTickets, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the tickets: %s", hipGetErrorString(e));
     a.ticket = tickets;
     e = launch_sweep(a, p, st);
@@ -436,7 +437,7 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     // last-level cache), units in the order the workgroups start (walk lengths differ, so a
     // fixed assignment would load some XCDs more than others)
     a.xcd_map = -1;
-    a.ticket = tickets + 1;
+    a.ticket = tickets + bsfa::kSweepTickets;
   }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
@@ -612,8 +613,8 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
   const WorkspaceLayout l = workspace_layout(p);
   if (!fp8 && mask_bytes >= l.total) {
     a.ticket = reinterpret_cast<unsigned*>(reinterpret_cast<char*>(keep_mask) + l.ticket);
-    hipError_t e = bsfa::launch_zero_u64(reinterpret_cast<unsigned long long*>(a.ticket),
-                                         static_cast<hipStream_t>(stream));
+    hipError_t e = bsfa::launch_zero_words(a.ticket, bsfa::kSweepTickets,
+                                           static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
   }
   hipError_t e = launch_sweep(a, p, static_cast<hipStream_t>(stream));

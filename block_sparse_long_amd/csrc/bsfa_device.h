@@ -1376,15 +1376,38 @@ void gate_sweep_kernel(PrefillArgs a) {
   zero_tail();
   };
 
-  // Workgroup L runs unit L; with a ticket counter (zero at the launch) the launch holds the
+  // Workgroup L runs unit L; with ticket counters (zero at the launch) the launch holds the
   // workgroups resident at once and each takes units in turn until none is left, so that the
   // XCDs, whose speeds differ by a few per cent under this load, share the work as they go.
+  // With the XCD assignment (xcd_map = 1: unit place L belongs to XCD L mod 8, one KV head per
+  // XCD when B * Hkv = 8), each XCD has its own queue, the places L = 8 t + x in order of t,
+  // so that its workgroups stream one K sequence through its L2; a workgroup takes from its
+  // own XCD's queue (the XCC_ID register) and, once that is empty, from the others'. Otherwise
+  // one counter hands out every place in turn.
   if (a.ticket) {
+    const int U = a.units * a.nqb;
+    int q = a.xcd_map == 1 ? (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & 7) : 0;
     for (;;) {
-      if (tid == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
+      if (tid == 0) {
+        int L = -1;
+        if (a.xcd_map == 1) {
+          for (int k = 0; k < 8 && L < 0; ++k) {   // the queue in hand first, then the others
+            const int y = (q + k) & 7;
+            const int t = (int)atomicAdd(a.ticket + y, 1u);
+            if (t < (U - y + 7) / 8) {
+              L = 8 * t + y;
+              q = y;
+            }
+          }
+        } else {
+          const int t = (int)atomicAdd(a.ticket, 1u);
+          L = t < U ? t : -1;
+        }
+        sUnit = L;
+      }
       __syncthreads();
       const int L = __builtin_amdgcn_readfirstlane(sUnit);
-      if (L >= a.units * a.nqb) break;   // uniform: every unit taken
+      if (L < 0) break;   // uniform: every unit taken
       run_unit(L);
       __syncthreads();   // every wave is done with this unit's LDS (and has read sUnit)
     }

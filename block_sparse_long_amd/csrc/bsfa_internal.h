@@ -41,9 +41,10 @@ struct PrefillArgs {
                                    // -1: KV-head-major order over all XCDs
   int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
                                    // blocks (0: never)
-  unsigned* ticket;                // prefill kernel: a counter, zero at the launch, from which
-                                   // the workgroups resident at once take units in turn until
-                                   // all are taken; nullptr: one workgroup per unit
+  unsigned* ticket;                // counters, zero at the launch, from which the workgroups
+                                   // resident at once take units in turn until all are taken
+                                   // (the gate sweep with xcd_map = 1: one per XCD queue);
+                                   // nullptr: one workgroup per unit
   float scale;                     // softmax scale applied to fp32 scores
   float c_log2;                    // scale * log2(e)
   float log_lambda;                // RELATIVE threshold
@@ -126,6 +127,12 @@ hipError_t launch_gate_sweep(const PrefillArgs& a, int head_dim, int block_q, hi
 // Heads per workgroup of the gate sweep (bf16 or FP8 scores).
 int gate_sweep_heads(int block_q, int group, bool fp8);
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream);
+// n (1..64) consecutive 32-bit words set to zero by a kernel (no memset node in a graph)
+hipError_t launch_zero_words(unsigned* p, int n, hipStream_t stream);
+// The ticket counters at the end of the absolute gate's workspace: the gate sweep's, one per
+// XCD queue (kSweepTickets), then the walk's.
+constexpr int kSweepTickets = 8;
+constexpr int kTickets = kSweepTickets + 1;
 // The MFMA rate probe: workgroups x 4 waves, each 4 * iters bf16 32x32x16 MFMAs; sink holds
 // workgroups * 256 floats.
 hipError_t launch_mfma_rate(int workgroups, int iters, float* sink, hipStream_t stream);

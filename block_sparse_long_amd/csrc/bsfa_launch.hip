@@ -10,6 +10,9 @@ namespace bsfa {
 namespace {
 
 __global__ void zero_u64_kernel(unsigned long long* p) { *p = 0ull; }
+__global__ void zero_words_kernel(unsigned* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0u;
+}
 
 }  // namespace
 
@@ -116,6 +119,12 @@ int resident_workgroups(const void* kernel, int block, int fallback) {
 
 hipError_t launch_zero_u64(unsigned long long* p, hipStream_t stream) {
   hipLaunchKernelGGL(zero_u64_kernel, dim3(1), dim3(1), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_zero_words(unsigned* p, int n, hipStream_t stream) {
+  if (n < 1 || n > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(zero_words_kernel, dim3(1), dim3(64), 0, stream, p, n);
   return hipGetLastError();
 }
 
