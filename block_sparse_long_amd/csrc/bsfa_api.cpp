@@ -113,13 +113,16 @@ bsfa_status check_table(const bsfa_problem* p, const bsfa_table* table, int32_t 
   return BSFA_OK;
 }
 
-// The share of off-diagonal gate blocks a budget of k blocks per (b, h, i) keeps if it held
-// exactly, sum_i min(n_off(i), k) / sum_i n_off(i), above 1/2 (the budget is a target count of
-// kept blocks per query block, "Block Sparse Flash Attention", Method > Key Designs 1). With
-// most blocks kept, a second pass over them costs more than deciding inside the softmax loop.
-// Unknown budgets (no array, k <= 0) count as not keeping most. For a variable-length batch
-// the longest sequence stands for all.
-bool budget_keeps_most(const bsfa_problem* p, const bsfa_table* table, int32_t budget_slice) {
+// Whether one launch (decisions inside the softmax loop) beats two (gate sweep, then a walk
+// over the kept tiles) for this call. Only when the table records the slice's budget k: then
+// (a) if the share of off-diagonal gate blocks the budget keeps if it held exactly,
+// sum_i min(n_off(i), k) / sum_i n_off(i), is above 1/2 (the budget is a target count of kept
+// blocks per query block, "Block Sparse Flash Attention", Method > Key Designs 1): with most
+// blocks kept, a second pass over them costs more than deciding inside the softmax loop; or
+// (b) if the call has fewer than 2^16 off-diagonal tiles in all (B * Hq * sum_i n_off(i)):
+// then the second launch's fixed costs outweigh the work it saves. Unknown budgets (no array,
+// k <= 0) keep two launches. For a variable-length batch the longest sequence stands for all.
+bool one_launch_pays(const bsfa_problem* p, const bsfa_table* table, int32_t budget_slice) {
   if (!table || !table->budgets) return false;
   const long long k = table->budgets[budget_slice];
   if (k <= 0) return false;
@@ -130,7 +133,8 @@ bool budget_keeps_most(const bsfa_problem* p, const bsfa_table* table, int32_t b
     kept += n_off < k ? n_off : k;
     all += n_off;
   }
-  return all > 0 && 2 * kept > all;
+  if (all > 0 && 2 * kept > all) return true;
+  return (long long)p->batch * p->heads_q * all < (1ll << 16);
 }
 
 // Kernel arguments common to the prefill kernel and the gate sweep.
@@ -362,11 +366,12 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   if ((long long)p->batch * p->heads_q * nqb > 0x7fffffffll)
     return fail(BSFA_ERR_UNSUPPORTED, "grid too large");
   const uint64_t ws_need = bsfa_prefill_workspace_bytes(p, gate_mode);
-  // the absolute gate with a workspace takes two launches unless the slice's budget keeps
-  // most blocks (then one launch; mean correction, FP8 scores and 128-key blocks need two)
+  // the absolute gate with a workspace takes two launches unless one pays (the slice's
+  // budget keeps most blocks, or the call is small); mean correction, FP8 scores and 128-key
+  // blocks always take two
   const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty &&
                          (mean || fp8 || p->block_k != bsfa::kBlockK ||
-                          !budget_keeps_most(p, table, budget_slice));
+                          !one_launch_pays(p, table, budget_slice));
   if (use_masks && workspace_bytes < ws_need)
     return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
                 (unsigned long long)workspace_bytes, (unsigned long long)ws_need);

@@ -181,10 +181,13 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 the kept blocks only; or one launch that decides each block inside the
  *                 softmax loop. Without a workspace the call takes one launch. With a
  *                 workspace of at least bsfa_prefill_workspace_bytes(p, gate_mode) bytes it
- *                 takes two, unless the table records the slice's budget k and
+ *                 takes two, unless the table records the slice's budget k and either
  *                 sum_i min(n_off(i), k) / sum_i n_off(i) (the share of off-diagonal blocks
- *                 the budget keeps) exceeds 1/2 for this problem: when most blocks are kept
- *                 the second pass over them costs more than deciding inside the loop. A
+ *                 the budget keeps) exceeds 1/2 for this problem — when most blocks are kept
+ *                 the second pass over them costs more than deciding inside the loop — or
+ *                 the call has fewer than 65536 off-diagonal tiles in all
+ *                 (B * Hq * sum_i n_off(i)), where the second launch's fixed costs
+ *                 outweigh the work it saves. A
  *                 non-NULL workspace that is too small is an error (BSFA_ERR_ARG). With
  *                 mean_correction, an FP8 gate or block_k = 128 it is required (two launches
  *                 always) and must be 16-byte aligned; a launch before the sweep computes the
