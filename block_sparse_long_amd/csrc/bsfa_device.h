@@ -661,7 +661,7 @@ constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
 // Prefill kernels that take their units from a ticket counter when given one (the mask walk).
 template <int GATE, bool MEAN>
-constexpr bool kResidentLoop = GATE == kAbsolute && !MEAN;
+constexpr bool kResidentLoop = GATE == kAbsolute;
 
 // PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
 // kernels carry no page lookups). MEAN (absolute walk only): the pruned gate blocks' stand-ins
@@ -693,9 +693,6 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int sKept;
   __shared__ int sUnit;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index, in a scalar register
-  const int hw = w / WPH, rw = w % WPH;
   // Workgroup L runs unit L, except in the mask walk: its launch holds as many workgroups as
   // stay resident, and each takes units in turn from a ticket counter (zero at the launch)
   // until none is left. Workgroups go to the XCDs in turn whatever their work, and a new one
@@ -706,11 +703,22 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   int L = blockIdx.x;
 next_unit:
   if constexpr (kLoop) {
-    if (tid == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
+    if (threadIdx.x == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
     __syncthreads();
     L = __builtin_amdgcn_readfirstlane(sUnit);
     if (L >= a.units * a.nqb) return;   // uniform: every unit taken
   }
+  // (with mean correction the lane and wave indices are made opaque per unit: otherwise the
+  // compiler computes the mean pass's lane-dependent copy offsets once ahead of the unit loop
+  // and holds them through the walk, which spills)
+  int tid_u = threadIdx.x, w_u = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  if constexpr (kLoop && MEAN) {
+    asm volatile("" : "+v"(tid_u));
+    asm volatile("" : "+s"(w_u));
+  }
+  const int tid = tid_u, lane = tid & 63;
+  const int w = w_u;   // wave index, in a scalar register
+  const int hw = w / WPH, rw = w % WPH;
   const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
