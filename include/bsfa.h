@@ -17,8 +17,8 @@
  *     - Diagonal-region blocks (n_off(i) <= j < n_end(i)) always run, with the causal mask.
  *     - A kept block updates the online-softmax state (running max m, sum l, accumulator O)
  *       and accumulates P V_j; a skipped block loads no V, adds nothing and leaves m, l and O
- *       untouched (Key Designs 3). (Where the decision is voted inside the softmax loop, a
- *       skipped tile's exponentials may be evaluated and discarded; results are unaffected.)
+ *       untouched (Key Designs 3); it gets no exponentials either, also where the decision is
+ *       voted inside the softmax loop (the vote comes before them).
  *     - Output O_i = O / l: attention renormalised over the kept blocks and the diagonal
  *       region (Overall Architecture; Key Designs 3).
  *   T_eff(h, i) = T[budget_slice][h][min(P/Bq + i, t_len - 1)] (the absolute query block):
@@ -27,16 +27,18 @@
  *
  * Conventions for every entry point:
  *   - Device pointers are caller-owned device memory on the current HIP device; the library
- *     allocates nothing, frees nothing and keeps no state between calls except the thread-local
- *     error string.
+ *     allocates nothing and frees nothing. Between calls it keeps only the thread-local error
+ *     string and per-device facts it looks up once (the static scratch's address, how many
+ *     workgroups of a kernel the device holds at once).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and is asynchronous:
  *     results are valid once the caller has synchronised the stream. The library never
  *     synchronises.
  *   - Arguments are validated on the host before anything is enqueued. On any status other
  *     than BSFA_OK and BSFA_ERR_HIP nothing was enqueued and every output is untouched;
  *     bsfa_last_error() then describes the problem. BSFA_ERR_HIP means a launch failed; earlier
- *     launches of the same call (zeroing kept_total, FP8 copies, block means, the gate sweep)
- *     may already be enqueued, and the outputs are then undefined. No C++ exception crosses
+ *     launches of the same call (zeroing kept_total or the workspace's counters, FP8 copies,
+ *     block means, the gate sweep) may already be enqueued, and the outputs are then
+ *     undefined. No C++ exception crosses
  *     the ABI.
  *   - Tensors are indexed [batch][token][head][dim] with element strides given per tensor for
  *     batch, token and head; the dim axis is contiguous. Base pointers and every row
