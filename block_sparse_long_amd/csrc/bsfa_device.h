@@ -1258,6 +1258,24 @@ __device__ __forceinline__ float tile_max64(f32x16 (&s)[2][2], bool ragged, int 
   return block_max(mx, s[1][1]);
 }
 
+// Copy whole key tile j of the sweep (all rounds of this wave) into the LDS buffer at byte
+// address dst.
+template <int D, int NW, bool PAGED>
+__device__ __forceinline__ void sweep_load_k(const PrefillArgs& a, int b, int j, const __bf16* Kb,
+                                             long long kst,
+                                             const unsigned (&koff)[copy_iters<Tile<D>::STR, NW>()],
+                                             unsigned dst, int w) {
+  constexpr int STR = Tile<D>::STR, MK = copy_iters<STR, NW>();
+  const __bf16* const g = Kb + tile_offset<PAGED>(a, b, j, kst, a.ks[0]);
+  // (the wave index opaque here: otherwise the last round's test is computed once per kernel
+  // and held, under this kernel's register pressure, in a spilled vector register whose reload
+  // waits for every copy in flight)
+  int wc = w;
+  asm volatile("" : "+s"(wc));
+#pragma unroll
+  for (int m = 0; m < MK; ++m) copy_round_full<D, STR, NW>(m, koff, g, dst, wc);
+}
+
 template <int D, int BQ, int HPW, bool PAGED>
 __global__ __launch_bounds__(HPW * (BQ / 64) * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void gate_sweep_kernel(PrefillArgs a) {
@@ -1278,7 +1296,7 @@ void gate_sweep_kernel(PrefillArgs a) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hw = w / WPH, rw = w % WPH;
   // one unit (b, KV head, head pair, query block) at place L of the unit order
-  auto run_unit = [&](const int L) {
+  auto run_unit = [&](const int L) __attribute__((always_inline)) {
   const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
@@ -1306,13 +1324,10 @@ void gate_sweep_kernel(PrefillArgs a) {
   const __bf16* Qb = static_cast<const __bf16*>(a.q) + sq.q + h * a.qs[2];
   const __bf16* Kb = static_cast<const __bf16*>(a.k) + sq.k + g * a.ks[2];
   const long long kst = a.ks[1];
-  const unsigned krow = (unsigned)kst * 2u;
   unsigned koff[MK];
   copy_offsets<D, STR, NW>(koff, kst, w, lane);
-  auto load_k = [&](int j, __bf16* dst) {
-    copy_tile<D, STR, NW>(koff, Kb + tile_offset<PAGED>(a, b, j, kst, a.ks[0]), krow, BK, dst, w,
-                          lane);
-  };
+  // off-diagonal key tiles are whole: every round is a plain copy to a precomputed LDS address
+  const unsigned lKa = lds_addr(sKa), lKb = lds_addr(sKb), lKc = lds_addr(sKc);
   auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
   const int tcol = min(pre / BQ + i, a.t_len - 1);   // the absolute query block's threshold
   const float thr = a.thr[h * a.t_len + tcol];
@@ -1359,15 +1374,18 @@ void gate_sweep_kernel(PrefillArgs a) {
     }
   };
 
-  load_k(0, sKa);
-  if (n_off > 1) load_k(1, sKb);
+  sweep_load_k<D, NW, PAGED>(a, b, 0, Kb, kst, koff, lKa, w);
+  if (n_off > 1) sweep_load_k<D, NW, PAGED>(a, b, 1, Kb, kst, koff, lKb, w);
   bf16x8 qf[2][KS];
   load_q32<D>(Qb, a.qs[1], row0, N, qf[0], lane);
   load_q32<D>(Qb, a.qs[1], row0 + 32, N, qf[1], lane);
   wait_vmem();
   __syncthreads();
   for (int j = 0; j < n_off; ++j) {
-    if (j + 2 < n_off) load_k(j + 2, kbuf((j + 2) % 3));   // the buffer tile j - 1 used
+    if (j + 2 < n_off) {   // into the buffer tile j - 1 used
+      const int x = (j + 2) % 3;
+      sweep_load_k<D, NW, PAGED>(a, b, j + 2, Kb, kst, koff, x == 0 ? lKa : x == 1 ? lKb : lKc, w);
+    }
     f32x16 s[2][2];
     qk64<D>(kbuf(j % 3), qf, s, lane);
     const float m = wave_max(tile_max64(s, ragged_rows, row0, N, lane));
