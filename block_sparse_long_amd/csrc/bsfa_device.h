@@ -135,6 +135,16 @@ __device__ __forceinline__ float wave_max(float x) {
   return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
 }
 
+// Wave-uniform sum over the 64 lanes, the butterfly of wave_max with additions.
+__device__ __forceinline__ int wave_sum(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0xB1, 0xf, 0xf, false);    // quad_perm [1,0,3,2]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x4E, 0xf, 0xf, false);    // quad_perm [2,3,0,1]
+  x += __builtin_amdgcn_update_dpp(0, x, 0x141, 0xf, 0xf, false);   // row_half_mirror
+  x += __builtin_amdgcn_update_dpp(0, x, 0x140, 0xf, 0xf, false);   // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
 // Wait for this wave's outstanding global loads (including those writing LDS directly).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
@@ -690,7 +700,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ __attribute__((aligned(16))) __bf16 sV1[64 * STRV];
   __shared__ __attribute__((aligned(16))) float sGate[2][NW * kRows];   // per-row gate statistics
   __shared__ unsigned long long sMask[kAbs ? kMaskWords : 1];           // kept off-diagonal tiles
-  __shared__ int sKept;
+  __shared__ int sKept[kAbs ? NW : 1];   // per-wave kept-tile counts of the mask walk
   __shared__ int sUnit;
 
   // Workgroup L runs unit L, except in the mask walk: its launch holds as many workgroups as
@@ -788,15 +798,19 @@ next_unit:
     const int nw64 = (n_off + 63) >> 6;
     const unsigned long long* gm =
         a.keep_mask + (((long long)b * a.Hq + h) * a.nqb + i) * a.mask_words;
-    for (int x = tid; x < nw64; x += NW * 64) sMask[x] = gm[x];
-    __syncthreads();
-    if (w == 0 && lane == 0) {
-      for (int x = 0; x < nw64; ++x) kept += __builtin_popcountll(sMask[x]);
-      sKept = kept;
-      kept /= a.kpb;          // kept gate blocks (a kept block sets all its tiles' bits)
+    // each word counted by the thread that stages it; a wave sum, then the waves' sums
+    int cnt = 0;
+    for (int x = tid; x < nw64; x += NW * 64) {
+      const unsigned long long word = gm[x];
+      sMask[x] = word;
+      cnt += __builtin_popcountll(word);
     }
+    cnt = wave_sum(cnt);
+    if (lane == 0) sKept[w] = cnt;
     __syncthreads();
-    kept_all = sKept;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) kept_all += sKept[k];
+    kept = kept_all / a.kpb;   // kept gate blocks (a kept block sets all its tiles' bits)
   } else if (!loop_gate) {
     // dense, or an absolute threshold of -inf: every off-diagonal gate block kept
     kept = (pre + i * BQ) / (BK * a.kpb);
