@@ -165,7 +165,8 @@ def summarise_counters(args):
 
 def profile_once(args):
     """The command the counter summaries are taken from: a plain 1 GiB device copy (the
-    scale reference for FETCH_SIZE / WRITE_SIZE), then one gated call of the workload."""
+    scale reference for FETCH_SIZE / WRITE_SIZE), then one gated call of the workload (and,
+    with bf16 gate scores, one dense call: the softmax loop without a gate)."""
     import torch
     from block_sparse_long_amd import _lib
     _lib.load_library()
@@ -182,6 +183,8 @@ def profile_once(args):
         path = os.path.join(GOLDEN, f"thresholds_{args.workload}_fp8.bin")
         kw.update(gate_dtype="fp8", table=ThresholdTable.load(path).to_device(dev))
     w.call(mode, **kw)
+    if args.gate_dtype == "bf16":
+        w.call("dense")
     torch.cuda.synchronize()
     print(json.dumps({"profile_once": args.workload, "gate_dtype": args.gate_dtype,
                       "copy_bytes": COPY_BYTES,
