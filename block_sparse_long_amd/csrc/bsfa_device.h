@@ -1015,24 +1015,28 @@ next_unit:
     const __bf16* const kb = (P ? sK0 : sK1) + kfo;   // K of t1
     float mx = kNegInf;
     constexpr int NPV = kVote ? 0 : kPairsPV;
-    constexpr int VQ = kVote ? kFlag : kNever;
+    // the V_t copy in the voting kernels: with one head per workgroup some head keeps t
+    // exactly when this one does, so each form copies always or never; with more heads a flag
+    constexpr int VQK = kVote ? (HPW == 1 ? kAlways : kFlag) : kNever;   // t kept here
+    constexpr int VQS = kVote ? (HPW == 1 ? kNever : kFlag) : kNever;    // t skipped here
     if (!kVote || mykeep) {
       if (kfast)
-        qk_phase<D, MKR, kAlways, kAlways, NPV, MVR, VQ>(true, true, kb, qf, sb[P ^ 1], sb[P], off,
-                                                         c, pb[P], sum, mx, copy_k, anyv, copy_v);
+        qk_phase<D, MKR, kAlways, kAlways, NPV, MVR, VQK>(true, true, kb, qf, sb[P ^ 1], sb[P],
+                                                          off, c, pb[P], sum, mx, copy_k, anyv,
+                                                          copy_v);
       else
-        qk_phase<D, MKR, kAlways, kNever, NPV, MVR, VQ>(true, false, kb, qf, sb[P ^ 1], sb[P],
-                                                        off, c, pb[P], sum, mx, copy_k, anyv,
-                                                        copy_v);
+        qk_phase<D, MKR, kAlways, kNever, NPV, MVR, VQK>(true, false, kb, qf, sb[P ^ 1], sb[P],
+                                                         off, c, pb[P], sum, mx, copy_k, anyv,
+                                                         copy_v);
     } else {
       if (kfast)
-        qk_phase<D, MKR, kNever, kAlways, NPV, MVR, VQ>(false, true, kb, qf, sb[P ^ 1], sb[P],
+        qk_phase<D, MKR, kNever, kAlways, NPV, MVR, VQS>(false, true, kb, qf, sb[P ^ 1], sb[P],
+                                                         off, c, pb[P], sum, mx, copy_k, anyv,
+                                                         copy_v);
+      else
+        qk_phase<D, MKR, kNever, kNever, NPV, MVR, VQS>(false, false, kb, qf, sb[P ^ 1], sb[P],
                                                         off, c, pb[P], sum, mx, copy_k, anyv,
                                                         copy_v);
-      else
-        qk_phase<D, MKR, kNever, kNever, NPV, MVR, VQ>(false, false, kb, qf, sb[P ^ 1], sb[P],
-                                                       off, c, pb[P], sum, mx, copy_k, anyv,
-                                                       copy_v);
     }
     if (kload && !kfast) load_k(t2, P ? sK1 : sK0);
     if constexpr (kVote) {
