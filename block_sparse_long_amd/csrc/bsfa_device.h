@@ -198,22 +198,21 @@ __device__ __forceinline__ void copy_offsets(unsigned* off, long long gst, int w
   }
 }
 
-// One direct global -> LDS copy instruction (16 bytes per lane, lane l to LDS lds + 16 l),
-// issued through inline asm: the compiler then does not track it, and in particular does not
-// make later LDS reads (of other buffers) wait for it; whoever reads the destination waits
-// for it with wait_vmem() before a barrier. gbase and lds are wave-uniform, voff per lane.
-// M0 (the LDS destination) is saved and restored around the copy. The scalar operands may have
-// just been written by v_readfirstlane, and a memory instruction reading an SGPR written by a
-// vector instruction needs 5 wait states; the asm supplies them itself (the compiler cannot
-// see the read): two moves plus s_nop 2.
 // 32-bit LDS byte address of a __shared__ object (the cast checks for null, so it is done once
-// per buffer, outside the loops).
+// per buffer, outside the loops; the copies take these addresses, never generic pointers).
 __device__ __forceinline__ unsigned lds_addr(const void* lds) {
   typedef __attribute__((address_space(3))) const char lds_char;
   return __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)lds);
 }
 
-// dma16 with the LDS destination as a 32-bit LDS byte address (wave-uniform).
+// One direct global -> LDS copy instruction (16 bytes per lane, lane l to LDS byte address
+// lds + 16 l), issued through inline asm: the compiler then does not track it, and in
+// particular does not make later LDS reads (of other buffers) wait for it; whoever reads the
+// destination waits for it with wait_vmem() before a barrier. gbase and lds are wave-uniform,
+// voff per lane. M0 (the LDS destination) is saved and restored around the copy. The scalar
+// operands may have just been written by v_readfirstlane, and a memory instruction reading an
+// SGPR written by a vector instruction needs 5 wait states; the asm supplies them itself (the
+// compiler cannot see the read): two moves plus s_nop 2.
 __device__ __forceinline__ void dma16_at(const void* gbase, unsigned voff, unsigned lds) {
   const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
   const unsigned glo = __builtin_amdgcn_readfirstlane((unsigned)g);
@@ -232,31 +231,13 @@ __device__ __forceinline__ void dma16_at(const void* gbase, unsigned voff, unsig
       : "memory");
 }
 
-__device__ __forceinline__ void dma16(const void* gbase, unsigned voff, const void* lds) {
-  typedef __attribute__((address_space(3))) const char lds_char;
-  const unsigned long long g = reinterpret_cast<unsigned long long>(gbase);
-  const unsigned glo = __builtin_amdgcn_readfirstlane((unsigned)g);
-  const unsigned ghi = __builtin_amdgcn_readfirstlane((unsigned)(g >> 32));
-  const unsigned long long gs = ((unsigned long long)ghi << 32) | glo;
-  const unsigned m0 = __builtin_amdgcn_readfirstlane((unsigned)(size_t)(lds_char*)lds);
-  unsigned saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %3\n\t"
-      "s_nop 2\n\t"
-      "global_load_lds_dwordx4 %1, %2\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(voff), "s"(gs), "s"(m0)
-      : "memory");
-}
-
-// Round m of a tile copy: instruction k = w + NW*m of the tile, if it exists (wave-uniform;
-// only the last round can run past the tile). For a ragged tile (valid < 64 rows) the chunks
-// of rows at or past `valid` are redirected to row valid - 1.
+// Round m of a tile copy into the LDS buffer at byte address lds: instruction k = w + NW*m
+// of the tile, if it exists (wave-uniform; only the last round can run past the tile). For a
+// ragged tile (valid < 64 rows) the chunks of rows at or past `valid` are redirected to row
+// valid - 1.
 template <int D, int STRIDE, int NW>
 __device__ __forceinline__ void copy_round(int m, const unsigned* off, const __bf16* gbase,
-                                           unsigned row_bytes, int valid, __bf16* tile, int w,
+                                           unsigned row_bytes, int valid, unsigned lds, int w,
                                            int lane) {
   constexpr int CPS = STRIDE / 8, M = copy_iters<STRIDE, NW>();
   const int k = w + NW * m;
@@ -266,7 +247,7 @@ __device__ __forceinline__ void copy_round(int m, const unsigned* off, const __b
       const int r = (64 * k + lane) / CPS;
       o -= (unsigned)max(r - (valid - 1), 0) * row_bytes;
     }
-    dma16(gbase, o, tile + k * 512);
+    dma16_at(gbase, o, lds + k * 1024u);
   }
 }
 
@@ -281,14 +262,14 @@ __device__ __forceinline__ void copy_round_full(int m, const unsigned* off, cons
   if (m + 1 < M || k < CPS) dma16_at(gbase, off[m], lds + k * 1024u);
 }
 
-// Copy one 64-row tile starting at gbase (all rounds).
+// Copy one 64-row tile starting at gbase (all rounds) into the LDS buffer at byte address lds.
 template <int D, int STRIDE, int NW>
 __device__ __forceinline__ void copy_tile(const unsigned* off, const __bf16* gbase,
-                                          unsigned row_bytes, int valid, __bf16* tile, int w,
+                                          unsigned row_bytes, int valid, unsigned lds, int w,
                                           int lane) {
 #pragma unroll
   for (int m = 0; m < copy_iters<STRIDE, NW>(); ++m)
-    copy_round<D, STRIDE, NW>(m, off, gbase, row_bytes, valid, tile, w, lane);
+    copy_round<D, STRIDE, NW>(m, off, gbase, row_bytes, valid, lds, w, lane);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -709,6 +690,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   // waits for a slot on its own XCD; as walk lengths vary, slots would sit idle on the other
   // XCDs meanwhile. Resident workgroups that take the next unit as they finish one keep every
   // slot busy until the work runs out. (In the other kernels the work per unit is even.)
+  const unsigned lK0 = lds_addr(sK0), lK1 = lds_addr(sK1);
+  const unsigned lV0 = lds_addr(sV0), lV1 = lds_addr(sV1);
   constexpr bool kLoop = kResidentLoop<GATE, MEAN>;
   int L = blockIdx.x;
 next_unit:
@@ -783,7 +766,7 @@ next_unit:
   copy_offsets<D, STRV, NW>(voff, vst, w, lane);
   auto key_valid = [&](int j) { return min(BK, Nk - j * BK); };
   const unsigned krow = (unsigned)kst * 2u, vrow = (unsigned)vst * 2u;
-  auto load_k = [&](int j, __bf16* dst) {
+  auto load_k = [&](int j, unsigned dst) {
     copy_tile<D, STR, NW>(koff, Kb + tile_offset<PAGED>(a, b, j, kst, a.ks[0]), krow, key_valid(j),
                           dst, w, lane);
   };
@@ -855,10 +838,10 @@ next_unit:
   // ---- prologue: the first two tiles of the sequence staged, scores of the first published ----
   int t = next_tile(-1);
   int t1 = next_tile(t);
-  load_k(t, sK0);
+  load_k(t, lK0);
   wait_vmem();
   __syncthreads();
-  if (t1 < n_end) load_k(t1, sK1);
+  if (t1 < n_end) load_k(t1, lK1);
   f32x16 sb[2][2];     // scores of the last tiles of each parity
   float rc;            // row max of the newest scores
   qk32<D>(sK0, qf, sb[0], lane);
@@ -869,8 +852,6 @@ next_unit:
 
   bool keep_prev = false;
   bf16x8 pb[2][4];     // P of the last tiles of each parity; PV of the previous tile reads pb[P ^ 1]
-  const unsigned lK0 = lds_addr(sK0), lK1 = lds_addr(sK1);
-  const unsigned lV0 = lds_addr(sV0), lV1 = lds_addr(sV1);
   const int kfo = (lane & 31) * STR + 8 * (lane >> 5);
   constexpr int NSTEP = 4 * MD;               // PV MFMA steps
   // PV steps issued before the decision on tile t: all of them in the voting kernels; dense
@@ -919,11 +900,14 @@ next_unit:
     const bool kfast = kload && key_valid(t2) == BK;
     const bool vfast = key_valid(t) == BK;
     auto copy_k = [&](int r) { copy_round_full<D, STR, NW>(r, koff, kg, P ? lK1 : lK0, w); };
-    auto copy_v = [&](int r) {
+    // V_t copy rounds: tested per round in dense and the walk; the voting kernels' forms that
+    // issue them run only when tile t is whole
+    auto copy_v_tested = [&](int r) {
       if (vfast) copy_round_full<D, STRV, NW>(r, voff, vg, P ? lV1 : lV0, w);
     };
+    auto copy_v = [&](int r) { copy_round_full<D, STRV, NW>(r, voff, vg, P ? lV1 : lV0, w); };
     auto copy_v_ragged = [&]() {
-      if (!vfast) copy_tile<D, STRV, NW>(voff, vg, vrow, key_valid(t), P ? sV1 : sV0, w, lane);
+      if (!vfast) copy_tile<D, STRV, NW>(voff, vg, vrow, key_valid(t), P ? lV1 : lV0, w, lane);
     };
     const __bf16* const sv = P ? sV0 : sV1;     // V of the previous tile
     bf16x8 vb[3];
@@ -988,10 +972,12 @@ next_unit:
     if constexpr (!kVote) {
       if (keep_prev)
         pv_steps<D, DEC, NSTEP, DEC, MVR, kAlways, kAlways, kAlways>(
-            true, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+            true, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane,
+            copy_v_tested);
       else
         pv_steps<D, DEC, NSTEP, DEC, MVR, kNever, kAlways, kAlways>(
-            false, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane, copy_v);
+            false, true, true, sv, pb[P ^ 1], o, vb, sb[P], off, c, pb[P], sum, lane,
+            copy_v_tested);
       copy_v_ragged();
     }
     // the previous P is dead from here on (the next write of its buffer precedes the next read)
@@ -1019,26 +1005,31 @@ next_unit:
     // exactly when this one does, so each form copies always or never; with more heads a flag
     constexpr int VQK = kVote ? (HPW == 1 ? kAlways : kFlag) : kNever;   // t kept here
     constexpr int VQS = kVote ? (HPW == 1 ? kNever : kFlag) : kNever;    // t skipped here
+    // (the straight-line forms need whole tiles: K_{t2} copied in rounds, and in the voting
+    // kernels V_t as well; otherwise a form with flags, the ragged tile copied after it)
+    constexpr int VQG = kVote ? kFlag : kNever;
+    constexpr int KLG = kVote ? kFlag : kNever;   // (dense and the walk: only when K is ragged)
+    const bool vq = anyv && vfast;
     if (!kVote || mykeep) {
-      if (kfast)
+      if (kfast && (!kVote || vfast))
         qk_phase<D, MKR, kAlways, kAlways, NPV, MVR, VQK>(true, true, kb, qf, sb[P ^ 1], sb[P],
-                                                          off, c, pb[P], sum, mx, copy_k, anyv,
+                                                          off, c, pb[P], sum, mx, copy_k, vq,
                                                           copy_v);
       else
-        qk_phase<D, MKR, kAlways, kNever, NPV, MVR, VQK>(true, false, kb, qf, sb[P ^ 1], sb[P],
-                                                         off, c, pb[P], sum, mx, copy_k, anyv,
-                                                         copy_v);
+        qk_phase<D, MKR, kAlways, KLG, NPV, MVR, VQG>(true, kfast, kb, qf, sb[P ^ 1], sb[P],
+                                                        off, c, pb[P], sum, mx, copy_k, vq,
+                                                        copy_v);
     } else {
       if (kfast)
         qk_phase<D, MKR, kNever, kAlways, NPV, MVR, VQS>(false, true, kb, qf, sb[P ^ 1], sb[P],
-                                                         off, c, pb[P], sum, mx, copy_k, anyv,
+                                                         off, c, pb[P], sum, mx, copy_k, vq,
                                                          copy_v);
       else
-        qk_phase<D, MKR, kNever, kNever, NPV, MVR, VQS>(false, false, kb, qf, sb[P ^ 1], sb[P],
-                                                        off, c, pb[P], sum, mx, copy_k, anyv,
-                                                        copy_v);
+        qk_phase<D, MKR, kNever, kFlag, NPV, MVR, VQS>(false, false, kb, qf, sb[P ^ 1], sb[P],
+                                                       off, c, pb[P], sum, mx, copy_k, vq,
+                                                       copy_v);
     }
-    if (kload && !kfast) load_k(t2, P ? sK1 : sK0);
+    if (kload && !kfast) load_k(t2, P ? lK1 : lK0);
     if constexpr (kVote) {
       if (anyv) copy_v_ragged();
     }
@@ -1108,23 +1099,23 @@ next_unit:
       // barrier), during the exponentials and the PV product.
       auto stage_k = [&](int m) {
         const int valid = min(64, n_gb - m);
-        copy_tile<D, STR, NW>(mko, khi + (long long)m * D, 2u * D, valid, sK0, w, lane);
-        copy_tile<D, STR, NW>(mko, klo + (long long)m * D, 2u * D, valid, sK1, w, lane);
+        copy_tile<D, STR, NW>(mko, khi + (long long)m * D, 2u * D, valid, lK0, w, lane);
+        copy_tile<D, STR, NW>(mko, klo + (long long)m * D, 2u * D, valid, lK1, w, lane);
       };
-      auto stage_v = [&](int m, __bf16* dst) {
+      auto stage_v = [&](int m, unsigned dst) {
         copy_tile<D, STRV, NW>(mvo, vme + (long long)m * D, 2u * D, min(64, n_gb - m), dst, w,
                                lane);
       };
       __syncthreads();   // every wave is done with the walk's tile buffers
       stage_k(0);
-      stage_v(0, sV0);
+      stage_v(0, lV0);
       bool par = false;
       for (int m0 = 0; m0 < n_gb; m0 += 64, par = !par) {
         __bf16* const sv = par ? sV1 : sV0;
         const bool more = m0 + 64 < n_gb;
         wait_vmem();
         __syncthreads();   // tile m0 visible; every wave is done with the other V buffer
-        if (more) stage_v(m0 + 64, par ? sV0 : sV1);
+        if (more) stage_v(m0 + 64, par ? lV0 : lV1);
         // S^T of the pseudo-keys: the high and low parts into one accumulator
         f32x16 sm[2];
 #pragma unroll
@@ -1620,9 +1611,7 @@ void gate_sweep_fp8_kernel(PrefillArgs a) {
   const unsigned krow = (unsigned)(a.Hkv * D);
   unsigned koff[MK];
   copy_offsets<D2, STR8, NW>(koff, kst2, w, lane);
-  auto load_k = [&](int j, __bf16* dst) {
-    copy_tile<D2, STR8, NW>(koff, K8 + (long long)j * kBlockK * kst2, krow, BK, dst, w, lane);
-  };
+  const unsigned lKa = lds_addr(sKa), lKb = lds_addr(sKb), lKc = lds_addr(sKc);
   auto kbuf = [&](int x) { return x == 0 ? sKa : x == 1 ? sKb : sKc; };
   // without a table (the calibration's maxima dump) nothing is kept
   const int tcol = min(pre / BQ + i, a.t_len - 1);
@@ -1663,8 +1652,8 @@ void gate_sweep_fp8_kernel(PrefillArgs a) {
     }
   };
 
-  load_k(0, sKa);
-  if (n_off > 1) load_k(1, sKb);
+  copy_tile<D2, STR8, NW>(koff, K8, krow, BK, lKa, w, lane);
+  if (n_off > 1) copy_tile<D2, STR8, NW>(koff, K8 + (long long)kBlockK * kst2, krow, BK, lKb, w, lane);
   // Q rows row0 + 32 rb + lane % 32 (zero past N) and their scales
   i32x8 qf[2][KS8];
   float qs[2];
@@ -1690,7 +1679,11 @@ void gate_sweep_fp8_kernel(PrefillArgs a) {
   __syncthreads();
   const int kfo = (lane & 31) * (2 * STR8) + 32 * (lane >> 5);   // byte offset in a tile
   for (int j = 0; j < n_off; ++j) {
-    if (j + 2 < n_off) load_k(j + 2, kbuf((j + 2) % 3));
+    if (j + 2 < n_off) {   // into the buffer tile j - 1 used
+      const int x = (j + 2) % 3;
+      copy_tile<D2, STR8, NW>(koff, K8 + (long long)(j + 2) * kBlockK * kst2, krow, BK,
+                              x == 0 ? lKa : x == 1 ? lKb : lKc, w, lane);
+    }
     const unsigned char* const kt = reinterpret_cast<const unsigned char*>(kbuf(j % 3)) + kfo;
     f32x16 s[2][2];
 #pragma unroll
@@ -1776,14 +1769,15 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
     copy_offsets<D, STR, NW>(koff, kst, w, lane);
     bf16x8 qf[D / 16];
     const unsigned krow = (unsigned)kst * 2u;
-    copy_tile<D, STR, NW>(koff, Kb, krow, BK, sK[0], w, lane);
+    const unsigned lK0 = lds_addr(sK[0]), lK1 = lds_addr(sK[1]);
+    copy_tile<D, STR, NW>(koff, Kb, krow, BK, lK0, w, lane);
     load_q32<D>(Qb, a.qs[1], row0, N, qf, lane);
     wait_vmem();
     __syncthreads();
     for (int t = 0; t < n_off; ++t) {
       if (t + 1 < n_off)
         copy_tile<D, STR, NW>(koff, Kb + (long long)(t + 1) * BK * kst, krow, BK,
-                              sK[(t + 1) & 1], w, lane);
+                              ((t + 1) & 1) ? lK1 : lK0, w, lane);
       f32x16 s[2];
       qk32<D>(sK[t & 1], qf, s, lane);
       const float rmax = rowmax32(s, ragged_rows, t * BK, row, row < N, lane);
