@@ -47,11 +47,8 @@ int waves_per_workgroup(int block_q, int group) {
 }
 
 int prefill_waves_per_workgroup(int block_q, int group, int gate) {
-  if (gate == kAbsolute || gate == kAbsVote) return block_q / kRowsPerWave;   // one head
-  // dense at 128 query rows: two heads of a KV group per workgroup (8 waves, one workgroup per
-  // CU), each staged K/V tile serving both
-  if (gate == kDense && block_q == 128 && group % 2 == 0) return 8;
-  return waves_per_workgroup(block_q, group);
+  return gate == kAbsolute || gate == kAbsVote ? block_q / kRowsPerWave
+                                               : waves_per_workgroup(block_q, group);
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int block_q, int gate,
