@@ -60,7 +60,7 @@ typedef enum {
   BSFA_ERR_DTYPE = 3,        /* unsupported input or output dtype */
   BSFA_ERR_ALIGN = 4,        /* pointer or stride breaks the 16-byte row alignment */
   BSFA_ERR_TABLE = 5,        /* threshold table missing or its header disagrees with the problem */
-  BSFA_ERR_UNSUPPORTED = 6,  /* valid request outside what this build implements */
+  BSFA_ERR_UNSUPPORTED = 6,  /* valid request outside what this library implements */
   BSFA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
 } bsfa_status;
 
@@ -322,7 +322,7 @@ bsfa_status bsfa_gate_masks(const bsfa_problem* p, const void* Q, const void* K,
  *                 calibrated on its own scores (FP8 copies of Q and K, the FP8 gate sweep's
  *                 block maxima, then the k-th highest); the bf16 scores need none
  *   stream        hipStream_t
- * This build supports seqlen up to 262144 here, whole sequences only (kv_seqlen 0 or equal to
+ * This library supports seqlen up to 262144 here, whole sequences only (kv_seqlen 0 or equal to
  * seqlen; BSFA_ERR_UNSUPPORTED otherwise). */
 bsfa_status bsfa_calibrate_blockmax(const bsfa_problem* p, const void* Q, const void* K,
                                     const int32_t* budgets_host, int32_t n_budgets,
