@@ -358,6 +358,20 @@ def run_gate(w, mode, steps, warmup, **kw):
                 pct_peak=100.0 * flops / ev_ms / 1e9 / PEAK_BF16_TFLOPS)
 
 
+def paired_tax(w, mode, rounds, steps, warmup, **kw):
+    """Zero-skip tax of a gated call that skips nothing, against the dense path: `rounds`
+    rounds of `steps` dense calls then `steps` gated calls, alternating, so that both see the
+    same clock and thermal state. Returns the ratio of the medians of the rounds' means minus
+    one, and the gated call's median."""
+    import statistics
+    dense, gated = [], []
+    for _ in range(rounds):
+        dense.append(run_gate(w, "dense", steps, warmup)["ms"])
+        gated.append(run_gate(w, mode, steps, warmup, **kw)["ms"])
+    g = statistics.median(gated)
+    return g / statistics.median(dense) - 1, g
+
+
 def measured_mfma_rate(steps=5, warmup=2):
     """The device's sustained bf16 MFMA rate (bsfa_mfma_rate_probe), TFLOP/s."""
     from block_sparse_long_amd import _lib
@@ -708,14 +722,15 @@ def main():
     gated = run_gate(w, mode, args.steps, args.warmup, **gate_kw)
     sweep = run_sweep(w, args.steps, args.warmup) if mode == "absolute" else None
     dense = run_gate(w, "dense", args.steps, args.warmup)
-    # zero-skip taxes: the gated instantiations with a gate that never skips
-    ninf = None
+    # zero-skip taxes: the gated instantiations with a gate that never skips, each against
+    # dense calls made in alternation with it (three rounds)
+    tax_steps = max(2, args.steps // 3)
     if w.table is not None:
         T = np.full_like(w.table.T[:1], -np.inf)
         ninf = ThresholdTable(T=T, budgets=[0], block_q=w.table.block_q, block_k=64,
                               head_dim=w.d, softmax_scale=w.table.softmax_scale).to_device(dev)
-        abs_ninf = run_gate(w, "absolute", args.steps, args.warmup, table=ninf)
-    rel_zero = run_gate(w, "relative", args.steps, args.warmup, log_lambda=-math.inf)
+        tax_abs, _ = paired_tax(w, "absolute", 3, tax_steps, 1, table=ninf)
+    tax_rel, _ = paired_tax(w, "relative", 3, tax_steps, 1, log_lambda=-math.inf)
     extras = {
         "gated_ms": round(gated["ms"], 3), "dense_ms": round(dense["ms"], 3),
         "speedup_vs_dense": round(dense["ms"] / gated["ms"], 4),
@@ -726,10 +741,10 @@ def main():
         "dense_textbook_tflops": round(4.0 * w.N * w.N / 2 * w.Hq * w.d / dense["ms"] / 1e9, 2),
         "kept_fraction": round(gated["kept_fraction"], 4),
         "predicted_density": round(predicted_density(w.N, w.Bq, k), 4) if k else None,
-        "zero_skip_tax_relative": round(rel_zero["ms"] / dense["ms"] - 1, 4),
+        "zero_skip_tax_relative": round(tax_rel, 4),
     }
     if w.table is not None:
-        extras["zero_skip_tax_absolute"] = round(abs_ninf["ms"] / dense["ms"] - 1, 4)
+        extras["zero_skip_tax_absolute"] = round(tax_abs, 4)
     if oracle_main is not None:
         O = device_out_fp32(w, mode, **dict(gate_kw))
         extras["device_vs_oracle_sample"] = deviation(O, oracle_main["out"],
