@@ -258,11 +258,11 @@ class Workload:
              mean_correction=False, gate_dtype="bf16"):
         import torch
         from block_sparse_long_amd import _lib
-        if workspace is None and mode == "absolute":
-            attr = f"workspace_{int(mean_correction)}_{gate_dtype}"
+        if workspace is None:
+            attr = f"workspace_{mode}_{int(mean_correction)}_{gate_dtype}"
             if getattr(self, attr, None) is None:
                 n = _lib.bsfa_prefill_workspace_bytes(self.Qd, self.Kd, block_q=self.Bq,
-                                                      block_k=self.Bk,
+                                                      block_k=self.Bk, gate_mode=mode,
                                                       mean_correction=mean_correction,
                                                       gate_dtype=gate_dtype)
                 setattr(self, attr, torch.empty(n, dtype=torch.uint8, device=self.Qd.device))

@@ -240,9 +240,10 @@ def bsfa_prefill(Q, K, V, O=None, *, block_q: int, block_k: int = 64, gate_mode=
     kept_total (int64 [1], read as uint64) and debug_block_stat (fp32 [B, Hq, nqb, nkb]) are
     written by the kernel on ``stream`` (default: torch's current stream). ``table`` is a
     block_sparse_long_amd.table.DeviceTable (needed for gate_mode "absolute"). ``workspace`` is a
-    device uint8 tensor of at least bsfa_prefill_workspace_bytes bytes for the absolute gate's
-    keep masks (and, with ``mean_correction``, the block means); None allocates one, and an
-    empty tensor asks for the path without it. ``mean_correction``: pruned blocks add their
+    device uint8 tensor of at least bsfa_prefill_workspace_bytes bytes: the ticket counter of
+    dense and relative launches, the absolute gate's keep masks (and, with
+    ``mean_correction``, the block means); None allocates one, and an empty tensor asks for
+    the path without it. ``mean_correction``: pruned blocks add their
     mean-key / mean-value stand-ins (absolute gate with a workspace). ``gate_dtype`` "fp8":
     the absolute gate scores E4M3 copies of Q and K (the table must be calibrated on the same
     scores). Returns O.
@@ -283,7 +284,7 @@ def bsfa_prefill_noalloc(Q, K, V, O, *, block_q: int, block_k: int = 64, gate_mo
                          kept_counts=None, kept_total=None, debug_block_stat=None,
                          softmax_scale: float = 0.0, stream=None, mean_correction: bool = False,
                          gate_dtype="bf16"):
-    """bsfa_prefill with the absolute gate's workspace in the library's static device scratch:
+    """bsfa_prefill with its workspace in the library's static device scratch:
     neither this function nor the library allocates (O and every output are the caller's).
     Same arguments and results as bsfa_prefill with a workspace. Returns O."""
     lib = load_library()

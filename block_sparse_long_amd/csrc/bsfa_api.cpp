@@ -187,6 +187,9 @@ struct WorkspaceLayout {
 
 uint64_t align256(uint64_t x) { return (x + 255u) & ~uint64_t(255); }
 
+// DENSE and RELATIVE: the workspace holds only the softmax launch's ticket counter.
+constexpr uint64_t kTicketBytes = 256;
+
 WorkspaceLayout workspace_layout(const bsfa_problem* p) {
   WorkspaceLayout l;
   const uint64_t nqb = ceil_div(p->seqlen, p->block_q);
@@ -261,13 +264,14 @@ const char* bsfa_status_string(int32_t s) {
 
 const char* bsfa_last_error(void) { return g_last_error; }
 
-int32_t bsfa_version(void) { return (3 << 16) | 2; }
+int32_t bsfa_version(void) { return (3 << 16) | 3; }
 
 uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode) {
-  if (!p || gate_mode != BSFA_GATE_ABSOLUTE || p->batch <= 0 || p->seqlen <= 0 ||
-      p->block_q <= 0 || p->block_k <= 0 || p->heads_q <= 0)
+  if (!p || p->batch <= 0 || p->seqlen <= 0 || p->block_q <= 0 || p->block_k <= 0 ||
+      p->heads_q <= 0)
     return 0;
-  return workspace_layout(p).total;
+  if (gate_mode == BSFA_GATE_DENSE || gate_mode == BSFA_GATE_RELATIVE) return kTicketBytes;
+  return gate_mode == BSFA_GATE_ABSOLUTE ? workspace_layout(p).total : 0;
 }
 
 }  // extern "C"
@@ -372,7 +376,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty &&
                          (mean || fp8 || p->block_k != bsfa::kBlockK ||
                           !one_launch_pays(p, table, budget_slice));
-  if (use_masks && workspace_bytes < ws_need)
+  // dense and the relative gate: the softmax workgroups take their units from a counter in
+  // the workspace
+  const bool use_ticket = gate_mode != BSFA_GATE_ABSOLUTE && workspace && !empty;
+  if ((use_masks || use_ticket) && workspace_bytes < ws_need)
     return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
                 (unsigned long long)workspace_bytes, (unsigned long long)ws_need);
 
@@ -444,6 +451,12 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     a.xcd_map = -1;
     a.ticket = tickets + bsfa::kSweepTickets;
   }
+  if (use_ticket) {
+    unsigned* const ticket = static_cast<unsigned*>(workspace);
+    hipError_t e = bsfa::launch_zero_words(ticket, 1, st);
+    if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
+    a.ticket = ticket;
+  }
   hipError_t e = bsfa::launch_prefill(a, p->head_dim, p->block_q, kgate, st);
   if (e != hipSuccess) return fail(BSFA_ERR_HIP, "prefill launch: %s", hipGetErrorString(e));
   return ok();
@@ -498,11 +511,7 @@ bsfa_status bsfa_prefill_noalloc(const bsfa_problem* p, const void* Q, const voi
                                  float* debug_block_stat, void* stream) {
   bsfa_status s = check_problem(p, true);
   if (s != BSFA_OK) return s;
-  // DENSE and RELATIVE use no workspace; ABSOLUTE takes the static scratch as its workspace
-  if (gate_mode != BSFA_GATE_ABSOLUTE)
-    return prefill_impl(p, Q, K, V, nullptr, KeyLayout(), table, budget_slice, gate_mode,
-                        log_lambda, O, kept_counts, kept_total, debug_block_stat, nullptr, 0,
-                        stream);
+  // every gate takes the static scratch as its workspace
   const uint64_t need = bsfa_prefill_workspace_bytes(p, gate_mode);
   if (need > kScratchBytes)
     return fail(BSFA_ERR_UNSUPPORTED,

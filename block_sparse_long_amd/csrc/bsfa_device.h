@@ -650,9 +650,16 @@ constexpr int kRows = kRowsPerWave;
 
 constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
-// Prefill kernels that take their units from a ticket counter when given one (the mask walk).
-template <int GATE, bool MEAN>
-constexpr bool kResidentLoop = GATE == kAbsolute;
+// How a prefill launch hands out its units: the mask walk always takes them from a ticket
+// counter; dense, and the relative gate with one head per workgroup, do when the call brings
+// a counter (a workspace), else run one workgroup per unit, as the others always do. (The
+// unit loop holds a few more registers across units: the relative gate's two-head form and
+// the absolute gate decided in the loop would spill.)
+enum UnitLoop : int { kOnePerUnit, kTicketIfGiven, kTicketAlways };
+template <int GATE, int HPW>
+constexpr int kUnitLoop = GATE == kAbsolute                                   ? kTicketAlways
+                          : GATE == kDense || (GATE == kRelative && HPW == 1) ? kTicketIfGiven
+                                                                              : kOnePerUnit;
 
 // PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
 // kernels carry no page lookups). MEAN (absolute walk only): the pruned gate blocks' stand-ins
@@ -684,18 +691,20 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
   __shared__ int sKept[kAbs ? NW : 1];   // per-wave kept-tile counts of the mask walk
   __shared__ int sUnit;
 
-  // Workgroup L runs unit L, except in the mask walk: its launch holds as many workgroups as
-  // stay resident, and each takes units in turn from a ticket counter (zero at the launch)
-  // until none is left. Workgroups go to the XCDs in turn whatever their work, and a new one
-  // waits for a slot on its own XCD; as walk lengths vary, slots would sit idle on the other
-  // XCDs meanwhile. Resident workgroups that take the next unit as they finish one keep every
-  // slot busy until the work runs out. (In the other kernels the work per unit is even.)
+  // Workgroup L runs unit L, unless the launch has a ticket counter (zero at the launch): then
+  // it holds as many workgroups as stay resident, and each takes units in turn from the
+  // counter until none is left. Workgroups go to the XCDs in turn whatever their work, and a
+  // new one waits for a slot on its own XCD; as unit lengths vary (a walk's kept tiles, a
+  // query block's causal extent), slots would sit idle on the other XCDs meanwhile. Resident
+  // workgroups that take the next unit as they finish one keep every slot busy until the work
+  // runs out.
   const unsigned lK0 = lds_addr(sK0), lK1 = lds_addr(sK1);
   const unsigned lV0 = lds_addr(sV0), lV1 = lds_addr(sV1);
-  constexpr bool kLoop = kResidentLoop<GATE, MEAN>;
+  constexpr bool kLoop = kUnitLoop<GATE, HPW> != kOnePerUnit;
+  const bool tickets = kUnitLoop<GATE, HPW> == kTicketAlways || a.ticket != nullptr;   // uniform
   int L = blockIdx.x;
 next_unit:
-  if constexpr (kLoop) {
+  if (kLoop && tickets) {
     if (threadIdx.x == 0) sUnit = (int)atomicAdd(a.ticket, 1u);
     __syncthreads();
     L = __builtin_amdgcn_readfirstlane(sUnit);
@@ -705,7 +714,7 @@ next_unit:
   // compiler computes the mean pass's lane-dependent copy offsets once ahead of the unit loop
   // and holds them through the walk, which spills)
   int tid_u = threadIdx.x, w_u = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  if constexpr (kLoop && MEAN) {
+  if constexpr (kLoop && (MEAN || GATE == kRelative)) {
     asm volatile("" : "+v"(tid_u));
     asm volatile("" : "+s"(w_u));
   }
@@ -720,7 +729,7 @@ next_unit:
   // after a prefix of cached keys; pre = 0 for a whole prefill)
   const Seq sq = seq_of(a, b);
   if (i * BQ >= sq.N) {          // uniform: past this sequence's query blocks (variable length)
-    if constexpr (kLoop) {
+    if (kLoop && tickets) {
       __syncthreads();             // every wave has read sUnit
       goto next_unit;
     }
@@ -1196,7 +1205,7 @@ next_unit:
     if (a.kept_counts) a.kept_counts[((long long)b * a.Hq + h) * a.nqb + i] = kept;
     if (a.kept_total) atomicAdd(a.kept_total, (unsigned long long)kept);
   }
-  if constexpr (kLoop) {
+  if (kLoop && tickets) {
     __syncthreads();   // every wave is done with this unit's LDS (and has read sUnit)
     goto next_unit;
   }
@@ -1940,32 +1949,40 @@ __global__ __launch_bounds__(256) void block_mean_kernel(PrefillArgs a) {
 template <int D, int BQ, int NW, bool PAGED>
 hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
   const int units = a.units * a.nqb;
-  // one workgroup per unit; with a ticket counter, as many as stay resident at once (each
-  // takes units in turn)
-  auto go = [&](void (*kernel)(PrefillArgs), bool resident_loop) {
-    if (resident_loop && !a.ticket) return hipErrorInvalidValue;   // the mask walk needs one
-    const int n = resident_loop ? min(units, resident_workgroups(reinterpret_cast<const void*>(
-                                                                     kernel), NW * 64, units))
-                                : units;
-    hipLaunchKernelGGL(kernel, dim3(n), dim3(NW * 64), 0, stream, a);
+  // one workgroup per unit; with a ticket counter, as many as stay resident at once, each
+  // taking units in turn: then in the order the workgroups start, one KV head at a time on
+  // every XCD (its K/V stays in the last-level cache; a fixed KV-head-to-XCD assignment would
+  // not hold, as any workgroup may take any unit)
+  constexpr int HPW = NW / (BQ / kRows);
+  auto go = [&](void (*kernel)(PrefillArgs), int loop) {
+    if (loop == kTicketAlways && !a.ticket) return hipErrorInvalidValue;   // the mask walk
+    PrefillArgs k = a;
+    int n = units;
+    if (loop != kOnePerUnit && a.ticket) {
+      n = min(units, resident_workgroups(reinterpret_cast<const void*>(kernel), NW * 64, units));
+      k.xcd_map = -1;
+    } else {
+      k.ticket = nullptr;
+    }
+    hipLaunchKernelGGL(kernel, dim3(n), dim3(NW * 64), 0, stream, k);
     return hipGetLastError();
   };
   switch (gate) {
     case kDense:
-      return go(prefill_kernel<D, BQ, NW, kDense, PAGED>, kResidentLoop<kDense, false>);
+      return go(prefill_kernel<D, BQ, NW, kDense, PAGED>, kUnitLoop<kDense, HPW>);
     case kAbsolute:
     case kAbsVote:
       if constexpr (NW == BQ / kRows) {   // one head per workgroup
         if (gate == kAbsolute && a.kbar_hi)
           return go(prefill_kernel<D, BQ, NW, kAbsolute, PAGED, true>,
-                    kResidentLoop<kAbsolute, true>);
+                    kUnitLoop<kAbsolute, HPW>);
         if (gate == kAbsolute)
-          return go(prefill_kernel<D, BQ, NW, kAbsolute, PAGED>, kResidentLoop<kAbsolute, false>);
-        return go(prefill_kernel<D, BQ, NW, kAbsVote, PAGED>, kResidentLoop<kAbsVote, false>);
+          return go(prefill_kernel<D, BQ, NW, kAbsolute, PAGED>, kUnitLoop<kAbsolute, HPW>);
+        return go(prefill_kernel<D, BQ, NW, kAbsVote, PAGED>, kUnitLoop<kAbsVote, HPW>);
       }
       return hipErrorInvalidConfiguration;
     default:
-      return go(prefill_kernel<D, BQ, NW, kRelative, PAGED>, kResidentLoop<kRelative, false>);
+      return go(prefill_kernel<D, BQ, NW, kRelative, PAGED>, kUnitLoop<kRelative, HPW>);
   }
 }
 
@@ -2010,12 +2027,11 @@ hipError_t launch_sweep_hpw(const PrefillArgs& a, int hpw, hipStream_t stream) {
 // Per (head dimension, query tile, K/V layout): the prefill kernel for any workgroup width and
 // gate, the calibration kernel and the gate sweep. Each is instantiated explicitly by one
 // translation unit.
-// Waves per workgroup of the prefill kernel: BQ / 32 waves per head times 1, 2 or 4 heads
-// (BQ = 128: 4 or 8 waves; BQ = 64: 2, 4 or 8 waves).
+// Waves per workgroup of the prefill kernel: BQ / 32 waves per head times 1 or 2 heads
+// (BQ = 128: 4 waves; BQ = 64: 2 or 4 waves).
 template <int D, int BQ, bool PAGED>
 hipError_t launch_prefill_tile(const PrefillArgs& a, int nw, int gate, hipStream_t stream) {
   switch (nw) {
-    case 8: return launch_prefill_paged<D, BQ, 8, PAGED>(a, gate, stream);
     case 4: return launch_prefill_paged<D, BQ, 4, PAGED>(a, gate, stream);
     default: return launch_prefill_paged<D, BQ, BQ / kRows, PAGED>(a, gate, stream);
   }

@@ -148,8 +148,9 @@ typedef struct {
                               * gate (see bsfa_prefill's workspace). */
 } bsfa_table;
 
-/* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 when it uses none): for
- * ABSOLUTE, one keep bitmask per (b, h, i) with one bit per 64-key tile,
+/* Bytes of device workspace bsfa_prefill can use for `gate_mode` (0 for an invalid problem
+ * or gate_mode): for DENSE and RELATIVE, 256 bytes that hold a counter from which the
+ * workgroups take their (b, h, i) units in turn; for ABSOLUTE, one keep bitmask per (b, h, i) with one bit per 64-key tile,
  * B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) uint64 words; then, each part starting on a
  * 256-byte boundary: with gate_dtype FP8_E4M3 the E4M3 copies of Q [B][N][Hq][d] and K
  * [B][Nk][Hkv][d] (one byte per element) and their fp32 scales [B][Hq][N] and
@@ -176,7 +177,12 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
  *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
  *   workspace     device, 8-byte aligned, or NULL; caller-owned scratch of workspace_bytes
- *                 (its contents on return are unspecified). The absolute gate runs in one of
+ *                 (its contents on return are unspecified). DENSE and RELATIVE: with a
+ *                 workspace the launch holds as many workgroups as stay resident, which take
+ *                 the (b, h, i) units in turn from a counter in it; without one each unit
+ *                 runs in a workgroup of its own (the same results bit for bit; the first is
+ *                 faster where units differ in length, as causal ones do). The absolute gate
+ *                 runs in one of
  *                 two ways with the same results (O, kept counts and statistics bit for bit):
  *                 two launches, a gate sweep that decides every block from its scores alone
  *                 and writes keep masks into the workspace, then a softmax launch that walks
@@ -215,7 +221,7 @@ bsfa_status bsfa_prefill(const bsfa_problem* p, const void* Q, const void* K, co
  *   Limit: a call whose workspace would exceed 64 MiB returns BSFA_ERR_UNSUPPORTED before
  *   anything is enqueued (the keep masks take B * Hq * ceil(N/Bq) * ceil(ceil(Nk/64)/64) * 8
  *   bytes: 8 MiB for one 128K-token sequence with 32 query heads at Bq = 128; FP8 copies do
- *   not fit beyond short sequences). DENSE and RELATIVE use no workspace.
+ *   not fit beyond short sequences). DENSE and RELATIVE take their counter from the array.
  *   Sharing: every call on one device uses that device's one array, which keeps the last
  *   call's contents (each call writes before it reads; nothing needs clearing). Calls that
  *   overlap on one device (another stream, another thread) race on it: the caller orders them.
@@ -351,7 +357,8 @@ const char* bsfa_status_string(int32_t status);
 const char* bsfa_last_error(void);
 
 /* ABI version: (major << 16) | minor. Minor 1 adds bsfa_prefill_noalloc; minor 2 ends the
- * absolute gate's workspace with a ticket counter (256 bytes more). Major 3: bsfa_table ends
+ * absolute gate's workspace with a ticket counter (256 bytes more); minor 3 gives DENSE and
+ * RELATIVE a 256-byte workspace (their own ticket counter). Major 3: bsfa_table ends
  * with the budgets array
  * (major 2: bsfa_problem ends with mean_correction and gate_dtype, and
  * bsfa_calibrate_blockmax takes a workspace). */

@@ -157,9 +157,14 @@ def test_workspace_size_and_validation():
     # the masks, then (on a 256-byte boundary) the walk's 256-byte ticket counter
     need = -(-masks // 256) * 256 + 256
     assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), _lib.BSFA_GATE_ABSOLUTE) == need
+    # dense and the relative gate: a 256-byte ticket counter only
     for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
-        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 256
+        assert call_prefill(p, mode=mode, ws=FAKE, ws_bytes=255) == _lib.BSFA_ERR_ARG
+        assert "workspace" in _lib.bsfa_last_error()
+    assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), 7) == 0
     assert lib.bsfa_prefill_workspace_bytes(None, _lib.BSFA_GATE_ABSOLUTE) == 0
+    assert lib.bsfa_prefill_workspace_bytes(None, _lib.BSFA_GATE_DENSE) == 0
     # 65 key tiles need two mask words per query block
     p2 = problem(N=65 * 64)
     assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p2), _lib.BSFA_GATE_ABSOLUTE) == \
@@ -330,7 +335,7 @@ def test_mean_correction_workspace_and_validation():
     part = p.batch * p.heads_kv * (1000 // 64) * p.head_dim * 2
     assert need == r256(masks) + 3 * r256(part) + 256
     for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
-        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 256
     abs_call = dict(tbl=table(t_len=8), mode=_lib.BSFA_GATE_ABSOLUTE)
     # the block means live in the workspace: none, or an 8-byte-aligned one, is refused
     assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_UNSUPPORTED
@@ -366,7 +371,7 @@ def test_fp8_gate_workspace_and_validation():
     assert both == need + 3 * r256(B * Hkv * (N // 64) * d * 2)
     p.mean_correction = 0
     for mode in (_lib.BSFA_GATE_DENSE, _lib.BSFA_GATE_RELATIVE):
-        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 0
+        assert lib.bsfa_prefill_workspace_bytes(ctypes.byref(p), mode) == 256
     abs_call = dict(tbl=table(t_len=8), mode=_lib.BSFA_GATE_ABSOLUTE)
     assert call_prefill(p, **abs_call) == _lib.BSFA_ERR_UNSUPPORTED
     assert "workspace" in _lib.bsfa_last_error()

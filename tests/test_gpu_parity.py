@@ -174,6 +174,31 @@ def test_dense_equals_minus_inf_and_lambda_zero_bitwise(name):
     assert absm["total"] == rel0["total"] == n_off_total
 
 
+@pytest.mark.parametrize("name", list(SHAPES))
+@pytest.mark.parametrize("mode,lam", [("dense", 0.0), ("relative", 0.0), ("relative", 3e-2)])
+def test_ticket_launch_equals_one_workgroup_per_unit_bitwise(name, mode, lam):
+    # dense and the relative gate: with a workspace the resident workgroups take their units
+    # from a counter in it, without one each unit runs in a workgroup of its own. The order of
+    # the units changes nothing: output, counts and statistics agree bit for bit, also on a
+    # second call through the same workspace (each call zeroes its counter)
+    B, N, Hq, Hkv, d, Bq = SHAPES[name]
+    Q, K, V = _mid_inputs(name, 12)
+    (Qd, Kd, Vd), _ = bf16_pair(Q, K, V)
+    ll = math.log(lam) if lam > 0 else -math.inf
+    assert _lib.bsfa_prefill_workspace_bytes(Qd, Kd, block_q=Bq, gate_mode=mode) == 256
+    ws = torch.full((256,), 0xA5, dtype=torch.uint8, device="cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    kw = dict(block_q=Bq, mode=mode, log_lambda=ll)
+    one = run_device(Qd, Kd, Vd, workspace=none, **kw)
+    for _ in range(2):
+        tk = run_device(Qd, Kd, Vd, workspace=ws, **kw)
+        assert torch.equal(tk["O"], one["O"])
+        np.testing.assert_array_equal(tk["counts"], one["counts"])
+        assert tk["total"] == one["total"]
+        np.testing.assert_array_equal(np.nan_to_num(tk["stat"], nan=7.0),
+                                      np.nan_to_num(one["stat"], nan=7.0))
+
+
 def test_poisoned_skipped_values_bitwise(mid_tables):
     # a skipped block loads no V and adds nothing: with NaN in the V rows of key block j0,
     # every (head, query block) that skips j0 (outside the near-tie band) keeps a

@@ -1,7 +1,7 @@
-"""bsfa_prefill_noalloc (the absolute gate's workspace in the library's static device scratch)
-against bsfa_prefill with a caller workspace, through the C ABI: two calls in a row, the second
-on a shorter sequence, so that the scratch still holds the first call's masks and block means
-when the second call runs. Results must agree bit for bit."""
+"""bsfa_prefill_noalloc (the workspace in the library's static device scratch) against
+bsfa_prefill with a caller workspace, through the C ABI: two calls in a row, the second on a
+shorter sequence, so that the scratch still holds the first call's masks, block means and
+ticket counters when the second call runs. Results must agree bit for bit."""
 import math
 import os
 
@@ -64,13 +64,16 @@ def test_noalloc_equals_caller_workspace_twice_second_smaller():
         assert (a["counts"] < torch.tensor([(i * Bq) // 64 for i in range(-(-n // Bq))],
                                           device="cuda")).any(), "nothing pruned"
         _same(a, b)
-        # dense and relative through the same entry point (no workspace used)
+        # dense and relative through the same entry point (the scratch holds their ticket
+        # counter) against a caller workspace of stale bytes
         for mode, ll in (("dense", -math.inf), ("relative", math.log(1e-3))):
             a = _outputs(Qd, Bq, nkb)
             b = _outputs(Qd, Bq, nkb)
             _call(_lib.bsfa_prefill_noalloc, Qd, Kd, Vd, a, block_q=Bq, gate_mode=mode,
                   log_lambda=ll)
-            _call(_lib.bsfa_prefill, Qd, Kd, Vd, b, block_q=Bq, gate_mode=mode, log_lambda=ll)
+            ws = torch.full((256,), 0xA5, dtype=torch.uint8, device="cuda")
+            _call(_lib.bsfa_prefill, Qd, Kd, Vd, b, block_q=Bq, gate_mode=mode, log_lambda=ll,
+                  workspace=ws)
             torch.cuda.synchronize()
             _same(a, b)
         del Qd, Kd, Vd
