@@ -376,9 +376,9 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
   const bool use_masks = gate_mode == BSFA_GATE_ABSOLUTE && workspace && !empty &&
                          (mean || fp8 || p->block_k != bsfa::kBlockK ||
                           !one_launch_pays(p, table, budget_slice));
-  // dense and the relative gate: the softmax workgroups take their units from a counter in
-  // the workspace
-  const bool use_ticket = gate_mode != BSFA_GATE_ABSOLUTE && workspace && !empty;
+  // one softmax launch (dense, the relative gate, the absolute gate decided in the loop): its
+  // workgroups take their units from a counter in the workspace
+  const bool use_ticket = !use_masks && workspace && !empty;
   if ((use_masks || use_ticket) && workspace_bytes < ws_need)
     return fail(BSFA_ERR_ARG, "workspace_bytes %llu below the required %llu",
                 (unsigned long long)workspace_bytes, (unsigned long long)ws_need);
@@ -452,7 +452,10 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     a.ticket = tickets + bsfa::kSweepTickets;
   }
   if (use_ticket) {
-    unsigned* const ticket = static_cast<unsigned*>(workspace);
+    // the first word of the workspace, or of the absolute gate's ticket counters
+    unsigned* const ticket = reinterpret_cast<unsigned*>(
+        static_cast<char*>(workspace) +
+        (gate_mode == BSFA_GATE_ABSOLUTE ? workspace_layout(p).ticket : 0));
     hipError_t e = bsfa::launch_zero_words(ticket, 1, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "zeroing the ticket: %s", hipGetErrorString(e));
     a.ticket = ticket;

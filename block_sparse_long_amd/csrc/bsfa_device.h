@@ -651,15 +651,13 @@ constexpr int kRows = kRowsPerWave;
 constexpr int kMaskWords = kMaxGateTiles / 64;   // keep-bitmask words
 
 // How a prefill launch hands out its units: the mask walk always takes them from a ticket
-// counter; dense, and the relative gate with one head per workgroup, do when the call brings
-// a counter (a workspace), else run one workgroup per unit, as the others always do. (The
-// unit loop holds a few more registers across units: the relative gate's two-head form and
-// the absolute gate decided in the loop would spill.)
+// counter; dense, and the voting gates with one head per workgroup, do when the call brings
+// a counter (a workspace), else run one workgroup per unit. (The unit loop holds a few more
+// registers across units: the relative gate's two-head form would spill.)
 enum UnitLoop : int { kOnePerUnit, kTicketIfGiven, kTicketAlways };
 template <int GATE, int HPW>
-constexpr int kUnitLoop = GATE == kAbsolute                                   ? kTicketAlways
-                          : GATE == kDense || (GATE == kRelative && HPW == 1) ? kTicketIfGiven
-                                                                              : kOnePerUnit;
+constexpr int kUnitLoop = GATE == kAbsolute ? kTicketAlways
+                          : GATE == kDense || HPW == 1 ? kTicketIfGiven : kOnePerUnit;
 
 // PAGED: K and V tiles come from a paged cache (a compile-time choice, so that the contiguous
 // kernels carry no page lookups). MEAN (absolute walk only): the pruned gate blocks' stand-ins
@@ -710,11 +708,11 @@ next_unit:
     L = __builtin_amdgcn_readfirstlane(sUnit);
     if (L >= a.units * a.nqb) return;   // uniform: every unit taken
   }
-  // (with mean correction the lane and wave indices are made opaque per unit: otherwise the
-  // compiler computes the mean pass's lane-dependent copy offsets once ahead of the unit loop
-  // and holds them through the walk, which spills)
+  // (with mean correction and in the voting gates the lane and wave indices are made opaque
+  // per unit: otherwise the compiler computes some lane-dependent offsets once ahead of the
+  // unit loop and holds them through it, which spills)
   int tid_u = threadIdx.x, w_u = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-  if constexpr (kLoop && (MEAN || GATE == kRelative)) {
+  if constexpr (kLoop && (MEAN || GATE == kRelative || GATE == kAbsVote)) {
     asm volatile("" : "+v"(tid_u));
     asm volatile("" : "+s"(w_u));
   }

@@ -177,12 +177,12 @@ uint64_t bsfa_prefill_workspace_bytes(const bsfa_problem* p, int32_t gate_mode);
  *                 RELATIVE: max_r(rowmax_j[r] - m[r]) for off-diagonal blocks, s_max for the
  *                 diagonal region). Entries of invisible blocks (j >= n_end(i)) are not written.
  *   workspace     device, 8-byte aligned, or NULL; caller-owned scratch of workspace_bytes
- *                 (its contents on return are unspecified). DENSE and RELATIVE: with a
- *                 workspace the launch holds as many workgroups as stay resident, which take
- *                 the (b, h, i) units in turn from a counter in it; without one each unit
- *                 runs in a workgroup of its own (the same results bit for bit; the first is
- *                 faster where units differ in length, as causal ones do). The absolute gate
- *                 runs in one of
+ *                 (its contents on return are unspecified). A softmax launch over every
+ *                 block (DENSE, RELATIVE, and ABSOLUTE's one launch below) with a workspace
+ *                 holds as many workgroups as stay resident, which take the (b, h, i) units in
+ *                 turn from a counter in it; without one each unit runs in a workgroup of its
+ *                 own (the same results bit for bit; the first is faster where units differ
+ *                 in length, as causal ones do). The absolute gate runs in one of
  *                 two ways with the same results (O, kept counts and statistics bit for bit):
  *                 two launches, a gate sweep that decides every block from its scores alone
  *                 and writes keep masks into the workspace, then a softmax launch that walks

@@ -284,6 +284,14 @@ def test_full_size_two_launch_call_equals_single_launch_bitwise():
     np.testing.assert_array_equal(a["counts"], b["counts"])
     assert a["total"] == b["total"]
     np.testing.assert_array_equal(a["stat"], b["stat"])
+    # k = 256 keeps most blocks: with a workspace the library takes one launch whose
+    # workgroups draw units from the workspace's counter; the same bits as without one
+    a = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=2,
+                   dbg=False, record_budgets=True)
+    b = run_device(Qd, Kd, Vd, block_q=Bq, mode="absolute", table=tab, budget_slice=2,
+                   dbg=False, workspace=none)
+    assert torch.equal(a["O"], b["O"])
+    np.testing.assert_array_equal(a["counts"], b["counts"])
     # query blocks whose thresholds are finite for every head (the others keep all without a
     # mask)
     T = tab.T[1]
