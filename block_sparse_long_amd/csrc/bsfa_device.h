@@ -597,15 +597,16 @@ __device__ __forceinline__ Seq seq_of(const PrefillArgs& a, int b) {
 // in flight at once), so that over the launch every XCD serves every KV head equally often:
 // for walks whose length differs between heads, the XCDs then finish together.
 __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, int Hkv,
-                                            int xcd_map, int xcd_rot) {
+                                            int xcd_map, int xcd_rot, int tail = 0) {
   int i, u;
-  if (xcd_map < 0) {
+  if (xcd_map < 0 && L < (nqb - tail) * units) {
     // KV-head-major: every (batch, KV head) in turn, its query blocks from the last, its head
     // groups innermost. Consecutive workgroups still go to the 8 XCDs in turn, so all XCDs
     // work on the same KV head at a time and its K/V (64 MB at 128K, d = 128) stays in the
-    // last-level cache for every XCD's walk.
-    const int upg = units / (B * Hkv);
-    const int bh = L / (nqb * upg), rem = L % (nqb * upg);
+    // last-level cache for every XCD's walk. Only the query blocks at or above `tail` are
+    // taken in this order; the rest follow below.
+    const int upg = units / (B * Hkv), nb = nqb - tail;
+    const int bh = L / (nb * upg), rem = L % (nb * upg);
     Unit r;
     r.b = bh / Hkv;
     r.g = bh % Hkv;
@@ -613,7 +614,14 @@ __device__ __forceinline__ Unit decode_unit(int L, int units, int nqb, int B, in
     r.hg = rem % upg;
     return r;
   }
-  if (xcd_map) {
+  if (xcd_map < 0) {
+    // The query blocks below `tail`, last, heaviest first, each with the units of every KV
+    // head: the launch ends on the shortest units whatever the KV head order, so no workgroup
+    // is left with a long unit of the last KV head while the others have run out of work.
+    L -= (nqb - tail) * units;
+    i = tail - 1 - L / units;
+    u = L % units;
+  } else if (xcd_map) {
     const int x = L & 7, s = L >> 3, upx = units >> 3;
     i = nqb - 1 - s / upx;
     u = (s % upx) * 8 + (xcd_rot ? ((x + (nqb - 1 - i) / xcd_rot) & 7) : x);
@@ -719,7 +727,8 @@ next_unit:
   const int tid = tid_u, lane = tid & 63;
   const int w = w_u;   // wave index, in a scalar register
   const int hw = w / WPH, rw = w % WPH;
-  const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot);
+  const Unit un = decode_unit(L, a.units, a.nqb, a.B, a.Hkv, a.xcd_map, a.xcd_rot,
+                              a.tail_blocks);
   const int b = un.b, g = un.g, i = un.i;
   const int h0 = g * a.G + un.hg * HPW;
   const int h = h0 + hw;
@@ -1944,6 +1953,19 @@ __global__ __launch_bounds__(256) void block_mean_kernel(PrefillArgs a) {
   }
 }
 
+// How many of the lowest query blocks a ticket-ordered softmax launch takes last, heaviest
+// first across all KV heads (the blocks above go KV head by KV head). In KV-head order the
+// last KV head's longest unit, about nqb key tiles per 64 query rows, starts near the end; the
+// blocks below the cut, taken afterwards, must hold at least that much work per resident
+// workgroup to keep the others busy meanwhile. Causal units at block i hold about i + 1 tiles
+// per 64 rows, so the blocks below `cut` hold units * cut^2 / 2, i.e. units * cut^2 /
+// (2 * resident) per workgroup: cut = sqrt(2 * resident * nqb / units). (The mask walk's units
+// are shorter than causal ones, so the cut suits it too.)
+inline int tail_query_blocks(int nqb, int units, int resident) {
+  const double cut = ceil(sqrt(2.0 * resident * nqb / (double)units));
+  return (int)fmin((double)nqb, cut);
+}
+
 template <int D, int BQ, int NW, bool PAGED>
 hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stream) {
   const int units = a.units * a.nqb;
@@ -1959,6 +1981,7 @@ hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stre
     if (loop != kOnePerUnit && a.ticket) {
       n = min(units, resident_workgroups(reinterpret_cast<const void*>(kernel), NW * 64, units));
       k.xcd_map = -1;
+      k.tail_blocks = tail_query_blocks(a.nqb, a.units, n);
     } else {
       k.ticket = nullptr;
     }

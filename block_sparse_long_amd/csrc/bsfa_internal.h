@@ -41,6 +41,8 @@ struct PrefillArgs {
                                    // -1: KV-head-major order over all XCDs
   int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
                                    // blocks (0: never)
+  int tail_blocks;                 // with xcd_map = -1: query blocks below this come last,
+                                   // heaviest first, every KV head's units of a block together
   unsigned* ticket;                // counters, zero at the launch, from which the workgroups
                                    // resident at once take units in turn until all are taken
                                    // (the gate sweep with xcd_map = 1: one per XCD queue);

@@ -15,7 +15,8 @@ import torch
 import oracle
 from block_sparse_long_amd import _lib, synth
 from block_sparse_long_amd.table import ThresholdTable
-from gpu_util import BAND, MAX_ABS, MEAN_ABS, bf16_pair, check_parity, make_table, run_device
+from gpu_util import (BAND, MAX_ABS, MEAN_ABS, bf16_pair, check_parity, make_table,
+                      quantile_table, run_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -172,6 +173,39 @@ def test_dense_equals_minus_inf_and_lambda_zero_bitwise(name):
     assert torch.equal(dense, rel0["O"])
     n_off_total = B * Hq * sum(oracle.key_block_range(i, N, Bq, 64)[0] for i in range(nqb))
     assert absm["total"] == rel0["total"] == n_off_total
+
+
+@pytest.mark.parametrize("mode,Bq", [("dense", 128), ("relative", 128), ("absolute", 128),
+                                     ("dense", 64)])
+def test_ticket_order_with_heaviest_first_tail_bitwise(mode, Bq):
+    # 8100 tokens (ragged), 32 query / 8 KV heads: more units than resident workgroups, so a
+    # ticket launch takes the query blocks above a cut KV head by KV head and those below it
+    # last, heaviest first (Bq = 128: 64 blocks, cut about 46; Bq = 64: 127 blocks, cut about
+    # 91). Every unit still runs exactly once: output, counts and statistics equal those of one
+    # workgroup per unit (the absolute gate: its two launches, the walk taking tickets, equal
+    # the one launch without a workspace)
+    N, Hq, Hkv, d = 8100, 32, 8, 128
+    Q, K, V = synth.structured(21, N, heads_q=Hq, heads_kv=Hkv, d=d, needles=4)
+    (Qd, Kd, Vd), (Qh, Kh, _) = bf16_pair(Q, K, V)
+    kw = dict(block_q=Bq, mode=mode)
+    if mode == "relative":
+        kw["log_lambda"] = math.log(3e-2)
+    if mode == "absolute":
+        kw["table"] = quantile_table(Qh, Kh, Bq, 64)
+    need = _lib.bsfa_prefill_workspace_bytes(Qd, Kd, block_q=Bq, gate_mode=mode)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    none = torch.empty(0, dtype=torch.uint8, device="cuda")
+    one = run_device(Qd, Kd, Vd, workspace=none, **kw)
+    tk = run_device(Qd, Kd, Vd, workspace=ws, **kw)
+    assert torch.equal(tk["O"], one["O"])
+    np.testing.assert_array_equal(tk["counts"], one["counts"])
+    assert tk["total"] == one["total"]
+    np.testing.assert_array_equal(np.nan_to_num(tk["stat"], nan=7.0),
+                                  np.nan_to_num(one["stat"], nan=7.0))
+    if mode != "dense":   # the gate skipped some blocks and kept others
+        nqb = -(-N // Bq)
+        n_off = Hq * sum(oracle.key_block_range(i, N, Bq, 64)[0] for i in range(nqb))
+        assert 0 < tk["total"] < n_off
 
 
 @pytest.mark.parametrize("name", list(SHAPES))
