@@ -852,12 +852,14 @@ next_unit:
   };
 
   // ---- prologue: the first two tiles of the sequence staged, scores of the first published ----
+  // (both copies in flight together, so the first barrier costs one memory round trip; the
+  // wait covers the Q rows as well)
   int t = next_tile(-1);
   int t1 = next_tile(t);
   load_k(t, lK0);
+  if (t1 < n_end) load_k(t1, lK1);
   wait_vmem();
   __syncthreads();
-  if (t1 < n_end) load_k(t1, lK1);
   f32x16 sb[2][2];     // scores of the last tiles of each parity
   float rc;            // row max of the newest scores
   qk32<D>(sK0, qf, sb[0], lane);
