@@ -446,8 +446,9 @@ bsfa_status prefill_impl(const bsfa_problem* p, const void* Q, const void* K, co
     e = launch_sweep(a, p, st);
     if (e != hipSuccess) return fail(BSFA_ERR_HIP, "gate sweep launch: %s", hipGetErrorString(e));
     // the walk over kept tiles: one KV head at a time on all XCDs (its K/V stays in the
-    // last-level cache), units in the order the workgroups start (walk lengths differ, so a
-    // fixed assignment would load some XCDs more than others)
+    // last-level cache) but for the lowest query blocks, taken last, units in the order the
+    // workgroups start (walk lengths differ, so a fixed assignment would load some XCDs more
+    // than others)
     a.xcd_map = -1;
     a.ticket = tickets + bsfa::kSweepTickets;
   }

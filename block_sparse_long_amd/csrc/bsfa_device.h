@@ -1974,7 +1974,8 @@ hipError_t launch_prefill_paged(const PrefillArgs& a, int gate, hipStream_t stre
   // one workgroup per unit; with a ticket counter, as many as stay resident at once, each
   // taking units in turn: then in the order the workgroups start, one KV head at a time on
   // every XCD (its K/V stays in the last-level cache; a fixed KV-head-to-XCD assignment would
-  // not hold, as any workgroup may take any unit)
+  // not hold, as any workgroup may take any unit), the lowest query blocks last, heaviest first
+  // across all KV heads
   constexpr int HPW = NW / (BQ / kRows);
   auto go = [&](void (*kernel)(PrefillArgs), int loop) {
     if (loop == kTicketAlways && !a.ticket) return hipErrorInvalidValue;   // the mask walk

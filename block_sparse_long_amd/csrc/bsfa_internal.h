@@ -38,7 +38,8 @@ struct PrefillArgs {
   int pages_stride, page_tiles;
   int units;                       // B * Hkv * (G / heads per workgroup)
   int xcd_map;                     // 1: each XCD serves fixed units (whole KV heads);
-                                   // -1: KV-head-major order over all XCDs
+                                   // -1: KV-head-major order over all XCDs (the
+                                   // query blocks below tail_blocks excepted)
   int xcd_rot;                     // with xcd_map: turn that assignment every xcd_rot query
                                    // blocks (0: never)
   int tail_blocks;                 // with xcd_map = -1: query blocks below this come last,
