@@ -826,6 +826,14 @@ def main():
             ll = math.log(lam) if lam > 0 else -math.inf
             r = run_gate(w64, "relative", args.steps, args.warmup, log_lambda=ll)
             rows[f"lambda={lam:g}"] = gate_row(r, d64["ms"], w64.N, w64.Bq)
+        # the zero-skip tax as at 128K, from alternating rounds of dense and gated calls: at
+        # lambda = 0 and at 1e-4, which keeps every block of this workload with the gate
+        # deciding each one
+        rows["zero_skip_tax_alternating_rounds"] = {
+            f"lambda={lam:g}": round(paired_tax(w64, "relative", 3, args.steps, 1,
+                                                log_lambda=math.log(lam) if lam > 0
+                                                else -math.inf)[0], 4)
+            for lam in (0.0, 1e-4)}
         sweeps["llama_64k_relative"] = rows
         del w64
         torch.cuda.empty_cache()
